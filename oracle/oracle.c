@@ -1,0 +1,299 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for the decode-context-parallel
+ * (DCP) LSE merge and for the per-shard MLA decode partials that feed it.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the CPU
+ * baseline leg of the benchmark are the only callers.  The product library
+ * (the HIP code under context_lse_merge_amd/) never links, loads or calls this
+ * file, and this file includes none of its headers: the two share no code.
+ *
+ * Every value is widened to double before any arithmetic; bf16 inputs are
+ * decoded here, bit by bit, by this file's own routine.  No blocking, no
+ * fusion and no reordering beyond the definitions below.  OpenMP only spreads
+ * independent output rows over threads; each row's arithmetic is the same
+ * sequential loop whatever the thread count.
+ *
+ * What is computed, and where the pages fix it:
+ *
+ *  merge  -- "[DCP] Run fi_a2a on FlashInfer's fused all-to-all + LSE reduce"
+ *            (sglang PR #40539), Motivation: the received head partials are
+ *            combined by an LSE-weighted merge.  Modifications: the [B, H, D]
+ *            attention output is read as [B, H/cp, cp, D] and its LSE as
+ *            [B, H/cp, cp]; head h belongs to shard h // (H/cp), so shard s of
+ *            local head j is head s*(H/cp) + j.  Accuracy Tests: FlashMLA's
+ *            [B, H, 1] LSE layout is accepted as well; both LSE bases (2, e).
+ *            "[Attention] Add direct symmetric-memory DCP A2A" (vLLM PR
+ *            #48897), commit message: the combine weights received states by
+ *            their LSE in FP32; port commit: an empty shard publishes
+ *            LSE = -inf, its payload is not written, and zero-weight sources
+ *            are skipped.  "[DCP] Optimize shared Output, Query, and
+ *            Indexer/Top-K via peer memory" (sglang PR #32851), commit log:
+ *            zero-count rows contribute exp2(-inf) = 0, and rows with no
+ *            selected tokens must give 0, not NaN.
+ *            The pages name the merge but never print its formula; it is the
+ *            split-softmax identity
+ *                M   = max_s lse_s
+ *                w_s = base^(lse_s - M)            (0 for lse_s = -inf)
+ *                S   = sum_s w_s
+ *                out = sum_s (w_s / S) * O_s
+ *                L   = M + log_base(S)
+ *            which the tests pin against brute-force softmax attention.
+ *
+ *  attention partials -- the producer behind the merge: each DCP shard runs
+ *            MLA decode attention over its own slice of the latent KV cache
+ *            (PR #32851 commit log: KV tokens are owned by DCP ranks; the
+ *            backend returns the LSE with the output).  In the MLA absorbed
+ *            form the value is the first 512 latent columns of the cached row
+ *            (PR #48897 review thread: head_dim = kv_lora_rank = 512), and the
+ *            query/key dot product runs over all 576 columns (512 latent +
+ *            64 rope).  For one query row and a token set T:
+ *                z_t = scale * <q, k_t>
+ *                lse = ln sum_{t in T} exp(z_t)     (times log2 e in base 2)
+ *                O   = sum_{t in T} softmax(z)_t * v_t
+ *            An empty token set gives lse = -inf and O = 0.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* LSE bases and layouts, as the oracle numbers them. */
+#define ORACLE_BASE_E 0
+#define ORACLE_BASE_2 1
+#define ORACLE_LSE_BHC 0 /* [B, H/cp, cp] contiguous: element (b, j, s)        */
+#define ORACLE_LSE_BH1 1 /* [B, H, 1] contiguous: element (b, s*(H/cp) + j)    */
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+
+/* bf16 is the upper half of an IEEE binary32: widen the 16 bits into the top
+ * of a 32-bit word and reinterpret.  Exact for every finite value, infinity
+ * and NaN. */
+double oracle_bf16_to_f64(uint16_t bits) {
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+void oracle_decode_bf16(const uint16_t* src, double* dst, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = oracle_bf16_to_f64(src[i]);
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Offset of LSE element (b, j, s) in a contiguous array of the given layout. */
+static int64_t lse_offset(int layout, int64_t b, int64_t j, int64_t s, int64_t h_local, int64_t cp) {
+    if (layout == ORACLE_LSE_BHC) return (b * h_local + j) * cp + s;
+    return b * (h_local * cp) + s * h_local + j; /* BH1: head s*H_local + j */
+}
+
+/*
+ * LSE-weighted merge over cp shards, all in double.
+ *   O       [B, H, D] contiguous; shard s of local head j is head s*H_local + j
+ *   lse     contiguous, layout ORACLE_LSE_BHC or ORACLE_LSE_BH1
+ *   out     [B, H_local, D]      merged output
+ *   out_lse [B, H_local]         merged LSE, same base as the input (nullable)
+ *   out_abs [B, H_local, D]      sum_s (w_s/S) |O_s|, the magnitude the
+ *                                rounding tolerance is scaled by (nullable)
+ * An empty shard (lse = -inf) is never read.  An all-empty row gives out = 0
+ * and L = -inf.
+ */
+int oracle_merge_f64(const double* O, const double* lse, int64_t B, int64_t H, int64_t cp, int64_t D,
+                     int lse_layout, int lse_mode, double* out, double* out_lse, double* out_abs,
+                     int nthreads) {
+    if (B < 0 || H <= 0 || cp <= 0 || D <= 0 || H % cp != 0) return ORACLE_BAD_ARG;
+    if (lse_layout != ORACLE_LSE_BHC && lse_layout != ORACLE_LSE_BH1) return ORACLE_BAD_ARG;
+    if (lse_mode != ORACLE_BASE_E && lse_mode != ORACLE_BASE_2) return ORACLE_BAD_ARG;
+    const int64_t h_local = H / cp;
+    set_threads(nthreads);
+
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < B * h_local; ++row) {
+        const int64_t b = row / h_local;
+        const int64_t j = row % h_local;
+        double* w = (double*)malloc((size_t)cp * sizeof(double));
+
+        double M = -INFINITY;
+        for (int64_t s = 0; s < cp; ++s) {
+            double x = lse[lse_offset(lse_layout, b, j, s, h_local, cp)];
+            if (x > M) M = x;
+        }
+
+        double* o_row = out + row * D;
+        double* a_row = out_abs ? out_abs + row * D : NULL;
+        if (M == -INFINITY) {
+            for (int64_t d = 0; d < D; ++d) {
+                o_row[d] = 0.0;
+                if (a_row) a_row[d] = 0.0;
+            }
+            if (out_lse) out_lse[row] = -INFINITY;
+            free(w);
+            continue;
+        }
+
+        double S = 0.0;
+        for (int64_t s = 0; s < cp; ++s) {
+            double x = lse[lse_offset(lse_layout, b, j, s, h_local, cp)];
+            if (x == -INFINITY) {
+                w[s] = 0.0;
+            } else if (lse_mode == ORACLE_BASE_E) {
+                w[s] = exp(x - M);
+            } else {
+                w[s] = exp2(x - M);
+            }
+            S += w[s];
+        }
+
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0, acc_abs = 0.0;
+            for (int64_t s = 0; s < cp; ++s) {
+                if (w[s] == 0.0) continue; /* empty shard: payload never read */
+                double o = O[(b * H + s * h_local + j) * D + d];
+                acc += (w[s] / S) * o;
+                acc_abs += (w[s] / S) * fabs(o);
+            }
+            o_row[d] = acc;
+            if (a_row) a_row[d] = acc_abs;
+        }
+        if (out_lse) out_lse[row] = M + (lse_mode == ORACLE_BASE_E ? log(S) : log2(S));
+        free(w);
+    }
+    return ORACLE_OK;
+}
+
+/* Same merge on the product's input types: bf16 O (raw bits) and fp32 LSE.
+ * Both are widened exactly to double first. */
+int oracle_merge_bf16(const uint16_t* O, const float* lse, int64_t B, int64_t H, int64_t cp, int64_t D,
+                      int lse_layout, int lse_mode, double* out, double* out_lse, double* out_abs,
+                      int nthreads) {
+    if (B < 0 || H <= 0 || cp <= 0 || D <= 0 || H % cp != 0) return ORACLE_BAD_ARG;
+    const int64_t n_o = B * H * D, n_l = B * H;
+    double* Od = (double*)malloc((size_t)(n_o > 0 ? n_o : 1) * sizeof(double));
+    double* Ld = (double*)malloc((size_t)(n_l > 0 ? n_l : 1) * sizeof(double));
+    if (!Od || !Ld) {
+        free(Od);
+        free(Ld);
+        return ORACLE_BAD_ARG;
+    }
+    oracle_decode_bf16(O, Od, n_o);
+    for (int64_t i = 0; i < n_l; ++i) Ld[i] = (double)lse[i];
+    int rc = oracle_merge_f64(Od, Ld, B, H, cp, D, lse_layout, lse_mode, out, out_lse, out_abs, nthreads);
+    free(Od);
+    free(Ld);
+    return rc;
+}
+
+/*
+ * Softmax attention of one query row over KV rows [t0, t1): the definition,
+ * in two passes (max, then exponentials).  q has dqk columns, each kv row has
+ * kv_stride elements of which the first dqk are the key and the first dv the
+ * value.  Writes o[dv] and returns the natural-log LSE (-inf for t0 == t1).
+ */
+static double attend_row(const uint16_t* q, const uint16_t* kv, int64_t kv_stride, int64_t t0, int64_t t1,
+                         int64_t dqk, int64_t dv, double scale, double* qd, double* o) {
+    for (int64_t d = 0; d < dv; ++d) o[d] = 0.0;
+    if (t1 <= t0) return -INFINITY;
+    for (int64_t d = 0; d < dqk; ++d) qd[d] = oracle_bf16_to_f64(q[d]);
+
+    double m = -INFINITY;
+    for (int64_t t = t0; t < t1; ++t) {
+        const uint16_t* k = kv + t * kv_stride;
+        double z = 0.0;
+        for (int64_t d = 0; d < dqk; ++d) z += qd[d] * oracle_bf16_to_f64(k[d]);
+        z *= scale;
+        if (z > m) m = z;
+    }
+    double l = 0.0;
+    for (int64_t t = t0; t < t1; ++t) {
+        const uint16_t* k = kv + t * kv_stride;
+        double z = 0.0;
+        for (int64_t d = 0; d < dqk; ++d) z += qd[d] * oracle_bf16_to_f64(k[d]);
+        z *= scale;
+        double p = exp(z - m);
+        l += p;
+        for (int64_t d = 0; d < dv; ++d) o[d] += p * oracle_bf16_to_f64(k[d]);
+    }
+    for (int64_t d = 0; d < dv; ++d) o[d] /= l;
+    return m + log(l);
+}
+
+/* Shard s of a T-token cache split into cp contiguous shards covers
+ * [floor(s*T/cp), floor((s+1)*T/cp)). */
+static void shard_bounds(int64_t T, int64_t cp, int64_t s, int64_t* t0, int64_t* t1) {
+    *t0 = (s * T) / cp;
+    *t1 = ((s + 1) * T) / cp;
+}
+
+/*
+ * Per-shard decode partials for the query rows listed in `rows` (each row is
+ * b*hq + h; NULL means all B*hq rows in order).
+ *   q        [B, hq, dqk] contiguous bf16 bits
+ *   kv       [T, dqk] contiguous bf16 bits (value = first dv columns)
+ *   o_part   [n_rows, cp, dv]
+ *   lse_part [n_rows, cp]     base-e, or times log2 e for base 2
+ */
+int oracle_attention_partials(const uint16_t* q, const uint16_t* kv, int64_t B, int64_t hq, int64_t T,
+                              int64_t dqk, int64_t dv, int64_t cp, double scale, int lse_mode,
+                              const int64_t* rows, int64_t n_rows, double* o_part, double* lse_part,
+                              int nthreads) {
+    if (B < 0 || hq <= 0 || T < 0 || dqk <= 0 || dv <= 0 || dv > dqk || cp <= 0) return ORACLE_BAD_ARG;
+    if (lse_mode != ORACLE_BASE_E && lse_mode != ORACLE_BASE_2) return ORACLE_BAD_ARG;
+    if (!rows) n_rows = B * hq;
+    set_threads(nthreads);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t r = rows ? rows[i] : i;
+        double* qd = (double*)malloc((size_t)dqk * sizeof(double));
+        for (int64_t s = 0; s < cp; ++s) {
+            int64_t t0, t1;
+            shard_bounds(T, cp, s, &t0, &t1);
+            double lse = attend_row(q + r * dqk, kv, dqk, t0, t1, dqk, dv, scale, qd, o_part + (i * cp + s) * dv);
+            if (lse_mode == ORACLE_BASE_2) lse *= M_LOG2E;
+            lse_part[i * cp + s] = lse;
+        }
+        free(qd);
+    }
+    return ORACLE_OK;
+}
+
+/* Full (unsharded) decode attention over all T rows: the brute-force answer
+ * the merged partials must reproduce.  o [n_rows, dv], lse [n_rows]. */
+int oracle_attention_full(const uint16_t* q, const uint16_t* kv, int64_t B, int64_t hq, int64_t T, int64_t dqk,
+                          int64_t dv, double scale, int lse_mode, const int64_t* rows, int64_t n_rows, double* o,
+                          double* lse, int nthreads) {
+    if (B < 0 || hq <= 0 || T < 0 || dqk <= 0 || dv <= 0 || dv > dqk) return ORACLE_BAD_ARG;
+    if (lse_mode != ORACLE_BASE_E && lse_mode != ORACLE_BASE_2) return ORACLE_BAD_ARG;
+    if (!rows) n_rows = B * hq;
+    set_threads(nthreads);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t r = rows ? rows[i] : i;
+        double* qd = (double*)malloc((size_t)dqk * sizeof(double));
+        double l = attend_row(q + r * dqk, kv, dqk, 0, T, dqk, dv, scale, qd, o + i * dv);
+        if (lse_mode == ORACLE_BASE_2) l *= M_LOG2E;
+        lse[i] = l;
+        free(qd);
+    }
+    return ORACLE_OK;
+}
