@@ -1,0 +1,181 @@
+"""Python binding of libdcp.so, the MI355X DCP LSE merge (C ABI in include/dcp.h).
+
+Argument marshalling only: every function here has the name of the C entry
+point it calls, turns torch tensors into device pointers, element strides and
+the current HIP stream, and raises ``DcpError`` on a nonzero status.  Every
+step of the computation runs in the library's HIP kernels; there is no other
+path.  If the library has not been built, importing this package fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdcp.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dcp.h")
+
+
+def _header_constants(path):
+    consts = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"#define\s+(DCP_[A-Z0-9_]+)\s+(-?\d+)\b", line)
+            if m:
+                consts[m.group(1)] = int(m.group(2))
+    return consts
+
+
+_C = _header_constants(HEADER_PATH)
+DCP_OK = _C["DCP_OK"]
+DCP_ERR_INVALID_ARG = _C["DCP_ERR_INVALID_ARG"]
+DCP_ERR_LAYOUT = _C["DCP_ERR_LAYOUT"]
+DCP_ERR_ALIGN = _C["DCP_ERR_ALIGN"]
+DCP_ERR_STREAM = _C["DCP_ERR_STREAM"]
+DCP_ERR_WORKSPACE = _C["DCP_ERR_WORKSPACE"]
+DCP_ERR_HIP = _C["DCP_ERR_HIP"]
+DCP_LSE_BASE_E = _C["DCP_LSE_BASE_E"]
+DCP_LSE_BASE_2 = _C["DCP_LSE_BASE_2"]
+DCP_LSE_BHC = _C["DCP_LSE_BHC"]
+DCP_LSE_BH1 = _C["DCP_LSE_BH1"]
+DCP_DTYPE_BF16 = _C["DCP_DTYPE_BF16"]
+DCP_HEAD_DIM = _C["DCP_HEAD_DIM"]
+DCP_MAX_CP = _C["DCP_MAX_CP"]
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "context_lse_merge_amd: %s is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+        "(or python -m context_lse_merge_amd._build) first" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+_lib.dcp_workspace_create.argtypes = [_i64, _i32, _i32, _i32, _i32, _vp, ctypes.POINTER(_vp)]
+_lib.dcp_workspace_destroy.argtypes = [_vp]
+_lib.dcp_lse_combine.argtypes = [_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _i64,
+                                 _i64, _vp, _i64, _vp]
+_lib.dcp_last_error.restype = ctypes.c_char_p
+_lib.dcp_status_string.argtypes = [_i32]
+_lib.dcp_status_string.restype = ctypes.c_char_p
+for _f in ("dcp_workspace_create", "dcp_workspace_destroy", "dcp_lse_combine"):
+    getattr(_lib, _f).restype = _i32
+
+
+class DcpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (dcp_status_string(status), message))
+        self.status = status
+
+
+def dcp_last_error() -> str:
+    return _lib.dcp_last_error().decode()
+
+
+def dcp_status_string(status: int) -> str:
+    return _lib.dcp_status_string(status).decode()
+
+
+def _check(rc: int):
+    if rc != DCP_OK:
+        raise DcpError(rc, dcp_last_error())
+
+
+def _stream_handle(stream):
+    """A hipStream_t as an integer: None -> torch's current stream on the current device."""
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev_ptr(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (got device %s)" % (name, t.device))
+    return t.data_ptr()
+
+
+class Workspace:
+    """Owns a dcp_workspace handle; ``handle`` is what the C calls take."""
+
+    def __init__(self, handle: int, capacity: int, h_local: int, cp: int, stream: int):
+        self.handle = handle
+        self.capacity = capacity
+        self.h_local = h_local
+        self.cp = cp
+        self.stream = stream
+
+    def close(self):
+        if self.handle:
+            _check(_lib.dcp_workspace_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def dcp_workspace_create(capacity_tokens: int, h_local: int, cp: int, d: int = DCP_HEAD_DIM,
+                         dtype: int = DCP_DTYPE_BF16, stream=None) -> Workspace:
+    """Create a workspace bound to ``stream`` (default: torch's current stream)."""
+    s = _stream_handle(stream)
+    h = _vp()
+    _check(_lib.dcp_workspace_create(capacity_tokens, h_local, cp, d, dtype, s, ctypes.byref(h)))
+    return Workspace(h.value, capacity_tokens, h_local, cp, s)
+
+
+def dcp_workspace_destroy(ws: Workspace):
+    ws.close()
+
+
+def dcp_lse_combine(ws: Workspace, attn, lse, lse_layout: int, lse_mode: int, out, out_lse=None, stream=None):
+    """Merge the cp shard partials of ``attn`` [B, H, D] (bf16, any token/head strides)
+    into ``out`` [B, H/cp, D] and optionally ``out_lse`` [B, H/cp].
+
+    ``lse`` is [B, H/cp, cp] for ``DCP_LSE_BHC`` or [B, H, 1] / [B, H] for
+    ``DCP_LSE_BH1``; strides are taken from the tensors.  ``stream`` defaults
+    to torch's current stream."""
+    import torch
+    if attn.dim() != 3 or out.dim() != 3:
+        raise ValueError("attn and out must be 3-D [B, H, D] / [B, H/cp, D]")
+    if attn.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("attn and out must be bfloat16")
+    if lse.dtype != torch.float32 or (out_lse is not None and out_lse.dtype != torch.float32):
+        raise ValueError("lse and out_lse must be float32")
+    B, H, D = attn.shape
+    if out.shape[0] != B or out.shape[2] != D or (out_lse is not None and out_lse.shape[0] != B):
+        raise ValueError("out / out_lse shapes do not match attn")
+    if attn.stride(2) != 1 or out.stride(2) != 1:
+        raise ValueError("the innermost (D) stride of attn and out must be 1")
+    if out.shape[1] * ws.cp != H or (out_lse is not None and out_lse.shape[1] * ws.cp != H):
+        raise ValueError("out has %d heads; expected H / cp = %d" % (out.shape[1], H // ws.cp))
+    if lse_layout == DCP_LSE_BHC:
+        if lse.dim() != 3 or tuple(lse.shape) != (B, H // ws.cp, ws.cp):
+            raise ValueError("DCP_LSE_BHC lse must be [B, H/cp, cp] = %s" % ((B, H // ws.cp, ws.cp),))
+        l0, l1, l2 = lse.stride()
+    else:
+        if lse.dim() not in (2, 3) or lse.shape[0] != B or lse.shape[1] != H or (lse.dim() == 3 and lse.shape[2] != 1):
+            raise ValueError("DCP_LSE_BH1 lse must be [B, H, 1] or [B, H]")
+        l0, l1, l2 = lse.stride(0), lse.stride(1), 0
+    if out_lse is not None and out_lse.dim() != 2:
+        raise ValueError("out_lse must be [B, H/cp]")
+    if out_lse is not None and out_lse.stride(1) != 1:
+        raise ValueError("out_lse must have unit head stride")
+    s = _stream_handle(stream)
+    _check(_lib.dcp_lse_combine(
+        ws.handle, _dev_ptr(attn, "attn"), B, H, attn.stride(0), attn.stride(1),
+        _dev_ptr(lse, "lse"), lse_layout, l0, l1, l2, lse_mode,
+        _dev_ptr(out, "out"), out.stride(0), out.stride(1),
+        _dev_ptr(out_lse, "out_lse"), out_lse.stride(0) if out_lse is not None else 0, s))
+    return out, out_lse

@@ -1,0 +1,63 @@
+"""Build libdcp.so (the HIP library behind include/dcp.h) in-tree for gfx950.
+
+``python -m context_lse_merge_amd._build`` or ``build()`` compiles every source
+under ``csrc/`` with hipcc.  Packed-FP32 instructions are switched off for all
+device code (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libdcp.so")
+ARCH = "gfx950"
+
+SOURCES = ["dcp_host.cpp", "merge.hip"]
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
+    "--offload-arch=" + ARCH,
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I" + INCLUDE, "-I" + CSRC,
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the DCP library needs ROCm's hipcc to build")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libdcp.so; returns its path."""
+    cc = hipcc()
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(objdir, src + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [cc] + lang + HIPCC_FLAGS + ["-c", path, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

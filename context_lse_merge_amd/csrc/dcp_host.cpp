@@ -1,0 +1,263 @@
+// dcp_host.cpp -- argument validation, the strided-view layout adapter and the
+// ordered chunk planner of the DCP LSE merge, plus the workspace object and
+// error reporting.  Pure host C++: no HIP call, no device access.
+//
+// Layout adapter ("[DCP] Run fi_a2a on FlashInfer's fused all-to-all + LSE
+// reduce", sglang PR #40539, Modifications): the [B, H, D] attention output is
+// viewed as [B, H/cp, cp, D] without a copy, head h belonging to shard
+// h / (H/cp); so element (b, j, s, d) sits at b*sb + (s*H_local + j)*sh + d,
+// i.e. local-head stride sh and shard stride H_local*sh.  The LSE is either
+// [B, H/cp, cp] or FlashMLA's [B, H, 1] (PR #40539, Accuracy Tests); the
+// latter is the same view with shard stride H_local*l1.
+//
+// Chunk planner (PR #40539, Modifications and Coordination): batches wider
+// than the workspace run as several launches over consecutive token ranges,
+// in order, on the workspace's stream.  A call on any other stream is rejected
+// before anything is enqueued (PR #40539, Accuracy Tests: a third stream is
+// rejected before the collective).
+//
+// Input checks: the later text of PR #40539 drops the copy of strided or
+// misaligned partials and lets the kernel check its inputs; here an input the
+// kernel cannot read directly is rejected with an error, never copied.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "dcp_internal.h"
+
+namespace dcp {
+
+namespace {
+thread_local char g_error[512] = "";
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Half-open byte range [lo, hi) covered by a strided 2-D set of rows:
+// n1 x n2 rows of `row_elems` elements of `elem` bytes, row (i, k) at
+// base + i*s1 + k*s2 (elements).  Strides are non-negative here.
+struct Extent {
+    uintptr_t lo, hi;
+};
+Extent extent(const void* base, int64_t n1, int64_t s1, int64_t n2, int64_t s2, int64_t row_elems, size_t elem) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(base);
+    int64_t last = (n1 - 1) * s1 + (n2 - 1) * s2 + row_elems;
+    return Extent{lo, lo + static_cast<uintptr_t>(last) * elem};
+}
+bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Rows of `row` elements at offsets i*s1 + k*s2 (0 <= i < n1, 0 <= k < n2)
+// are pairwise disjoint if, with the strides sorted, the small one clears a
+// row and the big one clears a full run of the small one.
+bool rows_disjoint(int64_t n1, int64_t s1, int64_t n2, int64_t s2, int64_t row) {
+    if (n1 <= 1) return n2 <= 1 || s2 >= row;
+    if (n2 <= 1) return s1 >= row;
+    int64_t ns = n1, ss = s1, sb = s2;  // the smaller stride, its count, and the bigger stride
+    if (s2 < s1) {
+        ns = n2; ss = s2; sb = s1;
+    }
+    return ss >= row && sb >= (ns - 1) * ss + row;
+}
+}  // namespace
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_error[0] = '\0';
+    return DCP_OK;
+}
+
+int plan_merge(const dcp_workspace* ws, const void* attn, int64_t B, int H, int64_t attn_sb, int64_t attn_sh,
+               const float* lse, int lse_layout, int64_t l0, int64_t l1, int64_t l2, int lse_mode, void* out,
+               int64_t out_sb, int64_t out_sh, float* out_lse, int64_t out_lse_sb, void* hip_stream,
+               MergePlan* plan) {
+    if (!ws || ws->magic != kWorkspaceMagic)
+        return fail(DCP_ERR_WORKSPACE, "dcp_lse_combine: no valid workspace (create one with dcp_workspace_create)");
+    if (hip_stream != ws->stream)
+        return fail(DCP_ERR_STREAM,
+                    "dcp_lse_combine: called on stream %p but the workspace serves stream %p; a workspace serves "
+                    "one ordered stream, create another workspace for this stream",
+                    hip_stream, ws->stream);
+    const int cp = ws->cp, h_local = ws->h_local;
+    if (B < 0) return fail(DCP_ERR_INVALID_ARG, "dcp_lse_combine: B = %lld is negative", (long long)B);
+    if (H <= 0 || H % cp != 0)
+        return fail(DCP_ERR_INVALID_ARG, "dcp_lse_combine: H = %d is not a positive multiple of cp = %d", H, cp);
+    if (H / cp != h_local)
+        return fail(DCP_ERR_WORKSPACE,
+                    "dcp_lse_combine: H / cp = %d local heads but the workspace was created for h_local = %d", H / cp,
+                    h_local);
+    if (lse_layout != DCP_LSE_BHC && lse_layout != DCP_LSE_BH1)
+        return fail(DCP_ERR_INVALID_ARG, "dcp_lse_combine: lse_layout %d is neither DCP_LSE_BHC nor DCP_LSE_BH1",
+                    lse_layout);
+    if (lse_mode != DCP_LSE_BASE_E && lse_mode != DCP_LSE_BASE_2)
+        return fail(DCP_ERR_INVALID_ARG, "dcp_lse_combine: lse_mode %d is neither DCP_LSE_BASE_E nor DCP_LSE_BASE_2",
+                    lse_mode);
+    if (B == 0) {
+        *plan = MergePlan{};
+        return ok();
+    }
+    if (!attn || !lse || !out)
+        return fail(DCP_ERR_INVALID_ARG, "dcp_lse_combine: attn, lse and out must be non-null when B > 0");
+
+    const int64_t D = ws->d;
+    if (attn_sb < 0 || attn_sh < 0 || l0 < 0 || l1 < 0 || out_sb < 0 || out_sh < 0 || out_lse_sb < 0 ||
+        (lse_layout == DCP_LSE_BHC && l2 < 0))
+        return fail(DCP_ERR_LAYOUT, "dcp_lse_combine: strides must be non-negative");
+    if (!rows_disjoint(B, out_sb, h_local, out_sh, D))
+        return fail(DCP_ERR_LAYOUT,
+                    "dcp_lse_combine: out rows overlap (out_sb = %lld, out_sh = %lld, D = %lld): each of the "
+                    "B x h_local output rows needs D elements of its own",
+                    (long long)out_sb, (long long)out_sh, (long long)D);
+    if (out_lse && !rows_disjoint(B, out_lse_sb, h_local, 1, 1))
+        return fail(DCP_ERR_LAYOUT, "dcp_lse_combine: out_lse_sb = %lld < h_local = %d makes out_lse rows overlap",
+                    (long long)out_lse_sb, h_local);
+
+    if (!aligned(attn, 16) || !aligned(out, 16))
+        return fail(DCP_ERR_ALIGN, "dcp_lse_combine: attn (%p) and out (%p) must be 16-byte aligned", attn, out);
+    if (attn_sb % 8 || attn_sh % 8 || out_sb % 8 || out_sh % 8)
+        return fail(DCP_ERR_ALIGN,
+                    "dcp_lse_combine: attn_sb, attn_sh, out_sb and out_sh must be multiples of 8 elements "
+                    "(16 bytes); got %lld, %lld, %lld, %lld",
+                    (long long)attn_sb, (long long)attn_sh, (long long)out_sb, (long long)out_sh);
+    if (!aligned(lse, 4) || (out_lse && !aligned(out_lse, 4)))
+        return fail(DCP_ERR_ALIGN, "dcp_lse_combine: lse and out_lse must be 4-byte aligned");
+
+    // Layout adapter: (b, j, s) strides of O and of the LSE.
+    MergeArgs a{};
+    a.attn = static_cast<const uint16_t*>(attn);
+    a.lse = lse;
+    a.out = static_cast<uint16_t*>(out);
+    a.out_lse = out_lse;
+    a.a_sb = attn_sb;
+    a.a_sj = attn_sh;
+    a.a_ss = static_cast<int64_t>(h_local) * attn_sh;
+    a.l_sb = l0;
+    if (lse_layout == DCP_LSE_BHC) {
+        a.l_sj = l1;
+        a.l_ss = l2;
+    } else {
+        a.l_sj = l1;
+        a.l_ss = static_cast<int64_t>(h_local) * l1;
+    }
+    a.o_sb = out_sb;
+    a.o_sj = out_sh;
+    a.ol_sb = out_lse_sb;
+    a.h_local = h_local;
+    a.cp = cp;
+    if (lse_mode == DCP_LSE_BASE_2) {
+        a.to_log2 = 1.0f;
+        a.from_log2 = 1.0f;
+    } else {
+        a.to_log2 = 1.4426950408889634f;  // log2 e
+        a.from_log2 = 0.6931471805599453f; // ln 2
+    }
+
+    // Outputs may not overlap inputs or each other.
+    const Extent e_attn = extent(attn, B, attn_sb, H, attn_sh, D, 2);
+    const Extent e_out = extent(out, B, out_sb, h_local, out_sh, D, 2);
+    int64_t lse_last;
+    if (lse_layout == DCP_LSE_BHC)
+        lse_last = (B - 1) * l0 + (h_local - 1) * l1 + (cp - 1) * l2 + 1;
+    else
+        lse_last = (B - 1) * l0 + (H - 1) * l1 + 1;
+    const Extent e_lse{reinterpret_cast<uintptr_t>(lse),
+                       reinterpret_cast<uintptr_t>(lse) + static_cast<uintptr_t>(lse_last) * 4};
+    if (overlaps(e_out, e_attn) || overlaps(e_out, e_lse))
+        return fail(DCP_ERR_INVALID_ARG, "dcp_lse_combine: out overlaps attn or lse; the merge is out of place");
+    if (out_lse) {
+        const Extent e_ol = extent(out_lse, B, out_lse_sb, 1, 0, h_local, 4);
+        if (overlaps(e_ol, e_attn) || overlaps(e_ol, e_lse) || overlaps(e_ol, e_out))
+            return fail(DCP_ERR_INVALID_ARG, "dcp_lse_combine: out_lse overlaps attn, lse or out");
+    }
+
+    plan->args = a;
+    plan->B = B;
+    plan->chunk = ws->capacity;
+    plan->n_chunks = (B + ws->capacity - 1) / ws->capacity;
+    plan->args.rows = static_cast<int32_t>((B < ws->capacity ? B : ws->capacity) * h_local);
+    return ok();
+}
+
+MergeArgs chunk_args(const MergePlan& plan, int64_t k) {
+    MergeArgs a = plan.args;
+    const int64_t t0 = k * plan.chunk;
+    const int64_t t1 = (t0 + plan.chunk < plan.B) ? t0 + plan.chunk : plan.B;
+    a.attn += t0 * a.a_sb;
+    a.lse += t0 * a.l_sb;
+    a.out += t0 * a.o_sb;
+    if (a.out_lse) a.out_lse += t0 * a.ol_sb;
+    a.rows = static_cast<int32_t>((t1 - t0) * a.h_local);
+    return a;
+}
+
+}  // namespace dcp
+
+extern "C" {
+
+int dcp_workspace_create(int64_t capacity_tokens, int h_local, int cp, int d, int dtype, void* hip_stream,
+                         dcp_workspace** ws) {
+    if (!ws) return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_workspace_create: ws (the output handle) is null");
+    *ws = nullptr;
+    if (capacity_tokens < 1)
+        return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_workspace_create: capacity_tokens = %lld must be >= 1",
+                         (long long)capacity_tokens);
+    if (h_local < 1 || cp < 1 || cp > DCP_MAX_CP)
+        return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_workspace_create: need h_local >= 1 and 1 <= cp <= %d (got %d, %d)",
+                         DCP_MAX_CP, h_local, cp);
+    if (d != DCP_HEAD_DIM)
+        return dcp::fail(DCP_ERR_LAYOUT, "dcp_workspace_create: head dimension %d is not supported (only %d)", d,
+                         DCP_HEAD_DIM);
+    if (dtype != DCP_DTYPE_BF16)
+        return dcp::fail(DCP_ERR_LAYOUT, "dcp_workspace_create: dtype %d is not supported (only DCP_DTYPE_BF16)",
+                         dtype);
+    // One launch covers capacity * h_local rows, counted in 32 bits.
+    if (capacity_tokens * static_cast<int64_t>(h_local) > (int64_t{1} << 30))
+        return dcp::fail(DCP_ERR_INVALID_ARG,
+                         "dcp_workspace_create: capacity_tokens * h_local = %lld exceeds 2^30 rows per launch",
+                         (long long)(capacity_tokens * h_local));
+    dcp_workspace* w = new (std::nothrow) dcp_workspace;
+    if (!w) return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_workspace_create: out of host memory");
+    w->capacity = capacity_tokens;
+    w->h_local = h_local;
+    w->cp = cp;
+    w->d = d;
+    w->dtype = dtype;
+    w->stream = hip_stream;
+    w->magic = dcp::kWorkspaceMagic;
+    *ws = w;
+    return dcp::ok();
+}
+
+int dcp_workspace_destroy(dcp_workspace* ws) {
+    if (!ws) return dcp::ok();
+    if (ws->magic != dcp::kWorkspaceMagic)
+        return dcp::fail(DCP_ERR_WORKSPACE, "dcp_workspace_destroy: not a workspace (or destroyed twice)");
+    ws->magic = 0;
+    delete ws;
+    return dcp::ok();
+}
+
+const char* dcp_last_error(void) { return dcp::g_error; }
+
+const char* dcp_status_string(int status) {
+    switch (status) {
+        case DCP_OK: return "DCP_OK";
+        case DCP_ERR_INVALID_ARG: return "DCP_ERR_INVALID_ARG";
+        case DCP_ERR_LAYOUT: return "DCP_ERR_LAYOUT";
+        case DCP_ERR_ALIGN: return "DCP_ERR_ALIGN";
+        case DCP_ERR_STREAM: return "DCP_ERR_STREAM";
+        case DCP_ERR_WORKSPACE: return "DCP_ERR_WORKSPACE";
+        case DCP_ERR_HIP: return "DCP_ERR_HIP";
+        default: return "DCP_ERR_UNKNOWN";
+    }
+}
+
+}  // extern "C"

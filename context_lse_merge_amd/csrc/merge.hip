@@ -1,0 +1,275 @@
+// merge.hip -- the DCP LSE merge on gfx950 (MI355X) and the dcp_lse_combine
+// entry point.
+//
+// What it computes: for every token b and local head j, the LSE-weighted merge
+// of the cp shard partials of that head ("[DCP] Run fi_a2a on FlashInfer's
+// fused all-to-all + LSE reduce", sglang PR #40539, Motivation/Modifications;
+// "[Attention] Add direct symmetric-memory DCP A2A", vLLM PR #48897: FP32 LSE
+// weighting, empty shards publish -inf and their payload is skipped):
+//     M = max_s lse_s, w_s = 2^((lse_s - M) * c), S = sum_s w_s,
+//     out = sum_s (w_s / S) O_s, L = M + log2(S) / c,
+// with c = 1 for base-2 LSEs and c = log2 e for natural-log LSEs.
+//
+// Mapping to CDNA4.  The work is a pure stream: every partial is read once and
+// every output written once, so the kernel is bound by HBM bandwidth, not by
+// arithmetic, and is built to keep as many bytes in flight as possible:
+//  * one 64-lane wavefront per (b, j) row; lane l owns columns [8l, 8l + 8) of
+//    D = 512, so one 16-byte load per lane fetches a shard's whole 1 KiB
+//    D-vector, fully coalesced;
+//  * all of a row's shard loads are issued before any arithmetic waits on
+//    them, together with the LSE loads, so a wave has cp KiB in flight and a
+//    launch needs a single memory round trip;
+//  * lane s holds lse_s; the max and the sum over shards are wavefront DPP
+//    reductions inside a 16-lane row (cp <= 16) plus lane reads across rows
+//    (cp <= 64); the normalised weights are broadcast to scalar registers, so
+//    the empty-shard test (weight exactly 0, which covers lse = -inf) is a
+//    uniform scalar branch and an empty shard's payload is never used;
+//  * fp32 FMAs in ascending shard order, then the hardware round-to-nearest-
+//    even bf16 convert and one 16-byte store per lane.
+// The per-element arithmetic does not depend on B, on the chunking or on the
+// grid, so chunked and unchunked calls give identical bits.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "dcp_internal.h"
+
+namespace dcp {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = 64 * kWavesPerBlock;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// DPP controls (gfx9 encoding): quad_perm [1,0,3,2] and [2,3,0,1], then
+// row_half_mirror and row_mirror.  Applied in that order they combine all 16
+// lanes of a row, and every lane of the row ends up holding the result.
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, dpp<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp<kDppQuadXor2>(v));
+    v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppRowMirror>(v));
+    return v;
+}
+
+__device__ __forceinline__ float row_sum16(float v) {
+    v = v + dpp<kDppQuadXor1>(v);
+    v = v + dpp<kDppQuadXor2>(v);
+    v = v + dpp<kDppRowHalfMirror>(v);
+    v = v + dpp<kDppRowMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Reduce over the first `cp` lanes (cp <= 64) and return the result in a
+// scalar register.  Lanes >= cp must hold the identity of the reduction.
+template <int MaxCp>
+__device__ __forceinline__ float wave_max(float v, int cp) {
+    v = row_max16(v);
+    float m = lane_value(v, 0);
+    if (MaxCp > 16) {
+        if (cp > 16) m = fmaxf(m, lane_value(v, 16));
+        if (cp > 32) m = fmaxf(fmaxf(m, lane_value(v, 32)), lane_value(v, 48));
+    }
+    return m;
+}
+
+template <int MaxCp>
+__device__ __forceinline__ float wave_sum(float v, int cp) {
+    v = row_sum16(v);
+    float s = lane_value(v, 0);
+    if (MaxCp > 16) {
+        if (cp > 16) s = s + lane_value(v, 16);
+        if (cp > 32) s = s + (lane_value(v, 32) + lane_value(v, 48));
+    }
+    return s;
+}
+
+// acc += w * v for the 8 bf16 columns of v, unless w == 0: then acc is left
+// exactly as it was, whatever v holds (an empty shard's payload may be NaN).
+// A select rather than a branch, so the payload loads stay ahead of their use.
+__device__ __forceinline__ void fma8(float (&acc)[8], float w, u32x4 v) {
+    const bool use = (w != 0.0f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // bf16 -> fp32 is exact: the bf16 bits are the high half of the float.
+        const uint32_t p = v[i];
+        const float lo = fmaf(w, __uint_as_float(p << 16), acc[2 * i]);
+        const float hi = fmaf(w, __uint_as_float(p & 0xFFFF0000u), acc[2 * i + 1]);
+        acc[2 * i] = use ? lo : acc[2 * i];
+        acc[2 * i + 1] = use ? hi : acc[2 * i + 1];
+    }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const uint16_t a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
+    const uint16_t b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
+    return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+}
+
+struct Row {
+    int b, j;
+};
+
+__device__ __forceinline__ Row row_of(const MergeArgs& a, int row) {
+    Row r;
+    r.b = row / a.h_local;
+    r.j = row - r.b * a.h_local;
+    return r;
+}
+
+// Weights of one row from the LSE held by lane s (lanes >= cp hold -inf).
+// Returns the normalised weight of the lane's shard; S receives the sum of
+// the unnormalised weights (0 when every shard is empty) and M the maximum.
+// An all-empty row needs no branch: every weight is 0, S = 0, the guarded
+// reciprocal is 0, and the merged LSE M + log2(0) is -inf.
+template <int MaxCp>
+__device__ __forceinline__ float row_weights(const MergeArgs& a, float x, int cp, float& M, float& S) {
+    M = wave_max<MaxCp>(x, cp);
+    const float w = (x == -INFINITY) ? 0.0f : exp2f((x - M) * a.to_log2);
+    S = wave_sum<MaxCp>(w, cp);
+    const float inv = (S > 0.0f) ? 1.0f / S : 0.0f;
+    return w * inv;
+}
+
+__device__ __forceinline__ void store_row(const MergeArgs& a, Row r, int lane, const float (&acc)[8], float L) {
+    u32x4 packed;
+    packed[0] = pack_bf16x2(acc[0], acc[1]);
+    packed[1] = pack_bf16x2(acc[2], acc[3]);
+    packed[2] = pack_bf16x2(acc[4], acc[5]);
+    packed[3] = pack_bf16x2(acc[6], acc[7]);
+    __builtin_nontemporal_store(packed, reinterpret_cast<u32x4*>(a.out + r.b * a.o_sb + r.j * a.o_sj + lane * 8));
+    if (a.out_lse && lane == 0) a.out_lse[r.b * a.ol_sb + r.j] = L;
+}
+
+// cp = CP <= 16 shards, known at compile time: one wavefront per (b, j) row,
+// the LSE load and all CP payload loads in flight at once, no branch between
+// the loads and their use.
+template <int CP>
+__global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+    if (row >= a.rows) return;  // whole wavefront
+    const Row r = row_of(a, row);
+
+    const int ls = lane < CP ? lane : CP - 1;
+    const float xl = a.lse[r.b * a.l_sb + r.j * a.l_sj + ls * a.l_ss];
+    const uint16_t* orow = a.attn + r.b * a.a_sb + r.j * a.a_sj + lane * 8;
+    u32x4 v[CP];
+#pragma unroll
+    for (int s = 0; s < CP; ++s) v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(orow + s * a.a_ss));
+
+    const float x = lane < CP ? xl : -INFINITY;  // lane s holds lse_s
+    float M, S;
+    const float wn = row_weights<16>(a, x, CP, M, S);
+
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < CP; ++s) fma8(acc, lane_value(wn, s), v[s]);
+    store_row(a, r, lane, acc, M + log2f(S) * a.from_log2);
+}
+
+// 16 < cp <= 64: the same row algorithm with the shards taken G at a time.
+// Loads past the last shard re-read shard cp-1 (an address already being
+// fetched) and get weight 0.
+template <int G>
+__global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+    if (row >= a.rows) return;
+    const Row r = row_of(a, row);
+    const int cp = a.cp;
+
+    const int ls = lane < cp ? lane : cp - 1;
+    const float xl = a.lse[r.b * a.l_sb + r.j * a.l_sj + ls * a.l_ss];
+    const uint16_t* orow = a.attn + r.b * a.a_sb + r.j * a.a_sj + lane * 8;
+    u32x4 v[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+        v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(orow + min(i, cp - 1) * a.a_ss));
+
+    const float x = lane < cp ? xl : -INFINITY;
+    float M, S;
+    const float wn = row_weights<64>(a, x, cp, M, S);
+
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < cp; s0 += G) {
+        if (s0 > 0) {
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+                v[i] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(orow + min(s0 + i, cp - 1) * a.a_ss));
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const float ws = (s0 + i < cp) ? lane_value(wn, min(s0 + i, 63)) : 0.0f;
+            fma8(acc, ws, v[i]);
+        }
+    }
+    store_row(a, r, lane, acc, M + log2f(S) * a.from_log2);
+}
+
+template <int CP>
+void launch_fixed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
+    merge_kernel<CP><<<grid, dim3(kBlock), 0, stream>>>(a);
+}
+
+hipError_t launch(const MergeArgs& a, hipStream_t stream) {
+    const dim3 grid((a.rows + kWavesPerBlock - 1) / kWavesPerBlock);
+    switch (a.cp) {
+        case 1: launch_fixed<1>(a, grid, stream); break;
+        case 2: launch_fixed<2>(a, grid, stream); break;
+        case 3: launch_fixed<3>(a, grid, stream); break;
+        case 4: launch_fixed<4>(a, grid, stream); break;
+        case 5: launch_fixed<5>(a, grid, stream); break;
+        case 6: launch_fixed<6>(a, grid, stream); break;
+        case 7: launch_fixed<7>(a, grid, stream); break;
+        case 8: launch_fixed<8>(a, grid, stream); break;
+        case 9: launch_fixed<9>(a, grid, stream); break;
+        case 10: launch_fixed<10>(a, grid, stream); break;
+        case 11: launch_fixed<11>(a, grid, stream); break;
+        case 12: launch_fixed<12>(a, grid, stream); break;
+        case 13: launch_fixed<13>(a, grid, stream); break;
+        case 14: launch_fixed<14>(a, grid, stream); break;
+        case 15: launch_fixed<15>(a, grid, stream); break;
+        case 16: launch_fixed<16>(a, grid, stream); break;
+        default: merge_kernel_wide<16><<<grid, dim3(kBlock), 0, stream>>>(a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace dcp
+
+extern "C" int dcp_lse_combine(dcp_workspace* ws, const void* attn, int64_t B, int H, int64_t attn_sb,
+                               int64_t attn_sh, const float* lse, int lse_layout, int64_t l0, int64_t l1, int64_t l2,
+                               int lse_mode, void* out, int64_t out_sb, int64_t out_sh, float* out_lse,
+                               int64_t out_lse_sb, void* hip_stream) {
+    dcp::MergePlan plan;
+    const int rc = dcp::plan_merge(ws, attn, B, H, attn_sb, attn_sh, lse, lse_layout, l0, l1, l2, lse_mode, out,
+                                   out_sb, out_sh, out_lse, out_lse_sb, hip_stream, &plan);
+    if (rc != DCP_OK) return rc;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    for (int64_t k = 0; k < plan.n_chunks; ++k) {
+        const hipError_t e = dcp::launch(dcp::chunk_args(plan, k), stream);
+        if (e != hipSuccess)
+            return dcp::fail(DCP_ERR_HIP, "dcp_lse_combine: launch of chunk %lld of %lld failed: %s", (long long)k,
+                             (long long)plan.n_chunks, hipGetErrorString(e));
+    }
+    return dcp::ok();
+}

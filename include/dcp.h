@@ -1,0 +1,134 @@
+/*
+ * dcp.h -- C ABI of the MI355X (gfx950) decode-context-parallel LSE merge.
+ *
+ * Decode context parallelism (DCP) splits the latent KV cache of an MLA model
+ * over cp shards.  Each shard runs decode attention for every head over its
+ * own tokens and yields a partial output O_s and a log-sum-exp lse_s per
+ * (token, head).  The exact attention output is the LSE-weighted merge of the
+ * shards' partials ("[DCP] Run fi_a2a on FlashInfer's fused all-to-all + LSE
+ * reduce", sglang PR #40539, Motivation; "[Attention] Add direct
+ * symmetric-memory DCP A2A", vLLM PR #48897, commit message: states are
+ * combined with FP32 LSE weighting):
+ *
+ *     M = max_s lse_s,  w_s = base^(lse_s - M),  S = sum_s w_s
+ *     out = sum_s (w_s / S) O_s,                 L = M + log_base S
+ *
+ * On one GPU the cp shards are resident buffers: the caller's [B, H, D]
+ * attention output is read in place as a [B, H/cp, cp, D] view, head h
+ * belonging to shard h / (H/cp) (PR #40539, Modifications).
+ *
+ * Conventions for every entry point:
+ *  - All pointers to tensors are DEVICE pointers owned by the caller; the
+ *    library never allocates, frees, synchronises or prints, so every call may
+ *    be captured into a HIP graph.  Host-side objects (a workspace) are the
+ *    only memory the library allocates, and only in dcp_workspace_create.
+ *  - Sizes and strides are in ELEMENTS, not bytes.  The innermost (D) stride
+ *    of every tensor is 1.
+ *  - Every argument is checked before anything is enqueued: on any error the
+ *    call returns a nonzero status, nothing has been launched, and
+ *    dcp_last_error() (thread-local) names what to change.
+ *  - hip_stream is a hipStream_t passed as void*; NULL is the null stream.
+ *  - D (the head dimension, the MLA kv_lora_rank) is 512; partial outputs and
+ *    merged outputs are bf16; every LSE is fp32.
+ */
+#ifndef DCP_H
+#define DCP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define DCP_OK 0
+#define DCP_ERR_INVALID_ARG 1 /* bad size, null pointer, H % cp != 0, out aliases an input      */
+#define DCP_ERR_LAYOUT 2      /* unsupported D or dtype, negative or overlapping strides         */
+#define DCP_ERR_ALIGN 3       /* a pointer or row stride breaks the 16-byte alignment rule      */
+#define DCP_ERR_STREAM 4      /* called on a stream other than the workspace's                  */
+#define DCP_ERR_WORKSPACE 5   /* geometry differs from the workspace's, or no workspace given    */
+#define DCP_ERR_HIP 6         /* the HIP runtime refused a launch                               */
+
+/* LSE base: the attention backend decides which one its LSE is in
+ * (PR #40539, Modifications: lse_mode comes from the backend). */
+#define DCP_LSE_BASE_E 0 /* lse = ln  sum exp(z)             */
+#define DCP_LSE_BASE_2 1 /* lse = log2 sum 2^(z * log2 e)    */
+
+/* LSE layouts (PR #40539, Modifications and Accuracy Tests). */
+#define DCP_LSE_BHC 0 /* [B, H/cp, cp]: element (b, j, s) at b*l0 + j*l1 + s*l2              */
+#define DCP_LSE_BH1 1 /* FlashMLA [B, H, 1]: element (b, h) at b*l0 + h*l1, h = s*(H/cp) + j */
+
+/* Element types. */
+#define DCP_DTYPE_BF16 0
+
+#define DCP_HEAD_DIM 512
+#define DCP_MAX_CP 64
+
+typedef struct dcp_workspace dcp_workspace;
+
+/*
+ * Create a merge workspace: a host-side object that fixes the geometry
+ * (h_local = H/cp local heads, cp shards, head dimension d, dtype), the token
+ * capacity and the ONE stream it serves.  Mirrors the pages' workspaces: one
+ * per ordered stream, sized by the widest decode batch (PR #40539,
+ * Modifications and Coordination), created once before graph capture.
+ *
+ * capacity_tokens  >= 1; dcp_lse_combine splits wider batches into ordered
+ *                  chunks of at most this many tokens.
+ * h_local, cp      >= 1; cp <= DCP_MAX_CP.
+ * d                DCP_HEAD_DIM; dtype DCP_DTYPE_BF16.
+ * hip_stream       the stream every dcp_lse_combine call on this workspace
+ *                  must use (opaque value, compared, never dereferenced).
+ * ws               receives the handle; release it with dcp_workspace_destroy.
+ *
+ * On one GPU the shards' receive buffers are the caller's resident attention
+ * output, so the workspace holds no device memory.
+ */
+int dcp_workspace_create(int64_t capacity_tokens, int h_local, int cp, int d, int dtype, void* hip_stream,
+                         dcp_workspace** ws);
+
+/* Release a workspace (host memory only).  NULL is accepted. */
+int dcp_workspace_destroy(dcp_workspace* ws);
+
+/*
+ * LSE-weighted merge of cp shard partials, read in place.
+ *
+ * attn      [B, H, D] bf16 attention output, H = cp * h_local of ws.  Token b,
+ *           head h, column d at attn + b*attn_sb + h*attn_sh + d.  Shard s of
+ *           local head j is head s*h_local + j.  Padded token strides and
+ *           heads taken from a wider backing buffer are allowed.
+ * lse       fp32, layout DCP_LSE_BHC (strides l0, l1, l2) or DCP_LSE_BH1
+ *           (strides l0, l1; l2 ignored).  lse = -inf marks an empty shard:
+ *           its attn rows are never used, whatever they hold (vLLM PR #48897,
+ *           port commit: empty shards publish -inf and skip their payload).
+ * lse_mode  DCP_LSE_BASE_E or DCP_LSE_BASE_2; the merged LSE is in the same base.
+ * out       [B, h_local, D] bf16 (round to nearest even), row (b, j) at
+ *           out + b*out_sb + j*out_sh.  Must not overlap attn.
+ * out_lse   [B, h_local] fp32 merged LSE at out_lse + b*out_lse_sb + j, or NULL.
+ *
+ * A row whose shards are all empty gives out = +0.0 and out_lse = -inf (sglang
+ * PR #32851, commit log: such rows give 0, not NaN).  Arithmetic is fp32 with
+ * a fixed, ascending shard order that does not depend on B, the chunking or
+ * the launch, so chunked and unchunked calls give identical bits.
+ * B = 0 is a no-op.  B > capacity runs ceil(B / capacity) launches over
+ * consecutive token ranges, in order, on hip_stream (PR #40539, Modifications).
+ *
+ * Alignment: attn and out 16-byte aligned; attn_sb, attn_sh, out_sb, out_sh
+ * multiples of 8 elements; lse and out_lse 4-byte aligned.
+ */
+int dcp_lse_combine(dcp_workspace* ws, const void* attn, int64_t B, int H, int64_t attn_sb, int64_t attn_sh,
+                    const float* lse, int lse_layout, int64_t l0, int64_t l1, int64_t l2, int lse_mode, void* out,
+                    int64_t out_sb, int64_t out_sh, float* out_lse, int64_t out_lse_sb, void* hip_stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* dcp_last_error(void);
+
+/* Name of a status code. */
+const char* dcp_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCP_H */

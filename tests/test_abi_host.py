@@ -1,0 +1,72 @@
+"""CPU checks of the C ABI: the library loads and exports every declared entry
+point, and the host-side validator, layout adapter and chunk planner behave
+(built with g++ under AddressSanitizer/UBSan, no GPU involved)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcp.h")
+CSRC = os.path.join(ROOT, "context_lse_merge_amd", "csrc")
+LIB = os.path.join(ROOT, "context_lse_merge_amd", "libdcp.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dcp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("dcp_workspace_create", "dcp_workspace_destroy", "dcp_lse_combine", "dcp_last_error",
+              "dcp_status_string"):
+        assert n in names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    assert os.path.exists(LIB), "libdcp.so is not built"
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, "declared in dcp.h but not exported: %s" % missing
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dcp_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_binding_imports_and_status_strings():
+    import context_lse_merge_amd as dcp
+    assert dcp.dcp_status_string(dcp.DCP_ERR_STREAM) == "DCP_ERR_STREAM"
+    assert dcp.dcp_status_string(12345) == "DCP_ERR_UNKNOWN"
+    assert dcp.DCP_HEAD_DIM == 512
+
+
+def test_workspace_errors_through_the_binding():
+    import context_lse_merge_amd as dcp
+    with pytest.raises(dcp.DcpError) as e:
+        dcp.dcp_workspace_create(0, 16, 4, stream=0x1000)
+    assert e.value.status == dcp.DCP_ERR_INVALID_ARG and "capacity" in str(e.value)
+    with pytest.raises(dcp.DcpError) as e:
+        dcp.dcp_workspace_create(8, 16, 4, d=128, stream=0x1000)
+    assert e.value.status == dcp.DCP_ERR_LAYOUT
+    ws = dcp.dcp_workspace_create(8, 16, 4, stream=0x1000)
+    assert ws.handle
+    dcp.dcp_workspace_destroy(ws)
+    assert ws.handle is None
+
+
+def test_host_planner_under_sanitizers(tmp_path):
+    exe = tmp_path / "host_plan_check"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+           os.path.join(ROOT, "tests", "host_plan_check.cpp"), os.path.join(CSRC, "dcp_host.cpp"), "-o", str(exe)]
+    subprocess.run(cmd, check=True)
+    env = dict(os.environ)
+    # a library preloaded by the environment may sit before the ASan runtime
+    env["ASAN_OPTIONS"] = "verify_asan_link_order=0:detect_leaks=1"
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env)
+    assert r.returncode == 0, r.stderr + r.stdout
+    assert "host plan checks passed" in r.stdout
