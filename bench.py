@@ -1,0 +1,353 @@
+#!/usr/bin/env python
+"""Benchmark of the DCP LSE merge (dcp_lse_combine) on one MI355X.
+
+A step is one layer-merge: one dcp_lse_combine call over all B tokens of one
+synthetic batch (every chunk included), i.e. the whole hot path -- layout
+adapter, chunk planner, LSE reduction, weighted accumulation, store.
+
+Timing.  Inputs are resident in HBM before the timed region starts.  Calls
+are captured into HIP graphs of 60 calls each (one per MLA layer of a decode
+step), cycling over enough copies of the input that consecutive uses of the
+same bytes are at least 1 GiB apart -- more than the 256 MB Infinity Cache --
+so the figure is an HBM (cold-cache) figure.  The timed region is bracketed by
+a barrier and torch.cuda.synchronize(), and measured with HIP events on the
+stream the graphs are launched on.  A hot-cache figure (same buffers every
+call) is reported beside it.
+
+Output: one JSON line (rank 0).  ``value`` is achieved HBM throughput in GB/s
+= algorithmic bytes per layer-merge / time per layer-merge, where algorithmic
+bytes = sum over (token, local head) of (non-empty shards * 1024 + cp * 4 +
+1024 + 4): each non-empty shard's bf16 D-row and every LSE read once, the
+merged row and merged LSE written once.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs per layer-merge + achieved HBM GB/s (% of peak) at B=1..512, 1×MI355X"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+COLD_BYTES = 1 << 30            # distance between reuses of the same input bytes
+GRAPH_CALLS = 60                # calls per captured graph (one per MLA layer)
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "dcp_merge_kimi_b128_counters.txt")
+MERGE_SRC = os.path.join(ROOT, "context_lse_merge_amd", "csrc", "merge.hip")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=600, help="timed layer-merges (a multiple of 60 above 60)")
+    p.add_argument("--warmup", type=int, default=120)
+    p.add_argument("--workload", choices=["kimi", "dsv2", "stress"], default="kimi")
+    p.add_argument("--B", type=int, default=128)
+    p.add_argument("--no-sweep", action="store_true", help="skip the B = 1..512 sweep")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-hot", action="store_true", help="skip the hot-cache figure")
+    p.add_argument("--calibrate", action="store_true",
+                   help="also run a plain 256 MiB elementwise copy kernel (reference for HBM byte counters)")
+    return p.parse_args()
+
+
+def make_case(workload, B):
+    import synth
+    if workload == "kimi":
+        return synth.kimi_merge(B)
+    if workload == "dsv2":
+        return synth.dsv2_merge(B)
+    return synth.stress_merge(B)
+
+
+def workload_name(case, workload):
+    desc = {"kimi": "Kimi-K2.5-like merge, [B,H/cp,cp] base-e LSE",
+            "dsv2": "DeepSeek-V2-236B-like merge, FlashMLA [B,H,1] base-2 LSE",
+            "stress": "stress merge, 10% empty shards, capacity 128 (ordered chunks)"}[workload]
+    return "%s: B=%d H=%d cp=%d H_local=%d D=512 bf16" % (desc, case.B, case.H, case.cp, case.h_local)
+
+
+def algorithmic_bytes(case):
+    """sum over (b, j) of (#non-empty shards * 2D + cp * 4 + 2D + 4)."""
+    import torch
+    lse = case.lse
+    B, H, cp = case.B, case.H, case.cp
+    hl = H // cp
+    if case.lse_layout == "bh1":
+        lse = lse.reshape(B, cp, hl).permute(0, 2, 1)
+    nonempty = int(torch.isfinite(lse).sum()) + int((lse == math.inf).sum())
+    rows = B * hl
+    return nonempty * 1024 + rows * (cp * 4 + 1024 + 4)
+
+
+class GpuCase:
+    """Device copies of one case, replicated into `nsets` input sets."""
+
+    def __init__(self, case, nsets, capacity):
+        import torch
+        import context_lse_merge_amd as dcp
+        self.dcp = dcp
+        self.case = case
+        dev = torch.device("cuda:0")
+        attn0 = case.attn.to(dev)
+        lse0 = case.lse.to(dev)
+        self.sets = []
+        for _ in range(nsets):
+            attn = torch.empty_like(attn0)
+            attn.copy_(attn0)
+            lse = torch.empty_like(lse0)
+            lse.copy_(lse0)
+            out = torch.empty((case.B, case.h_local, 512), dtype=torch.bfloat16, device=dev)
+            out_lse = torch.empty((case.B, case.h_local), dtype=torch.float32, device=dev)
+            self.sets.append((attn, lse, out, out_lse))
+        self.capacity = capacity
+        self.layout = dcp.DCP_LSE_BHC if case.lse_layout == "bhc" else dcp.DCP_LSE_BH1
+        self.mode = dcp.DCP_LSE_BASE_E if case.lse_mode == "e" else dcp.DCP_LSE_BASE_2
+
+    def call(self, ws, k, stream):
+        attn, lse, out, out_lse = self.sets[k % len(self.sets)]
+        self.dcp.dcp_lse_combine(ws, attn, lse, self.layout, self.mode, out, out_lse, stream=stream)
+
+    def capture(self, ngraphs, calls_per_graph):
+        """HIP graphs of `calls_per_graph` calls each, together cycling over every set."""
+        import torch
+        stream = torch.cuda.Stream()
+        ws = self.dcp.dcp_workspace_create(self.capacity, self.case.h_local, self.case.cp, stream=stream)
+        # one eager pass on the capture stream first
+        with torch.cuda.stream(stream):
+            for k in range(len(self.sets)):
+                self.call(ws, k, stream)
+        torch.cuda.synchronize()
+        graphs = []
+        k = 0
+        for _ in range(ngraphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(calls_per_graph):
+                    self.call(ws, k, stream)
+                    k += 1
+            graphs.append(g)
+        torch.cuda.synchronize()
+        self.ws = ws
+        return graphs
+
+
+def barrier():
+    import torch.distributed as dist
+    if dist.is_available() and dist.is_initialized():
+        dist.barrier()
+
+
+def time_graphs(graphs, replays):
+    """Replay graphs round-robin `replays` times; returns elapsed ms (HIP events on
+    the stream the replays are launched on)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    barrier()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for r in range(replays):
+        graphs[r % len(graphs)].replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    barrier()
+    return start.elapsed_time(end)
+
+
+def measure(case, steps, warmup, capacity=None, cold=True):
+    """Returns (us per layer-merge, number of input sets, footprint bytes)."""
+    per_set = case.attn.numel() * 2 + case.lse.numel() * 4 + case.B * case.h_local * (1024 + 4)
+    calls = min(GRAPH_CALLS, steps)
+    if steps % calls:
+        raise SystemExit("--steps must be a multiple of %d" % calls)
+    # The graphs together call every set exactly once, round-robin, so the same
+    # bytes come back only after all the other sets (>= 1 GiB, or 1020 sets).
+    ngraphs = max(1, min(1024 // calls, math.ceil(COLD_BYTES / per_set / calls))) if cold else 1
+    nsets = ngraphs * calls if cold else 1
+    g = GpuCase(case, nsets, capacity or case.B)
+    graphs = g.capture(ngraphs, calls)
+    wrep = max(1, math.ceil(warmup / calls))
+    time_graphs(graphs, wrep)
+    ms = time_graphs(graphs, steps // calls)
+    us = ms * 1000.0 / steps
+    first = g.sets[0]
+    g.ws.close()
+    return us, nsets, nsets * per_set, first
+
+
+def parity_check(case, out, out_lse):
+    """The bench's own sanity check of its first input set against the oracle."""
+    import numpy as np
+    import oracle
+    import synth
+    olay = oracle.LSE_BHC if case.lse_layout == "bhc" else oracle.LSE_BH1
+    omode = oracle.BASE_E if case.lse_mode == "e" else oracle.BASE_2
+    r, rL, A = oracle.merge(synth.bf16_bits(case.attn), case.lse.contiguous().numpy(), case.cp, olay, omode)
+    g = out.float().cpu().double().numpy()
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126))) - 7)
+    ok = bool(np.all(np.abs(g - r) <= 2 * ulp + 2.0 ** -16 * A))
+    gL = out_lse.cpu().double().numpy()
+    fin = np.isfinite(rL)
+    ok = ok and bool(np.all(np.abs(gL[fin] - rL[fin]) <= 1e-5 * np.maximum(np.abs(rL[fin]), 1)))
+    return ok
+
+
+def cpu_baseline(case, seconds):
+    """The fp64 oracle, as it stands, on the same workload: whole layer-merges
+    repeated for about `seconds` (at least 2), all host cores it is allowed."""
+    import oracle
+    import synth
+    bits = synth.bf16_bits(case.attn)
+    lse = case.lse.contiguous().numpy()
+    olay = oracle.LSE_BHC if case.lse_layout == "bhc" else oracle.LSE_BH1
+    omode = oracle.BASE_E if case.lse_mode == "e" else oracle.BASE_2
+    threads = len(os.sched_getaffinity(0))
+    oracle.merge(bits, lse, case.cp, olay, omode, threads=threads)          # warm-up
+    times = []
+    t_end = time.perf_counter() + seconds
+    while len(times) < 2 or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        oracle.merge(bits, lse, case.cp, olay, omode, threads=threads)
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    med = times[len(times) // 2]
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return med * 1e6, threads, len(times), model
+
+
+CALIBRATION_BYTES = 256 << 20
+
+
+def calibration_copy():
+    """A plain elementwise kernel that reads and writes exactly CALIBRATION_BYTES
+    each (bf16 negation), launched 5 times: what FETCH_SIZE / WRITE_SIZE read for
+    it converts the counters' units into bytes."""
+    import torch
+    src = torch.ones(CALIBRATION_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def counters_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when that summary is missing or was taken on a different merge.hip."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    kv = {}
+    with open(PROFILE_COUNTERS) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    src_hash = hashlib.sha256(open(MERGE_SRC, "rb").read()).hexdigest()
+    if kv.get("merge_hip_sha256") != src_hash:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the merge of one rank's shards is the whole path here, and no "
+              "multi-GPU exchange is built; run with --gpus 1", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    import context_lse_merge_amd  # noqa: F401  (fails loudly if the HIP library is missing)
+
+    case = make_case(args.workload, args.B)
+    capacity = 128 if args.workload == "stress" else case.B
+    alg = algorithmic_bytes(case)
+    print("[bench] %s: %d algorithmic bytes per layer-merge" % (workload_name(case, args.workload), alg),
+          file=sys.stderr, flush=True)
+    us, nsets, footprint, first = measure(case, args.steps, args.warmup, capacity=capacity, cold=True)
+    ok = parity_check(case, first[2], first[3])
+    us_hot = None if args.no_hot else measure(case, args.steps, args.warmup, capacity=capacity, cold=False)[0]
+    gbs = alg / (us * 1e-6) / 1e9
+    print("[bench] cold %.3f us (%.1f GB/s), hot %s us, parity %s" % (us, gbs, us_hot, ok), file=sys.stderr,
+          flush=True)
+
+    sweep = []
+    if not args.no_sweep:
+        for wl, Bs in (("kimi", [1, 8, 16, 32, 64, 128, 256, 512]), ("dsv2", [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]),
+                       ("stress", [512])):
+            for B in Bs:
+                c = make_case(wl, B)
+                cap = 128 if wl == "stress" else B
+                u, n, fp, _ = measure(c, 120, 60, capacity=cap, cold=True)
+                a = algorithmic_bytes(c)
+                sweep.append({"workload": wl, "B": B, "us": round(u, 3), "GBps": round(a / (u * 1e-6) / 1e9, 1),
+                              "frac_of_peak": round(a / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": a,
+                              "input_sets": n, "footprint_MB": round(fp / 1e6, 1)})
+                print("[bench] sweep %s B=%d: %.3f us, %.1f GB/s" % (wl, B, u, sweep[-1]["GBps"]), file=sys.stderr,
+                      flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cu, threads, reps, model = cpu_baseline(case, args.cpu_seconds)
+        cpu = {"value": round(alg / (cu * 1e-6) / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "us_per_layer_merge": round(cu, 1),
+               "sample": "%d whole layer-merges of the same workload (fp64 C oracle, OpenMP over rows, %s); "
+                         "median" % (reps, model or "host CPU")}
+
+    if args.calibrate:
+        calibration_copy()
+    traffic = counters_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1000.0, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "storage_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload_name(case, args.workload), "B": case.B, "H": case.H, "cp": case.cp,
+                   "D": 512, "lse_layout": case.lse_layout, "lse_mode": case.lse_mode, "capacity": capacity,
+                   "graph_calls": GRAPH_CALLS, "input_sets": nsets, "footprint_MB": round(footprint / 1e6, 1),
+                   "cache": "cold: each input reused only after >= 1 GiB of other inputs"},
+        "us_per_layer_merge": round(us, 3),
+        "us_per_layer_merge_hot": None if us_hot is None else round(us_hot, 3),
+        "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "parity_vs_oracle": ok,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg // max(1, math.ceil(case.B / capacity))},
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
