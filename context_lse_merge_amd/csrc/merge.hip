@@ -100,19 +100,18 @@ __device__ __forceinline__ float wave_sum(float v, int cp) {
     return s;
 }
 
-// acc += w * v for the 8 bf16 columns of v, unless w == 0: then acc is left
-// exactly as it was, whatever v holds (an empty shard's payload may be NaN).
-// A select rather than a branch, so the payload loads stay ahead of their use.
+// acc += w * v for the 8 bf16 columns of v.  A shard with weight exactly 0
+// (an empty one) has its payload replaced by zeros first -- a select on the
+// four packed words, not a branch, so the payload loads stay ahead of their
+// use -- and then adds exactly +0, whatever the payload held (NaN included).
 __device__ __forceinline__ void fma8(float (&acc)[8], float w, u32x4 v) {
     const bool use = (w != 0.0f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        const uint32_t p = use ? v[i] : 0u;
         // bf16 -> fp32 is exact: the bf16 bits are the high half of the float.
-        const uint32_t p = v[i];
-        const float lo = fmaf(w, __uint_as_float(p << 16), acc[2 * i]);
-        const float hi = fmaf(w, __uint_as_float(p & 0xFFFF0000u), acc[2 * i + 1]);
-        acc[2 * i] = use ? lo : acc[2 * i];
-        acc[2 * i + 1] = use ? hi : acc[2 * i + 1];
+        acc[2 * i] = fmaf(w, __uint_as_float(p << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, __uint_as_float(p & 0xFFFF0000u), acc[2 * i + 1]);
     }
 }
 
@@ -122,14 +121,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
 }
 
+// Grid: x = token b of the chunk, y = group of kWavesPerBlock local heads;
+// wavefront w of block (b, y) merges local head j = y * kWavesPerBlock + w.
+// No integer division, and no branch anywhere between the loads and the
+// store, so the compiler keeps every load of the row ahead of the first wait.
+// When h_local is not a multiple of kWavesPerBlock the spare wavefronts of
+// the last group take j = h_local - 1: they read what that row's wavefront
+// reads and store the very same bits to the same place.
 struct Row {
     int b, j;
 };
 
-__device__ __forceinline__ Row row_of(const MergeArgs& a, int row) {
+__device__ __forceinline__ Row row_of(const MergeArgs& a) {
     Row r;
-    r.b = row / a.h_local;
-    r.j = row - r.b * a.h_local;
+    r.b = blockIdx.x;
+    const int j = __builtin_amdgcn_readfirstlane(blockIdx.y * kWavesPerBlock + (threadIdx.x >> 6));
+    r.j = j < a.h_local ? j : a.h_local - 1;
     return r;
 }
 
@@ -138,13 +145,21 @@ __device__ __forceinline__ Row row_of(const MergeArgs& a, int row) {
 // the unnormalised weights (0 when every shard is empty) and M the maximum.
 // An all-empty row needs no branch: every weight is 0, S = 0, the guarded
 // reciprocal is 0, and the merged LSE M + log2(0) is -inf.
+// v_exp_f32 / v_log_f32 / v_rcp_f32 are the hardware's 1-ulp instructions;
+// exponents below -126 flush the weight to 0, i.e. a shard whose weight is
+// under 2^-126 of the largest is skipped.
 template <int MaxCp>
 __device__ __forceinline__ float row_weights(const MergeArgs& a, float x, int cp, float& M, float& S) {
     M = wave_max<MaxCp>(x, cp);
-    const float w = (x == -INFINITY) ? 0.0f : exp2f((x - M) * a.to_log2);
+    const float w = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x - M) * a.to_log2);
     S = wave_sum<MaxCp>(w, cp);
-    const float inv = (S > 0.0f) ? 1.0f / S : 0.0f;
+    const float inv = (S > 0.0f) ? __builtin_amdgcn_rcpf(S) : 0.0f;
     return w * inv;
+}
+
+__device__ __forceinline__ float merged_lse(const MergeArgs& a, float M, float S) {
+    // S = 0 (all shards empty) gives log2(0) = -inf and M = -inf: L = -inf.
+    return M + __builtin_amdgcn_logf(S) * a.from_log2;
 }
 
 __device__ __forceinline__ void store_row(const MergeArgs& a, Row r, int lane, const float (&acc)[8], float L) {
@@ -157,15 +172,13 @@ __device__ __forceinline__ void store_row(const MergeArgs& a, Row r, int lane, c
     if (a.out_lse && lane == 0) a.out_lse[r.b * a.ol_sb + r.j] = L;
 }
 
-// cp = CP <= 16 shards, known at compile time: one wavefront per (b, j) row,
-// the LSE load and all CP payload loads in flight at once, no branch between
-// the loads and their use.
+// cp = CP <= 16 shards, known at compile time: the LSE load and all CP
+// payload loads of the row are in flight at once, no branch between the
+// loads and their use.
 template <int CP>
 __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
     const int lane = threadIdx.x & 63;
-    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-    if (row >= a.rows) return;  // whole wavefront
-    const Row r = row_of(a, row);
+    const Row r = row_of(a);
 
     const int ls = lane < CP ? lane : CP - 1;
     const float xl = a.lse[r.b * a.l_sb + r.j * a.l_sj + ls * a.l_ss];
@@ -173,6 +186,9 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
     u32x4 v[CP];
 #pragma unroll
     for (int s = 0; s < CP; ++s) v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(orow + s * a.a_ss));
+    // Keep every load above this point: nothing that waits on them may be
+    // scheduled before the last one is issued.
+    __builtin_amdgcn_sched_barrier(0);
 
     const float x = lane < CP ? xl : -INFINITY;  // lane s holds lse_s
     float M, S;
@@ -181,7 +197,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < CP; ++s) fma8(acc, lane_value(wn, s), v[s]);
-    store_row(a, r, lane, acc, M + log2f(S) * a.from_log2);
+    store_row(a, r, lane, acc, merged_lse(a, M, S));
 }
 
 // 16 < cp <= 64: the same row algorithm with the shards taken G at a time.
@@ -190,9 +206,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
 template <int G>
 __global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
     const int lane = threadIdx.x & 63;
-    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-    if (row >= a.rows) return;
-    const Row r = row_of(a, row);
+    const Row r = row_of(a);
     const int cp = a.cp;
 
     const int ls = lane < cp ? lane : cp - 1;
@@ -202,6 +216,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
 #pragma unroll
     for (int i = 0; i < G; ++i)
         v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(orow + min(i, cp - 1) * a.a_ss));
+    __builtin_amdgcn_sched_barrier(0);
 
     const float x = lane < cp ? xl : -INFINITY;
     float M, S;
@@ -221,7 +236,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
             fma8(acc, ws, v[i]);
         }
     }
-    store_row(a, r, lane, acc, M + log2f(S) * a.from_log2);
+    store_row(a, r, lane, acc, merged_lse(a, M, S));
 }
 
 template <int CP>
@@ -230,7 +245,8 @@ void launch_fixed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
 }
 
 hipError_t launch(const MergeArgs& a, hipStream_t stream) {
-    const dim3 grid((a.rows + kWavesPerBlock - 1) / kWavesPerBlock);
+    const int tokens = a.rows / a.h_local;
+    const dim3 grid(tokens, (a.h_local + kWavesPerBlock - 1) / kWavesPerBlock);
     switch (a.cp) {
         case 1: launch_fixed<1>(a, grid, stream); break;
         case 2: launch_fixed<2>(a, grid, stream); break;
