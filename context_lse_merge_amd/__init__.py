@@ -41,12 +41,13 @@ DCP_LSE_BHC = _C["DCP_LSE_BHC"]
 DCP_LSE_BH1 = _C["DCP_LSE_BH1"]
 DCP_DTYPE_BF16 = _C["DCP_DTYPE_BF16"]
 DCP_HEAD_DIM = _C["DCP_HEAD_DIM"]
+DCP_QK_DIM = _C["DCP_QK_DIM"]
 DCP_MAX_CP = _C["DCP_MAX_CP"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         "context_lse_merge_amd: %s is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
-        "(or python -m context_lse_merge_amd._build) first" % LIB_PATH)
+        "(or python context_lse_merge_amd/_build.py) first" % LIB_PATH)
 
 _lib = ctypes.CDLL(LIB_PATH)
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
@@ -54,10 +55,14 @@ _lib.dcp_workspace_create.argtypes = [_i64, _i32, _i32, _i32, _i32, _vp, ctypes.
 _lib.dcp_workspace_destroy.argtypes = [_vp]
 _lib.dcp_lse_combine.argtypes = [_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _i64,
                                  _i64, _vp, _i64, _vp]
+_lib.dcp_mla_partial_decode_scratch_size.argtypes = [_i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
+_lib.dcp_mla_partial_decode.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, _i64, _i32, ctypes.c_float, _i32,
+                                        _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]
 _lib.dcp_last_error.restype = ctypes.c_char_p
 _lib.dcp_status_string.argtypes = [_i32]
 _lib.dcp_status_string.restype = ctypes.c_char_p
-for _f in ("dcp_workspace_create", "dcp_workspace_destroy", "dcp_lse_combine"):
+for _f in ("dcp_workspace_create", "dcp_workspace_destroy", "dcp_lse_combine",
+           "dcp_mla_partial_decode_scratch_size", "dcp_mla_partial_decode"):
     getattr(_lib, _f).restype = _i32
 
 
@@ -179,3 +184,41 @@ def dcp_lse_combine(ws: Workspace, attn, lse, lse_layout: int, lse_mode: int, ou
         _dev_ptr(out, "out"), out.stride(0), out.stride(1),
         _dev_ptr(out_lse, "out_lse"), out_lse.stride(0) if out_lse is not None else 0, s))
     return out, out_lse
+
+
+def dcp_mla_partial_decode_scratch_size(B: int, hq: int, kv_tokens: int, cp: int) -> int:
+    """Bytes of scratch dcp_mla_partial_decode needs for this shape (0: none)."""
+    n = _sz()
+    _check(_lib.dcp_mla_partial_decode_scratch_size(B, hq, kv_tokens, cp, ctypes.byref(n)))
+    return n.value
+
+
+def dcp_mla_partial_decode(q, kv, cp: int, softmax_scale: float, lse_mode: int, o_part, lse_part, scratch=None,
+                           stream=None):
+    """Per-shard MLA decode partials.  ``q`` [B, hq, 576] bf16, ``kv`` [T, 576] bf16,
+    ``o_part`` [B, cp*hq, 512] bf16, ``lse_part`` [B, cp*hq] fp32, ``scratch`` a GPU
+    tensor of at least dcp_mla_partial_decode_scratch_size() bytes (or None when 0)."""
+    import torch
+    if q.dim() != 3 or kv.dim() != 2 or o_part.dim() != 3 or lse_part.dim() != 2:
+        raise ValueError("q [B,hq,576], kv [T,576], o_part [B,cp*hq,512], lse_part [B,cp*hq] expected")
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16 or o_part.dtype != torch.bfloat16:
+        raise ValueError("q, kv and o_part must be bfloat16")
+    if lse_part.dtype != torch.float32:
+        raise ValueError("lse_part must be float32")
+    B, hq, dqk = q.shape
+    T = kv.shape[0]
+    if dqk != DCP_QK_DIM or kv.shape[1] != DCP_QK_DIM:
+        raise ValueError("q and kv rows must have %d columns" % DCP_QK_DIM)
+    if tuple(o_part.shape) != (B, cp * hq, DCP_HEAD_DIM) or tuple(lse_part.shape) != (B, cp * hq):
+        raise ValueError("o_part must be [B, cp*hq, %d] and lse_part [B, cp*hq]" % DCP_HEAD_DIM)
+    if q.stride(2) != 1 or kv.stride(1) != 1 or o_part.stride(2) != 1 or lse_part.stride(1) != 1:
+        raise ValueError("innermost strides must be 1")
+    nbytes = 0
+    if scratch is not None:
+        nbytes = scratch.numel() * scratch.element_size()
+    s = _stream_handle(stream)
+    _check(_lib.dcp_mla_partial_decode(
+        _dev_ptr(q, "q"), B, hq, q.stride(0), q.stride(1), _dev_ptr(kv, "kv") if T > 0 else None, T, kv.stride(0),
+        cp, float(softmax_scale), lse_mode, _dev_ptr(o_part, "o_part"), o_part.stride(0), o_part.stride(1),
+        _dev_ptr(lse_part, "lse_part"), lse_part.stride(0), _dev_ptr(scratch, "scratch"), nbytes, s))
+    return o_part, lse_part

@@ -1,6 +1,6 @@
 """Build libdcp.so (the HIP library behind include/dcp.h) in-tree for gfx950.
 
-``python -m context_lse_merge_amd._build`` or ``build()`` compiles every source
+``python context_lse_merge_amd/_build.py`` or ``build()`` compiles every source
 under ``csrc/`` with hipcc.  Packed-FP32 instructions are switched off for all
 device code (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
 """
@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdcp.so")
 ARCH = "gfx950"
 
-SOURCES = ["dcp_host.cpp", "merge.hip"]
+SOURCES = ["dcp_host.cpp", "merge.hip", "mla_decode.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",

@@ -198,9 +198,150 @@ MergeArgs chunk_args(const MergePlan& plan, int64_t k) {
     return a;
 }
 
+// ------------------------------------------------------------- MLA decode plan
+//
+// Split-KV: with B*hq query rows in workgroups of 64 and cp shards there are
+// ceil(B*hq/64)*cp units of work -- 8 at B = 1 with 128 heads and cp = 4, far
+// too few for 256 compute units.  Each shard's keys are therefore split into
+// nsplit ranges processed by separate workgroups, whose fp32 partials (running
+// max, running sum, unnormalised output) are reduced afterwards; the split
+// count aims at about kMlaTargetBlocks workgroups and never gives a split
+// fewer than kMlaMinSplitKeys keys.
+
+void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* split_len, size_t* scratch_bytes) {
+    const int64_t rows = B * hq;
+    const int64_t row_blocks = (rows + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
+    const int64_t shard_max = (T + cp - 1) / cp;  // longest shard
+    int64_t n = 1;
+    if (row_blocks > 0 && shard_max > 0) {
+        const int64_t base = row_blocks * cp;
+        n = (kMlaTargetBlocks + base - 1) / base;
+        const int64_t n_max = (shard_max + kMlaMinSplitKeys - 1) / kMlaMinSplitKeys;
+        if (n > n_max) n = n_max;
+        if (n < 1) n = 1;
+    }
+    int64_t len = (shard_max + n - 1) / n;
+    len = ((len + kMlaKeysPerTile - 1) / kMlaKeysPerTile) * kMlaKeysPerTile;
+    if (len < kMlaKeysPerTile) len = kMlaKeysPerTile;
+    if (shard_max > 0) n = (shard_max + len - 1) / len;  // no split beyond the longest shard
+    *nsplit = static_cast<int32_t>(n);
+    *split_len = len;
+    if (n <= 1) {
+        *scratch_bytes = 0;
+    } else {
+        const int64_t parts = static_cast<int64_t>(cp) * n * rows;
+        const int64_t o_bytes = parts * kMlaVDim * 4;
+        *scratch_bytes = static_cast<size_t>(o_bytes + parts * 2 * 4);
+    }
+}
+
+int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv, int64_t T, int64_t kv_st,
+             int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb, int64_t o_sh, float* lse,
+             int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan) {
+    const char* fn = "dcp_mla_partial_decode";
+    if (B < 0 || hq < 1 || T < 0)
+        return fail(DCP_ERR_INVALID_ARG, "%s: need B >= 0, hq >= 1, kv_tokens >= 0 (got %lld, %d, %lld)", fn,
+                    (long long)B, hq, (long long)T);
+    if (cp < 1 || cp > DCP_MAX_CP)
+        return fail(DCP_ERR_INVALID_ARG, "%s: cp = %d is outside [1, %d]", fn, cp, DCP_MAX_CP);
+    if (lse_mode != DCP_LSE_BASE_E && lse_mode != DCP_LSE_BASE_2)
+        return fail(DCP_ERR_INVALID_ARG, "%s: lse_mode %d is neither DCP_LSE_BASE_E nor DCP_LSE_BASE_2", fn,
+                    lse_mode);
+    if (!(softmax_scale > 0.0f) || std::isinf(softmax_scale))
+        return fail(DCP_ERR_INVALID_ARG, "%s: softmax_scale must be a positive finite number", fn);
+    if (B * static_cast<int64_t>(hq) > (int64_t{1} << 30))
+        return fail(DCP_ERR_INVALID_ARG, "%s: B * hq = %lld query rows exceeds 2^30", fn, (long long)(B * hq));
+    if (B == 0) {
+        *plan = MlaPlan{};
+        return ok();
+    }
+    if (!q || !o || !lse || (T > 0 && !kv))
+        return fail(DCP_ERR_INVALID_ARG, "%s: q, o_part, lse_part (and kv when kv_tokens > 0) must be non-null", fn);
+    if (q_sb < 0 || q_sh < 0 || kv_st < 0 || o_sb < 0 || o_sh < 0 || lse_sb < 0)
+        return fail(DCP_ERR_LAYOUT, "%s: strides must be non-negative", fn);
+    const int64_t H = static_cast<int64_t>(cp) * hq;
+    if (!rows_disjoint(B, o_sb, H, o_sh, kMlaVDim))
+        return fail(DCP_ERR_LAYOUT, "%s: o_part rows overlap (o_sb = %lld, o_sh = %lld)", fn, (long long)o_sb,
+                    (long long)o_sh);
+    if (!rows_disjoint(B, lse_sb, H, 1, 1))
+        return fail(DCP_ERR_LAYOUT, "%s: lse_sb = %lld < cp*hq = %lld makes lse_part rows overlap", fn,
+                    (long long)lse_sb, (long long)H);
+    if (!aligned(q, 16) || !aligned(o, 16) || (kv && !aligned(kv, 16)))
+        return fail(DCP_ERR_ALIGN, "%s: q, kv and o_part must be 16-byte aligned", fn);
+    if (q_sb % 8 || q_sh % 8 || kv_st % 8 || o_sb % 8 || o_sh % 8)
+        return fail(DCP_ERR_ALIGN, "%s: q_sb, q_sh, kv_st, o_sb and o_sh must be multiples of 8 elements", fn);
+    if (!aligned(lse, 4)) return fail(DCP_ERR_ALIGN, "%s: lse_part must be 4-byte aligned", fn);
+
+    int32_t nsplit;
+    int64_t split_len;
+    size_t need;
+    mla_split(B, hq, T, cp, &nsplit, &split_len, &need);
+    if (need > 0 && (!scratch || scratch_bytes < need))
+        return fail(DCP_ERR_WORKSPACE, "%s: needs %zu bytes of scratch (dcp_mla_partial_decode_scratch_size), got %zu",
+                    fn, need, scratch ? scratch_bytes : size_t{0});
+    if (need > 0 && !aligned(scratch, 16)) return fail(DCP_ERR_ALIGN, "%s: scratch must be 16-byte aligned", fn);
+
+    const Extent e_q = extent(q, B, q_sb, hq, q_sh, kMlaQkDim, 2);
+    const Extent e_kv = T > 0 ? extent(kv, T, kv_st, 1, 0, kMlaQkDim, 2) : Extent{0, 0};
+    const Extent e_o = extent(o, B, o_sb, H, o_sh, kMlaVDim, 2);
+    const Extent e_l = extent(lse, B, lse_sb, 1, 0, H, 4);
+    if (overlaps(e_o, e_q) || overlaps(e_o, e_kv) || overlaps(e_l, e_q) || overlaps(e_l, e_kv) ||
+        overlaps(e_l, e_o))
+        return fail(DCP_ERR_INVALID_ARG, "%s: o_part / lse_part overlap an input or each other", fn);
+    if (need > 0) {
+        const Extent e_s{reinterpret_cast<uintptr_t>(scratch), reinterpret_cast<uintptr_t>(scratch) + need};
+        if (overlaps(e_s, e_q) || overlaps(e_s, e_kv) || overlaps(e_s, e_o) || overlaps(e_s, e_l))
+            return fail(DCP_ERR_INVALID_ARG, "%s: scratch overlaps an input or an output", fn);
+    }
+
+    MlaArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.kv = static_cast<const uint16_t*>(kv);
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    a.q_sb = q_sb;
+    a.q_sh = q_sh;
+    a.kv_st = kv_st;
+    a.o_sb = o_sb;
+    a.o_sh = o_sh;
+    a.lse_sb = lse_sb;
+    a.T = T;
+    a.split_len = split_len;
+    a.rows = static_cast<int32_t>(B * hq);
+    a.hq = hq;
+    a.cp = cp;
+    a.nsplit = nsplit;
+    a.row_blocks = (a.rows + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
+    a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+    a.lse_scale = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;
+    if (nsplit > 1) {
+        const int64_t parts = static_cast<int64_t>(cp) * nsplit * a.rows;
+        a.part_o = static_cast<float*>(scratch);
+        a.part_ml = static_cast<float*>(scratch) + parts * kMlaVDim;
+    }
+    plan->args = a;
+    plan->scratch_bytes = need;
+    plan->blocks = static_cast<int64_t>(a.row_blocks) * cp * nsplit;
+    return ok();
+}
+
 }  // namespace dcp
 
 extern "C" {
+
+int dcp_mla_partial_decode_scratch_size(int64_t B, int hq, int64_t kv_tokens, int cp, size_t* bytes) {
+    if (!bytes) return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_mla_partial_decode_scratch_size: bytes is null");
+    if (B < 0 || hq < 1 || kv_tokens < 0 || cp < 1 || cp > DCP_MAX_CP)
+        return dcp::fail(DCP_ERR_INVALID_ARG,
+                         "dcp_mla_partial_decode_scratch_size: need B >= 0, hq >= 1, kv_tokens >= 0, 1 <= cp <= %d",
+                         DCP_MAX_CP);
+    if (B * static_cast<int64_t>(hq) > (int64_t{1} << 30))
+        return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_mla_partial_decode_scratch_size: B * hq exceeds 2^30");
+    int32_t n;
+    int64_t len;
+    dcp::mla_split(B, hq, kv_tokens, cp, &n, &len, bytes);
+    return dcp::ok();
+}
 
 int dcp_workspace_create(int64_t capacity_tokens, int h_local, int cp, int d, int dtype, void* hip_stream,
                          dcp_workspace** ws) {

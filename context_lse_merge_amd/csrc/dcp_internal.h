@@ -75,4 +75,49 @@ int plan_merge(const dcp_workspace* ws, const void* attn, int64_t B, int H, int6
 // Arguments of chunk k of a plan (token range [k*chunk, min((k+1)*chunk, B))).
 MergeArgs chunk_args(const MergePlan& plan, int64_t k);
 
+// ---------------------------------------------------------------- MLA decode
+
+constexpr int kMlaQkDim = DCP_QK_DIM;   // 576 query/key columns
+constexpr int kMlaVDim = DCP_HEAD_DIM;  // 512 value columns
+constexpr int kMlaRowsPerBlock = 64;    // query rows per workgroup
+constexpr int kMlaKeysPerTile = 32;     // keys per LDS tile
+constexpr int kMlaTargetBlocks = 256;   // split the KV until about this many workgroups (one per CU)
+constexpr int kMlaMinSplitKeys = 256;   // ... but never below this many keys per split
+
+// Kernel parameters of the MLA split-KV decode.  Query row r = b*hq + h.
+// The keys of shard s are [floor(s*T/cp), floor((s+1)*T/cp)); split p of a
+// shard covers its keys [p*split_len, (p+1)*split_len).
+struct MlaArgs {
+    const uint16_t* q;      // row r at q + b*q_sb + h*q_sh, 576 columns
+    const uint16_t* kv;     // token t at kv + t*kv_st, 576 columns
+    uint16_t* o;            // (b, s*hq + h) at o + b*o_sb + (s*hq + h)*o_sh, 512 columns
+    float* lse;             // (b, s*hq + h) at lse + b*lse_sb + s*hq + h
+    float* part_o;          // [cp*nsplit][rows][512] unnormalised fp32 (nsplit > 1)
+    float* part_ml;         // [cp*nsplit][rows][2]: running max (log2 units) and sum
+    int64_t q_sb, q_sh, kv_st, o_sb, o_sh, lse_sb;
+    int64_t T;
+    int64_t split_len;      // multiple of kMlaKeysPerTile
+    int32_t rows;           // B * hq
+    int32_t hq;
+    int32_t cp;
+    int32_t nsplit;
+    int32_t row_blocks;     // ceil(rows / kMlaRowsPerBlock)
+    float scale_log2;       // softmax_scale * log2 e
+    float lse_scale;        // lse = log2-domain LSE * lse_scale (1 for base 2, ln 2 for base e)
+};
+
+struct MlaPlan {
+    MlaArgs args;
+    size_t scratch_bytes;   // needed scratch (0 when nsplit == 1)
+    int64_t blocks;         // workgroups of the main kernel (0: nothing to do)
+};
+
+// Split decision and scratch size; pure arithmetic on the shape.
+void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* split_len, size_t* scratch_bytes);
+
+// Validate every argument of dcp_mla_partial_decode and build its plan.
+int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv, int64_t T, int64_t kv_st,
+             int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb, int64_t o_sh, float* lse,
+             int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan);
+
 }  // namespace dcp

@@ -62,7 +62,8 @@ extern "C" {
 /* Element types. */
 #define DCP_DTYPE_BF16 0
 
-#define DCP_HEAD_DIM 512
+#define DCP_HEAD_DIM 512 /* value / merged head dimension (the MLA kv_lora_rank)   */
+#define DCP_QK_DIM 576   /* query/key columns of the MLA decode: 512 latent + 64 rope */
 #define DCP_MAX_CP 64
 
 typedef struct dcp_workspace dcp_workspace;
@@ -120,6 +121,49 @@ int dcp_workspace_destroy(dcp_workspace* ws);
 int dcp_lse_combine(dcp_workspace* ws, const void* attn, int64_t B, int H, int64_t attn_sb, int64_t attn_sh,
                     const float* lse, int lse_layout, int64_t l0, int64_t l1, int64_t l2, int lse_mode, void* out,
                     int64_t out_sb, int64_t out_sh, float* out_lse, int64_t out_lse_sb, void* hip_stream);
+
+/*
+ * MLA split-KV decode partials: the producer of the shard partials that
+ * dcp_lse_combine merges.  Each DCP shard owns a contiguous slice of the
+ * latent KV cache and runs decode attention for every query head over its own
+ * tokens, returning the partial output and its LSE ("[DCP] Optimize shared
+ * Output, Query, and Indexer/Top-K via peer memory", sglang PR #32851, commit
+ * log: KV tokens are owned by DCP ranks and the attention backend returns the
+ * LSE for the cross-rank combine).  In the MLA absorbed form the key is the
+ * whole 576-column cached row (512 latent + 64 rope columns) and the value is
+ * its first 512 columns ("[Attention] Add direct symmetric-memory DCP A2A",
+ * vLLM PR #48897, review thread: head_dim = kv_lora_rank = 512).
+ *
+ * For query row (b, h) and shard s, with the shard's tokens
+ * t in [floor(s*T/cp), floor((s+1)*T/cp)):
+ *     z_t = softmax_scale * <q[b,h,:], kv[t,:]>          (576 columns)
+ *     o_part[b, s*hq + h, :] = sum_t softmax(z)_t * kv[t, 0:512]
+ *     lse_part[b, s*hq + h]  = ln sum_t exp(z_t)   (DCP_LSE_BASE_E)
+ *                            = log2 sum_t exp(z_t) (DCP_LSE_BASE_2)
+ * A shard with no tokens gives o_part = 0 and lse_part = -inf.  The outputs
+ * are laid out so that dcp_lse_combine with H = cp*hq, h_local = hq and
+ * DCP_LSE_BH1 (l0 = lse_sb, l1 = 1) merges the shards into exact attention
+ * over all T tokens.
+ *
+ * q         [B, hq, 576] bf16, row (b, h) at q + b*q_sb + h*q_sh.
+ * kv        [T, 576] bf16, token t at kv + t*kv_st (one cache shared by all
+ *           B query tokens).  May be NULL when T == 0.
+ * o_part    [B, cp*hq, 512] bf16, row (b, s*hq + h) at o_part + b*o_sb + (s*hq+h)*o_sh.
+ * lse_part  [B, cp*hq] fp32 at lse_part + b*lse_sb + s*hq + h.
+ * scratch   device buffer of at least dcp_mla_partial_decode_scratch_size()
+ *           bytes for the split-KV partials (fp32); NULL allowed when that
+ *           size is 0.  Contents on entry are ignored.
+ * Arithmetic: bf16 MFMA products with fp32 accumulation for q.k and p.v,
+ * fp32 online softmax; p is rounded to bf16 before the p.v product.
+ * Alignment: q, kv, o_part 16-byte aligned; q_sb, q_sh, kv_st, o_sb, o_sh
+ * multiples of 8 elements; lse_part 4-byte aligned.
+ */
+int dcp_mla_partial_decode_scratch_size(int64_t B, int hq, int64_t kv_tokens, int cp, size_t* bytes);
+
+int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv,
+                           int64_t kv_tokens, int64_t kv_st, int cp, float softmax_scale, int lse_mode,
+                           void* o_part, int64_t o_sb, int64_t o_sh, float* lse_part, int64_t lse_sb, void* scratch,
+                           size_t scratch_bytes, void* hip_stream);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char* dcp_last_error(void);
