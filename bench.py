@@ -53,6 +53,8 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-hot", action="store_true", help="skip the hot-cache figure")
+    p.add_argument("--no-producer", action="store_true", help="skip the MLA producer (B = 1, 8, 32, 64) leg")
+    p.add_argument("--producer-B", type=int, nargs="*", default=[1, 8, 32, 64])
     p.add_argument("--calibrate", action="store_true",
                    help="also run a plain 256 MiB elementwise copy kernel (reference for HBM byte counters)")
     return p.parse_args()
@@ -232,6 +234,73 @@ def cpu_baseline(case, seconds):
     return med * 1e6, threads, len(times), model
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16, published
+
+
+def producer_flops(B, hq, T):
+    """q.k over 576 columns and p.v over 512, per query row per key."""
+    return 2.0 * B * hq * T * (576 + 512)
+
+
+def measure_producer(B, kv_copies, reps=10):
+    """dcp_mla_partial_decode (+ the merge of its output) on the full-size MLA
+    decode workload: q [B,128,576], one 131072 x 576 cache, 4 shards.  The cache
+    is rotated over `kv_copies` device copies (>= 1 GiB together) so every call
+    reads it from HBM.  Returns (producer us, merge us)."""
+    import torch
+    import context_lse_merge_amd as dcp
+    import synth
+    dev = torch.device("cuda:0")
+    hq, cp, T = 128, 4, kv_copies[0].shape[0]
+    q = synth.normal_bf16((B, hq, 576), synth.gen(3000 + B)).to(dev)
+    o = torch.empty((B, cp * hq, 512), dtype=torch.bfloat16, device=dev)
+    l = torch.empty((B, cp * hq), dtype=torch.float32, device=dev)
+    out = torch.empty((B, hq, 512), dtype=torch.bfloat16, device=dev)
+    out_lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    nbytes = dcp.dcp_mla_partial_decode_scratch_size(B, hq, T, cp)
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    ws = dcp.dcp_workspace_create(B, hq, cp)
+    for k in range(2):
+        dcp.dcp_mla_partial_decode(q, kv_copies[k % len(kv_copies)], cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l,
+                                   scratch)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps + 1)]
+    ev[0].record()
+    for r in range(reps):
+        dcp.dcp_mla_partial_decode(q, kv_copies[r % len(kv_copies)], cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o,
+                                   l, scratch)
+        ev[2 * r + 1].record()
+        dcp.dcp_lse_combine(ws, o, l, dcp.DCP_LSE_BH1, dcp.DCP_LSE_BASE_E, out, out_lse)
+        ev[2 * r + 2].record()
+    torch.cuda.synchronize()
+    prod = sorted(ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(reps))
+    merge = sorted(ev[2 * r + 1].elapsed_time(ev[2 * r + 2]) for r in range(reps))
+    ws.close()
+    return prod[reps // 2] * 1000.0, merge[reps // 2] * 1000.0
+
+
+def producer_leg(Bs):
+    import torch
+    import synth
+    _, kv = synth.mla_decode(1)
+    kv_dev = kv.to("cuda:0")
+    copies = [kv_dev] + [kv_dev.clone() for _ in range(7)]   # 8 x 151 MB
+    rows = []
+    for B in Bs:
+        us, us_m = measure_producer(B, copies)
+        fl = producer_flops(B, 128, kv.shape[0])
+        tflops = fl / (us * 1e-6) / 1e12
+        kv_gbs = kv.numel() * 2 / (us * 1e-6) / 1e9
+        rows.append({"B": B, "producer_us": round(us, 1), "merge_us": round(us_m, 3),
+                     "TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "kv_GBps": round(kv_gbs, 1), "flop": fl})
+        print("[bench] producer B=%d: %.1f us (%.1f TFLOP/s, %.1f%% of bf16 peak), merge %.2f us"
+              % (B, us, tflops, 100 * tflops / MFMA_BF16_PEAK_TFLOPS, us_m), file=sys.stderr, flush=True)
+    del copies, kv_dev
+    torch.cuda.empty_cache()
+    return rows
+
+
 CALIBRATION_BYTES = 256 << 20
 
 
@@ -314,6 +383,7 @@ def main():
                "sample": "%d whole layer-merges of the same workload (fp64 C oracle, OpenMP over rows, %s); "
                          "median" % (reps, model or "host CPU")}
 
+    producer = [] if args.no_producer else producer_leg(args.producer_B)
     if args.calibrate:
         calibration_copy()
     traffic = counters_traffic()
@@ -344,6 +414,10 @@ def main():
                      "algorithmic_bytes_per_launch": alg // max(1, math.ceil(case.B / capacity))},
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "producer": {"workload": "MLA split-KV decode, q [B,128,576] bf16, latent KV cache 131072 x 576 bf16 in "
+                                 "4 contiguous shards, scale 1/sqrt(192), then the merge of its partials",
+                     "bound": "mfma (B >= 2), hbm (B = 1)", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                     "rows": producer},
     }
     print(json.dumps(line), flush=True)
     return 0

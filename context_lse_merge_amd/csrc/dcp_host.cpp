@@ -218,6 +218,7 @@ void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* s
         n = (kMlaTargetBlocks + base - 1) / base;
         const int64_t n_max = (shard_max + kMlaMinSplitKeys - 1) / kMlaMinSplitKeys;
         if (n > n_max) n = n_max;
+        if (n > kMlaMaxSplits) n = kMlaMaxSplits;
         if (n < 1) n = 1;
     }
     int64_t len = (shard_max + n - 1) / n;
@@ -271,6 +272,10 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     if (q_sb % 8 || q_sh % 8 || kv_st % 8 || o_sb % 8 || o_sh % 8)
         return fail(DCP_ERR_ALIGN, "%s: q_sb, q_sh, kv_st, o_sb and o_sh must be multiples of 8 elements", fn);
     if (!aligned(lse, 4)) return fail(DCP_ERR_ALIGN, "%s: lse_part must be 4-byte aligned", fn);
+    // Offsets inside one key tile are 32-bit element counts.
+    if (kv_st > ((int64_t{1} << 31) - kMlaQkDim) / kMlaKeysPerTile)
+        return fail(DCP_ERR_LAYOUT, "%s: kv_st = %lld is too large (at most %lld elements)", fn, (long long)kv_st,
+                    (long long)(((int64_t{1} << 31) - kMlaQkDim) / kMlaKeysPerTile));
 
     int32_t nsplit;
     int64_t split_len;

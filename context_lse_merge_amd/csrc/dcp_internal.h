@@ -79,10 +79,11 @@ MergeArgs chunk_args(const MergePlan& plan, int64_t k);
 
 constexpr int kMlaQkDim = DCP_QK_DIM;   // 576 query/key columns
 constexpr int kMlaVDim = DCP_HEAD_DIM;  // 512 value columns
-constexpr int kMlaRowsPerBlock = 64;    // query rows per workgroup
+constexpr int kMlaRowsPerBlock = 128;   // query rows per workgroup
 constexpr int kMlaKeysPerTile = 32;     // keys per LDS tile
 constexpr int kMlaTargetBlocks = 256;   // split the KV until about this many workgroups (one per CU)
 constexpr int kMlaMinSplitKeys = 256;   // ... but never below this many keys per split
+constexpr int kMlaMaxSplits = 64;       // ... nor above this many splits (one lane each in the reduction)
 
 // Kernel parameters of the MLA split-KV decode.  Query row r = b*hq + h.
 // The keys of shard s are [floor(s*T/cp), floor((s+1)*T/cp)); split p of a

@@ -13,28 +13,38 @@
 // Mapping to CDNA4.  Every query token attends over the same cache, so one
 // shard is a flash-attention pass over M = B*hq query rows: a dense
 // contraction, run on MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
-//  * A workgroup owns 64 query rows (16 per wavefront) and one key range (a
-//    split of one shard).  Each wavefront keeps its 16 query rows in registers
-//    for the whole kernel, as 18 MFMA operand fragments of 32 columns.
-//  * Keys stream through LDS 32 at a time, twice: row-major (for q.k) and
-//    transposed (value column-major, for p.v), so every MFMA operand is read
-//    as contiguous 8- or 16-byte LDS words.  The next tile's global loads are
-//    issued before the current tile's MFMAs.
+//  * A workgroup owns 128 query rows, 16 per wavefront, 8 wavefronts (two per
+//    SIMD, so one wavefront's softmax and waits overlap the other's MFMAs),
+//    and one key range (a split of one shard).  Each wavefront keeps its 16
+//    query rows in registers for the whole kernel, as 18 MFMA operand
+//    fragments of 32 columns.
+//  * Keys stream through LDS 32 at a time, row-major, double-buffered (one
+//    barrier per tile).  Tiles are copied global -> LDS by the gfx950 direct
+//    loads (global_load_lds_dwordx4), issued a whole tile ahead, with no
+//    register staging.  The 16-byte chunks of each LDS row are XOR-swizzled
+//    by sigma(key) = 2 (key & 3) | ((key >> 2) & 1), which makes both operand
+//    reads below free of bank conflicts.
 //  * The wavefront computes S^T = K Q^T (A = K, B = Q^T) and O^T += V^T P^T
 //    (A = V^T, B = P^T).  In this orientation a lane holds eight scores of
 //    query row lane % 16 and, with the k index of p.v permuted the same way in
 //    V^T and P^T, exactly the B operand of the p.v MFMA: no shuffle between
 //    the two products, and the running max/sum of row lane % 16 sit in the
-//    same lanes as that row's output accumulators.
+//    same lanes as that row's output accumulators.  The q.k operand is read
+//    as 16-byte LDS words; the p.v operand, which needs the value transposed,
+//    is read from the same row-major tile with the transpose load
+//    ds_read_b64_tr_b16: within each 16-lane group it returns lane j element
+//    i of the 8-byte chunk lane 4i + j/4 pointed at, so lanes pointing at
+//    V[key][d0 + 4(j%4)] of four keys receive a column of V^T.
 //  * Online softmax in base 2 (scale * log2 e folded into one multiply); the
 //    row max is a 4-lane reduction per tile, the row sum stays lane-partial
-//    until the end.  p is rounded to bf16 for the p.v MFMA; the sum uses the
-//    fp32 p.
+//    until the end, and the output accumulators are rescaled only on tiles
+//    where some row's maximum grew.  p is rounded to bf16 for the p.v MFMA;
+//    the sum uses the fp32 p.
 //  * Split-KV: shards are split into key ranges so that about 256 workgroups
 //    (one per compute unit) exist even at B = 1; each split leaves an fp32
 //    partial (running max, running sum, unnormalised output) in the scratch
-//    buffer and a second kernel reduces them.  With a single split the first kernel
-//    writes the final bf16 output and LSE itself.
+//    buffer and a second kernel reduces them.  With a single split the first
+//    kernel writes the final bf16 output and LSE itself.
 //  * Workgroups that share a key range are placed on the same XCD (block ids
 //    are dealt round-robin over the 8 XCDs), so a KV tile is fetched from HBM
 //    about once per XCD-L2 rather than once per workgroup.
@@ -50,34 +60,43 @@ namespace {
 
 constexpr int kDqk = kMlaQkDim;                  // 576
 constexpr int kDv = kMlaVDim;                    // 512
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 16;
 constexpr int kKeys = kMlaKeysPerTile;           // 32
-constexpr int kKStride = kDqk + 8;               // padded LDS row of K (elements)
-constexpr int kVStride = kKeys + 4;              // padded LDS row of V^T (elements)
+constexpr int kRowChunks = kDqk / 8;             // 72 chunks of 16 bytes per K row
+constexpr int kTileChunks = kKeys * kRowChunks;  // 2304 per tile
+constexpr int kTileElems = kKeys * kDqk;
+constexpr int kDmaPerTile = kTileChunks / 64;    // 36 wavefront-wide 1 KiB copies
 constexpr int kQSteps = kDqk / 32;               // 18 fragments of 32 columns
 constexpr int kDTiles = kDv / 16;                // 32 output tiles of 16 columns
-constexpr int kChunks = kKeys * kDqk / 8;        // 16-byte pieces of one K tile
-constexpr int kChunksPerThread = kChunks / kThreads;
 constexpr int kXcds = 8;
 
 static_assert(kRowsPerWave * kWaves == kMlaRowsPerBlock, "rows per workgroup");
-static_assert(kChunks % kThreads == 0, "K tile pieces per thread");
+static_assert(kTileChunks % 64 == 0, "a tile is whole 1 KiB wavefront copies");
+static_assert(kRowChunks % 8 == 0, "the chunk swizzle stays inside the row");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-struct __align__(16) Smem {
-    uint16_t k[kKeys * kKStride];  // K tile, row-major: key x 576 (+8 pad)
-    uint16_t vt[kDv * kVStride];   // value part transposed: 512 x key (+4 pad)
-};
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Swizzle of the 16-byte chunks of LDS row `key`: logical chunk c lives at
+// physical chunk c ^ sigma(key).  Eight consecutive keys get eight different
+// sigma, and the four keys 4g..4g+3 get 2q | (g & 1).
+__device__ __forceinline__ int sigma(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
 
 __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Transpose load of 8 bytes at LDS element offset `off` of `base`.
+__device__ __forceinline__ bf16x4 ds_read_tr(const uint16_t* base, int off) {
+    auto p = (const __attribute__((address_space(3))) char*)(base) + 2 * off;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
 
 // Which (row block, shard, split) a workgroup computes.  Block ids are dealt
 // round-robin over the XCDs; consecutive work items -- the row blocks of one
@@ -98,45 +117,136 @@ __device__ __forceinline__ Work work_of(const MlaArgs& a) {
     return k;
 }
 
-// Global -> registers: piece c = tid + kThreads*i of the K tile starting at
-// key t0 is key c % kKeys, columns [8*(c / kKeys), +8).  Keys at or past k1
-// re-read key k1 - 1 (their scores are masked).
-__device__ __forceinline__ void load_tile(const MlaArgs& a, int64_t t0, int64_t k1, int tid,
-                                          u32x4 (&r)[kChunksPerThread]) {
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-        const int c = tid + kThreads * i;
-        const int key = c % kKeys;
-        const int col = 8 * (c / kKeys);
-        int64_t t = t0 + key;
-        t = t < k1 ? t : k1 - 1;
-        r[i] = *reinterpret_cast<const u32x4*>(a.kv + t * a.kv_st + col);
-    }
+// Copy the K tile of keys [t0, t0 + 32) into LDS tile `dst` with direct
+// loads: copy i of wavefront w fills physical chunks [64 (w + 8 i), +64),
+// lane l the one at 64 (w + 8 i) + l, which holds logical chunk
+// (phys ^ sigma(key)) of key phys / 72.  `coff` keeps, per copy, the lane's
+// source offset from the tile's first key (32-bit elements).  In a ragged last
+// tile, keys at or past k1 re-read key k1 - 1 (their scores are masked).
+constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;
+
+struct DmaPlan {
+    int coff[kDmaPerWave];
+};
+
+__device__ __forceinline__ int dma_key(int copy, int lane) { return (64 * copy + lane) / kRowChunks; }
+
+__device__ __forceinline__ int dma_col(int copy, int lane) {
+    const int slot = 64 * copy + lane;
+    const int key = slot / kRowChunks;
+    return 8 * ((slot - key * kRowChunks) ^ sigma(key));
 }
 
-// Registers -> LDS, row-major and, for the 512 value columns, transposed.
-__device__ __forceinline__ void store_tile(Smem& sm, int tid, const u32x4 (&r)[kChunksPerThread]) {
+__device__ __forceinline__ DmaPlan dma_plan(const MlaArgs& a, int wave, int lane) {
+    DmaPlan d;
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-        const int c = tid + kThreads * i;
-        const int key = c % kKeys;
-        const int col = 8 * (c / kKeys);
-        *reinterpret_cast<u32x4*>(&sm.k[key * kKStride + col]) = r[i];
-        if (col < kDv) {
+    for (int i = 0; i < kDmaPerWave; ++i) {
+        const int copy = wave + kWaves * i;
+        d.coff[i] = dma_key(copy, lane) * static_cast<int>(a.kv_st) + dma_col(copy, lane);
+    }
+    return d;
+}
+
+__device__ __forceinline__ void dma_tile(const MlaArgs& a, const DmaPlan& d, uint16_t* dst, int64_t t0, int64_t k1,
+                                         int wave, int lane) {
+    const uint16_t* base = a.kv + t0 * a.kv_st;
+    const bool full = t0 + kKeys <= k1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sm.vt[(col + 2 * e) * kVStride + key] = static_cast<uint16_t>(r[i][e] & 0xFFFFu);
-                sm.vt[(col + 2 * e + 1) * kVStride + key] = static_cast<uint16_t>(r[i][e] >> 16);
+    for (int i = 0; i < kDmaPerWave; ++i) {
+        const int copy = wave + kWaves * i;
+        if (copy < kDmaPerTile) {
+            int o = d.coff[i];
+            if (!full) {
+                const int last = static_cast<int>(k1 - 1 - t0);
+                const int key = min(dma_key(copy, lane), last);
+                o = key * static_cast<int>(a.kv_st) + dma_col(copy, lane);
             }
+            __builtin_amdgcn_global_load_lds(base + o, dst + 64 * 8 * copy, 16, 0, 0);
         }
     }
 }
 
+// Wait until this wavefront's direct loads have landed, then for everyone's.
+__device__ __forceinline__ void tile_ready() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
+    __syncthreads();
+}
+
+// Per-lane LDS offsets (elements, before the tile base) of the operands.
+struct LaneOffsets {
+    int s_even, s_odd;  // q.k operand of key r16, for fragment f even / odd, before + 64 (f / 2)
+    int tr[4];          // p.v operand (low k half), output tile t with t % 4 == u, before + 64 (t / 4)
+};
+
+struct RowState {
+    f32x4 oacc[kDTiles];
+    float m_run, l_run;
+};
+
+// One 32-key tile: scores, online softmax, p.v.
+__device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* kt, const LaneOffsets& off,
+                                             const bf16x8 (&qf)[kQSteps], RowState& st, int64_t t0, int64_t k1,
+                                             int g) {
+    // S^T = K Q^T for keys [t0, t0+16) (sa) and [t0+16, t0+32) (sb): the lane
+    // holds the scores of row r16 with keys 4g+i and 16+4g+i.
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int f = 0; f < kQSteps; ++f) {
+        const int o = ((f & 1) ? off.s_odd : off.s_even) + 64 * (f >> 1);
+        const bf16x8 fa = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o));
+        const bf16x8 fb = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o + 16 * kDqk));
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, qf[f], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, qf[f], sb, 0, 0, 0);
+    }
+
+    float z[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        z[i] = (t0 + 4 * g + i < k1) ? sa[i] * a.scale_log2 : -INFINITY;
+        z[4 + i] = (t0 + 16 + 4 * g + i < k1) ? sb[i] * a.scale_log2 : -INFINITY;
+    }
+    float tmax = z[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
+    tmax = xor_max(tmax, 16);
+    tmax = xor_max(tmax, 32);
+    const float m_new = fmaxf(st.m_run, tmax);  // finite: the tile has a valid key
+    if (__any(m_new > st.m_run)) {
+        // Some row's maximum grew: rescale the accumulators (alpha = 1 for the others).
+        const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);  // 0 on the first tile
+        st.l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < kDTiles; ++t) st.oacc[t] *= alpha;
+    }
+    st.m_run = m_new;
+    float psum = 0.0f;
+    bf16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(z[i] - m_new);
+        psum += p;
+        pb[i] = static_cast<__bf16>(p);
+    }
+    st.l_run += psum;
+
+    // O^T += V^T P^T: output tile t is columns [16t, 16t+16); the k index runs
+    // over keys 4g..4g+3 and 16+4g..16+4g+3, in P^T (pb) and V^T alike.
+#pragma unroll
+    for (int t = 0; t < kDTiles; ++t) {
+        const int o = off.tr[t & 3] + 64 * (t >> 2);
+        const bf16x4 lo = ds_read_tr(kt, o);
+        const bf16x4 hi = ds_read_tr(kt, o + 16 * kDqk);
+        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        st.oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.oacc[t], 0, 0, 0);
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
-    __shared__ Smem sm;
+    __shared__ __attribute__((aligned(16))) uint16_t tile0[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t tile1[kTileElems];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15;  // query row of this lane within the wavefront
     const int g = lane >> 4;    // lane group: keys 4g..4g+3 of each 16-key half
     const Work wk = work_of(a);
@@ -146,6 +256,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     const int64_t s1 = (static_cast<int64_t>(wk.s + 1) * a.T) / a.cp;
     const int64_t k0 = s0 + static_cast<int64_t>(wk.p) * a.split_len;
     const int64_t k1 = min(k0 + a.split_len, s1);
+    const int ntiles = k0 < k1 ? static_cast<int>((k1 - k0 + kKeys - 1) / kKeys) : 0;
+    const DmaPlan dp = dma_plan(a, wave, lane);
+    if (ntiles > 0) dma_tile(a, dp, tile0, k0, k1, wave, lane);
 
     // Query row of this lane (rows past the end repeat the last row and are not stored).
     const int row_raw = wk.rb * kMlaRowsPerBlock + wave * kRowsPerWave + r16;
@@ -161,72 +274,45 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
         for (int f = 0; f < kQSteps; ++f) qf[f] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * f));
     }
 
-    f32x4 oacc[kDTiles];
+    // Operand offsets.  q.k: key r16, logical chunk 4f + g at physical
+    // (4f + g) ^ sigma(r16) = 8 (f/2) + ((4 (f%2) + g) ^ sigma(r16)).  p.v:
+    // key 4g + r16/4 (sigma = 2 (r16/4) | (g & 1)), logical column
+    // 16t + 4 (r16%4): chunk 2t + (r16%4)/2 at physical 8 (t/4) +
+    // ((2 (t%4) + (r16%4)/2) ^ sigma), plus 4 (r16 % 2) elements.
+    LaneOffsets off;
+    {
+        const int sq = sigma(r16);
+        off.s_even = r16 * kDqk + 8 * (g ^ sq);
+        off.s_odd = r16 * kDqk + 8 * ((4 + g) ^ sq);
+        const int key = 4 * g + (r16 >> 2);
+        const int sv = sigma(key);
+        const int m = (r16 & 3) >> 1;
 #pragma unroll
-    for (int t = 0; t < kDTiles; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;  // running max of row r16, log2 units
-    float l_run = 0.0f;       // lane-partial running sum of row r16
+        for (int u = 0; u < 4; ++u) off.tr[u] = key * kDqk + 8 * ((2 * u + m) ^ sv) + 4 * (r16 & 1);
+    }
 
-    u32x4 pre[kChunksPerThread];
-    if (k0 < k1) load_tile(a, k0, k1, tid, pre);
+    RowState st;
+#pragma unroll
+    for (int t = 0; t < kDTiles; ++t) st.oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m_run = -INFINITY;  // running max of row r16, log2 units
+    st.l_run = 0.0f;       // lane-partial running sum of row r16
 
-    for (int64_t t0 = k0; t0 < k1; t0 += kKeys) {
-        __syncthreads();  // the previous tile's LDS reads are done
-        store_tile(sm, tid, pre);
-        __syncthreads();
-        if (t0 + kKeys < k1) load_tile(a, t0 + kKeys, k1, tid, pre);
-
-        // S^T = K Q^T for keys [t0, t0+16) and [t0+16, t0+32): lane holds
-        // scores of row r16 with keys 4g+i and 16+4g+i.
-        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* ka = &sm.k[r16 * kKStride + 8 * g];
-        const uint16_t* kb = &sm.k[(16 + r16) * kKStride + 8 * g];
-#pragma unroll
-        for (int f = 0; f < kQSteps; ++f) {
-            const bf16x8 fa = as_bf16x8(*reinterpret_cast<const u32x4*>(ka + 32 * f));
-            const bf16x8 fb = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + 32 * f));
-            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, qf[f], sa, 0, 0, 0);
-            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, qf[f], sb, 0, 0, 0);
-        }
-
-        // Online softmax (base 2) for row r16 over this tile.
-        float z[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            z[i] = (t0 + 4 * g + i < k1) ? sa[i] * a.scale_log2 : -INFINITY;
-            z[4 + i] = (t0 + 16 + 4 * g + i < k1) ? sb[i] * a.scale_log2 : -INFINITY;
-        }
-        float tmax = z[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
-        tmax = xor_max(tmax, 16);
-        tmax = xor_max(tmax, 32);
-        const float m_new = fmaxf(m_run, tmax);            // finite: the tile has a valid key
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
-        float psum = 0.0f;
-        bf16x8 pb;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = __builtin_amdgcn_exp2f(z[i] - m_new);
-            psum += p;
-            pb[i] = static_cast<__bf16>(p);
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-
-        // O^T += V^T P^T: output tile t is columns [16t, 16t+16); the k index
-        // runs over keys 4g..4g+3 and 16+4g..16+4g+3, in P^T (pb) and V^T alike.
-#pragma unroll
-        for (int t = 0; t < kDTiles; ++t) {
-            const uint16_t* vrow = &sm.vt[(16 * t + r16) * kVStride];
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 4 * g);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 + 4 * g);
-            const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[t] * alpha, 0, 0, 0);
+    if (ntiles > 0) tile_ready();
+    for (int it = 0; it < ntiles; it += 2) {
+        const int64_t t0 = k0 + static_cast<int64_t>(it) * kKeys;
+        if (it + 1 < ntiles) dma_tile(a, dp, tile1, t0 + kKeys, k1, wave, lane);
+        compute_tile(a, tile0, off, qf, st, t0, k1, g);
+        tile_ready();
+        if (it + 1 < ntiles) {
+            if (it + 2 < ntiles) dma_tile(a, dp, tile0, t0 + 2 * kKeys, k1, wave, lane);
+            compute_tile(a, tile1, off, qf, st, t0 + kKeys, k1, g);
+            tile_ready();
         }
     }
 
     // Row sums across the four lane groups; every lane of a row ends with the same l.
+    const float l_run = st.l_run;
+    const float m_run = st.m_run;
     const float l_tot = (l_run + __shfl_xor(l_run, 16, 64)) + (__shfl_xor(l_run, 32, 64) + __shfl_xor(l_run, 48, 64));
     if (row_raw >= a.rows) return;
 
@@ -236,11 +322,12 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
         uint16_t* orow = a.o + b * a.o_sb + (static_cast<int64_t>(wk.s) * a.hq + h) * a.o_sh + 4 * g;
 #pragma unroll
         for (int t = 0; t < kDTiles; ++t) {
-            const uint32_t lo = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(oacc[t][0] * inv))) |
-                                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(oacc[t][1] * inv))) << 16);
-            const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(oacc[t][2] * inv))) |
-                                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(oacc[t][3] * inv))) << 16);
-            *reinterpret_cast<u32x2*>(orow + 16 * t) = u32x2{lo, hi};
+            const f32x4 v = st.oacc[t];
+            const uint32_t lo = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[0] * inv))) |
+                                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[1] * inv))) << 16);
+            const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2] * inv))) |
+                                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[3] * inv))) << 16);
+            *reinterpret_cast<uint2*>(orow + 16 * t) = make_uint2(lo, hi);
         }
         if (g == 0)
             a.lse[b * a.lse_sb + static_cast<int64_t>(wk.s) * a.hq + h] =
@@ -250,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
         const int64_t part = (static_cast<int64_t>(wk.s) * a.nsplit + wk.p) * a.rows + row;
         float* prow = a.part_o + part * kDv + 4 * g;
 #pragma unroll
-        for (int t = 0; t < kDTiles; ++t) *reinterpret_cast<f32x4*>(prow + 16 * t) = oacc[t];
+        for (int t = 0; t < kDTiles; ++t) *reinterpret_cast<f32x4*>(prow + 16 * t) = st.oacc[t];
         if (g == 0) {
             a.part_ml[2 * part] = l_tot > 0.0f ? m_run : -INFINITY;
             a.part_ml[2 * part + 1] = l_tot;
@@ -258,34 +345,56 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     }
 }
 
-// Reduce the nsplit partials of every (shard, row): one wavefront per row,
-// lane l owning columns [8l, 8l+8).  Grid: x = row groups of 4, y = shard.
-// M = max_p m_p, w_p = 2^(m_p - M), L = sum_p w_p l_p, O = sum_p w_p O_p / L,
-// in ascending p.  An all-empty row gives O = 0 and LSE = -inf.
+// Reduce the nsplit (<= 64) partials of every (shard, row): one wavefront
+// per row.  Lane p holds split p's running max m_p and sum l_p; the row's
+// M = max_p m_p, w_p = 2^(m_p - M) (0 for an empty split), L = sum_p w_p l_p
+// come from wavefront reductions, and then lane l accumulates columns
+// [8l, 8l+8) of sum_p w_p O_p in ascending p, loading 8 splits' payload per
+// round trip.  O = that sum / L; an all-empty row gives O = 0 and LSE = -inf.
+// Grid: x = groups of 4 rows, y = shard.
+constexpr int kReduceBatch = 8;
+
 __global__ __launch_bounds__(256) void mla_split_reduce_kernel(MlaArgs a) {
     const int lane = threadIdx.x & 63;
     const int row_raw = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int row = __builtin_amdgcn_readfirstlane(min(row_raw, a.rows - 1));
     const int s = blockIdx.y;
-    const int64_t base = static_cast<int64_t>(s) * a.nsplit * a.rows + row;  // part index of split 0
+    const int n = a.nsplit;
+    const int64_t base = static_cast<int64_t>(s) * n * a.rows + row;  // part index of split 0
 
-    float M = -INFINITY;
-    for (int p = 0; p < a.nsplit; ++p) M = fmaxf(M, a.part_ml[2 * (base + static_cast<int64_t>(p) * a.rows)]);
-    float L = 0.0f;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-        for (int p = 0; p < a.nsplit; ++p) {
-            const int64_t part = base + static_cast<int64_t>(p) * a.rows;
-            const float m = a.part_ml[2 * part];
-            if (m == -INFINITY) continue;  // empty split: its output is never read
-            const float w = __builtin_amdgcn_exp2f(m - M);
-            L += w * a.part_ml[2 * part + 1];
-            const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + part * kDv + 8 * lane);
-            const f32x4 x0 = src[0], x1 = src[1];
+    const int lp = lane < n ? lane : n - 1;
+    const int64_t my = base + static_cast<int64_t>(lp) * a.rows;
+    const float m_l = lane < n ? a.part_ml[2 * my] : -INFINITY;
+    const float l_l = a.part_ml[2 * my + 1];
+    float M = m_l;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[i] = fmaf(w, x0[i], acc[i]);
-                acc[4 + i] = fmaf(w, x1[i], acc[4 + i]);
+    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float w = (m_l == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_l - M);
+    float L = w * l_l;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off, 64);
+
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < n; p0 += kReduceBatch) {
+        f32x4 x[kReduceBatch][2];
+#pragma unroll
+        for (int i = 0; i < kReduceBatch; ++i) {
+            const int p = min(p0 + i, n - 1);
+            const f32x4* src =
+                reinterpret_cast<const f32x4*>(a.part_o + (base + static_cast<int64_t>(p) * a.rows) * kDv + 8 * lane);
+            x[i][0] = src[0];
+            x[i][1] = src[1];
+        }
+#pragma unroll
+        for (int i = 0; i < kReduceBatch; ++i) {
+            // An empty (or past-the-end) split has weight 0 and its payload is
+            // replaced by 0 (a select, so the loads above stay batched).
+            const float wp = (p0 + i < n) ? __shfl(w, p0 + i, 64) : 0.0f;
+            const bool use = wp != 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] = fmaf(wp, use ? x[i][0][e] : 0.0f, acc[e]);
+                acc[4 + e] = fmaf(wp, use ? x[i][1][e] : 0.0f, acc[4 + e]);
             }
         }
     }
