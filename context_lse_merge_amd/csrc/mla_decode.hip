@@ -18,10 +18,10 @@
 //    and one key range (a split of one shard).  Each wavefront keeps its 16
 //    query rows in registers for the whole kernel, as 18 MFMA operand
 //    fragments of 32 columns.
-//  * Keys stream through LDS 32 at a time, row-major, double-buffered (one
+//  * Keys stream through LDS 32 at a time, row-major, in three buffers (one
 //    barrier per tile).  Tiles are copied global -> LDS by the gfx950 direct
-//    loads (global_load_lds_dwordx4), issued a whole tile ahead, with no
-//    register staging.  The 16-byte chunks of each LDS row are XOR-swizzled
+//    loads (global_load_lds_dwordx4), issued two tiles ahead, with no
+//    register staging; each barrier waits only for the older tile.  The 16-byte chunks of each LDS row are XOR-swizzled
 //    by sigma(key) = 2 (key & 3) | ((key >> 2) & 1), which makes both operand
 //    reads below free of bank conflicts.
 //  * The wavefront computes S^T = K Q^T (A = K, B = Q^T) and O^T += V^T P^T
@@ -117,58 +117,71 @@ __device__ __forceinline__ Work work_of(const MlaArgs& a) {
     return k;
 }
 
+// A value the compiler must treat as unknown: addresses derived from it are
+// recomputed where they are used instead of being hoisted out of the key loop
+// and kept (or spilled) across it -- registers are the scarce resource here.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // Copy the K tile of keys [t0, t0 + 32) into LDS tile `dst` with direct
 // loads: copy i of wavefront w fills physical chunks [64 (w + 8 i), +64),
 // lane l the one at 64 (w + 8 i) + l, which holds logical chunk
-// (phys ^ sigma(key)) of key phys / 72.  `coff` keeps, per copy, the lane's
-// source offset from the tile's first key (32-bit elements).  In a ragged last
-// tile, keys at or past k1 re-read key k1 - 1 (their scores are masked).
+// (phys ^ sigma(key)) of key phys / 72.  In a ragged last tile, keys at or
+// past k1 re-read key k1 - 1 (their scores are masked).
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS
+// byte address lds + 16 l.  Issued as inline assembly so that the compiler
+// does not track it: its automatic waits would otherwise stall every tile on
+// the copies just issued (it cannot tell which LDS buffer they write).  The
+// kernel therefore waits for these copies itself (vmcnt) before the barrier
+// that publishes a tile; nothing else in the key loop issues vector memory
+// instructions.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+    return static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)(p)));
+}
+
+__device__ __forceinline__ void lds_dma16(const uint16_t* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
+}
+
 constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;
+// Every wavefront issues kDmaPerWave copies per tile, so its count of
+// outstanding tile copies is always a multiple of kDmaPerWave; the copies past
+// the tile's end refill a slack area behind it with the tile's last row.
+constexpr int kTileSlack = (kDmaPerWave * kWaves - kDmaPerTile) * 64 * 8;  // elements
+constexpr int kTileAlloc = kTileElems + kTileSlack;
 
-struct DmaPlan {
-    int coff[kDmaPerWave];
-};
-
-__device__ __forceinline__ int dma_key(int copy, int lane) { return (64 * copy + lane) / kRowChunks; }
-
-__device__ __forceinline__ int dma_col(int copy, int lane) {
-    const int slot = 64 * copy + lane;
-    const int key = slot / kRowChunks;
-    return 8 * ((slot - key * kRowChunks) ^ sigma(key));
-}
-
-__device__ __forceinline__ DmaPlan dma_plan(const MlaArgs& a, int wave, int lane) {
-    DmaPlan d;
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) {
-        const int copy = wave + kWaves * i;
-        d.coff[i] = dma_key(copy, lane) * static_cast<int>(a.kv_st) + dma_col(copy, lane);
-    }
-    return d;
-}
-
-__device__ __forceinline__ void dma_tile(const MlaArgs& a, const DmaPlan& d, uint16_t* dst, int64_t t0, int64_t k1,
-                                         int wave, int lane) {
+__device__ __forceinline__ void dma_tile(const MlaArgs& a, uint16_t* dst, int64_t t0, int64_t k1, int wave,
+                                         int lane_in) {
     const uint16_t* base = a.kv + t0 * a.kv_st;
-    const bool full = t0 + kKeys <= k1;
+    const int last = static_cast<int>(min(k1 - 1 - t0, static_cast<int64_t>(kKeys - 1)));
+    const int lane = opaque(lane_in);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
         const int copy = wave + kWaves * i;
-        if (copy < kDmaPerTile) {
-            int o = d.coff[i];
-            if (!full) {
-                const int last = static_cast<int>(k1 - 1 - t0);
-                const int key = min(dma_key(copy, lane), last);
-                o = key * static_cast<int>(a.kv_st) + dma_col(copy, lane);
-            }
-            __builtin_amdgcn_global_load_lds(base + o, dst + 64 * 8 * copy, 16, 0, 0);
-        }
+        const int slot = 64 * copy + lane;
+        const int key = slot / kRowChunks;
+        const int col = 8 * ((slot - key * kRowChunks) ^ sigma(min(key, kKeys - 1)));
+        const int o = min(key, last) * static_cast<int>(a.kv_st) + min(col, kDqk - 8);
+        lds_dma16(base + o, lds_addr(dst + 64 * 8 * copy));
     }
 }
 
-// Wait until this wavefront's direct loads have landed, then for everyone's.
-__device__ __forceinline__ void tile_ready() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
+// Wait until this wavefront's copies of all but the newest tile have landed
+// (vmcnt <= kDmaPerWave: the newest tile's copies may still be in flight;
+// expcnt and lgkmcnt untouched), then synchronise the workgroup: the older
+// tile is then complete for every wavefront.
+__device__ __forceinline__ void older_tile_ready() {
+    static_assert(kDmaPerWave < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerWave);
+    __syncthreads();
+}
+
+// Wait for all of this wavefront's tile copies, then synchronise.
+__device__ __forceinline__ void all_tiles_ready() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
 }
 
@@ -189,14 +202,34 @@ __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* k
                                              int g) {
     // S^T = K Q^T for keys [t0, t0+16) (sa) and [t0+16, t0+32) (sb): the lane
     // holds the scores of row r16 with keys 4g+i and 16+4g+i.
+    // Operand fragments are read kAhead steps before the MFMA that uses them
+    // (a ring of kAhead + 1), and the scheduler is told to interleave the
+    // reads with the MFMAs: without this every MFMA waits out a full LDS
+    // latency.
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    {
+        constexpr int kAhead = 1;
+        bf16x8 ra[kAhead + 1], rb[kAhead + 1];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int f = 0; f < kQSteps; ++f) {
-        const int o = ((f & 1) ? off.s_odd : off.s_even) + 64 * (f >> 1);
-        const bf16x8 fa = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o));
-        const bf16x8 fb = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o + 16 * kDqk));
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, qf[f], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, qf[f], sb, 0, 0, 0);
+        for (int f = 0; f < kQSteps + kAhead; ++f) {
+            if (f < kQSteps) {
+                const int o = ((f & 1) ? off.s_odd : off.s_even) + 64 * (f >> 1);
+                ra[f % (kAhead + 1)] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o));
+                rb[f % (kAhead + 1)] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o + 16 * kDqk));
+            }
+            if (f >= kAhead) {
+                const int u = f - kAhead;
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[u % (kAhead + 1)], qf[u], sa, 0, 0, 0);
+                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[u % (kAhead + 1)], qf[u], sb, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < kQSteps + kAhead; ++f) {
+            if (f < kQSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+            if (f >= kAhead) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     float z[8];
@@ -231,19 +264,37 @@ __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* k
 
     // O^T += V^T P^T: output tile t is columns [16t, 16t+16); the k index runs
     // over keys 4g..4g+3 and 16+4g..16+4g+3, in P^T (pb) and V^T alike.
+    {
+        constexpr int kAhead = 2;
+        bf16x4 rl[kAhead + 1], rh[kAhead + 1];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < kDTiles; ++t) {
-        const int o = off.tr[t & 3] + 64 * (t >> 2);
-        const bf16x4 lo = ds_read_tr(kt, o);
-        const bf16x4 hi = ds_read_tr(kt, o + 16 * kDqk);
-        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        st.oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.oacc[t], 0, 0, 0);
+        for (int t = 0; t < kDTiles + kAhead; ++t) {
+            if (t < kDTiles) {
+                const int o = off.tr[t & 3] + 64 * (t >> 2);
+                rl[t % (kAhead + 1)] = ds_read_tr(kt, o);
+                rh[t % (kAhead + 1)] = ds_read_tr(kt, o + 16 * kDqk);
+            }
+            if (t >= kAhead) {
+                const int u = t - kAhead;
+                const bf16x4 lo = rl[u % (kAhead + 1)], hi = rh[u % (kAhead + 1)];
+                const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                st.oacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.oacc[u], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kDTiles + kAhead; ++t) {
+            if (t < kDTiles) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 transpose reads
+            if (t >= kAhead) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t tile0[kTileElems];
-    __shared__ __attribute__((aligned(16))) uint16_t tile1[kTileElems];
+    __shared__ __attribute__((aligned(16))) uint16_t tile0[kTileAlloc];
+    __shared__ __attribute__((aligned(16))) uint16_t tile1[kTileAlloc];
+    __shared__ __attribute__((aligned(16))) uint16_t tile2[kTileAlloc];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -257,8 +308,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     const int64_t k0 = s0 + static_cast<int64_t>(wk.p) * a.split_len;
     const int64_t k1 = min(k0 + a.split_len, s1);
     const int ntiles = k0 < k1 ? static_cast<int>((k1 - k0 + kKeys - 1) / kKeys) : 0;
-    const DmaPlan dp = dma_plan(a, wave, lane);
-    if (ntiles > 0) dma_tile(a, dp, tile0, k0, k1, wave, lane);
+    if (ntiles > 0) dma_tile(a, tile0, k0, k1, wave, lane);
 
     // Query row of this lane (rows past the end repeat the last row and are not stored).
     const int row_raw = wk.rb * kMlaRowsPerBlock + wave * kRowsPerWave + r16;
@@ -272,6 +322,9 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
         const uint16_t* qrow = a.q + b * a.q_sb + h * a.q_sh + 8 * g;
 #pragma unroll
         for (int f = 0; f < kQSteps; ++f) qf[f] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * f));
+        // Settle these loads here: a wait for them left inside the key loop
+        // would also wait for the tile copies in flight there.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
     }
 
     // Operand offsets.  q.k: key r16, logical chunk 4f + g at physical
@@ -297,17 +350,27 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     st.m_run = -INFINITY;  // running max of row r16, log2 units
     st.l_run = 0.0f;       // lane-partial running sum of row r16
 
-    if (ntiles > 0) tile_ready();
-    for (int it = 0; it < ntiles; it += 2) {
+    // Tile it lives in buffer it % 3 and is copied two tiles ahead: while
+    // tile it is computed, tiles it+1 and it+2 may be in flight, and the
+    // barrier that ends tile it waits only for tile it+1.
+    if (ntiles > 1) dma_tile(a, tile1, k0 + kKeys, k1, wave, lane);
+    if (ntiles > 0) {
+        if (ntiles > 1) older_tile_ready(); else all_tiles_ready();
+    }
+    for (int it = 0; it < ntiles; it += 3) {
         const int64_t t0 = k0 + static_cast<int64_t>(it) * kKeys;
-        if (it + 1 < ntiles) dma_tile(a, dp, tile1, t0 + kKeys, k1, wave, lane);
+        if (it + 2 < ntiles) dma_tile(a, tile2, t0 + 2 * kKeys, k1, wave, lane);
         compute_tile(a, tile0, off, qf, st, t0, k1, g);
-        tile_ready();
-        if (it + 1 < ntiles) {
-            if (it + 2 < ntiles) dma_tile(a, dp, tile0, t0 + 2 * kKeys, k1, wave, lane);
-            compute_tile(a, tile1, off, qf, st, t0 + kKeys, k1, g);
-            tile_ready();
-        }
+        if (it + 1 >= ntiles) break;
+        if (it + 2 < ntiles) older_tile_ready(); else all_tiles_ready();
+        if (it + 3 < ntiles) dma_tile(a, tile0, t0 + 3 * kKeys, k1, wave, lane);
+        compute_tile(a, tile1, off, qf, st, t0 + kKeys, k1, g);
+        if (it + 2 >= ntiles) break;
+        if (it + 3 < ntiles) older_tile_ready(); else all_tiles_ready();
+        if (it + 4 < ntiles) dma_tile(a, tile1, t0 + 4 * kKeys, k1, wave, lane);
+        compute_tile(a, tile2, off, qf, st, t0 + 2 * kKeys, k1, g);
+        if (it + 3 >= ntiles) break;
+        if (it + 4 < ntiles) older_tile_ready(); else all_tiles_ready();
     }
 
     // Row sums across the four lane groups; every lane of a row ends with the same l.
