@@ -19,11 +19,13 @@
 //  * all of a row's shard loads are issued before any arithmetic waits on
 //    them, together with the LSE loads, so a wave has cp KiB in flight and a
 //    launch needs a single memory round trip;
-//  * lane s holds lse_s; the max and the sum over shards are wavefront DPP
-//    reductions inside a 16-lane row (cp <= 16) plus lane reads across rows
-//    (cp <= 64); the normalised weights are broadcast to scalar registers, so
-//    the empty-shard test (weight exactly 0, which covers lse = -inf) is a
-//    uniform scalar branch and an empty shard's payload is never used;
+//  * cp <= 16: the row's LSEs have a wave-uniform address and are read with
+//    scalar loads, so max, exponentials and sum are formed once per wavefront
+//    with no cross-lane step; a row whose weights are all nonzero takes a
+//    plain FMA path, a row with an empty shard (weight exactly 0, which covers
+//    lse = -inf) zeroes that shard's payload first, so it is never used;
+//  * cp > 16: lane s holds lse_s and the max and the sum over shards are
+//    wavefront DPP reductions inside 16-lane rows plus lane reads across rows;
 //  * fp32 FMAs in ascending shard order, then the hardware round-to-nearest-
 //    even bf16 convert and one 16-byte store per lane.
 // The per-element arithmetic does not depend on B, on the chunking or on the
@@ -115,6 +117,15 @@ __device__ __forceinline__ void fma8(float (&acc)[8], float w, u32x4 v) {
     }
 }
 
+// acc += w * v for a shard known to be in use (w != 0).
+__device__ __forceinline__ void fma8_dense(float (&acc)[8], float w, u32x4 v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(w, __uint_as_float(v[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, __uint_as_float(v[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    }
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const uint16_t a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
     const uint16_t b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
@@ -172,17 +183,26 @@ __device__ __forceinline__ void store_row(const MergeArgs& a, Row r, int lane, c
     if (a.out_lse && lane == 0) a.out_lse[r.b * a.ol_sb + r.j] = L;
 }
 
-// cp = CP <= 16 shards, known at compile time: the LSE load and all CP
-// payload loads of the row are in flight at once, no branch between the
-// loads and their use.
+// cp = CP <= 16 shards, known at compile time.  The row's CP LSEs have a
+// wave-uniform address and are read with scalar loads, so the weights are
+// computed once per wavefront with no cross-lane step; the CP payload loads
+// are issued first and are all in flight while the weights are formed.
+// Rows whose every weight is nonzero (the common case) take the plain FMA
+// path; a row with an empty shard zeroes that shard's payload first.
 template <int CP>
 __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
     const int lane = threadIdx.x & 63;
     const Row r = row_of(a);
 
-    const int ls = lane < CP ? lane : CP - 1;
-    const float xl = a.lse[r.b * a.l_sb + r.j * a.l_sj + ls * a.l_ss];
     const uint16_t* orow = a.attn + r.b * a.a_sb + r.j * a.a_sj + lane * 8;
+    const float* lrow = a.lse + r.b * a.l_sb + r.j * a.l_sj;
+    // Every kernel argument the addresses need is read above this point, in
+    // one batch of scalar loads, rather than a second batch after the
+    // payload loads are issued.
+    __builtin_amdgcn_sched_barrier(0);
+    float x[CP];
+#pragma unroll
+    for (int s = 0; s < CP; ++s) x[s] = lrow[s * a.l_ss];
     u32x4 v[CP];
 #pragma unroll
     for (int s = 0; s < CP; ++s) v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(orow + s * a.a_ss));
@@ -190,13 +210,32 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
     // scheduled before the last one is issued.
     __builtin_amdgcn_sched_barrier(0);
 
-    const float x = lane < CP ? xl : -INFINITY;  // lane s holds lse_s
-    float M, S;
-    const float wn = row_weights<16>(a, x, CP, M, S);
+    float M = x[0];
+#pragma unroll
+    for (int s = 1; s < CP; ++s) M = fmaxf(M, x[s]);
+    float w[CP];
+    float S = 0.0f;
+#pragma unroll
+    for (int s = 0; s < CP; ++s) {
+        w[s] = (x[s] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x[s] - M) * a.to_log2);
+        S += w[s];
+    }
+    const float inv = (S > 0.0f) ? __builtin_amdgcn_rcpf(S) : 0.0f;
+    bool dense = true;
+#pragma unroll
+    for (int s = 0; s < CP; ++s) {
+        w[s] *= inv;
+        dense = dense && (w[s] != 0.0f);
+    }
 
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (dense) {
 #pragma unroll
-    for (int s = 0; s < CP; ++s) fma8(acc, lane_value(wn, s), v[s]);
+        for (int s = 0; s < CP; ++s) fma8_dense(acc, w[s], v[s]);
+    } else {
+#pragma unroll
+        for (int s = 0; s < CP; ++s) fma8(acc, w[s], v[s]);
+    }
     store_row(a, r, lane, acc, merged_lse(a, M, S));
 }
 
