@@ -180,9 +180,12 @@ int plan_merge(const dcp_workspace* ws, const void* attn, int64_t B, int H, int6
 
     plan->args = a;
     plan->B = B;
-    plan->chunk = ws->capacity;
-    plan->n_chunks = (B + ws->capacity - 1) / ws->capacity;
-    plan->args.rows = static_cast<int32_t>((B < ws->capacity ? B : ws->capacity) * h_local);
+    // Tokens are the second grid dimension, which holds at most kMaxLaunchTokens
+    // blocks: a wider capacity is split further.  Chunks give the same bits
+    // as one launch, so the extra split is invisible to the caller.
+    plan->chunk = ws->capacity < kMaxLaunchTokens ? ws->capacity : kMaxLaunchTokens;
+    plan->n_chunks = (B + plan->chunk - 1) / plan->chunk;
+    plan->args.rows = static_cast<int32_t>((B < plan->chunk ? B : plan->chunk) * h_local);
     return ok();
 }
 

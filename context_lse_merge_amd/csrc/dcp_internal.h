@@ -36,6 +36,9 @@ struct MergeArgs {
     float from_log2;
 };
 
+// Most tokens one merge launch covers (the grid's second dimension).
+constexpr int64_t kMaxLaunchTokens = 65535;
+
 // A validated merge call: the arguments of the first chunk plus how to step
 // to the next one.
 struct MergePlan {

@@ -132,8 +132,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
 }
 
-// Grid: x = token b of the chunk, y = group of kWavesPerBlock local heads;
-// wavefront w of block (b, y) merges local head j = y * kWavesPerBlock + w.
+// Grid: x = group g of kWavesPerBlock local heads, y = token b of the chunk;
+// wavefront w of block (g, b) merges local head j = g * kWavesPerBlock + w.
+// Blocks are dispatched x first, so consecutive blocks read consecutive head
+// groups of one token: the chip streams one contiguous token slab after
+// another rather than hopping between tokens.
 // No integer division, and no branch anywhere between the loads and the
 // store, so the compiler keeps every load of the row ahead of the first wait.
 // When h_local is not a multiple of kWavesPerBlock the spare wavefronts of
@@ -145,8 +148,8 @@ struct Row {
 
 __device__ __forceinline__ Row row_of(const MergeArgs& a) {
     Row r;
-    r.b = blockIdx.x;
-    const int j = __builtin_amdgcn_readfirstlane(blockIdx.y * kWavesPerBlock + (threadIdx.x >> 6));
+    r.b = blockIdx.y;
+    const int j = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
     r.j = j < a.h_local ? j : a.h_local - 1;
     return r;
 }
@@ -285,7 +288,7 @@ void launch_fixed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
 
 hipError_t launch(const MergeArgs& a, hipStream_t stream) {
     const int tokens = a.rows / a.h_local;
-    const dim3 grid(tokens, (a.h_local + kWavesPerBlock - 1) / kWavesPerBlock);
+    const dim3 grid((a.h_local + kWavesPerBlock - 1) / kWavesPerBlock, tokens);
     switch (a.cp) {
         case 1: launch_fixed<1>(a, grid, stream); break;
         case 2: launch_fixed<2>(a, grid, stream); break;

@@ -66,6 +66,18 @@ int main() {
                          0, DCP_LSE_BASE_E, fake(out), 6 * D, D, nullptr, 0, stream, &plan);
     CHECK(rc == DCP_OK && plan.n_chunks == 1 && plan.args.rows == 30 && plan.args.a_ss == 6 * D);
 
+    // A capacity above the per-launch token limit is split further: 70000
+    // tokens with capacity 100000 run as 65535 + 4465.
+    dcp_workspace* wsw = nullptr;
+    CHECK(dcp_workspace_create(100000, 16, 4, 512, DCP_DTYPE_BF16, stream, &wsw) == DCP_OK);
+    const uintptr_t wattn = uintptr_t{1} << 44, wlse = uintptr_t{2} << 44, wout = uintptr_t{3} << 44;
+    rc = dcp::plan_merge(wsw, fake(wattn), 70000, H, H * D, D, reinterpret_cast<const float*>(wlse), DCP_LSE_BHC,
+                         16 * 4, 4, 1, DCP_LSE_BASE_E, fake(wout), 16 * D, D, nullptr, 0, stream, &plan);
+    CHECK(rc == DCP_OK && plan.chunk == dcp::kMaxLaunchTokens && plan.n_chunks == 2);
+    CHECK(plan.args.rows == 65535 * 16 && dcp::chunk_args(plan, 1).rows == 4465 * 16);
+    CHECK(reinterpret_cast<uintptr_t>(dcp::chunk_args(plan, 1).attn) == wattn + 2 * int64_t{65535} * H * D);
+    CHECK(dcp_workspace_destroy(wsw) == DCP_OK);
+
     // B == 0 is a no-op plan.
     rc = dcp::plan_merge(ws, nullptr, 0, H, 0, 0, nullptr, DCP_LSE_BHC, 0, 0, 0, DCP_LSE_BASE_E, nullptr, 0, 0,
                          nullptr, 0, stream, &plan);
