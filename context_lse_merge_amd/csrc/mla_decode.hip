@@ -96,7 +96,25 @@ constexpr int kBlockElems = 512;                            // one 1 KiB LDS blo
 constexpr int kHalfBlocks = kRowChunks / 4;                  // 18 blocks per 16 keys
 constexpr int kHalfElems = kHalfBlocks * kBlockElems;        // keys 16..31 start here
 
-__device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+// Reductions over lane pairs (l, l ^ 16) and (l, l ^ 32) without an LDS round
+// trip: v_permlane16_swap / v_permlane32_swap of a value with itself return
+// the two rows (halves) of each pair, one in each result.
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -218,7 +236,7 @@ __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* k
     // latency.
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
     {
-        constexpr int kAhead = 1;
+        constexpr int kAhead = 2;
         bf16x8 ra[kAhead + 1], rb[kAhead + 1];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -251,8 +269,7 @@ __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* k
     float tmax = z[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
-    tmax = xor_max(tmax, 16);
-    tmax = xor_max(tmax, 32);
+    tmax = max_xor32(max_xor16(tmax));
     const float m_new = fmaxf(st.m_run, tmax);  // finite: the tile has a valid key
     if (__any(m_new > st.m_run)) {
         // Some row's maximum grew: rescale the accumulators (alpha = 1 for the others).
@@ -388,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     // Row sums across the four lane groups; every lane of a row ends with the same l.
     const float l_run = st.l_run;
     const float m_run = st.m_run;
-    const float l_tot = (l_run + __shfl_xor(l_run, 16, 64)) + (__shfl_xor(l_run, 32, 64) + __shfl_xor(l_run, 48, 64));
+    const float l_tot = sum_xor32(sum_xor16(l_run));
     if (row_raw >= a.rows) return;
 
     if (a.nsplit == 1) {
