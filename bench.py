@@ -222,6 +222,14 @@ def cpu_baseline(case, seconds):
         times.append(time.perf_counter() - t0)
     times.sort()
     med = times[len(times) // 2]
+    # One thread, for about a third of the budget (at least 2 runs).
+    t1 = []
+    t_end = time.perf_counter() + seconds / 3
+    while len(t1) < 2 or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        oracle.merge(bits, lse, case.cp, olay, omode, threads=1)
+        t1.append(time.perf_counter() - t0)
+    t1.sort()
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -231,7 +239,7 @@ def cpu_baseline(case, seconds):
                     break
     except OSError:
         pass
-    return med * 1e6, threads, len(times), model
+    return med * 1e6, threads, len(times), model, t1[len(t1) // 2] * 1e6, len(t1)
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16, published
@@ -299,6 +307,29 @@ def producer_leg(Bs):
     del copies, kv_dev
     torch.cuda.empty_cache()
     return rows
+
+
+def producer_oracle_baseline():
+    """The fp64 oracle of the producer (per-shard softmax partials) timed on the
+    whole B = 1 workload: 128 query rows over the 131072-key cache, 4 shards,
+    36.5 GFLOP, all host cores, one run after a one-row warm-up."""
+    import numpy as np
+    import oracle
+    import synth
+    q, kv = synth.mla_decode(1)
+    qb, kvb = synth.bf16_bits(q), synth.bf16_bits(kv)
+    threads = len(os.sched_getaffinity(0))
+    oracle.attention_partials(qb, kvb, 4, synth.MLA_SCALE, oracle.BASE_E, rows=np.arange(1), threads=threads)
+    t0 = time.perf_counter()
+    oracle.attention_partials(qb, kvb, 4, synth.MLA_SCALE, oracle.BASE_E, rows=np.arange(128), threads=threads)
+    dt = time.perf_counter() - t0
+    fl = producer_flops(1, 128, kv.shape[0])
+    print("[bench] producer oracle B=1: %.2f s (%.2f GFLOP/s fp64, %d threads)" % (dt, fl / dt / 1e9, threads),
+          file=sys.stderr, flush=True)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "us": round(dt * 1e6, 1),
+            "sample": "the whole B = 1 producer workload (128 query rows x 131072 keys, 4 shards; fp64 C oracle, "
+                      "OpenMP over rows), one run"}
 
 
 CALIBRATION_BYTES = 256 << 20
@@ -377,13 +408,18 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cu, threads, reps, model = cpu_baseline(case, args.cpu_seconds)
+        cu, threads, reps, model, cu1, reps1 = cpu_baseline(case, args.cpu_seconds)
         cpu = {"value": round(alg / (cu * 1e-6) / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "us_per_layer_merge": round(cu, 1),
                "sample": "%d whole layer-merges of the same workload (fp64 C oracle, OpenMP over rows, %s); "
-                         "median" % (reps, model or "host CPU")}
+                         "median" % (reps, model or "host CPU"),
+               "one_thread": {"value": round(alg / (cu1 * 1e-6) / 1e9, 3), "unit": "GB/s",
+                              "us_per_layer_merge": round(cu1, 1), "sample": "%d whole layer-merges, median" % reps1}}
 
     producer = [] if args.no_producer else producer_leg(args.producer_B)
+    producer_cpu = None
+    if not args.no_producer and not args.no_cpu_baseline:
+        producer_cpu = producer_oracle_baseline()
     if args.calibrate:
         calibration_copy()
     traffic = counters_traffic()
@@ -417,7 +453,7 @@ def main():
         "producer": {"workload": "MLA split-KV decode, q [B,128,576] bf16, latent KV cache 131072 x 576 bf16 in "
                                  "4 contiguous shards, scale 1/sqrt(192), then the merge of its partials",
                      "bound": "mfma (B >= 2), hbm (B = 1)", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
-                     "rows": producer},
+                     "rows": producer, "cpu_baseline": producer_cpu},
     }
     print(json.dumps(line), flush=True)
     return 0

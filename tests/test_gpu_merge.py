@@ -270,6 +270,33 @@ def test_zero_tokens_is_a_no_op():
     ws.close()
 
 
+def test_one_workspace_reused_across_batch_sizes():
+    """One workspace (capacity 64) serves calls of B = 64, 3, 130 (3 ordered
+    chunks), 1 and 64 again, in that order on its stream; each call matches the
+    oracle and the repeated B = 64 call gives the same bits as the first."""
+    import context_lse_merge_amd as dcp
+    ws = dcp.dcp_workspace_create(64, 16, 4)
+    try:
+        first = None
+        for k, B in enumerate([64, 3, 130, 1, 64]):
+            c = synth.kimi_merge(B)
+            attn, lse = c.attn.to(DEV), c.lse.to(DEV)
+            out = torch.empty((B, 16, synth.D), dtype=torch.bfloat16, device=DEV)
+            L = torch.empty((B, 16), dtype=torch.float32, device=DEV)
+            announce("workspace reuse call %d: B=%d capacity=64" % (k, B))
+            dcp.dcp_lse_combine(ws, attn, lse, dcp.DCP_LSE_BHC, dcp.DCP_LSE_BASE_E, out, L)
+            torch.cuda.synchronize()
+            check_against_oracle(c, out, L)
+            if B == 64:
+                if first is None:
+                    first = (out.clone(), L.clone())
+                else:
+                    assert torch.equal(out.view(torch.int16), first[0].view(torch.int16))
+                    assert torch.equal(L.view(torch.int32), first[1].view(torch.int32))
+    finally:
+        ws.close()
+
+
 # ------------------------------------------------------------ streams and graphs
 
 def test_call_on_another_stream_is_rejected_before_launch():
