@@ -203,13 +203,13 @@ MergeArgs chunk_args(const MergePlan& plan, int64_t k) {
 
 // ------------------------------------------------------------- MLA decode plan
 //
-// Split-KV: with B*hq query rows in workgroups of 64 and cp shards there are
-// ceil(B*hq/64)*cp units of work -- 8 at B = 1 with 128 heads and cp = 4, far
+// Split-KV: with B*hq query rows in workgroups of 128 and cp shards there are
+// ceil(B*hq/128)*cp units of work -- 4 at B = 1 with 128 heads and cp = 4, far
 // too few for 256 compute units.  Each shard's keys are therefore split into
-// nsplit ranges processed by separate workgroups, whose fp32 partials (running
-// max, running sum, unnormalised output) are reduced afterwards; the split
-// count aims at about kMlaTargetBlocks workgroups and never gives a split
-// fewer than kMlaMinSplitKeys keys.
+// nsplit ranges processed by separate workgroups; each leaves a normalised
+// bf16 partial and its LSE, and the merge kernel reduces the splits exactly
+// as it merges DCP shards.  The split count aims at about kMlaTargetBlocks
+// workgroups and never gives a split fewer than kMlaMinSplitKeys keys.
 
 void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* split_len, size_t* scratch_bytes) {
     const int64_t rows = B * hq;
@@ -233,9 +233,8 @@ void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* s
     if (n <= 1) {
         *scratch_bytes = 0;
     } else {
-        const int64_t parts = static_cast<int64_t>(cp) * n * rows;
-        const int64_t o_bytes = parts * kMlaVDim * 4;
-        *scratch_bytes = static_cast<size_t>(o_bytes + parts * 2 * 4);
+        const int64_t parts = static_cast<int64_t>(cp) * n * rows;  // (token, split, shard, head)
+        *scratch_bytes = static_cast<size_t>(parts * kMlaVDim * 2 + parts * 4);
     }
 }
 
@@ -305,14 +304,9 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     MlaArgs a{};
     a.q = static_cast<const uint16_t*>(q);
     a.kv = static_cast<const uint16_t*>(kv);
-    a.o = static_cast<uint16_t*>(o);
-    a.lse = lse;
     a.q_sb = q_sb;
     a.q_sh = q_sh;
     a.kv_st = kv_st;
-    a.o_sb = o_sb;
-    a.o_sh = o_sh;
-    a.lse_sb = lse_sb;
     a.T = T;
     a.split_len = split_len;
     a.rows = static_cast<int32_t>(B * hq);
@@ -322,14 +316,46 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     a.row_blocks = (a.rows + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
     a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
     a.lse_scale = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;
-    if (nsplit > 1) {
-        const int64_t parts = static_cast<int64_t>(cp) * nsplit * a.rows;
-        a.part_o = static_cast<float*>(scratch);
-        a.part_ml = static_cast<float*>(scratch) + parts * kMlaVDim;
+    *plan = MlaPlan{};
+    if (nsplit == 1) {
+        a.o = static_cast<uint16_t*>(o);
+        a.lse = lse;
+        a.o_sb = o_sb;
+        a.o_sh = o_sh;
+        a.lse_sb = lse_sb;
+    } else {
+        // Per-split partials in the scratch buffer, then the merge over splits.
+        const int64_t heads = static_cast<int64_t>(nsplit) * H;   // per token
+        a.o = static_cast<uint16_t*>(scratch);
+        a.lse = reinterpret_cast<float*>(static_cast<char*>(scratch) + B * heads * kMlaVDim * 2);
+        a.o_sb = heads * kMlaVDim;
+        a.o_sh = kMlaVDim;
+        a.lse_sb = heads;
+        MergeArgs m{};
+        m.attn = a.o;
+        m.lse = a.lse;
+        m.out = static_cast<uint16_t*>(o);
+        m.out_lse = lse;
+        m.a_sb = a.o_sb;
+        m.a_sj = kMlaVDim;             // local head j = s*hq + h
+        m.a_ss = H * kMlaVDim;         // split p
+        m.l_sb = heads;
+        m.l_sj = 1;
+        m.l_ss = H;
+        m.o_sb = o_sb;
+        m.o_sj = o_sh;
+        m.ol_sb = lse_sb;
+        m.h_local = static_cast<int32_t>(H);
+        m.cp = nsplit;
+        m.rows = 0;                    // set per token chunk at launch
+        m.to_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 1.4426950408889634f;
+        m.from_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;
+        plan->reduce = m;
     }
     plan->args = a;
     plan->scratch_bytes = need;
     plan->blocks = static_cast<int64_t>(a.row_blocks) * cp * nsplit;
+    plan->B = B;
     return ok();
 }
 

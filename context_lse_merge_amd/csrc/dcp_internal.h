@@ -78,6 +78,11 @@ int plan_merge(const dcp_workspace* ws, const void* attn, int64_t B, int H, int6
 // Arguments of chunk k of a plan (token range [k*chunk, min((k+1)*chunk, B))).
 MergeArgs chunk_args(const MergePlan& plan, int64_t k);
 
+// Enqueue one merge launch of already validated arguments (rows = tokens *
+// h_local with at most kMaxLaunchTokens tokens) on `stream` (a hipStream_t).
+// Returns the HIP error code of the launch (0 = success).
+int merge_launch(const MergeArgs& a, void* stream);
+
 // ---------------------------------------------------------------- MLA decode
 
 constexpr int kMlaQkDim = DCP_QK_DIM;   // 576 query/key columns
@@ -86,18 +91,23 @@ constexpr int kMlaRowsPerBlock = 128;   // query rows per workgroup
 constexpr int kMlaKeysPerTile = 32;     // keys per LDS tile
 constexpr int kMlaTargetBlocks = 256;   // split the KV until about this many workgroups (one per CU)
 constexpr int kMlaMinSplitKeys = 256;   // ... but never below this many keys per split
-constexpr int kMlaMaxSplits = 64;       // ... nor above this many splits (one lane each in the reduction)
+constexpr int kMlaMaxSplits = DCP_MAX_CP;  // ... nor above what the merge kernel reduces in one launch
 
 // Kernel parameters of the MLA split-KV decode.  Query row r = b*hq + h.
 // The keys of shard s are [floor(s*T/cp), floor((s+1)*T/cp)); split p of a
 // shard covers its keys [p*split_len, (p+1)*split_len).
+// The kernel writes the normalised bf16 output and the LSE of (b, split p,
+// shard s, head h) as head u = p*cp*hq + s*hq + h of
+//   o   + b*o_sb + u*o_sh   (512 columns)   and   lse + b*lse_sb + u.
+// With one split these are the caller's o_part / lse_part; with several they
+// are the scratch buffer, [B][nsplit*cp*hq][512] bf16 then [B][nsplit*cp*hq]
+// fp32, which the merge kernel then reduces over p (an LSE merge with
+// nsplit shards and cp*hq local heads) into o_part / lse_part.
 struct MlaArgs {
     const uint16_t* q;      // row r at q + b*q_sb + h*q_sh, 576 columns
     const uint16_t* kv;     // token t at kv + t*kv_st, 576 columns
-    uint16_t* o;            // (b, s*hq + h) at o + b*o_sb + (s*hq + h)*o_sh, 512 columns
-    float* lse;             // (b, s*hq + h) at lse + b*lse_sb + s*hq + h
-    float* part_o;          // [cp*nsplit][rows][512] unnormalised fp32 (nsplit > 1)
-    float* part_ml;         // [cp*nsplit][rows][2]: running max (log2 units) and sum
+    uint16_t* o;
+    float* lse;
     int64_t q_sb, q_sh, kv_st, o_sb, o_sh, lse_sb;
     int64_t T;
     int64_t split_len;      // multiple of kMlaKeysPerTile
@@ -114,6 +124,8 @@ struct MlaPlan {
     MlaArgs args;
     size_t scratch_bytes;   // needed scratch (0 when nsplit == 1)
     int64_t blocks;         // workgroups of the main kernel (0: nothing to do)
+    MergeArgs reduce;       // nsplit > 1: the merge over splits (all B tokens; launched in token chunks)
+    int64_t B;
 };
 
 // Split decision and scratch size; pure arithmetic on the shape.

@@ -312,6 +312,11 @@ hipError_t launch(const MergeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int merge_launch(const MergeArgs& a, void* stream) {
+    return static_cast<int>(launch(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace dcp
 
 extern "C" int dcp_lse_combine(dcp_workspace* ws, const void* attn, int64_t B, int H, int64_t attn_sb,

@@ -49,10 +49,11 @@
 //    where some row's maximum grew.  p is rounded to bf16 for the p.v MFMA;
 //    the sum uses the fp32 p.
 //  * Split-KV: shards are split into key ranges so that about 256 workgroups
-//    (one per compute unit) exist even at B = 1; each split leaves an fp32
-//    partial (running max, running sum, unnormalised output) in the scratch
-//    buffer and a second kernel reduces them.  With a single split the first
-//    kernel writes the final bf16 output and LSE itself.
+//    (one per compute unit) exist even at B = 1; each split leaves its
+//    normalised bf16 output and LSE in the scratch buffer, and the merge
+//    kernel of dcp_lse_combine reduces the splits of each (token, shard,
+//    head) exactly as it merges DCP shards.  With a single split the kernel
+//    writes the final bf16 output and LSE itself.
 //  * Workgroups that share a key range are placed on the same XCD (block ids
 //    are dealt round-robin over the 8 XCDs), so a KV tile is fetched from HBM
 //    about once per XCD-L2 rather than once per workgroup.
@@ -408,102 +409,23 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     const float l_tot = sum_xor32(sum_xor16(l_run));
     if (row_raw >= a.rows) return;
 
-    if (a.nsplit == 1) {
-        // Final output: O / l in bf16, LSE in the caller's base; an empty shard gives 0 and -inf.
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        uint16_t* orow = a.o + b * a.o_sb + (static_cast<int64_t>(wk.s) * a.hq + h) * a.o_sh + ocol;
+    // O / l in bf16 and the LSE in the caller's base, as head p*cp*hq + s*hq + h
+    // of the destination (the caller's outputs, or the per-split scratch that
+    // the merge kernel reduces); an empty shard or split gives 0 and -inf.
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const int64_t u = (static_cast<int64_t>(wk.p) * a.cp + wk.s) * a.hq + h;
+    uint16_t* orow = a.o + b * a.o_sb + u * a.o_sh + ocol;
 #pragma unroll
-        for (int t = 0; t < kDTiles; ++t) {
-            const f32x4 v = st.oacc[t];
-            const uint32_t lo = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[0] * inv))) |
-                                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[1] * inv))) << 16);
-            const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2] * inv))) |
-                                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[3] * inv))) << 16);
-            *reinterpret_cast<uint2*>(orow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
-        }
-        if (g == 0)
-            a.lse[b * a.lse_sb + static_cast<int64_t>(wk.s) * a.hq + h] =
-                l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * a.lse_scale : -INFINITY;
-    } else {
-        // Split partial: unnormalised fp32 output, running max and sum.
-        const int64_t part = (static_cast<int64_t>(wk.s) * a.nsplit + wk.p) * a.rows + row;
-        float* prow = a.part_o + part * kDv + ocol;
-#pragma unroll
-        for (int t = 0; t < kDTiles; ++t) *reinterpret_cast<f32x4*>(prow + 64 * (t >> 2) + 8 * (t & 3)) = st.oacc[t];
-        if (g == 0) {
-            a.part_ml[2 * part] = l_tot > 0.0f ? m_run : -INFINITY;
-            a.part_ml[2 * part + 1] = l_tot;
-        }
+    for (int t = 0; t < kDTiles; ++t) {
+        const f32x4 v = st.oacc[t];
+        const uint32_t lo = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[0] * inv))) |
+                            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[1] * inv))) << 16);
+        const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2] * inv))) |
+                            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[3] * inv))) << 16);
+        *reinterpret_cast<uint2*>(orow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
     }
-}
-
-// Reduce the nsplit (<= 64) partials of every (shard, row): one wavefront
-// per row.  Lane p holds split p's running max m_p and sum l_p; the row's
-// M = max_p m_p, w_p = 2^(m_p - M) (0 for an empty split), L = sum_p w_p l_p
-// come from wavefront reductions, and then lane l accumulates columns
-// [8l, 8l+8) of sum_p w_p O_p in ascending p, loading 8 splits' payload per
-// round trip.  O = that sum / L; an all-empty row gives O = 0 and LSE = -inf.
-// Grid: x = groups of 4 rows, y = shard.
-constexpr int kReduceBatch = 8;
-
-__global__ __launch_bounds__(256) void mla_split_reduce_kernel(MlaArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int row_raw = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int row = __builtin_amdgcn_readfirstlane(min(row_raw, a.rows - 1));
-    const int s = blockIdx.y;
-    const int n = a.nsplit;
-    const int64_t base = static_cast<int64_t>(s) * n * a.rows + row;  // part index of split 0
-
-    const int lp = lane < n ? lane : n - 1;
-    const int64_t my = base + static_cast<int64_t>(lp) * a.rows;
-    const float m_l = lane < n ? a.part_ml[2 * my] : -INFINITY;
-    const float l_l = a.part_ml[2 * my + 1];
-    float M = m_l;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    const float w = (m_l == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_l - M);
-    float L = w * l_l;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off, 64);
-
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int p0 = 0; p0 < n; p0 += kReduceBatch) {
-        f32x4 x[kReduceBatch][2];
-#pragma unroll
-        for (int i = 0; i < kReduceBatch; ++i) {
-            const int p = min(p0 + i, n - 1);
-            const f32x4* src =
-                reinterpret_cast<const f32x4*>(a.part_o + (base + static_cast<int64_t>(p) * a.rows) * kDv + 8 * lane);
-            x[i][0] = src[0];
-            x[i][1] = src[1];
-        }
-#pragma unroll
-        for (int i = 0; i < kReduceBatch; ++i) {
-            // An empty (or past-the-end) split has weight 0 and its payload is
-            // replaced by 0 (a select, so the loads above stay batched).
-            const float wp = (p0 + i < n) ? __shfl(w, p0 + i, 64) : 0.0f;
-            const bool use = wp != 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[e] = fmaf(wp, use ? x[i][0][e] : 0.0f, acc[e]);
-                acc[4 + e] = fmaf(wp, use ? x[i][1][e] : 0.0f, acc[4 + e]);
-            }
-        }
-    }
-    if (row_raw >= a.rows) return;
-    const int b = row / a.hq;
-    const int h = row - b * a.hq;
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    uint32_t packed[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        packed[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[2 * i] * inv))) |
-                    (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[2 * i + 1] * inv))) << 16);
-    uint16_t* orow = a.o + b * a.o_sb + (static_cast<int64_t>(s) * a.hq + h) * a.o_sh + 8 * lane;
-    *reinterpret_cast<u32x4*>(orow) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-    if (lane == 0)
-        a.lse[b * a.lse_sb + static_cast<int64_t>(s) * a.hq + h] =
-            L > 0.0f ? (M + __builtin_amdgcn_logf(L)) * a.lse_scale : -INFINITY;
+    if (g == 0)
+        a.lse[b * a.lse_sb + u] = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * a.lse_scale : -INFINITY;
 }
 
 }  // namespace
@@ -522,9 +444,20 @@ extern "C" int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t 
     dcp::mla_decode_kernel<<<dim3(static_cast<unsigned>(plan.blocks)), dim3(dcp::kThreads), 0, stream>>>(plan.args);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && plan.args.nsplit > 1) {
-        const dim3 grid((plan.args.rows + 3) / 4, plan.args.cp);
-        dcp::mla_split_reduce_kernel<<<grid, dim3(256), 0, stream>>>(plan.args);
-        e = hipGetLastError();
+        // The splits of every (token, shard, head) are merged like DCP shards.
+        const int64_t H = plan.reduce.h_local;
+        int64_t chunk = (int64_t{1} << 30) / H;
+        if (chunk > dcp::kMaxLaunchTokens) chunk = dcp::kMaxLaunchTokens;
+        for (int64_t t0 = 0; t0 < plan.B && e == hipSuccess; t0 += chunk) {
+            const int64_t n = plan.B - t0 < chunk ? plan.B - t0 : chunk;
+            dcp::MergeArgs m = plan.reduce;
+            m.attn += t0 * m.a_sb;
+            m.lse += t0 * m.l_sb;
+            m.out += t0 * m.o_sb;
+            m.out_lse += t0 * m.ol_sb;
+            m.rows = static_cast<int32_t>(n * H);
+            e = static_cast<hipError_t>(dcp::merge_launch(m, stream));
+        }
     }
     if (e != hipSuccess)
         return dcp::fail(DCP_ERR_HIP, "dcp_mla_partial_decode: launch failed: %s", hipGetErrorString(e));

@@ -151,8 +151,11 @@ int dcp_lse_combine(dcp_workspace* ws, const void* attn, int64_t B, int H, int64
  * o_part    [B, cp*hq, 512] bf16, row (b, s*hq + h) at o_part + b*o_sb + (s*hq+h)*o_sh.
  * lse_part  [B, cp*hq] fp32 at lse_part + b*lse_sb + s*hq + h.
  * scratch   device buffer of at least dcp_mla_partial_decode_scratch_size()
- *           bytes for the split-KV partials (fp32); NULL allowed when that
- *           size is 0.  Contents on entry are ignored.
+ *           bytes, 16-byte aligned, for the split-KV partials: when a shard's
+ *           keys are split over several workgroups, each split's normalised
+ *           bf16 output and LSE land here and are merged into o_part /
+ *           lse_part by the dcp_lse_combine kernel.  NULL allowed when the
+ *           size is 0 (one split per shard).  Contents on entry are ignored.
  * Arithmetic: bf16 MFMA products with fp32 accumulation for q.k and p.v,
  * fp32 online softmax; p is rounded to bf16 before the p.v product.
  * Alignment: q, kv, o_part 16-byte aligned; q_sb, q_sh, kv_st, o_sb, o_sh
