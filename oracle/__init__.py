@@ -60,13 +60,17 @@ def _configure(lib):
     i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
     lib.oracle_merge_f64.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32, vp, vp, vp, i32]
     lib.oracle_merge_bf16.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32, vp, vp, vp, i32]
+    lib.oracle_merge_f16.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32, vp, vp, vp, i32]
+    lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f64.restype = dbl
     lib.oracle_attention_partials.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, dbl, i32, vp, i64,
                                               vp, vp, i32]
     lib.oracle_attention_full.argtypes = [vp, vp, i64, i64, i64, i64, i64, dbl, i32, vp, i64, vp, vp, i32]
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f64.restype = dbl
     lib.oracle_max_threads.restype = i32
-    for f in ("oracle_merge_f64", "oracle_merge_bf16", "oracle_attention_partials", "oracle_attention_full"):
+    for f in ("oracle_merge_f64", "oracle_merge_bf16", "oracle_merge_f16", "oracle_attention_partials",
+              "oracle_attention_full"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -90,10 +94,22 @@ def bf16_to_f64(bits) -> np.ndarray:
     return out.reshape(bits.shape)
 
 
-def merge(O, lse, cp: int, lse_layout: int, lse_mode: int, threads: int = 0):
+def f16_to_f64(bits) -> np.ndarray:
+    """Decode raw IEEE binary16 bits (uint16 array) to float64 with the oracle's own routine."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    lib = _load()
+    flat = bits.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.float64)
+    for i, b in enumerate(flat):
+        out[i] = lib.oracle_f16_to_f64(int(b))
+    return out.reshape(bits.shape)
+
+
+def merge(O, lse, cp: int, lse_layout: int, lse_mode: int, threads: int = 0, dtype: str = "bf16"):
     """LSE-weighted merge of cp shards.
 
-    ``O``: [B, H, D], either uint16 (raw bf16 bits) or float64.
+    ``O``: [B, H, D], either uint16 (raw 16-bit payload bits: bf16, or IEEE
+    binary16 with ``dtype="f16"``) or float64.
     ``lse``: contiguous [B, H/cp, cp] (``LSE_BHC``) or [B, H] / [B, H, 1]
     (``LSE_BH1``); float32 with bf16 ``O``, float64 with float64 ``O``.
     Returns ``(out [B, H/cp, D], lse [B, H/cp], abs_weighted [B, H/cp, D])`` in float64.
@@ -106,7 +122,9 @@ def merge(O, lse, cp: int, lse_layout: int, lse_mode: int, threads: int = 0):
     if O.dtype == np.uint16:
         O = np.ascontiguousarray(O)
         lse = np.ascontiguousarray(lse, dtype=np.float32)
-        fn = lib.oracle_merge_bf16
+        if dtype not in ("bf16", "f16"):
+            raise ValueError("dtype must be 'bf16' or 'f16'")
+        fn = lib.oracle_merge_bf16 if dtype == "bf16" else lib.oracle_merge_f16
     else:
         O = np.ascontiguousarray(O, dtype=np.float64)
         lse = np.ascontiguousarray(lse, dtype=np.float64)

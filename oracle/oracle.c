@@ -84,6 +84,28 @@ void oracle_decode_bf16(const uint16_t* src, double* dst, int64_t n) {
     for (int64_t i = 0; i < n; ++i) dst[i] = oracle_bf16_to_f64(src[i]);
 }
 
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Exponent field 0 holds zero and the subnormals, fraction * 2^-24; field 31
+ * holds infinity (fraction 0) and NaN; otherwise the value is
+ * (1024 + fraction) * 2^(exponent - 25).  Every value is exact in double. */
+double oracle_f16_to_f64(uint16_t bits) {
+    const int sign = (bits >> 15) & 1;
+    const int expo = (bits >> 10) & 0x1F;
+    const int frac = bits & 0x3FF;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);
+    else if (expo == 31)
+        v = frac == 0 ? INFINITY : NAN;
+    else
+        v = ldexp((double)(1024 + frac), expo - 25);
+    return sign ? -v : v;
+}
+
+void oracle_decode_f16(const uint16_t* src, double* dst, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = oracle_f16_to_f64(src[i]);
+}
+
 static void set_threads(int nthreads) {
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -180,11 +202,11 @@ int oracle_merge_f64(const double* O, const double* lse, int64_t B, int64_t H, i
     return ORACLE_OK;
 }
 
-/* Same merge on the product's input types: bf16 O (raw bits) and fp32 LSE.
- * Both are widened exactly to double first. */
-int oracle_merge_bf16(const uint16_t* O, const float* lse, int64_t B, int64_t H, int64_t cp, int64_t D,
-                      int lse_layout, int lse_mode, double* out, double* out_lse, double* out_abs,
-                      int nthreads) {
+/* Same merge on the product's input types: 16-bit O (raw bits, decoded by
+ * `decode`) and fp32 LSE.  Both are widened exactly to double first. */
+static int merge_16bit(void (*decode)(const uint16_t*, double*, int64_t), const uint16_t* O, const float* lse,
+                       int64_t B, int64_t H, int64_t cp, int64_t D, int lse_layout, int lse_mode, double* out,
+                       double* out_lse, double* out_abs, int nthreads) {
     if (B < 0 || H <= 0 || cp <= 0 || D <= 0 || H % cp != 0) return ORACLE_BAD_ARG;
     const int64_t n_o = B * H * D, n_l = B * H;
     double* Od = (double*)malloc((size_t)(n_o > 0 ? n_o : 1) * sizeof(double));
@@ -194,12 +216,26 @@ int oracle_merge_bf16(const uint16_t* O, const float* lse, int64_t B, int64_t H,
         free(Ld);
         return ORACLE_BAD_ARG;
     }
-    oracle_decode_bf16(O, Od, n_o);
+    decode(O, Od, n_o);
     for (int64_t i = 0; i < n_l; ++i) Ld[i] = (double)lse[i];
     int rc = oracle_merge_f64(Od, Ld, B, H, cp, D, lse_layout, lse_mode, out, out_lse, out_abs, nthreads);
     free(Od);
     free(Ld);
     return rc;
+}
+
+int oracle_merge_bf16(const uint16_t* O, const float* lse, int64_t B, int64_t H, int64_t cp, int64_t D,
+                      int lse_layout, int lse_mode, double* out, double* out_lse, double* out_abs,
+                      int nthreads) {
+    return merge_16bit(oracle_decode_bf16, O, lse, B, H, cp, D, lse_layout, lse_mode, out, out_lse, out_abs,
+                       nthreads);
+}
+
+int oracle_merge_f16(const uint16_t* O, const float* lse, int64_t B, int64_t H, int64_t cp, int64_t D,
+                     int lse_layout, int lse_mode, double* out, double* out_lse, double* out_abs,
+                     int nthreads) {
+    return merge_16bit(oracle_decode_f16, O, lse, B, H, cp, D, lse_layout, lse_mode, out, out_lse, out_abs,
+                       nthreads);
 }
 
 /*

@@ -44,6 +44,9 @@ MUTANTS = {
                                  "if (lse_mode == ORACLE_BASE_2) lse /= M_LOG2E;"),
     "shard_bound_off_by_one": ("*t1 = ((s + 1) * T) / cp;", "*t1 = ((s + 1) * T) / cp + (s == 0);"),
     "bf16_decode_shift": ("((uint32_t)bits) << 16", "((uint32_t)bits) << 15"),
+    "f16_decode_bias": ("ldexp((double)(1024 + frac), expo - 25)", "ldexp((double)(1024 + frac), expo - 24)"),
+    "f16_subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
+    "f16_merge_decodes_as_bf16": ("return merge_16bit(oracle_decode_f16,", "return merge_16bit(oracle_decode_bf16,"),
 }
 
 
@@ -54,6 +57,8 @@ def _pin_checks():
     checks += [
         pins.test_all_empty_output_is_positive_zero,
         pins.test_bf16_decode_matches_torch,
+        pins.test_f16_decode_matches_numpy_for_every_bit_pattern,
+        pins.test_f16_entry_equals_f64_entry,
         lambda: pins.test_cp1_is_identity(E),
         lambda: pins.test_equal_lse_gives_mean(4, E),
         lambda: pins.test_equal_lse_gives_mean(8, T2),

@@ -100,6 +100,28 @@ def test_bf16_decode_matches_torch():
     assert np.array_equal(got[~both_nan], ref[~both_nan]) and np.array_equal(np.isnan(got), np.isnan(ref))
 
 
+def test_f16_decode_matches_numpy_for_every_bit_pattern():
+    """The oracle's own IEEE binary16 decode against numpy's float16 -> float64
+    conversion, exhaustively: all 65536 patterns (zeros, subnormals, normals,
+    infinities, NaNs)."""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    got = oracle.f16_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan]) and np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    assert got[0x3C00] == 1.0 and got[0x0001] == 2.0 ** -24 and got[0x7BFF] == 65504.0
+
+
+def test_f16_entry_equals_f64_entry():
+    rng = np.random.default_rng(11)
+    O16 = rng.standard_normal((3, 16, 64)).astype(np.float16)
+    lse = rng.uniform(-5, 15, size=(3, 8, 2)).astype(np.float32)
+    out_h, L_h, A_h = oracle.merge(O16.view(np.uint16), lse, 2, oracle.LSE_BHC, oracle.BASE_E, dtype="f16")
+    out_d, L_d, A_d = oracle.merge(O16.astype(np.float64), lse.astype(np.float64), 2, oracle.LSE_BHC, oracle.BASE_E)
+    assert np.array_equal(out_h, out_d) and np.array_equal(L_h, L_d) and np.array_equal(A_h, A_d)
+
+
 def _random_case(rng, B, H, cp, D=512):
     O = rng.standard_normal((B, H, D))
     lse = rng.uniform(-5, 15, size=(B, H // cp, cp))
