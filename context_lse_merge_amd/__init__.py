@@ -40,6 +40,7 @@ DCP_LSE_BASE_2 = _C["DCP_LSE_BASE_2"]
 DCP_LSE_BHC = _C["DCP_LSE_BHC"]
 DCP_LSE_BH1 = _C["DCP_LSE_BH1"]
 DCP_DTYPE_BF16 = _C["DCP_DTYPE_BF16"]
+DCP_DTYPE_FP16 = _C["DCP_DTYPE_FP16"]
 DCP_HEAD_DIM = _C["DCP_HEAD_DIM"]
 DCP_QK_DIM = _C["DCP_QK_DIM"]
 DCP_MAX_CP = _C["DCP_MAX_CP"]
@@ -106,12 +107,13 @@ def _dev_ptr(t, name):
 class Workspace:
     """Owns a dcp_workspace handle; ``handle`` is what the C calls take."""
 
-    def __init__(self, handle: int, capacity: int, h_local: int, cp: int, stream: int):
+    def __init__(self, handle: int, capacity: int, h_local: int, cp: int, stream: int, dtype: int):
         self.handle = handle
         self.capacity = capacity
         self.h_local = h_local
         self.cp = cp
         self.stream = stream
+        self.dtype = dtype
 
     def close(self):
         if self.handle:
@@ -133,11 +135,12 @@ class Workspace:
 
 def dcp_workspace_create(capacity_tokens: int, h_local: int, cp: int, d: int = DCP_HEAD_DIM,
                          dtype: int = DCP_DTYPE_BF16, stream=None) -> Workspace:
-    """Create a workspace bound to ``stream`` (default: torch's current stream)."""
+    """Create a workspace bound to ``stream`` (default: torch's current stream).
+    ``dtype`` is DCP_DTYPE_BF16 or DCP_DTYPE_FP16, the payload type of every call."""
     s = _stream_handle(stream)
     h = _vp()
     _check(_lib.dcp_workspace_create(capacity_tokens, h_local, cp, d, dtype, s, ctypes.byref(h)))
-    return Workspace(h.value, capacity_tokens, h_local, cp, s)
+    return Workspace(h.value, capacity_tokens, h_local, cp, s, dtype)
 
 
 def dcp_workspace_destroy(ws: Workspace):
@@ -145,7 +148,7 @@ def dcp_workspace_destroy(ws: Workspace):
 
 
 def dcp_lse_combine(ws: Workspace, attn, lse, lse_layout: int, lse_mode: int, out, out_lse=None, stream=None):
-    """Merge the cp shard partials of ``attn`` [B, H, D] (bf16, any token/head strides)
+    """Merge the cp shard partials of ``attn`` [B, H, D] (the workspace's bf16 or fp16, any token/head strides)
     into ``out`` [B, H/cp, D] and optionally ``out_lse`` [B, H/cp].
 
     ``lse`` is [B, H/cp, cp] for ``DCP_LSE_BHC`` or [B, H, 1] / [B, H] for
@@ -154,8 +157,9 @@ def dcp_lse_combine(ws: Workspace, attn, lse, lse_layout: int, lse_mode: int, ou
     import torch
     if attn.dim() != 3 or out.dim() != 3:
         raise ValueError("attn and out must be 3-D [B, H, D] / [B, H/cp, D]")
-    if attn.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
-        raise ValueError("attn and out must be bfloat16")
+    want = torch.float16 if ws.dtype == DCP_DTYPE_FP16 else torch.bfloat16
+    if attn.dtype != want or out.dtype != want:
+        raise ValueError("attn and out must be %s (the workspace's dtype)" % want)
     if lse.dtype != torch.float32 or (out_lse is not None and out_lse.dtype != torch.float32):
         raise ValueError("lse and out_lse must be float32")
     B, H, D = attn.shape

@@ -152,6 +152,7 @@ int plan_merge(const dcp_workspace* ws, const void* attn, int64_t B, int H, int6
     a.ol_sb = out_lse_sb;
     a.h_local = h_local;
     a.cp = cp;
+    a.dtype = ws->dtype;
     if (lse_mode == DCP_LSE_BASE_2) {
         a.to_log2 = 1.0f;
         a.from_log2 = 1.0f;
@@ -347,6 +348,7 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
         m.ol_sb = lse_sb;
         m.h_local = static_cast<int32_t>(H);
         m.cp = nsplit;
+        m.dtype = DCP_DTYPE_BF16;
         m.rows = 0;                    // set per token chunk at launch
         m.to_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 1.4426950408889634f;
         m.from_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;
@@ -390,8 +392,9 @@ int dcp_workspace_create(int64_t capacity_tokens, int h_local, int cp, int d, in
     if (d != DCP_HEAD_DIM)
         return dcp::fail(DCP_ERR_LAYOUT, "dcp_workspace_create: head dimension %d is not supported (only %d)", d,
                          DCP_HEAD_DIM);
-    if (dtype != DCP_DTYPE_BF16)
-        return dcp::fail(DCP_ERR_LAYOUT, "dcp_workspace_create: dtype %d is not supported (only DCP_DTYPE_BF16)",
+    if (dtype != DCP_DTYPE_BF16 && dtype != DCP_DTYPE_FP16)
+        return dcp::fail(DCP_ERR_LAYOUT,
+                         "dcp_workspace_create: dtype %d is not supported (DCP_DTYPE_BF16 or DCP_DTYPE_FP16)",
                          dtype);
     // One launch covers capacity * h_local rows, counted in 32 bits.
     if (capacity_tokens * static_cast<int64_t>(h_local) > (int64_t{1} << 30))

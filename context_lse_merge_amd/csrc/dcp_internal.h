@@ -30,6 +30,7 @@ struct MergeArgs {
     int32_t rows;
     int32_t h_local;
     int32_t cp;
+    int32_t dtype;      // DCP_DTYPE_BF16 or DCP_DTYPE_FP16 (attn and out)
     // (lse_s - M) * to_log2 is the exponent of 2 of the weight; log2(S) * from_log2
     // is added to M for the merged LSE.  Base 2: both 1.  Base e: log2 e and ln 2.
     float to_log2;

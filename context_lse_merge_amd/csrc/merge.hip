@@ -27,7 +27,9 @@
 //  * cp > 16: lane s holds lse_s and the max and the sum over shards are
 //    wavefront DPP reductions inside 16-lane rows plus lane reads across rows;
 //  * fp32 FMAs in ascending shard order, then the hardware round-to-nearest-
-//    even bf16 convert and one 16-byte store per lane.
+//    even convert to the payload type and one 16-byte store per lane.  The
+//    payload is bf16 or fp16 (both are the pages' payload types); one kernel
+//    instance per type, differing only in the widening and narrowing.
 // The per-element arithmetic does not depend on B, on the chunking or on the
 // grid, so chunked and unchunked calls give identical bits.
 #include <hip/hip_runtime.h>
@@ -102,34 +104,56 @@ __device__ __forceinline__ float wave_sum(float v, int cp) {
     return s;
 }
 
-// acc += w * v for the 8 bf16 columns of v.  A shard with weight exactly 0
-// (an empty one) has its payload replaced by zeros first -- a select on the
-// four packed words, not a branch, so the payload loads stay ahead of their
-// use -- and then adds exactly +0, whatever the payload held (NaN included).
+// The two 16-bit payload types.  A 32-bit word holds two elements, the
+// lower-addressed one in the low half; widening to fp32 is exact for both,
+// narrowing rounds to nearest even.
+struct Bf16 {
+    // bf16 is the high half of an fp32: shifting or masking widens it.
+    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+    }
+};
+
+struct F16 {
+    static __device__ __forceinline__ float lo(uint32_t w) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+    }
+    static __device__ __forceinline__ float hi(uint32_t w) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+    }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(a))) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(b))) << 16);
+    }
+};
+
+// acc += w * v for the 8 columns of v.  A shard with weight exactly 0 (an
+// empty one) has its payload replaced by zeros first -- a select on the four
+// packed words, not a branch, so the payload loads stay ahead of their use --
+// and then adds exactly +0, whatever the payload held (NaN included): the
+// all-zero word is +0 in both payload types.
+template <typename T>
 __device__ __forceinline__ void fma8(float (&acc)[8], float w, u32x4 v) {
     const bool use = (w != 0.0f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t p = use ? v[i] : 0u;
-        // bf16 -> fp32 is exact: the bf16 bits are the high half of the float.
-        acc[2 * i] = fmaf(w, __uint_as_float(p << 16), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(w, __uint_as_float(p & 0xFFFF0000u), acc[2 * i + 1]);
+        acc[2 * i] = fmaf(w, T::lo(p), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, T::hi(p), acc[2 * i + 1]);
     }
 }
 
 // acc += w * v for a shard known to be in use (w != 0).
+template <typename T>
 __device__ __forceinline__ void fma8_dense(float (&acc)[8], float w, u32x4 v) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(w, __uint_as_float(v[i] << 16), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(w, __uint_as_float(v[i] & 0xFFFF0000u), acc[2 * i + 1]);
+        acc[2 * i] = fmaf(w, T::lo(v[i]), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, T::hi(v[i]), acc[2 * i + 1]);
     }
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const uint16_t a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
-    const uint16_t b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
-    return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
 }
 
 // Grid: x = group g of kWavesPerBlock local heads, y = token b of the chunk;
@@ -176,12 +200,13 @@ __device__ __forceinline__ float merged_lse(const MergeArgs& a, float M, float S
     return M + __builtin_amdgcn_logf(S) * a.from_log2;
 }
 
+template <typename T>
 __device__ __forceinline__ void store_row(const MergeArgs& a, Row r, int lane, const float (&acc)[8], float L) {
     u32x4 packed;
-    packed[0] = pack_bf16x2(acc[0], acc[1]);
-    packed[1] = pack_bf16x2(acc[2], acc[3]);
-    packed[2] = pack_bf16x2(acc[4], acc[5]);
-    packed[3] = pack_bf16x2(acc[6], acc[7]);
+    packed[0] = T::pack(acc[0], acc[1]);
+    packed[1] = T::pack(acc[2], acc[3]);
+    packed[2] = T::pack(acc[4], acc[5]);
+    packed[3] = T::pack(acc[6], acc[7]);
     __builtin_nontemporal_store(packed, reinterpret_cast<u32x4*>(a.out + r.b * a.o_sb + r.j * a.o_sj + lane * 8));
     if (a.out_lse && lane == 0) a.out_lse[r.b * a.ol_sb + r.j] = L;
 }
@@ -192,7 +217,7 @@ __device__ __forceinline__ void store_row(const MergeArgs& a, Row r, int lane, c
 // are issued first and are all in flight while the weights are formed.
 // Rows whose every weight is nonzero (the common case) take the plain FMA
 // path; a row with an empty shard zeroes that shard's payload first.
-template <int CP>
+template <int CP, typename T>
 __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
     const int lane = threadIdx.x & 63;
     const Row r = row_of(a);
@@ -234,18 +259,18 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (dense) {
 #pragma unroll
-        for (int s = 0; s < CP; ++s) fma8_dense(acc, w[s], v[s]);
+        for (int s = 0; s < CP; ++s) fma8_dense<T>(acc, w[s], v[s]);
     } else {
 #pragma unroll
-        for (int s = 0; s < CP; ++s) fma8(acc, w[s], v[s]);
+        for (int s = 0; s < CP; ++s) fma8<T>(acc, w[s], v[s]);
     }
-    store_row(a, r, lane, acc, merged_lse(a, M, S));
+    store_row<T>(a, r, lane, acc, merged_lse(a, M, S));
 }
 
 // 16 < cp <= 64: the same row algorithm with the shards taken G at a time.
 // Loads past the last shard re-read shard cp-1 (an address already being
 // fetched) and get weight 0.
-template <int G>
+template <int G, typename T>
 __global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
     const int lane = threadIdx.x & 63;
     const Row r = row_of(a);
@@ -275,39 +300,47 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             const float ws = (s0 + i < cp) ? lane_value(wn, min(s0 + i, 63)) : 0.0f;
-            fma8(acc, ws, v[i]);
+            fma8<T>(acc, ws, v[i]);
         }
     }
-    store_row(a, r, lane, acc, merged_lse(a, M, S));
+    store_row<T>(a, r, lane, acc, merged_lse(a, M, S));
 }
 
-template <int CP>
+template <int CP, typename T>
 void launch_fixed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
-    merge_kernel<CP><<<grid, dim3(kBlock), 0, stream>>>(a);
+    merge_kernel<CP, T><<<grid, dim3(kBlock), 0, stream>>>(a);
+}
+
+template <typename T>
+void launch_typed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
+    switch (a.cp) {
+        case 1: launch_fixed<1, T>(a, grid, stream); break;
+        case 2: launch_fixed<2, T>(a, grid, stream); break;
+        case 3: launch_fixed<3, T>(a, grid, stream); break;
+        case 4: launch_fixed<4, T>(a, grid, stream); break;
+        case 5: launch_fixed<5, T>(a, grid, stream); break;
+        case 6: launch_fixed<6, T>(a, grid, stream); break;
+        case 7: launch_fixed<7, T>(a, grid, stream); break;
+        case 8: launch_fixed<8, T>(a, grid, stream); break;
+        case 9: launch_fixed<9, T>(a, grid, stream); break;
+        case 10: launch_fixed<10, T>(a, grid, stream); break;
+        case 11: launch_fixed<11, T>(a, grid, stream); break;
+        case 12: launch_fixed<12, T>(a, grid, stream); break;
+        case 13: launch_fixed<13, T>(a, grid, stream); break;
+        case 14: launch_fixed<14, T>(a, grid, stream); break;
+        case 15: launch_fixed<15, T>(a, grid, stream); break;
+        case 16: launch_fixed<16, T>(a, grid, stream); break;
+        default: merge_kernel_wide<16, T><<<grid, dim3(kBlock), 0, stream>>>(a); break;
+    }
 }
 
 hipError_t launch(const MergeArgs& a, hipStream_t stream) {
     const int tokens = a.rows / a.h_local;
     const dim3 grid((a.h_local + kWavesPerBlock - 1) / kWavesPerBlock, tokens);
-    switch (a.cp) {
-        case 1: launch_fixed<1>(a, grid, stream); break;
-        case 2: launch_fixed<2>(a, grid, stream); break;
-        case 3: launch_fixed<3>(a, grid, stream); break;
-        case 4: launch_fixed<4>(a, grid, stream); break;
-        case 5: launch_fixed<5>(a, grid, stream); break;
-        case 6: launch_fixed<6>(a, grid, stream); break;
-        case 7: launch_fixed<7>(a, grid, stream); break;
-        case 8: launch_fixed<8>(a, grid, stream); break;
-        case 9: launch_fixed<9>(a, grid, stream); break;
-        case 10: launch_fixed<10>(a, grid, stream); break;
-        case 11: launch_fixed<11>(a, grid, stream); break;
-        case 12: launch_fixed<12>(a, grid, stream); break;
-        case 13: launch_fixed<13>(a, grid, stream); break;
-        case 14: launch_fixed<14>(a, grid, stream); break;
-        case 15: launch_fixed<15>(a, grid, stream); break;
-        case 16: launch_fixed<16>(a, grid, stream); break;
-        default: merge_kernel_wide<16><<<grid, dim3(kBlock), 0, stream>>>(a); break;
-    }
+    if (a.dtype == DCP_DTYPE_FP16)
+        launch_typed<F16>(a, grid, stream);
+    else
+        launch_typed<Bf16>(a, grid, stream);
     return hipGetLastError();
 }
 

@@ -28,8 +28,9 @@
  *    call returns a nonzero status, nothing has been launched, and
  *    dcp_last_error() (thread-local) names what to change.
  *  - hip_stream is a hipStream_t passed as void*; NULL is the null stream.
- *  - D (the head dimension, the MLA kv_lora_rank) is 512; partial outputs and
- *    merged outputs are bf16; every LSE is fp32.
+ *  - D (the head dimension, the MLA kv_lora_rank) is 512; the merge's partial
+ *    and merged outputs are bf16 or fp16 (the workspace's dtype), the MLA
+ *    decode's are bf16; every LSE is fp32.
  */
 #ifndef DCP_H
 #define DCP_H
@@ -59,8 +60,9 @@ extern "C" {
 #define DCP_LSE_BHC 0 /* [B, H/cp, cp]: element (b, j, s) at b*l0 + j*l1 + s*l2              */
 #define DCP_LSE_BH1 1 /* FlashMLA [B, H, 1]: element (b, h) at b*l0 + h*l1, h = s*(H/cp) + j */
 
-/* Element types. */
+/* Element types of the merge payload (attn and out). */
 #define DCP_DTYPE_BF16 0
+#define DCP_DTYPE_FP16 1 /* IEEE binary16 */
 
 #define DCP_HEAD_DIM 512 /* value / merged head dimension (the MLA kv_lora_rank)   */
 #define DCP_QK_DIM 576   /* query/key columns of the MLA decode: 512 latent + 64 rope */
@@ -78,7 +80,11 @@ typedef struct dcp_workspace dcp_workspace;
  * capacity_tokens  >= 1; dcp_lse_combine splits wider batches into ordered
  *                  chunks of at most this many tokens.
  * h_local, cp      >= 1; cp <= DCP_MAX_CP.
- * d                DCP_HEAD_DIM; dtype DCP_DTYPE_BF16.
+ * d                DCP_HEAD_DIM.
+ * dtype            DCP_DTYPE_BF16 or DCP_DTYPE_FP16: the element type of the
+ *                  attn and out buffers of every call on this workspace (the
+ *                  pages' merge kernels take fp16 and bf16 payloads, PR #40539
+ *                  Motivation; vLLM PR #48897, port commit).
  * hip_stream       the stream every dcp_lse_combine call on this workspace
  *                  must use (opaque value, compared, never dereferenced).
  * ws               receives the handle; release it with dcp_workspace_destroy.
@@ -95,7 +101,8 @@ int dcp_workspace_destroy(dcp_workspace* ws);
 /*
  * LSE-weighted merge of cp shard partials, read in place.
  *
- * attn      [B, H, D] bf16 attention output, H = cp * h_local of ws.  Token b,
+ * attn      [B, H, D] attention output in the workspace's dtype (bf16 or
+ *           fp16), H = cp * h_local of ws.  Token b,
  *           head h, column d at attn + b*attn_sb + h*attn_sh + d.  Shard s of
  *           local head j is head s*h_local + j.  Padded token strides and
  *           heads taken from a wider backing buffer are allowed.
@@ -104,7 +111,8 @@ int dcp_workspace_destroy(dcp_workspace* ws);
  *           its attn rows are never used, whatever they hold (vLLM PR #48897,
  *           port commit: empty shards publish -inf and skip their payload).
  * lse_mode  DCP_LSE_BASE_E or DCP_LSE_BASE_2; the merged LSE is in the same base.
- * out       [B, h_local, D] bf16 (round to nearest even), row (b, j) at
+ * out       [B, h_local, D] in the workspace's dtype (fp32 result rounded to
+ *           nearest even), row (b, j) at
  *           out + b*out_sb + j*out_sh.  Must not overlap attn.
  * out_lse   [B, h_local] fp32 merged LSE at out_lse + b*out_lse_sb + j, or NULL.
  *

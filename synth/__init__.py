@@ -50,6 +50,22 @@ def normal_bf16(shape, g, mean=0.0, std=1.0) -> torch.Tensor:
     return (torch.randn(shape, generator=g, dtype=torch.float32) * std + mean).to(torch.bfloat16)
 
 
+def normal_16(shape, g, dtype, mean=0.0, std=1.0) -> torch.Tensor:
+    """N(mean, std) drawn in fp32 and rounded to the 16-bit payload type (bf16 or fp16)."""
+    return (torch.randn(shape, generator=g, dtype=torch.float32) * std + mean).to(dtype)
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    """Raw bits of a CPU bf16 or fp16 tensor as a uint16 numpy array (same shape, contiguous)."""
+    assert t.dtype in (torch.bfloat16, torch.float16)
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def payload_name(t: torch.Tensor) -> str:
+    """'bf16' or 'f16': the payload type of a merge input."""
+    return "bf16" if t.dtype == torch.bfloat16 else "f16"
+
+
 def uniform_f32(shape, g, lo, hi) -> torch.Tensor:
     return torch.rand(shape, generator=g, dtype=torch.float32) * (hi - lo) + lo
 
@@ -63,7 +79,7 @@ class MergeCase:
 
     def __init__(self, name, attn, lse, cp, lse_layout, lse_mode, capacity=None):
         self.name = name
-        self.attn = attn              # torch bf16 [B, H, D] (may be a strided view)
+        self.attn = attn              # torch bf16 or fp16 [B, H, D] (may be a strided view)
         self.lse = lse                # torch fp32, [B, H/cp, cp] ("bhc") or [B, H, 1] ("bh1")
         self.cp = cp
         self.lse_layout = lse_layout  # "bhc" | "bh1"
@@ -83,28 +99,32 @@ class MergeCase:
         return self.attn.shape[1] // self.cp
 
 
-def tiny_merge(seed: int = SEED_BASE + 1) -> MergeCase:
+def _sfx(dtype):
+    return "" if dtype == torch.bfloat16 else " fp16"
+
+
+def tiny_merge(seed: int = SEED_BASE + 1, dtype=torch.bfloat16) -> MergeCase:
     g = gen(seed)
     B, H, cp = 3, 16, 2
-    attn = normal_bf16((B, H, D), g)
+    attn = normal_16((B, H, D), g, dtype)
     lse = uniform_f32((B, H // cp, cp), g, -5.0, 15.0)
-    return MergeCase("tiny B=3 H=16 cp=2", attn, lse, cp, "bhc", "e")
+    return MergeCase("tiny B=3 H=16 cp=2" + _sfx(dtype), attn, lse, cp, "bhc", "e")
 
 
-def kimi_merge(B: int, seed: int = SEED_BASE + 2) -> MergeCase:
+def kimi_merge(B: int, seed: int = SEED_BASE + 2, dtype=torch.bfloat16) -> MergeCase:
     g = gen(seed * 1009 + B)
     H, cp = 64, 4
-    attn = normal_bf16((B, H, D), g)
+    attn = normal_16((B, H, D), g, dtype)
     lse = uniform_f32((B, H // cp, cp), g, 0.0, 20.0)
-    return MergeCase("kimi-k2.5-like H=64 cp=4 B=%d" % B, attn, lse, cp, "bhc", "e")
+    return MergeCase("kimi-k2.5-like H=64 cp=4 B=%d" % B + _sfx(dtype), attn, lse, cp, "bhc", "e")
 
 
-def dsv2_merge(B: int, seed: int = SEED_BASE + 3) -> MergeCase:
+def dsv2_merge(B: int, seed: int = SEED_BASE + 3, dtype=torch.bfloat16) -> MergeCase:
     g = gen(seed * 1009 + B)
     H, cp = 128, 8
-    attn = normal_bf16((B, H, D), g)
+    attn = normal_16((B, H, D), g, dtype)
     lse = normal_f32((B, H, 1), g, 10.0, 4.0)
-    return MergeCase("dsv2-236b-like H=128 cp=8 B=%d" % B, attn, lse, cp, "bh1", "2")
+    return MergeCase("dsv2-236b-like H=128 cp=8 B=%d" % B + _sfx(dtype), attn, lse, cp, "bh1", "2")
 
 
 def empty_pairs(B: int, cp: int, frac: float, g: torch.Generator) -> torch.Tensor:
@@ -116,18 +136,18 @@ def empty_pairs(B: int, cp: int, frac: float, g: torch.Generator) -> torch.Tenso
     return mask.view(B, cp)
 
 
-def stress_merge(B: int = 512, seed: int = SEED_BASE + 4, empty_frac: float = 0.1) -> MergeCase:
+def stress_merge(B: int = 512, seed: int = SEED_BASE + 4, empty_frac: float = 0.1, dtype=torch.bfloat16) -> MergeCase:
     g = gen(seed)
     H, cp = 64, 4
     hl = H // cp
-    attn = normal_bf16((B, H, D), g)
+    attn = normal_16((B, H, D), g, dtype)
     lse = uniform_f32((B, hl, cp), g, -30.0, 30.0)
     mask = empty_pairs(B, cp, empty_frac, g)               # [B, cp]
     lse.masked_fill_(mask[:, None, :].expand(B, hl, cp), -math.inf)
     # an empty shard's payload is never written: fill it with NaN so any read shows
     head_mask = mask[:, :, None].expand(B, cp, hl).reshape(B, H)
     attn[head_mask] = float("nan")
-    return MergeCase("stress B=%d H=64 cp=4 10%% empty" % B, attn, lse, cp, "bhc", "e", capacity=128)
+    return MergeCase("stress B=%d H=64 cp=4 10%% empty" % B + _sfx(dtype), attn, lse, cp, "bhc", "e", capacity=128)
 
 
 def tiny_attention(seed: int = SEED_BASE + 1, B: int = 3, hq: int = 8, T: int = 128):

@@ -4,7 +4,8 @@ run the same host tensors through the fp64 oracle, and compare.
 Tolerance (the reading of "within 2 bf16 ULP" used throughout): with r the
 fp64 oracle value and A = sum_s (w_s/S)|O_s| the magnitude of the terms that
 were summed,
-    |g - r| <= 2 ulp_bf16(r) + 2^-16 A,   ulp_bf16(r) = 2^(floor(log2 |r|) - 7).
+    |g - r| <= 2 ulp_bf16(r) + 2^-16 A,   ulp_bf16(r) = 2^(floor(log2 |r|) - 7);
+for fp16 payloads the same with ulp_f16(r) = 2^(max(floor(log2 |r|), -14) - 10).
 The second term only matters under cancellation (|r| << A), where fp32
 accumulation error of order cp * 2^-24 A can exceed 2 ulp(r) although every
 step is correctly rounded.  The merged LSE must satisfy
@@ -35,6 +36,16 @@ def bf16_ulp(r):
     return np.exp2(np.floor(np.log2(a)) - 7)
 
 
+def f16_ulp(r):
+    """Spacing of IEEE binary16 at |r|: 2^(e - 10), with e >= -14 (subnormals are 2^-24 apart)."""
+    a = np.maximum(np.abs(r), 2.0 ** -14)
+    return np.exp2(np.floor(np.log2(a)) - 10)
+
+
+def payload_ulp(r, dtype):
+    return f16_ulp(r) if dtype == torch.float16 else bf16_ulp(r)
+
+
 def bits_of(t):
     """Raw bf16 bits of a (GPU or CPU) bf16 tensor as uint16 numpy."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
@@ -50,13 +61,14 @@ def gpu_merge(case, capacity=None, with_lse=True, attn=None, lse=None, out=None,
         lse = case.lse.to(dev)
     B, hl = case.B, case.h_local
     if out is None:
-        out = torch.empty((B, hl, synth.D), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((B, hl, synth.D), dtype=case.attn.dtype, device=dev)
     if with_lse and out_lse is None:
         out_lse = torch.empty((B, hl), dtype=torch.float32, device=dev)
     cap = capacity or max(B, 1)
     announce("dcp_lse_combine %s capacity=%d attn=%s strides=%s lse=%s%s" % (
         case.name, cap, tuple(attn.shape), attn.stride(), case.lse_layout, tuple(lse.shape)))
-    ws = dcp.dcp_workspace_create(cap, hl, case.cp, stream=stream)
+    dtype = dcp.DCP_DTYPE_FP16 if case.attn.dtype == torch.float16 else dcp.DCP_DTYPE_BF16
+    ws = dcp.dcp_workspace_create(cap, hl, case.cp, dtype=dtype, stream=stream)
     try:
         dcp.dcp_lse_combine(ws, attn, lse, LAYOUT[case.lse_layout], MODE[case.lse_mode], out,
                             out_lse if with_lse else None, stream=stream)
@@ -68,8 +80,8 @@ def gpu_merge(case, capacity=None, with_lse=True, attn=None, lse=None, out=None,
 
 def oracle_merge(case, lse=None):
     lse_np = (case.lse if lse is None else lse).contiguous().numpy()
-    return oracle.merge(synth.bf16_bits(case.attn.contiguous()), lse_np, case.cp, OLAYOUT[case.lse_layout],
-                        OMODE[case.lse_mode])
+    return oracle.merge(synth.bits16(case.attn.contiguous()), lse_np, case.cp, OLAYOUT[case.lse_layout],
+                        OMODE[case.lse_mode], dtype=synth.payload_name(case.attn))
 
 
 def check_against_oracle(case, out, out_lse, ref=None):
@@ -78,13 +90,14 @@ def check_against_oracle(case, out, out_lse, ref=None):
     g = out.float().cpu().double().numpy()
     assert not np.isnan(g).any(), "%s: NaN in the merged output" % case.name
     err = np.abs(g - r)
-    ulp_tol = 2 * bf16_ulp(r)
+    ulp = payload_ulp(r, case.attn.dtype)
+    ulp_tol = 2 * ulp
     tol = ulp_tol + 2.0 ** -16 * A
     bad = err > tol
     assert not bad.any(), "%s: %d elements out of tolerance; worst |g-r| = %.4g at %s (r = %.6g, tol %.3g)" % (
         case.name, int(bad.sum()), err.max(), np.unravel_index(np.argmax(err - tol), err.shape),
         r.flat[np.argmax(err - tol)], tol.flat[np.argmax(err - tol)])
-    report = {"max_err_ulps": float(np.max(err / bf16_ulp(r))), "needed_floor": int((err > ulp_tol).sum())}
+    report = {"max_err_ulps": float(np.max(err / ulp)), "needed_floor": int((err > ulp_tol).sum())}
     if out_lse is not None:
         gL = out_lse.cpu().double().numpy()
         inf = np.isneginf(rL)
