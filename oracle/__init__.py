@@ -30,6 +30,7 @@ BASE_E = 0
 BASE_2 = 1
 LSE_BHC = 0  # [B, H/cp, cp]
 LSE_BH1 = 1  # [B, H, 1]
+_DTYPE = {"bf16": 0, "f16": 1}  # 16-bit payload types of the attention oracle
 
 _lib = None
 
@@ -63,9 +64,9 @@ def _configure(lib):
     lib.oracle_merge_f16.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32, vp, vp, vp, i32]
     lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_f16_to_f64.restype = dbl
-    lib.oracle_attention_partials.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, dbl, i32, vp, i64,
+    lib.oracle_attention_partials.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, dbl, i32, i32, vp, i64,
                                               vp, vp, i32]
-    lib.oracle_attention_full.argtypes = [vp, vp, i64, i64, i64, i64, i64, dbl, i32, vp, i64, vp, vp, i32]
+    lib.oracle_attention_full.argtypes = [vp, vp, i64, i64, i64, i64, i64, dbl, i32, i32, vp, i64, vp, vp, i32]
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f64.restype = dbl
     lib.oracle_max_threads.restype = i32
@@ -151,9 +152,10 @@ def _rows_arg(rows, B, hq):
 
 
 def attention_partials(q_bits, kv_bits, cp: int, scale: float, lse_mode: int, dv: int = 512, rows=None,
-                       threads: int = 0):
+                       threads: int = 0, dtype: str = "bf16"):
     """Per-shard softmax partials.  ``q_bits`` [B, hq, dqk] and ``kv_bits`` [T, dqk]
-    are uint16 bf16 bits.  Returns ``(o [n_rows, cp, dv], lse [n_rows, cp])``."""
+    are uint16 bits of ``dtype`` ("bf16" or "f16").  Returns
+    ``(o [n_rows, cp, dv], lse [n_rows, cp])``."""
     lib = _load()
     q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
     kv_bits = np.ascontiguousarray(kv_bits, dtype=np.uint16)
@@ -164,13 +166,14 @@ def attention_partials(q_bits, kv_bits, cp: int, scale: float, lse_mode: int, dv
     o = np.empty((n, cp, dv), dtype=np.float64)
     lse = np.empty((n, cp), dtype=np.float64)
     rc = lib.oracle_attention_partials(_ptr(q_bits), _ptr(kv_bits), B, hq, T, dqk, dv, cp, float(scale), lse_mode,
-                                       _ptr(rows), n, _ptr(o), _ptr(lse), threads)
+                                       _DTYPE[dtype], _ptr(rows), n, _ptr(o), _ptr(lse), threads)
     if rc:
         raise ValueError("oracle_attention_partials rejected its arguments (rc=%d)" % rc)
     return o, lse
 
 
-def attention_full(q_bits, kv_bits, scale: float, lse_mode: int, dv: int = 512, rows=None, threads: int = 0):
+def attention_full(q_bits, kv_bits, scale: float, lse_mode: int, dv: int = 512, rows=None, threads: int = 0,
+                   dtype: str = "bf16"):
     """Unsharded softmax decode attention.  Returns ``(o [n_rows, dv], lse [n_rows])``."""
     lib = _load()
     q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
@@ -181,7 +184,7 @@ def attention_full(q_bits, kv_bits, scale: float, lse_mode: int, dv: int = 512, 
     o = np.empty((n, dv), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
     rc = lib.oracle_attention_full(_ptr(q_bits), _ptr(kv_bits), B, hq, T, dqk, dv, float(scale), lse_mode,
-                                   _ptr(rows), n, _ptr(o), _ptr(lse), threads)
+                                   _DTYPE[dtype], _ptr(rows), n, _ptr(o), _ptr(lse), threads)
     if rc:
         raise ValueError("oracle_attention_full rejected its arguments (rc=%d)" % rc)
     return o, lse

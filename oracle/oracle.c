@@ -67,6 +67,8 @@
 #define ORACLE_LSE_BHC 0 /* [B, H/cp, cp] contiguous: element (b, j, s)        */
 #define ORACLE_LSE_BH1 1 /* [B, H, 1] contiguous: element (b, s*(H/cp) + j)    */
 
+#define ORACLE_BF16 0
+#define ORACLE_F16 1
 #define ORACLE_OK 0
 #define ORACLE_BAD_ARG 1
 
@@ -244,17 +246,21 @@ int oracle_merge_f16(const uint16_t* O, const float* lse, int64_t B, int64_t H, 
  * kv_stride elements of which the first dqk are the key and the first dv the
  * value.  Writes o[dv] and returns the natural-log LSE (-inf for t0 == t1).
  */
-static double attend_row(const uint16_t* q, const uint16_t* kv, int64_t kv_stride, int64_t t0, int64_t t1,
-                         int64_t dqk, int64_t dv, double scale, double* qd, double* o) {
+typedef double (*decode16_fn)(uint16_t);
+
+static decode16_fn decoder(int dtype) { return dtype == ORACLE_F16 ? oracle_f16_to_f64 : oracle_bf16_to_f64; }
+
+static double attend_row(decode16_fn dec, const uint16_t* q, const uint16_t* kv, int64_t kv_stride, int64_t t0,
+                         int64_t t1, int64_t dqk, int64_t dv, double scale, double* qd, double* o) {
     for (int64_t d = 0; d < dv; ++d) o[d] = 0.0;
     if (t1 <= t0) return -INFINITY;
-    for (int64_t d = 0; d < dqk; ++d) qd[d] = oracle_bf16_to_f64(q[d]);
+    for (int64_t d = 0; d < dqk; ++d) qd[d] = dec(q[d]);
 
     double m = -INFINITY;
     for (int64_t t = t0; t < t1; ++t) {
         const uint16_t* k = kv + t * kv_stride;
         double z = 0.0;
-        for (int64_t d = 0; d < dqk; ++d) z += qd[d] * oracle_bf16_to_f64(k[d]);
+        for (int64_t d = 0; d < dqk; ++d) z += qd[d] * dec(k[d]);
         z *= scale;
         if (z > m) m = z;
     }
@@ -262,11 +268,11 @@ static double attend_row(const uint16_t* q, const uint16_t* kv, int64_t kv_strid
     for (int64_t t = t0; t < t1; ++t) {
         const uint16_t* k = kv + t * kv_stride;
         double z = 0.0;
-        for (int64_t d = 0; d < dqk; ++d) z += qd[d] * oracle_bf16_to_f64(k[d]);
+        for (int64_t d = 0; d < dqk; ++d) z += qd[d] * dec(k[d]);
         z *= scale;
         double p = exp(z - m);
         l += p;
-        for (int64_t d = 0; d < dv; ++d) o[d] += p * oracle_bf16_to_f64(k[d]);
+        for (int64_t d = 0; d < dv; ++d) o[d] += p * dec(k[d]);
     }
     for (int64_t d = 0; d < dv; ++d) o[d] /= l;
     return m + log(l);
@@ -282,16 +288,18 @@ static void shard_bounds(int64_t T, int64_t cp, int64_t s, int64_t* t0, int64_t*
 /*
  * Per-shard decode partials for the query rows listed in `rows` (each row is
  * b*hq + h; NULL means all B*hq rows in order).
- *   q        [B, hq, dqk] contiguous bf16 bits
- *   kv       [T, dqk] contiguous bf16 bits (value = first dv columns)
+ *   q        [B, hq, dqk] contiguous 16-bit bits (dtype ORACLE_BF16 or ORACLE_F16)
+ *   kv       [T, dqk] contiguous 16-bit bits of the same type (value = first dv columns)
  *   o_part   [n_rows, cp, dv]
  *   lse_part [n_rows, cp]     base-e, or times log2 e for base 2
  */
 int oracle_attention_partials(const uint16_t* q, const uint16_t* kv, int64_t B, int64_t hq, int64_t T,
-                              int64_t dqk, int64_t dv, int64_t cp, double scale, int lse_mode,
+                              int64_t dqk, int64_t dv, int64_t cp, double scale, int lse_mode, int dtype,
                               const int64_t* rows, int64_t n_rows, double* o_part, double* lse_part,
                               int nthreads) {
     if (B < 0 || hq <= 0 || T < 0 || dqk <= 0 || dv <= 0 || dv > dqk || cp <= 0) return ORACLE_BAD_ARG;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F16) return ORACLE_BAD_ARG;
+    const decode16_fn dec = decoder(dtype);
     if (lse_mode != ORACLE_BASE_E && lse_mode != ORACLE_BASE_2) return ORACLE_BAD_ARG;
     if (!rows) n_rows = B * hq;
     set_threads(nthreads);
@@ -303,7 +311,8 @@ int oracle_attention_partials(const uint16_t* q, const uint16_t* kv, int64_t B, 
         for (int64_t s = 0; s < cp; ++s) {
             int64_t t0, t1;
             shard_bounds(T, cp, s, &t0, &t1);
-            double lse = attend_row(q + r * dqk, kv, dqk, t0, t1, dqk, dv, scale, qd, o_part + (i * cp + s) * dv);
+            double lse =
+                attend_row(dec, q + r * dqk, kv, dqk, t0, t1, dqk, dv, scale, qd, o_part + (i * cp + s) * dv);
             if (lse_mode == ORACLE_BASE_2) lse *= M_LOG2E;
             lse_part[i * cp + s] = lse;
         }
@@ -315,9 +324,11 @@ int oracle_attention_partials(const uint16_t* q, const uint16_t* kv, int64_t B, 
 /* Full (unsharded) decode attention over all T rows: the brute-force answer
  * the merged partials must reproduce.  o [n_rows, dv], lse [n_rows]. */
 int oracle_attention_full(const uint16_t* q, const uint16_t* kv, int64_t B, int64_t hq, int64_t T, int64_t dqk,
-                          int64_t dv, double scale, int lse_mode, const int64_t* rows, int64_t n_rows, double* o,
-                          double* lse, int nthreads) {
+                          int64_t dv, double scale, int lse_mode, int dtype, const int64_t* rows, int64_t n_rows,
+                          double* o, double* lse, int nthreads) {
     if (B < 0 || hq <= 0 || T < 0 || dqk <= 0 || dv <= 0 || dv > dqk) return ORACLE_BAD_ARG;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F16) return ORACLE_BAD_ARG;
+    const decode16_fn dec = decoder(dtype);
     if (lse_mode != ORACLE_BASE_E && lse_mode != ORACLE_BASE_2) return ORACLE_BAD_ARG;
     if (!rows) n_rows = B * hq;
     set_threads(nthreads);
@@ -326,7 +337,7 @@ int oracle_attention_full(const uint16_t* q, const uint16_t* kv, int64_t B, int6
     for (int64_t i = 0; i < n_rows; ++i) {
         const int64_t r = rows ? rows[i] : i;
         double* qd = (double*)malloc((size_t)dqk * sizeof(double));
-        double l = attend_row(q + r * dqk, kv, dqk, 0, T, dqk, dv, scale, qd, o + i * dv);
+        double l = attend_row(dec, q + r * dqk, kv, dqk, 0, T, dqk, dv, scale, qd, o + i * dv);
         if (lse_mode == ORACLE_BASE_2) l *= M_LOG2E;
         lse[i] = l;
         free(qd);

@@ -37,8 +37,9 @@ MUTANTS = {
                                 "for (int64_t s = 1; s < cp; ++s) {\n            double x = lse[lse_offset"
                                 "(lse_layout, b, j, s, h_local, cp)];\n            if (x > M)"),
     "attention_no_scale": ("        z *= scale;\n        double p", "        double p"),
-    "attention_value_from_tail": ("o[d] += p * oracle_bf16_to_f64(k[d]);",
-                                  "o[d] += p * oracle_bf16_to_f64(k[d + (dqk - dv)]);"),
+    "attention_value_from_tail": ("o[d] += p * dec(k[d]);", "o[d] += p * dec(k[d + (dqk - dv)]);"),
+    "attention_f16_decoded_as_bf16": ("return dtype == ORACLE_F16 ? oracle_f16_to_f64 : oracle_bf16_to_f64;",
+                                      "return oracle_bf16_to_f64;"),
     "attention_lse_drops_max": ("return m + log(l);", "return log(l);"),
     "attention_base2_inverted": ("if (lse_mode == ORACLE_BASE_2) lse *= M_LOG2E;",
                                  "if (lse_mode == ORACLE_BASE_2) lse /= M_LOG2E;"),
@@ -71,6 +72,7 @@ def _pin_checks():
         pins.test_bhc_and_bh1_layouts_agree,
         pins.test_empty_shards_equal_merge_without_them,
         pins.test_full_attention_matches_scipy,
+        pins.test_f16_attention_matches_scipy,
         lambda: pins.test_partials_are_softmax_over_contiguous_shards(130, 4),
         lambda: pins.test_merged_partials_equal_full_attention(256, 4, T2),
     ]

@@ -322,6 +322,26 @@ def _scipy_attention(q_bits, kv_bits, scale, t0, t1, dv=512):
     return softmax(z, axis=1) @ k[:, :dv], logsumexp(z, axis=1)
 
 
+def test_f16_attention_matches_scipy():
+    """fp16 q and KV (the pages' other payload type): the oracle's per-shard
+    partials and full attention against numpy/scipy on the fp16 values."""
+    g = synth.gen(515)
+    q = synth.normal_16((2, 4, synth.D_QK), g, torch.float16)
+    kv = synth.normal_16((96, synth.D_QK), g, torch.float16, std=0.5)
+    qb, kb = synth.bits16(q), synth.bits16(kv)
+    qd = qb.view(np.float16).astype(np.float64).reshape(8, synth.D_QK)
+    kd = kb.view(np.float16).astype(np.float64)
+    z = synth.MLA_SCALE * (qd @ kd.T)
+    o, lse = oracle.attention_full(qb, kb, synth.MLA_SCALE, oracle.BASE_E, dtype="f16")
+    np.testing.assert_allclose(o, softmax(z, axis=1) @ kd[:, :512], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(lse, logsumexp(z, axis=1), rtol=1e-13)
+    op, lp = oracle.attention_partials(qb, kb, 3, synth.MLA_SCALE, oracle.BASE_2, dtype="f16")
+    for s, (t0, t1) in enumerate([(0, 32), (32, 64), (64, 96)]):
+        zz = z[:, t0:t1]
+        np.testing.assert_allclose(op[:, s], softmax(zz, axis=1) @ kd[t0:t1, :512], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(lp[:, s], logsumexp(zz, axis=1) / LN2, rtol=1e-13)
+
+
 def test_full_attention_matches_scipy():
     q, kv = synth.tiny_attention(B=2, hq=4, T=96)
     qb, kb = synth.bf16_bits(q), synth.bf16_bits(kv)
