@@ -57,8 +57,8 @@ _lib.dcp_workspace_destroy.argtypes = [_vp]
 _lib.dcp_lse_combine.argtypes = [_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _i64,
                                  _i64, _vp, _i64, _vp]
 _lib.dcp_mla_partial_decode_scratch_size.argtypes = [_i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
-_lib.dcp_mla_partial_decode.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, _i64, _i32, ctypes.c_float, _i32,
-                                        _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]
+_lib.dcp_mla_partial_decode.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, _i64, _i32, _i32, ctypes.c_float,
+                                        _i32, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]
 _lib.dcp_last_error.restype = ctypes.c_char_p
 _lib.dcp_status_string.argtypes = [_i32]
 _lib.dcp_status_string.restype = ctypes.c_char_p
@@ -199,14 +199,16 @@ def dcp_mla_partial_decode_scratch_size(B: int, hq: int, kv_tokens: int, cp: int
 
 def dcp_mla_partial_decode(q, kv, cp: int, softmax_scale: float, lse_mode: int, o_part, lse_part, scratch=None,
                            stream=None):
-    """Per-shard MLA decode partials.  ``q`` [B, hq, 576] bf16, ``kv`` [T, 576] bf16,
-    ``o_part`` [B, cp*hq, 512] bf16, ``lse_part`` [B, cp*hq] fp32, ``scratch`` a GPU
-    tensor of at least dcp_mla_partial_decode_scratch_size() bytes (or None when 0)."""
+    """Per-shard MLA decode partials.  ``q`` [B, hq, 576], ``kv`` [T, 576] and
+    ``o_part`` [B, cp*hq, 512] all bf16 or all fp16 (the element type passed on),
+    ``lse_part`` [B, cp*hq] fp32, ``scratch`` a GPU tensor of at least
+    dcp_mla_partial_decode_scratch_size() bytes (or None when 0)."""
     import torch
     if q.dim() != 3 or kv.dim() != 2 or o_part.dim() != 3 or lse_part.dim() != 2:
         raise ValueError("q [B,hq,576], kv [T,576], o_part [B,cp*hq,512], lse_part [B,cp*hq] expected")
-    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16 or o_part.dtype != torch.bfloat16:
-        raise ValueError("q, kv and o_part must be bfloat16")
+    if q.dtype not in (torch.bfloat16, torch.float16) or kv.dtype != q.dtype or o_part.dtype != q.dtype:
+        raise ValueError("q, kv and o_part must all be bfloat16 or all float16")
+    dtype = DCP_DTYPE_FP16 if q.dtype == torch.float16 else DCP_DTYPE_BF16
     if lse_part.dtype != torch.float32:
         raise ValueError("lse_part must be float32")
     B, hq, dqk = q.shape
@@ -223,6 +225,6 @@ def dcp_mla_partial_decode(q, kv, cp: int, softmax_scale: float, lse_mode: int, 
     s = _stream_handle(stream)
     _check(_lib.dcp_mla_partial_decode(
         _dev_ptr(q, "q"), B, hq, q.stride(0), q.stride(1), _dev_ptr(kv, "kv") if T > 0 else None, T, kv.stride(0),
-        cp, float(softmax_scale), lse_mode, _dev_ptr(o_part, "o_part"), o_part.stride(0), o_part.stride(1),
+        dtype, cp, float(softmax_scale), lse_mode, _dev_ptr(o_part, "o_part"), o_part.stride(0), o_part.stride(1),
         _dev_ptr(lse_part, "lse_part"), lse_part.stride(0), _dev_ptr(scratch, "scratch"), nbytes, s))
     return o_part, lse_part

@@ -240,7 +240,7 @@ void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* s
 }
 
 int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv, int64_t T, int64_t kv_st,
-             int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb, int64_t o_sh, float* lse,
+             int dtype, int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb, int64_t o_sh, float* lse,
              int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan) {
     const char* fn = "dcp_mla_partial_decode";
     if (B < 0 || hq < 1 || T < 0)
@@ -251,6 +251,8 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     if (lse_mode != DCP_LSE_BASE_E && lse_mode != DCP_LSE_BASE_2)
         return fail(DCP_ERR_INVALID_ARG, "%s: lse_mode %d is neither DCP_LSE_BASE_E nor DCP_LSE_BASE_2", fn,
                     lse_mode);
+    if (dtype != DCP_DTYPE_BF16 && dtype != DCP_DTYPE_FP16)
+        return fail(DCP_ERR_LAYOUT, "%s: dtype %d is neither DCP_DTYPE_BF16 nor DCP_DTYPE_FP16", fn, dtype);
     if (!(softmax_scale > 0.0f) || std::isinf(softmax_scale))
         return fail(DCP_ERR_INVALID_ARG, "%s: softmax_scale must be a positive finite number", fn);
     if (B * static_cast<int64_t>(hq) > (int64_t{1} << 30))
@@ -315,6 +317,7 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     a.cp = cp;
     a.nsplit = nsplit;
     a.row_blocks = (a.rows + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
+    a.dtype = dtype;
     a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
     a.lse_scale = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;
     *plan = MlaPlan{};
@@ -348,7 +351,7 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
         m.ol_sb = lse_sb;
         m.h_local = static_cast<int32_t>(H);
         m.cp = nsplit;
-        m.dtype = DCP_DTYPE_BF16;
+        m.dtype = dtype;
         m.rows = 0;                    // set per token chunk at launch
         m.to_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 1.4426950408889634f;
         m.from_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;

@@ -117,6 +117,7 @@ struct MlaArgs {
     int32_t cp;
     int32_t nsplit;
     int32_t row_blocks;     // ceil(rows / kMlaRowsPerBlock)
+    int32_t dtype;          // DCP_DTYPE_BF16 or DCP_DTYPE_FP16 (q, kv, o)
     float scale_log2;       // softmax_scale * log2 e
     float lse_scale;        // lse = log2-domain LSE * lse_scale (1 for base 2, ln 2 for base e)
 };
@@ -134,7 +135,7 @@ void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* s
 
 // Validate every argument of dcp_mla_partial_decode and build its plan.
 int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv, int64_t T, int64_t kv_st,
-             int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb, int64_t o_sh, float* lse,
+             int dtype, int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb, int64_t o_sh, float* lse,
              int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan);
 
 }  // namespace dcp

@@ -12,7 +12,8 @@
 //
 // Mapping to CDNA4.  Every query token attends over the same cache, so one
 // shard is a flash-attention pass over M = B*hq query rows: a dense
-// contraction, run on MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
+// contraction, run on MFMA (v_mfma_f32_16x16x32_bf16, or _f16 for fp16
+// inputs; fp32 accumulate).
 //  * A workgroup owns 128 query rows, 16 per wavefront, 8 wavefronts (two per
 //    SIMD, so one wavefront's softmax and waits overlap the other's MFMAs),
 //    and one key range (a split of one shard).  Each wavefront keeps its 16
@@ -88,10 +89,14 @@ static_assert(kTileChunks == 64 * 2 * (kRowChunks / 4), "a tile is 2 x 18 blocks
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __fp16 fp16x4 __attribute__((ext_vector_type(4)));  // the transpose load's fp16 vector type
+typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
 
 constexpr int kBlockElems = 512;                            // one 1 KiB LDS block
 constexpr int kHalfBlocks = kRowChunks / 4;                  // 18 blocks per 16 keys
@@ -117,12 +122,46 @@ __device__ __forceinline__ float sum_xor32(float v) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+// The two 16-bit element types of q, the cache and the output: the MFMA,
+// the transpose load and the conversions of each.  Everything else in the
+// kernel moves raw 16-bit words and is shared.
+struct Bf16 {
+    typedef __bf16 elem;
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    static __device__ __forceinline__ f32x4 mfma(v8 a, v8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ v4 tr(const __attribute__((address_space(3))) char* p) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+    }
+};
+
+struct F16 {
+    typedef _Float16 elem;
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+    static __device__ __forceinline__ f32x4 mfma(v8 a, v8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ v4 tr(const __attribute__((address_space(3))) char* p) {
+        return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(p)));
+    }
+};
+
+template <typename T>
+__device__ __forceinline__ typename T::v8 as_v8(u32x4 v) { return __builtin_bit_cast(typename T::v8, v); }
 
 // Transpose load of 8 bytes at LDS element offset `off` of `base`.
-__device__ __forceinline__ bf16x4 ds_read_tr(const uint16_t* base, int off) {
-    auto p = (const __attribute__((address_space(3))) char*)(base) + 2 * off;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+template <typename T>
+__device__ __forceinline__ typename T::v4 ds_read_tr(const uint16_t* base, int off) {
+    return T::tr((const __attribute__((address_space(3))) char*)(base) + 2 * off);
+}
+
+// Round to nearest even in the element type, as raw bits.
+template <typename T>
+__device__ __forceinline__ uint32_t to_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<typename T::elem>(x));
 }
 
 // Which (row block, shard, split) a workgroup computes.  Block ids are dealt
@@ -226,8 +265,9 @@ struct RowState {
 };
 
 // One 32-key tile: scores, online softmax, p.v.
+template <typename T>
 __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* kt, const LaneOffsets& off,
-                                             const bf16x8 (&qf)[kQSteps], RowState& st, int64_t t0, int64_t k1,
+                                             const typename T::v8 (&qf)[kQSteps], RowState& st, int64_t t0, int64_t k1,
                                              int g) {
     // S^T = K Q^T for keys [t0, t0+16) (sa) and [t0+16, t0+32) (sb): the lane
     // holds the scores of row r16 with keys 4g+i and 16+4g+i.
@@ -238,19 +278,19 @@ __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* k
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
     {
         constexpr int kAhead = 2;
-        bf16x8 ra[kAhead + 1], rb[kAhead + 1];
+        typename T::v8 ra[kAhead + 1], rb[kAhead + 1];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int f = 0; f < kQSteps + kAhead; ++f) {
             if (f < kQSteps) {
                 const int o = ((f & 1) ? off.s_odd : off.s_even) + kBlockElems * f;
-                ra[f % (kAhead + 1)] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o));
-                rb[f % (kAhead + 1)] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + o + kHalfElems));
+                ra[f % (kAhead + 1)] = as_v8<T>(*reinterpret_cast<const u32x4*>(kt + o));
+                rb[f % (kAhead + 1)] = as_v8<T>(*reinterpret_cast<const u32x4*>(kt + o + kHalfElems));
             }
             if (f >= kAhead) {
                 const int u = f - kAhead;
-                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[u % (kAhead + 1)], qf[u], sa, 0, 0, 0);
-                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[u % (kAhead + 1)], qf[u], sb, 0, 0, 0);
+                sa = T::mfma(ra[u % (kAhead + 1)], qf[u], sa);
+                sb = T::mfma(rb[u % (kAhead + 1)], qf[u], sb);
             }
         }
 #pragma unroll
@@ -281,12 +321,12 @@ __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* k
     }
     st.m_run = m_new;
     float psum = 0.0f;
-    bf16x8 pb;
+    typename T::v8 pb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float p = __builtin_amdgcn_exp2f(z[i] - m_new);
         psum += p;
-        pb[i] = static_cast<__bf16>(p);
+        pb[i] = static_cast<typename T::elem>(p);
     }
     st.l_run += psum;
 
@@ -295,20 +335,20 @@ __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* k
     // keys 4g..4g+3 and 16+4g..16+4g+3, in P^T (pb) and V^T alike.
     {
         constexpr int kAhead = 2;
-        bf16x4 rl[kAhead + 1], rh[kAhead + 1];
+        typename T::v4 rl[kAhead + 1], rh[kAhead + 1];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < kDTiles + kAhead; ++t) {
             if (t < kDTiles) {
                 const int o = off.tr[t & 3] + 2 * kBlockElems * (t >> 2);
-                rl[t % (kAhead + 1)] = ds_read_tr(kt, o);
-                rh[t % (kAhead + 1)] = ds_read_tr(kt, o + kHalfElems);
+                rl[t % (kAhead + 1)] = ds_read_tr<T>(kt, o);
+                rh[t % (kAhead + 1)] = ds_read_tr<T>(kt, o + kHalfElems);
             }
             if (t >= kAhead) {
                 const int u = t - kAhead;
-                const bf16x4 lo = rl[u % (kAhead + 1)], hi = rh[u % (kAhead + 1)];
-                const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                st.oacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.oacc[u], 0, 0, 0);
+                const typename T::v4 lo = rl[u % (kAhead + 1)], hi = rh[u % (kAhead + 1)];
+                const typename T::v8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                st.oacc[u] = T::mfma(va, pb, st.oacc[u]);
             }
         }
 #pragma unroll
@@ -320,6 +360,7 @@ __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* k
     }
 }
 
+template <typename T>
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t tile0[kTileAlloc];
     __shared__ __attribute__((aligned(16))) uint16_t tile1[kTileAlloc];
@@ -346,11 +387,11 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     const int h = row - b * a.hq;
 
     // Q fragments: fragment f holds columns 32f + 8g .. +7 of this lane's row.
-    bf16x8 qf[kQSteps];
+    typename T::v8 qf[kQSteps];
     {
         const uint16_t* qrow = a.q + b * a.q_sb + h * a.q_sh + 8 * g;
 #pragma unroll
-        for (int f = 0; f < kQSteps; ++f) qf[f] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * f));
+        for (int f = 0; f < kQSteps; ++f) qf[f] = as_v8<T>(*reinterpret_cast<const u32x4*>(qrow + 32 * f));
         // Settle these loads here: a wait for them left inside the key loop
         // would also wait for the tile copies in flight there.
         __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -390,15 +431,15 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     for (int it = 0; it < ntiles; it += 3) {
         const int64_t t0 = k0 + static_cast<int64_t>(it) * kKeys;
         if (it + 2 < ntiles) dma_tile(a, tile2, t0 + 2 * kKeys, k1, wave, lane);
-        compute_tile(a, tile0, off, qf, st, t0, k1, g);
+        compute_tile<T>(a, tile0, off, qf, st, t0, k1, g);
         if (it + 1 >= ntiles) break;
         if (it + 2 < ntiles) older_tile_ready(); else all_tiles_ready();
         if (it + 3 < ntiles) dma_tile(a, tile0, t0 + 3 * kKeys, k1, wave, lane);
-        compute_tile(a, tile1, off, qf, st, t0 + kKeys, k1, g);
+        compute_tile<T>(a, tile1, off, qf, st, t0 + kKeys, k1, g);
         if (it + 2 >= ntiles) break;
         if (it + 3 < ntiles) older_tile_ready(); else all_tiles_ready();
         if (it + 4 < ntiles) dma_tile(a, tile1, t0 + 4 * kKeys, k1, wave, lane);
-        compute_tile(a, tile2, off, qf, st, t0 + 2 * kKeys, k1, g);
+        compute_tile<T>(a, tile2, off, qf, st, t0 + 2 * kKeys, k1, g);
         if (it + 3 >= ntiles) break;
         if (it + 4 < ntiles) older_tile_ready(); else all_tiles_ready();
     }
@@ -418,10 +459,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
 #pragma unroll
     for (int t = 0; t < kDTiles; ++t) {
         const f32x4 v = st.oacc[t];
-        const uint32_t lo = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[0] * inv))) |
-                            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[1] * inv))) << 16);
-        const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2] * inv))) |
-                            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[3] * inv))) << 16);
+        const uint32_t lo = to_bits<T>(v[0] * inv) | (to_bits<T>(v[1] * inv) << 16);
+        const uint32_t hi = to_bits<T>(v[2] * inv) | (to_bits<T>(v[3] * inv) << 16);
         *reinterpret_cast<uint2*>(orow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
     }
     if (g == 0)
@@ -432,16 +471,21 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
 }  // namespace dcp
 
 extern "C" int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv,
-                                      int64_t kv_tokens, int64_t kv_st, int cp, float softmax_scale, int lse_mode,
+                                      int64_t kv_tokens, int64_t kv_st, int dtype, int cp, float softmax_scale,
+                                      int lse_mode,
                                       void* o_part, int64_t o_sb, int64_t o_sh, float* lse_part, int64_t lse_sb,
                                       void* scratch, size_t scratch_bytes, void* hip_stream) {
     dcp::MlaPlan plan;
-    const int rc = dcp::plan_mla(q, B, hq, q_sb, q_sh, kv, kv_tokens, kv_st, cp, softmax_scale, lse_mode, o_part,
+    const int rc = dcp::plan_mla(q, B, hq, q_sb, q_sh, kv, kv_tokens, kv_st, dtype, cp, softmax_scale, lse_mode, o_part,
                                  o_sb, o_sh, lse_part, lse_sb, scratch, scratch_bytes, &plan);
     if (rc != DCP_OK) return rc;
     if (plan.blocks == 0) return dcp::ok();
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    dcp::mla_decode_kernel<<<dim3(static_cast<unsigned>(plan.blocks)), dim3(dcp::kThreads), 0, stream>>>(plan.args);
+    const dim3 grid(static_cast<unsigned>(plan.blocks));
+    if (plan.args.dtype == DCP_DTYPE_FP16)
+        dcp::mla_decode_kernel<dcp::F16><<<grid, dim3(dcp::kThreads), 0, stream>>>(plan.args);
+    else
+        dcp::mla_decode_kernel<dcp::Bf16><<<grid, dim3(dcp::kThreads), 0, stream>>>(plan.args);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && plan.args.nsplit > 1) {
         // The splits of every (token, shard, head) are merged like DCP shards.

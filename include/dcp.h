@@ -28,9 +28,9 @@
  *    call returns a nonzero status, nothing has been launched, and
  *    dcp_last_error() (thread-local) names what to change.
  *  - hip_stream is a hipStream_t passed as void*; NULL is the null stream.
- *  - D (the head dimension, the MLA kv_lora_rank) is 512; the merge's partial
- *    and merged outputs are bf16 or fp16 (the workspace's dtype), the MLA
- *    decode's are bf16; every LSE is fp32.
+ *  - D (the head dimension, the MLA kv_lora_rank) is 512; payloads are bf16
+ *    or fp16 (the merge: the workspace's dtype; the MLA decode: its dtype
+ *    argument); every LSE is fp32.
  */
 #ifndef DCP_H
 #define DCP_H
@@ -153,26 +153,29 @@ int dcp_lse_combine(dcp_workspace* ws, const void* attn, int64_t B, int H, int64
  * DCP_LSE_BH1 (l0 = lse_sb, l1 = 1) merges the shards into exact attention
  * over all T tokens.
  *
- * q         [B, hq, 576] bf16, row (b, h) at q + b*q_sb + h*q_sh.
- * kv        [T, 576] bf16, token t at kv + t*kv_st (one cache shared by all
+ * dtype     DCP_DTYPE_BF16 or DCP_DTYPE_FP16: the element type of q, kv and
+ *           o_part (the pages' kernels take both).
+ * q         [B, hq, 576], row (b, h) at q + b*q_sb + h*q_sh.
+ * kv        [T, 576], token t at kv + t*kv_st (one cache shared by all
  *           B query tokens).  May be NULL when T == 0.
- * o_part    [B, cp*hq, 512] bf16, row (b, s*hq + h) at o_part + b*o_sb + (s*hq+h)*o_sh.
+ * o_part    [B, cp*hq, 512], row (b, s*hq + h) at o_part + b*o_sb + (s*hq+h)*o_sh.
  * lse_part  [B, cp*hq] fp32 at lse_part + b*lse_sb + s*hq + h.
  * scratch   device buffer of at least dcp_mla_partial_decode_scratch_size()
  *           bytes, 16-byte aligned, for the split-KV partials: when a shard's
  *           keys are split over several workgroups, each split's normalised
- *           bf16 output and LSE land here and are merged into o_part /
+ *           output (in dtype) and LSE land here and are merged into o_part /
  *           lse_part by the dcp_lse_combine kernel.  NULL allowed when the
  *           size is 0 (one split per shard).  Contents on entry are ignored.
- * Arithmetic: bf16 MFMA products with fp32 accumulation for q.k and p.v,
- * fp32 online softmax; p is rounded to bf16 before the p.v product.
+ * Arithmetic: MFMA products of the 16-bit inputs with fp32 accumulation for
+ * q.k and p.v, fp32 online softmax; p is rounded to dtype before the p.v
+ * product.
  * Alignment: q, kv, o_part 16-byte aligned; q_sb, q_sh, kv_st, o_sb, o_sh
  * multiples of 8 elements; lse_part 4-byte aligned.
  */
 int dcp_mla_partial_decode_scratch_size(int64_t B, int hq, int64_t kv_tokens, int cp, size_t* bytes);
 
 int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv,
-                           int64_t kv_tokens, int64_t kv_st, int cp, float softmax_scale, int lse_mode,
+                           int64_t kv_tokens, int64_t kv_st, int dtype, int cp, float softmax_scale, int lse_mode,
                            void* o_part, int64_t o_sb, int64_t o_sh, float* lse_part, int64_t lse_sb, void* scratch,
                            size_t scratch_bytes, void* hip_stream);
 

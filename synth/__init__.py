@@ -150,20 +150,20 @@ def stress_merge(B: int = 512, seed: int = SEED_BASE + 4, empty_frac: float = 0.
     return MergeCase("stress B=%d H=64 cp=4 10%% empty" % B + _sfx(dtype), attn, lse, cp, "bhc", "e", capacity=128)
 
 
-def tiny_attention(seed: int = SEED_BASE + 1, B: int = 3, hq: int = 8, T: int = 128):
+def tiny_attention(seed: int = SEED_BASE + 1, B: int = 3, hq: int = 8, T: int = 128, dtype=torch.bfloat16):
     g = gen(seed * 7 + 5)
-    q = normal_bf16((B, hq, D_QK), g)
-    kv = normal_bf16((T, D_QK), g, 0.0, 0.5)
+    q = normal_16((B, hq, D_QK), g, dtype)
+    kv = normal_16((T, D_QK), g, dtype, 0.0, 0.5)
     return q, kv
 
 
-def mla_decode(B: int, T: int = 131072, hq: int = 128, seed: int = SEED_BASE + 5, kv_seed=None):
-    """q [B, hq, 576] ~ N(0,1) and one latent KV cache [T, 576] ~ N(0, 0.5), both bf16.
-    The cache is drawn from its own seed so every B sees the same cache."""
+def mla_decode(B: int, T: int = 131072, hq: int = 128, seed: int = SEED_BASE + 5, kv_seed=None, dtype=torch.bfloat16):
+    """q [B, hq, 576] ~ N(0,1) and one latent KV cache [T, 576] ~ N(0, 0.5), both bf16
+    (or fp16).  The cache is drawn from its own seed so every B sees the same cache."""
     gq = gen(seed * 1009 + B)
-    q = normal_bf16((B, hq, D_QK), gq)
+    q = normal_16((B, hq, D_QK), gq, dtype)
     gk = gen(kv_seed if kv_seed is not None else seed * 1013 + T)
-    kv = normal_bf16((T, D_QK), gk, 0.0, 0.5)
+    kv = normal_16((T, D_QK), gk, dtype, 0.0, 0.5)
     return q, kv
 
 

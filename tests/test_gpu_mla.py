@@ -43,11 +43,12 @@ def run_producer(q, kv, cp, scale, mode, q_dev=None, o_part=None):
         q_dev = q.to(DEV)
     kv_dev = kv.to(DEV)
     if o_part is None:
-        o_part = torch.empty((B, cp * hq, 512), dtype=torch.bfloat16, device=DEV)
+        o_part = torch.empty((B, cp * hq, 512), dtype=q.dtype, device=DEV)
     lse_part = torch.empty((B, cp * hq), dtype=torch.float32, device=DEV)
     nbytes = dcp.dcp_mla_partial_decode_scratch_size(B, hq, T, cp)
     scratch = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV) if nbytes else None
-    announce("dcp_mla_partial_decode B=%d hq=%d T=%d cp=%d mode=%d scratch=%d" % (B, hq, T, cp, mode, nbytes))
+    announce("dcp_mla_partial_decode %s B=%d hq=%d T=%d cp=%d mode=%d scratch=%d" % (
+        synth.payload_name(q), B, hq, T, cp, mode, nbytes))
     dcp.dcp_mla_partial_decode(q_dev, kv_dev, cp, scale, mode, o_part, lse_part, scratch)
     torch.cuda.synchronize()
     return o_part, lse_part
@@ -56,8 +57,8 @@ def run_producer(q, kv, cp, scale, mode, q_dev=None, o_part=None):
 def check_partials(q, kv, cp, scale, mode, o_part, lse_part, rows=None):
     """Compare the GPU partials of the listed query rows (b*hq + h) with the oracle."""
     B, hq, _ = q.shape
-    o_r, l_r = oracle.attention_partials(synth.bf16_bits(q), synth.bf16_bits(kv), cp, scale, OMODE[mode],
-                                         rows=rows, threads=THREADS)
+    o_r, l_r = oracle.attention_partials(synth.bits16(q), synth.bits16(kv), cp, scale, OMODE[mode],
+                                         rows=rows, threads=THREADS, dtype=synth.payload_name(q))
     rows = np.arange(B * hq) if rows is None else np.asarray(rows)
     o_g = o_part.float().cpu().double().numpy().reshape(B, cp, hq, 512)
     l_g = lse_part.cpu().double().numpy().reshape(B, cp, hq)
@@ -81,9 +82,10 @@ def check_partials(q, kv, cp, scale, mode, o_part, lse_part, rows=None):
 def check_end_to_end(q, kv, cp, scale, mode, o_part, lse_part, rows):
     """Merge the GPU partials with dcp_lse_combine and compare with full attention."""
     B, hq, _ = q.shape
-    out = torch.empty((B, hq, 512), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((B, hq, 512), dtype=q.dtype, device=DEV)
     out_lse = torch.empty((B, hq), dtype=torch.float32, device=DEV)
-    ws = dcp.dcp_workspace_create(B, hq, cp)
+    ws = dcp.dcp_workspace_create(B, hq, cp,
+                                  dtype=dcp.DCP_DTYPE_FP16 if q.dtype == torch.float16 else dcp.DCP_DTYPE_BF16)
     announce("dcp_lse_combine of producer output B=%d hq=%d cp=%d" % (B, hq, cp))
     dcp.dcp_lse_combine(ws, o_part, lse_part, dcp.DCP_LSE_BH1, mode, out, out_lse)
     torch.cuda.synchronize()
@@ -93,8 +95,8 @@ def check_end_to_end(q, kv, cp, scale, mode, o_part, lse_part, rows):
                            "e" if mode == dcp.DCP_LSE_BASE_E else "2")
     check_against_oracle(case, out, out_lse)
     # end to end against full attention
-    o_f, l_f = oracle.attention_full(synth.bf16_bits(q), synth.bf16_bits(kv), scale, OMODE[mode], rows=rows,
-                                     threads=THREADS)
+    o_f, l_f = oracle.attention_full(synth.bits16(q), synth.bits16(kv), scale, OMODE[mode], rows=rows,
+                                     threads=THREADS, dtype=synth.payload_name(q))
     g = out.float().cpu().double().numpy().reshape(B * hq, 512)
     gl = out_lse.cpu().double().numpy().reshape(B * hq)
     for i, r in enumerate(rows):
@@ -194,3 +196,58 @@ def test_full_size_config_sampled_rows(B):
     worst = check_partials(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
     announce("full size B=%d: worst partial row error %.3g of row max" % (B, worst))
     check_end_to_end(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
+
+
+# ------------------------------------------------------------- fp16 payloads
+
+F16 = torch.float16
+
+
+@pytest.mark.parametrize("mode", [dcp.DCP_LSE_BASE_E, dcp.DCP_LSE_BASE_2])
+def test_tiny_f16(mode):
+    """fp16 q and cache (the pages' other payload type) through the fp16 MFMA."""
+    q, kv = synth.tiny_attention(dtype=F16)
+    o, l = run_producer(q, kv, 2, synth.MLA_SCALE, mode)
+    assert o.dtype == F16
+    check_partials(q, kv, 2, synth.MLA_SCALE, mode, o, l)
+    check_end_to_end(q, kv, 2, synth.MLA_SCALE, mode, o, l, rows=np.arange(24))
+
+
+@pytest.mark.parametrize("B,hq,T,cp", [(2, 128, 4096, 4), (5, 24, 777, 3)])
+def test_split_kv_shapes_f16(B, hq, T, cp):
+    """Several splits per shard: the fp16 per-split partials are reduced by the
+    fp16 instance of the merge kernel."""
+    q, kv = synth.mla_decode(B, T=T, hq=hq, seed=2100 + T, dtype=F16)
+    o, l = run_producer(q, kv, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E)
+    rows = np.unique(np.concatenate([np.arange(min(8, B * hq)), np.arange(B * hq)[-8:],
+                                     np.random.default_rng(T).integers(0, B * hq, 16)]))
+    check_partials(q, kv, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
+    check_end_to_end(q, kv, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
+
+
+def test_empty_shards_f16():
+    q, kv = synth.mla_decode(2, T=3, hq=16, seed=177, dtype=F16)
+    o, l = run_producer(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_2)
+    check_partials(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_2, o, l)
+    assert torch.all(torch.isneginf(l.cpu().reshape(2, 4, 16)[:, 0]))
+
+
+@pytest.mark.parametrize("B", [1, 64])
+def test_full_size_config_sampled_rows_f16(B):
+    _, kv = synth.mla_decode(1, dtype=F16)
+    q = synth.normal_16((B, 128, 576), synth.gen(3100 + B), F16)
+    o, l = run_producer(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E)
+    rng = np.random.default_rng(100 + B)
+    rows = np.unique(np.concatenate([[0, B * 128 - 1], rng.integers(0, B * 128, 6)]))
+    worst = check_partials(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
+    announce("full size fp16 B=%d: worst partial row error %.3g of row max" % (B, worst))
+    check_end_to_end(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
+
+
+def test_mixed_element_types_are_rejected():
+    q, kv = synth.tiny_attention()
+    o = torch.empty((3, 16, 512), dtype=F16, device=DEV)
+    l = torch.empty((3, 16), dtype=torch.float32, device=DEV)
+    announce("producer with bf16 q and fp16 o_part (rejected in the binding)")
+    with pytest.raises(ValueError):
+        dcp.dcp_mla_partial_decode(q.to(DEV), kv.to(DEV), 2, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, None)
