@@ -132,7 +132,8 @@ int plan_merge(const dcp_workspace* ws, const void* attn, int64_t B, int H, int6
 
     // Layout adapter: (b, j, s) strides of O and of the LSE.
     MergeArgs a{};
-    a.attn = static_cast<const uint16_t*>(attn);
+    a.attn = attn;
+    a.in_dtype = ws->dtype;
     a.lse = lse;
     a.out = static_cast<uint16_t*>(out);
     a.out_lse = out_lse;
@@ -190,16 +191,20 @@ int plan_merge(const dcp_workspace* ws, const void* attn, int64_t B, int H, int6
     return ok();
 }
 
-MergeArgs chunk_args(const MergePlan& plan, int64_t k) {
-    MergeArgs a = plan.args;
-    const int64_t t0 = k * plan.chunk;
-    const int64_t t1 = (t0 + plan.chunk < plan.B) ? t0 + plan.chunk : plan.B;
-    a.attn += t0 * a.a_sb;
+MergeArgs merge_args_at(const MergeArgs& a0, int64_t t0, int64_t tokens) {
+    MergeArgs a = a0;
+    a.attn = static_cast<const char*>(a.attn) + t0 * a.a_sb * payload_bytes(a.in_dtype);
     a.lse += t0 * a.l_sb;
     a.out += t0 * a.o_sb;
     if (a.out_lse) a.out_lse += t0 * a.ol_sb;
-    a.rows = static_cast<int32_t>((t1 - t0) * a.h_local);
+    a.rows = static_cast<int32_t>(tokens * a.h_local);
     return a;
+}
+
+MergeArgs chunk_args(const MergePlan& plan, int64_t k) {
+    const int64_t t0 = k * plan.chunk;
+    const int64_t t1 = (t0 + plan.chunk < plan.B) ? t0 + plan.chunk : plan.B;
+    return merge_args_at(plan.args, t0, t1 - t0);
 }
 
 // ------------------------------------------------------------- MLA decode plan
@@ -208,7 +213,7 @@ MergeArgs chunk_args(const MergePlan& plan, int64_t k) {
 // ceil(B*hq/128)*cp units of work -- 4 at B = 1 with 128 heads and cp = 4, far
 // too few for 256 compute units.  Each shard's keys are therefore split into
 // nsplit ranges processed by separate workgroups; each leaves a normalised
-// bf16 partial and its LSE, and the merge kernel reduces the splits exactly
+// fp32 partial and its LSE, and the merge kernel reduces the splits exactly
 // as it merges DCP shards.  The split count aims at about kMlaTargetBlocks
 // workgroups and never gives a split fewer than kMlaMinSplitKeys keys.
 
@@ -235,7 +240,7 @@ void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* s
         *scratch_bytes = 0;
     } else {
         const int64_t parts = static_cast<int64_t>(cp) * n * rows;  // (token, split, shard, head)
-        *scratch_bytes = static_cast<size_t>(parts * kMlaVDim * 2 + parts * 4);
+        *scratch_bytes = static_cast<size_t>(parts * kMlaVDim * 4 + parts * 4);
     }
 }
 
@@ -321,26 +326,24 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
     a.lse_scale = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;
     *plan = MlaPlan{};
-    if (nsplit == 1) {
-        a.o = static_cast<uint16_t*>(o);
-        a.lse = lse;
-        a.o_sb = o_sb;
-        a.o_sh = o_sh;
-        a.lse_sb = lse_sb;
-    } else {
-        // Per-split partials in the scratch buffer, then the merge over splits.
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    a.o_sb = o_sb;
+    a.o_sh = o_sh;
+    a.lse_sb = lse_sb;
+    if (nsplit > 1) {
+        // Per-split fp32 partials in the scratch buffer, then the merge over splits.
         const int64_t heads = static_cast<int64_t>(nsplit) * H;   // per token
-        a.o = static_cast<uint16_t*>(scratch);
-        a.lse = reinterpret_cast<float*>(static_cast<char*>(scratch) + B * heads * kMlaVDim * 2);
-        a.o_sb = heads * kMlaVDim;
-        a.o_sh = kMlaVDim;
-        a.lse_sb = heads;
+        a.part_o = static_cast<float*>(scratch);
+        a.part_lse = static_cast<float*>(scratch) + B * heads * kMlaVDim;
+        a.part_sb = heads;
         MergeArgs m{};
-        m.attn = a.o;
-        m.lse = a.lse;
+        m.attn = a.part_o;
+        m.in_dtype = kPayloadF32;
+        m.lse = a.part_lse;
         m.out = static_cast<uint16_t*>(o);
         m.out_lse = lse;
-        m.a_sb = a.o_sb;
+        m.a_sb = heads * kMlaVDim;
         m.a_sj = kMlaVDim;             // local head j = s*hq + h
         m.a_ss = H * kMlaVDim;         // split p
         m.l_sb = heads;

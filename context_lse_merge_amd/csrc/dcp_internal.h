@@ -13,13 +13,13 @@ namespace dcp {
 // Kernel parameters of one merge launch, after the layout adapter has turned
 // the caller's [B, H, D] attention buffer and its LSE layout into one strided
 // (token b, local head j, shard s) addressing scheme:
-//   O(b, j, s, :)  at attn    + b*a_sb + j*a_sj + s*a_ss      (bf16 elements)
+//   O(b, j, s, :)  at attn    + b*a_sb + j*a_sj + s*a_ss      (elements of in_dtype)
 //   lse(b, j, s)   at lse     + b*l_sb + j*l_sj + s*l_ss      (fp32 elements)
 //   out(b, j, :)   at out     + b*o_sb + j*o_sj               (bf16 elements)
 //   L(b, j)        at out_lse + b*ol_sb + j                   (fp32, optional)
 // Rows are r = b*h_local + j, r < rows.
 struct MergeArgs {
-    const uint16_t* attn;
+    const void* attn;
     const float* lse;
     uint16_t* out;
     float* out_lse;
@@ -30,7 +30,8 @@ struct MergeArgs {
     int32_t rows;
     int32_t h_local;
     int32_t cp;
-    int32_t dtype;      // DCP_DTYPE_BF16 or DCP_DTYPE_FP16 (attn and out)
+    int32_t in_dtype;   // attn: DCP_DTYPE_BF16, DCP_DTYPE_FP16 or kPayloadF32 (internal)
+    int32_t dtype;      // out: DCP_DTYPE_BF16 or DCP_DTYPE_FP16
     // (lse_s - M) * to_log2 is the exponent of 2 of the weight; log2(S) * from_log2
     // is added to M for the merged LSE.  Base 2: both 1.  Base e: log2 e and ln 2.
     float to_log2;
@@ -39,6 +40,16 @@ struct MergeArgs {
 
 // Most tokens one merge launch covers (the grid's second dimension).
 constexpr int64_t kMaxLaunchTokens = 65535;
+
+// Payload type of the merge input used only inside the library: fp32
+// partials (the MLA decode's split partials).  Never accepted from callers.
+constexpr int32_t kPayloadF32 = 100;
+
+// Bytes of one payload element of a merge input type.
+inline int64_t payload_bytes(int32_t in_dtype) { return in_dtype == kPayloadF32 ? 4 : 2; }
+
+// The arguments `a` moved to start at token t0 and cover `tokens` tokens.
+MergeArgs merge_args_at(const MergeArgs& a, int64_t t0, int64_t tokens);
 
 // A validated merge call: the arguments of the first chunk plus how to step
 // to the next one.
@@ -97,19 +108,22 @@ constexpr int kMlaMaxSplits = DCP_MAX_CP;  // ... nor above what the merge kerne
 // Kernel parameters of the MLA split-KV decode.  Query row r = b*hq + h.
 // The keys of shard s are [floor(s*T/cp), floor((s+1)*T/cp)); split p of a
 // shard covers its keys [p*split_len, (p+1)*split_len).
-// The kernel writes the normalised bf16 output and the LSE of (b, split p,
-// shard s, head h) as head u = p*cp*hq + s*hq + h of
-//   o   + b*o_sb + u*o_sh   (512 columns)   and   lse + b*lse_sb + u.
-// With one split these are the caller's o_part / lse_part; with several they
-// are the scratch buffer, [B][nsplit*cp*hq][512] bf16 then [B][nsplit*cp*hq]
-// fp32, which the merge kernel then reduces over p (an LSE merge with
-// nsplit shards and cp*hq local heads) into o_part / lse_part.
+// With one split the kernel writes the output of (b, shard s, head h) in the
+// element type to o + b*o_sb + (s*hq + h)*o_sh and its LSE to
+// lse + b*lse_sb + s*hq + h.  With several, split p writes its normalised
+// fp32 output and LSE as head u = p*cp*hq + s*hq + h of the scratch buffer,
+// part_o [B][nsplit*cp*hq][512] fp32 then part_lse [B][nsplit*cp*hq] fp32,
+// which the merge kernel then reduces over p (an LSE merge with nsplit
+// shards and cp*hq local heads, fp32 input) into o / lse.
 struct MlaArgs {
     const uint16_t* q;      // row r at q + b*q_sb + h*q_sh, 576 columns
     const uint16_t* kv;     // token t at kv + t*kv_st, 576 columns
     uint16_t* o;
     float* lse;
+    float* part_o;          // nsplit > 1
+    float* part_lse;
     int64_t q_sb, q_sh, kv_st, o_sb, o_sh, lse_sb;
+    int64_t part_sb;        // nsplit*cp*hq
     int64_t T;
     int64_t split_len;      // multiple of kMlaKeysPerTile
     int32_t rows;           // B * hq

@@ -130,30 +130,67 @@ struct F16 {
     }
 };
 
-// acc += w * v for the 8 columns of v.  A shard with weight exactly 0 (an
-// empty one) has its payload replaced by zeros first -- a select on the four
-// packed words, not a branch, so the payload loads stay ahead of their use --
-// and then adds exactly +0, whatever the payload held (NaN included): the
-// all-zero word is +0 in both payload types.
+// How a lane reads its 8 columns of one shard row and accumulates them.
+// 16-bit payloads (bf16, fp16): one 16-byte load.  fp32 payloads (the MLA
+// decode's split partials, inside the library only): two 16-byte loads.
+// `zero` replaces the row by zeros -- a select on the loaded words, not a
+// branch, so the loads stay ahead of their use -- and the all-zero word is +0
+// in every payload type, so an empty shard adds exactly +0 whatever it held
+// (NaN included).
 template <typename T>
-__device__ __forceinline__ void fma8(float (&acc)[8], float w, u32x4 v) {
-    const bool use = (w != 0.0f);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t p = use ? v[i] : 0u;
-        acc[2 * i] = fmaf(w, T::lo(p), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(w, T::hi(p), acc[2 * i + 1]);
+struct Payload16 {
+    typedef u32x4 row_t;
+    static __device__ __forceinline__ row_t load(const void* base, int64_t off) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off));
     }
-}
+    static __device__ __forceinline__ row_t zero_unless(bool use, row_t v) {
+        row_t z;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = use ? v[i] : 0u;
+        return z;
+    }
+    static __device__ __forceinline__ void fma(float (&acc)[8], float w, row_t v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(w, T::lo(v[i]), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(w, T::hi(v[i]), acc[2 * i + 1]);
+        }
+    }
+};
 
-// acc += w * v for a shard known to be in use (w != 0).
-template <typename T>
-__device__ __forceinline__ void fma8_dense(float (&acc)[8], float w, u32x4 v) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(w, T::lo(v[i]), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(w, T::hi(v[i]), acc[2 * i + 1]);
+struct PayloadF32 {
+    struct row_t {
+        u32x4 a, b;
+    };
+    static __device__ __forceinline__ row_t load(const void* base, int64_t off) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + off);
+        row_t r;
+        r.a = __builtin_nontemporal_load(p);
+        r.b = __builtin_nontemporal_load(p + 1);
+        return r;
     }
+    static __device__ __forceinline__ row_t zero_unless(bool use, row_t v) {
+        row_t z;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            z.a[i] = use ? v.a[i] : 0u;
+            z.b[i] = use ? v.b[i] : 0u;
+        }
+        return z;
+    }
+    static __device__ __forceinline__ void fma(float (&acc)[8], float w, row_t v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[i] = fmaf(w, __uint_as_float(v.a[i]), acc[i]);
+            acc[4 + i] = fmaf(w, __uint_as_float(v.b[i]), acc[4 + i]);
+        }
+    }
+};
+
+// acc += w * v; a shard with weight exactly 0 (an empty one) adds +0.
+template <typename In>
+__device__ __forceinline__ void fma8(float (&acc)[8], float w, typename In::row_t v) {
+    In::fma(acc, w, In::zero_unless(w != 0.0f, v));
 }
 
 // Grid: x = group g of kWavesPerBlock local heads, y = token b of the chunk;
@@ -211,18 +248,19 @@ __device__ __forceinline__ void store_row(const MergeArgs& a, Row r, int lane, c
     if (a.out_lse && lane == 0) a.out_lse[r.b * a.ol_sb + r.j] = L;
 }
 
-// cp = CP <= 16 shards, known at compile time.  The row's CP LSEs have a
+// cp = CP <= 16 shards, known at compile time; In is the payload reader,
+// Out the output element type.  The row's CP LSEs have a
 // wave-uniform address and are read with scalar loads, so the weights are
 // computed once per wavefront with no cross-lane step; the CP payload loads
 // are issued first and are all in flight while the weights are formed.
 // Rows whose every weight is nonzero (the common case) take the plain FMA
 // path; a row with an empty shard zeroes that shard's payload first.
-template <int CP, typename T>
+template <int CP, typename In, typename Out>
 __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
     const int lane = threadIdx.x & 63;
     const Row r = row_of(a);
 
-    const uint16_t* orow = a.attn + r.b * a.a_sb + r.j * a.a_sj + lane * 8;
+    const int64_t orow = r.b * a.a_sb + r.j * a.a_sj + lane * 8;  // elements of the payload
     const float* lrow = a.lse + r.b * a.l_sb + r.j * a.l_sj;
     // Every kernel argument the addresses need is read above this point, in
     // one batch of scalar loads, rather than a second batch after the
@@ -231,9 +269,9 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
     float x[CP];
 #pragma unroll
     for (int s = 0; s < CP; ++s) x[s] = lrow[s * a.l_ss];
-    u32x4 v[CP];
+    typename In::row_t v[CP];
 #pragma unroll
-    for (int s = 0; s < CP; ++s) v[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(orow + s * a.a_ss));
+    for (int s = 0; s < CP; ++s) v[s] = In::load(a.attn, orow + s * a.a_ss);
     // Keep every load above this point: nothing that waits on them may be
     // scheduled before the last one is issued.
     __builtin_amdgcn_sched_barrier(0);
@@ -259,18 +297,18 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (dense) {
 #pragma unroll
-        for (int s = 0; s < CP; ++s) fma8_dense<T>(acc, w[s], v[s]);
+        for (int s = 0; s < CP; ++s) In::fma(acc, w[s], v[s]);
     } else {
 #pragma unroll
-        for (int s = 0; s < CP; ++s) fma8<T>(acc, w[s], v[s]);
+        for (int s = 0; s < CP; ++s) fma8<In>(acc, w[s], v[s]);
     }
-    store_row<T>(a, r, lane, acc, merged_lse(a, M, S));
+    store_row<Out>(a, r, lane, acc, merged_lse(a, M, S));
 }
 
 // 16 < cp <= 64: the same row algorithm with the shards taken G at a time.
 // Loads past the last shard re-read shard cp-1 (an address already being
 // fetched) and get weight 0.
-template <int G, typename T>
+template <int G, typename In, typename Out>
 __global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
     const int lane = threadIdx.x & 63;
     const Row r = row_of(a);
@@ -278,11 +316,10 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
 
     const int ls = lane < cp ? lane : cp - 1;
     const float xl = a.lse[r.b * a.l_sb + r.j * a.l_sj + ls * a.l_ss];
-    const uint16_t* orow = a.attn + r.b * a.a_sb + r.j * a.a_sj + lane * 8;
-    u32x4 v[G];
+    const int64_t orow = r.b * a.a_sb + r.j * a.a_sj + lane * 8;
+    typename In::row_t v[G];
 #pragma unroll
-    for (int i = 0; i < G; ++i)
-        v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(orow + min(i, cp - 1) * a.a_ss));
+    for (int i = 0; i < G; ++i) v[i] = In::load(a.attn, orow + min(i, cp - 1) * a.a_ss);
     __builtin_amdgcn_sched_barrier(0);
 
     const float x = lane < cp ? xl : -INFINITY;
@@ -293,54 +330,59 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
     for (int s0 = 0; s0 < cp; s0 += G) {
         if (s0 > 0) {
 #pragma unroll
-            for (int i = 0; i < G; ++i)
-                v[i] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(orow + min(s0 + i, cp - 1) * a.a_ss));
+            for (int i = 0; i < G; ++i) v[i] = In::load(a.attn, orow + min(s0 + i, cp - 1) * a.a_ss);
         }
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             const float ws = (s0 + i < cp) ? lane_value(wn, min(s0 + i, 63)) : 0.0f;
-            fma8<T>(acc, ws, v[i]);
+            fma8<In>(acc, ws, v[i]);
         }
     }
-    store_row<T>(a, r, lane, acc, merged_lse(a, M, S));
+    store_row<Out>(a, r, lane, acc, merged_lse(a, M, S));
 }
 
-template <int CP, typename T>
+template <int CP, typename In, typename Out>
 void launch_fixed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
-    merge_kernel<CP, T><<<grid, dim3(kBlock), 0, stream>>>(a);
+    merge_kernel<CP, In, Out><<<grid, dim3(kBlock), 0, stream>>>(a);
 }
 
-template <typename T>
+template <typename In, typename Out>
 void launch_typed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
     switch (a.cp) {
-        case 1: launch_fixed<1, T>(a, grid, stream); break;
-        case 2: launch_fixed<2, T>(a, grid, stream); break;
-        case 3: launch_fixed<3, T>(a, grid, stream); break;
-        case 4: launch_fixed<4, T>(a, grid, stream); break;
-        case 5: launch_fixed<5, T>(a, grid, stream); break;
-        case 6: launch_fixed<6, T>(a, grid, stream); break;
-        case 7: launch_fixed<7, T>(a, grid, stream); break;
-        case 8: launch_fixed<8, T>(a, grid, stream); break;
-        case 9: launch_fixed<9, T>(a, grid, stream); break;
-        case 10: launch_fixed<10, T>(a, grid, stream); break;
-        case 11: launch_fixed<11, T>(a, grid, stream); break;
-        case 12: launch_fixed<12, T>(a, grid, stream); break;
-        case 13: launch_fixed<13, T>(a, grid, stream); break;
-        case 14: launch_fixed<14, T>(a, grid, stream); break;
-        case 15: launch_fixed<15, T>(a, grid, stream); break;
-        case 16: launch_fixed<16, T>(a, grid, stream); break;
-        default: merge_kernel_wide<16, T><<<grid, dim3(kBlock), 0, stream>>>(a); break;
+        case 1: launch_fixed<1, In, Out>(a, grid, stream); break;
+        case 2: launch_fixed<2, In, Out>(a, grid, stream); break;
+        case 3: launch_fixed<3, In, Out>(a, grid, stream); break;
+        case 4: launch_fixed<4, In, Out>(a, grid, stream); break;
+        case 5: launch_fixed<5, In, Out>(a, grid, stream); break;
+        case 6: launch_fixed<6, In, Out>(a, grid, stream); break;
+        case 7: launch_fixed<7, In, Out>(a, grid, stream); break;
+        case 8: launch_fixed<8, In, Out>(a, grid, stream); break;
+        case 9: launch_fixed<9, In, Out>(a, grid, stream); break;
+        case 10: launch_fixed<10, In, Out>(a, grid, stream); break;
+        case 11: launch_fixed<11, In, Out>(a, grid, stream); break;
+        case 12: launch_fixed<12, In, Out>(a, grid, stream); break;
+        case 13: launch_fixed<13, In, Out>(a, grid, stream); break;
+        case 14: launch_fixed<14, In, Out>(a, grid, stream); break;
+        case 15: launch_fixed<15, In, Out>(a, grid, stream); break;
+        case 16: launch_fixed<16, In, Out>(a, grid, stream); break;
+        default: merge_kernel_wide<16, In, Out><<<grid, dim3(kBlock), 0, stream>>>(a); break;
     }
 }
 
 hipError_t launch(const MergeArgs& a, hipStream_t stream) {
     const int tokens = a.rows / a.h_local;
     const dim3 grid((a.h_local + kWavesPerBlock - 1) / kWavesPerBlock, tokens);
-    if (a.dtype == DCP_DTYPE_FP16)
-        launch_typed<F16>(a, grid, stream);
-    else
-        launch_typed<Bf16>(a, grid, stream);
+    const bool f16_out = a.dtype == DCP_DTYPE_FP16;
+    if (a.in_dtype == kPayloadF32) {
+        if (f16_out)
+            launch_typed<PayloadF32, F16>(a, grid, stream);
+        else
+            launch_typed<PayloadF32, Bf16>(a, grid, stream);
+    } else if (f16_out) {
+        launch_typed<Payload16<F16>, F16>(a, grid, stream);
+    } else {
+        launch_typed<Payload16<Bf16>, Bf16>(a, grid, stream);
+    }
     return hipGetLastError();
 }
 

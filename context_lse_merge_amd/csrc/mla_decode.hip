@@ -51,10 +51,10 @@
 //    the sum uses the fp32 p.
 //  * Split-KV: shards are split into key ranges so that about 256 workgroups
 //    (one per compute unit) exist even at B = 1; each split leaves its
-//    normalised bf16 output and LSE in the scratch buffer, and the merge
-//    kernel of dcp_lse_combine reduces the splits of each (token, shard,
-//    head) exactly as it merges DCP shards.  With a single split the kernel
-//    writes the final bf16 output and LSE itself.
+//    normalised fp32 output and LSE in the scratch buffer, and the merge
+//    kernel of dcp_lse_combine (its fp32-input instance) reduces the splits
+//    of each (token, shard, head) exactly as it merges DCP shards.  With a
+//    single split the kernel writes the final output and LSE itself.
 //  * Workgroups that share a key range are placed on the same XCD (block ids
 //    are dealt round-robin over the 8 XCDs), so a KV tile is fetched from HBM
 //    about once per XCD-L2 rather than once per workgroup.
@@ -450,21 +450,31 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     const float l_tot = sum_xor32(sum_xor16(l_run));
     if (row_raw >= a.rows) return;
 
-    // O / l in bf16 and the LSE in the caller's base, as head p*cp*hq + s*hq + h
-    // of the destination (the caller's outputs, or the per-split scratch that
-    // the merge kernel reduces); an empty shard or split gives 0 and -inf.
+    // O / l and the LSE in the caller's base; an empty shard or split gives 0
+    // and -inf.  One split: the element type, straight into o_part / lse_part.
+    // Several: fp32 into the scratch as head p*cp*hq + s*hq + h, for the merge
+    // kernel to reduce over the splits.
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const int64_t u = (static_cast<int64_t>(wk.p) * a.cp + wk.s) * a.hq + h;
-    uint16_t* orow = a.o + b * a.o_sb + u * a.o_sh + ocol;
+    const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * a.lse_scale : -INFINITY;
+    if (a.nsplit == 1) {
+        const int64_t u = static_cast<int64_t>(wk.s) * a.hq + h;
+        uint16_t* orow = a.o + b * a.o_sb + u * a.o_sh + ocol;
 #pragma unroll
-    for (int t = 0; t < kDTiles; ++t) {
-        const f32x4 v = st.oacc[t];
-        const uint32_t lo = to_bits<T>(v[0] * inv) | (to_bits<T>(v[1] * inv) << 16);
-        const uint32_t hi = to_bits<T>(v[2] * inv) | (to_bits<T>(v[3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
+        for (int t = 0; t < kDTiles; ++t) {
+            const f32x4 v = st.oacc[t];
+            const uint32_t lo = to_bits<T>(v[0] * inv) | (to_bits<T>(v[1] * inv) << 16);
+            const uint32_t hi = to_bits<T>(v[2] * inv) | (to_bits<T>(v[3] * inv) << 16);
+            *reinterpret_cast<uint2*>(orow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
+        }
+        if (g == 0) a.lse[b * a.lse_sb + u] = lse;
+    } else {
+        const int64_t u = (static_cast<int64_t>(wk.p) * a.cp + wk.s) * a.hq + h;
+        float* prow = a.part_o + (b * a.part_sb + u) * kDv + ocol;
+#pragma unroll
+        for (int t = 0; t < kDTiles; ++t)
+            *reinterpret_cast<f32x4*>(prow + 64 * (t >> 2) + 8 * (t & 3)) = st.oacc[t] * inv;
+        if (g == 0) a.part_lse[b * a.part_sb + u] = lse;
     }
-    if (g == 0)
-        a.lse[b * a.lse_sb + u] = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * a.lse_scale : -INFINITY;
 }
 
 }  // namespace
@@ -494,13 +504,7 @@ extern "C" int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t 
         if (chunk > dcp::kMaxLaunchTokens) chunk = dcp::kMaxLaunchTokens;
         for (int64_t t0 = 0; t0 < plan.B && e == hipSuccess; t0 += chunk) {
             const int64_t n = plan.B - t0 < chunk ? plan.B - t0 : chunk;
-            dcp::MergeArgs m = plan.reduce;
-            m.attn += t0 * m.a_sb;
-            m.lse += t0 * m.l_sb;
-            m.out += t0 * m.o_sb;
-            m.out_lse += t0 * m.ol_sb;
-            m.rows = static_cast<int32_t>(n * H);
-            e = static_cast<hipError_t>(dcp::merge_launch(m, stream));
+            e = static_cast<hipError_t>(dcp::merge_launch(dcp::merge_args_at(plan.reduce, t0, n), stream));
         }
     }
     if (e != hipSuccess)
