@@ -67,11 +67,13 @@ def _configure(lib):
     lib.oracle_attention_partials.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, dbl, i32, i32, vp, i64,
                                               vp, vp, i32]
     lib.oracle_attention_full.argtypes = [vp, vp, i64, i64, i64, i64, i64, dbl, i32, i32, vp, i64, vp, vp, i32]
+    lib.oracle_attention_partials_varlen.argtypes = [vp, vp, i64, i64, i64, vp, i32, i64, i64, i64, dbl, i32, i32,
+                                                     vp, i64, vp, vp, i32]
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f64.restype = dbl
     lib.oracle_max_threads.restype = i32
     for f in ("oracle_merge_f64", "oracle_merge_bf16", "oracle_merge_f16", "oracle_attention_partials",
-              "oracle_attention_full"):
+              "oracle_attention_full", "oracle_attention_partials_varlen"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -169,6 +171,38 @@ def attention_partials(q_bits, kv_bits, cp: int, scale: float, lse_mode: int, dv
                                        _DTYPE[dtype], _ptr(rows), n, _ptr(o), _ptr(lse), threads)
     if rc:
         raise ValueError("oracle_attention_partials rejected its arguments (rc=%d)" % rc)
+    return o, lse
+
+
+def attention_partials_varlen(q_bits, kv_bits, seq_lens, cp: int, scale: float, lse_mode: int,
+                              interleaved: bool = False, dv: int = 512, rows=None, threads: int = 0,
+                              dtype: str = "bf16"):
+    """Per-shard partials with one cache per query token.  ``q_bits`` [B, hq, dqk];
+    ``kv_bits`` [B, Tmax, dqk] (token b's cache) or [Tmax, dqk] (one cache shared by
+    every token); ``seq_lens`` [B] int.  Shard s owns a contiguous slice of token b's
+    first seq_lens[b] rows, or (``interleaved``) the rows t with t mod cp == s.
+    Returns ``(o [n_rows, cp, dv], lse [n_rows, cp])``."""
+    lib = _load()
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    kv_bits = np.ascontiguousarray(kv_bits, dtype=np.uint16)
+    seq = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B, hq, dqk = q_bits.shape
+    if kv_bits.ndim == 2:
+        kv_sb, tmax = 0, kv_bits.shape[0]
+    else:
+        assert kv_bits.shape[0] == B
+        kv_sb, tmax = kv_bits.shape[1], kv_bits.shape[1]
+    assert kv_bits.shape[-1] == dqk and seq.shape == (B,)
+    if seq.size and (seq.min() < 0 or seq.max() > tmax):
+        raise ValueError("seq_lens must lie in [0, %d]" % tmax)
+    rows, n = _rows_arg(rows, B, hq)
+    o = np.empty((n, cp, dv), dtype=np.float64)
+    lse = np.empty((n, cp), dtype=np.float64)
+    rc = lib.oracle_attention_partials_varlen(_ptr(q_bits), _ptr(kv_bits), B, hq, kv_sb, _ptr(seq), int(interleaved),
+                                              dqk, dv, cp, float(scale), lse_mode, _DTYPE[dtype], _ptr(rows), n,
+                                              _ptr(o), _ptr(lse), threads)
+    if rc:
+        raise ValueError("oracle_attention_partials_varlen rejected its arguments (rc=%d)" % rc)
     return o, lse
 
 

@@ -51,6 +51,16 @@
  *                lse = ln sum_{t in T} exp(z_t)     (times log2 e in base 2)
  *                O   = sum_{t in T} softmax(z)_t * v_t
  *            An empty token set gives lse = -inf and O = 0.
+ *
+ *  variable-length partials -- the same per query token b over its own
+ *            cache of L_b = seq_lens[b] tokens ("[Attention] Add direct
+ *            symmetric-memory DCP A2A", vLLM PR #48897, amended port commit:
+ *            the decode seq_lens decide which KV shards are empty; an empty
+ *            shard publishes -inf).  Shard s owns either a contiguous slice
+ *            [floor(s L/cp), floor((s+1) L/cp)) or, with the latent KV
+ *            interleaved across DCP ranks ("[DCP] Optimize shared Output,
+ *            Query, and Indexer/Top-K via peer memory", sglang PR #32851,
+ *            commit log), the tokens t < L with t mod cp = s.
  */
 #include <math.h>
 #include <stdint.h>
@@ -313,6 +323,90 @@ int oracle_attention_partials(const uint16_t* q, const uint16_t* kv, int64_t B, 
             shard_bounds(T, cp, s, &t0, &t1);
             double lse =
                 attend_row(dec, q + r * dqk, kv, dqk, t0, t1, dqk, dv, scale, qd, o_part + (i * cp + s) * dv);
+            if (lse_mode == ORACLE_BASE_2) lse *= M_LOG2E;
+            lse_part[i * cp + s] = lse;
+        }
+        free(qd);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Softmax attention of one query row over the cache rows t0, t0 + step, ...
+ * (n rows): the definition, as attend_row but over a strided token set.
+ */
+static double attend_rows_strided(decode16_fn dec, const uint16_t* q, const uint16_t* kv, int64_t kv_stride,
+                                  int64_t t0, int64_t step, int64_t n, int64_t dqk, int64_t dv, double scale,
+                                  double* qd, double* o) {
+    for (int64_t d = 0; d < dv; ++d) o[d] = 0.0;
+    if (n <= 0) return -INFINITY;
+    for (int64_t d = 0; d < dqk; ++d) qd[d] = dec(q[d]);
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n; ++i) {
+        const uint16_t* k = kv + (t0 + i * step) * kv_stride;
+        double z = 0.0;
+        for (int64_t d = 0; d < dqk; ++d) z += qd[d] * dec(k[d]);
+        z *= scale;
+        if (z > m) m = z;
+    }
+    double l = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        const uint16_t* k = kv + (t0 + i * step) * kv_stride;
+        double z = 0.0;
+        for (int64_t d = 0; d < dqk; ++d) z += qd[d] * dec(k[d]);
+        z *= scale;
+        double p = exp(z - m);
+        l += p;
+        for (int64_t d = 0; d < dv; ++d) o[d] += p * dec(k[d]);
+    }
+    for (int64_t d = 0; d < dv; ++d) o[d] /= l;
+    return m + log(l);
+}
+
+/*
+ * Per-shard partials with one cache per query token.
+ *   q         [B, hq, dqk] contiguous 16-bit bits
+ *   kv        token b's cache row t at kv + (b*kv_sb + t)*dqk (kv_sb in rows;
+ *             0 lets every token share one cache), 16-bit bits
+ *   seq_lens  [B]: token b attends over its rows t < seq_lens[b]
+ *   interleaved  0: shard s owns [floor(s L/cp), floor((s+1) L/cp));
+ *                1: shard s owns the rows t < L with t mod cp == s
+ *   o_part [n_rows, cp, dv], lse_part [n_rows, cp] as oracle_attention_partials.
+ */
+int oracle_attention_partials_varlen(const uint16_t* q, const uint16_t* kv, int64_t B, int64_t hq, int64_t kv_sb,
+                                     const int32_t* seq_lens, int interleaved, int64_t dqk, int64_t dv, int64_t cp,
+                                     double scale, int lse_mode, int dtype, const int64_t* rows, int64_t n_rows,
+                                     double* o_part, double* lse_part, int nthreads) {
+    if (B < 0 || hq <= 0 || kv_sb < 0 || dqk <= 0 || dv <= 0 || dv > dqk || cp <= 0) return ORACLE_BAD_ARG;
+    if (lse_mode != ORACLE_BASE_E && lse_mode != ORACLE_BASE_2) return ORACLE_BAD_ARG;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F16) return ORACLE_BAD_ARG;
+    for (int64_t b = 0; b < B; ++b)
+        if (seq_lens[b] < 0) return ORACLE_BAD_ARG;
+    const decode16_fn dec = decoder(dtype);
+    if (!rows) n_rows = B * hq;
+    set_threads(nthreads);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t r = rows ? rows[i] : i;
+        const int64_t b = r / hq;
+        const int64_t L = seq_lens[b];
+        const uint16_t* cache = kv + b * kv_sb * dqk;
+        double* qd = (double*)malloc((size_t)dqk * sizeof(double));
+        for (int64_t s = 0; s < cp; ++s) {
+            int64_t t0, step, n;
+            if (interleaved) {
+                t0 = s;
+                step = cp;
+                n = L > s ? (L - s + cp - 1) / cp : 0;
+            } else {
+                int64_t t1;
+                shard_bounds(L, cp, s, &t0, &t1);
+                step = 1;
+                n = t1 - t0;
+            }
+            double lse = attend_rows_strided(dec, q + r * dqk, cache, dqk, t0, step, n, dqk, dv, scale, qd,
+                                             o_part + (i * cp + s) * dv);
             if (lse_mode == ORACLE_BASE_2) lse *= M_LOG2E;
             lse_part[i * cp + s] = lse;
         }

@@ -45,6 +45,10 @@ MUTANTS = {
                                  "if (lse_mode == ORACLE_BASE_2) lse /= M_LOG2E;"),
     "shard_bound_off_by_one": ("*t1 = ((s + 1) * T) / cp;", "*t1 = ((s + 1) * T) / cp + (s == 0);"),
     "bf16_decode_shift": ("((uint32_t)bits) << 16", "((uint32_t)bits) << 15"),
+    "varlen_interleave_offset": ("                t0 = s;\n                step = cp;", "                t0 = s + 1;\n                step = cp;"),
+    "varlen_interleave_count": ("n = L > s ? (L - s + cp - 1) / cp : 0;", "n = L > s ? (L - s) / cp : 0;"),
+    "varlen_first_token_length": ("const int64_t L = seq_lens[b];", "const int64_t L = seq_lens[0];"),
+    "varlen_shared_cache_offset": ("const uint16_t* cache = kv + b * kv_sb * dqk;", "const uint16_t* cache = kv;"),
     "f16_decode_bias": ("ldexp((double)(1024 + frac), expo - 25)", "ldexp((double)(1024 + frac), expo - 24)"),
     "f16_subnormal_scale": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
     "f16_merge_decodes_as_bf16": ("return merge_16bit(oracle_decode_f16,", "return merge_16bit(oracle_decode_bf16,"),
@@ -73,6 +77,9 @@ def _pin_checks():
         pins.test_empty_shards_equal_merge_without_them,
         pins.test_full_attention_matches_scipy,
         pins.test_f16_attention_matches_scipy,
+        lambda: pins.test_varlen_partials_match_scipy(False),
+        lambda: pins.test_varlen_partials_match_scipy(True),
+        lambda: pins.test_varlen_merged_shards_equal_full_attention(True),
         lambda: pins.test_partials_are_softmax_over_contiguous_shards(130, 4),
         lambda: pins.test_merged_partials_equal_full_attention(256, 4, T2),
     ]

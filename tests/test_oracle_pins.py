@@ -342,6 +342,74 @@ def test_f16_attention_matches_scipy():
         np.testing.assert_allclose(lp[:, s], logsumexp(zz, axis=1) / LN2, rtol=1e-13)
 
 
+def _varlen_case(seed, B, hq, tmax, dtype=torch.bfloat16):
+    g = synth.gen(seed)
+    q = synth.normal_16((B, hq, synth.D_QK), g, dtype)
+    kv = synth.normal_16((B, tmax, synth.D_QK), g, dtype, std=0.5)
+    return q, kv
+
+
+def _owned_rows(L, cp, s, interleaved):
+    if interleaved:
+        return np.arange(s, L, cp)
+    return np.arange((s * L) // cp, ((s + 1) * L) // cp)
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_varlen_partials_match_scipy(interleaved):
+    """One cache per token, seq_lens 0, 1, 3 (< cp), 37 and 100 (= Tmax): each
+    shard's partial against numpy/scipy over exactly the rows it owns; shards
+    that own nothing are -inf and 0."""
+    B, hq, tmax, cp = 5, 2, 100, 4
+    q, kv = _varlen_case(601, B, hq, tmax)
+    seq = np.array([0, 1, 3, 37, 100], np.int32)
+    o, lse = oracle.attention_partials_varlen(synth.bf16_bits(q), synth.bf16_bits(kv), seq, cp, synth.MLA_SCALE,
+                                              oracle.BASE_E, interleaved=interleaved)
+    qd, kd = q.double().numpy(), kv.double().numpy()
+    for b in range(B):
+        for h in range(hq):
+            r = b * hq + h
+            for s in range(cp):
+                own = _owned_rows(int(seq[b]), cp, s, interleaved)
+                if own.size == 0:
+                    assert np.isneginf(lse[r, s]) and np.all(o[r, s] == 0)
+                    continue
+                z = synth.MLA_SCALE * (kd[b, own] @ qd[b, h])
+                np.testing.assert_allclose(o[r, s], softmax(z) @ kd[b, own, :512], rtol=1e-11, atol=1e-13)
+                assert abs(lse[r, s] - logsumexp(z)) <= 1e-12 * max(1.0, abs(logsumexp(z)))
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_varlen_merged_shards_equal_full_attention(interleaved):
+    """Merging the shards of a token (oracle merge, BH1 layout) gives attention
+    over all its seq_lens[b] rows, whichever way the rows are owned."""
+    B, hq, tmax, cp = 4, 3, 64, 8
+    q, kv = _varlen_case(602, B, hq, tmax)
+    seq = np.array([64, 5, 1, 29], np.int32)
+    o, lse = oracle.attention_partials_varlen(synth.bf16_bits(q), synth.bf16_bits(kv), seq, cp, synth.MLA_SCALE,
+                                              oracle.BASE_2, interleaved=interleaved)
+    O = o.reshape(B, hq, cp, 512).transpose(0, 2, 1, 3).reshape(B, cp * hq, 512)   # head s*hq + h
+    L = lse.reshape(B, hq, cp).transpose(0, 2, 1).reshape(B, cp * hq)
+    out, Lm, _ = oracle.merge(O, L, cp, oracle.LSE_BH1, oracle.BASE_2)
+    qd, kd = q.double().numpy(), kv.double().numpy()
+    for b in range(B):
+        n = int(seq[b])
+        z = synth.MLA_SCALE * (qd[b] @ kd[b, :n].T)                 # [hq, n]
+        np.testing.assert_allclose(out[b], softmax(z, axis=1) @ kd[b, :n, :512], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(Lm[b], logsumexp(z, axis=1) / LN2, rtol=1e-12)
+
+
+def test_varlen_with_one_shared_cache_equals_contiguous_partials():
+    """All tokens sharing one cache with seq_lens = T and contiguous ownership is
+    exactly the fixed-length producer's computation."""
+    q, kv = synth.tiny_attention(B=3, hq=4, T=130)
+    seq = np.full(3, 130, np.int32)
+    o_v, l_v = oracle.attention_partials_varlen(synth.bf16_bits(q), synth.bf16_bits(kv), seq, 4, synth.MLA_SCALE,
+                                                oracle.BASE_E)
+    o_f, l_f = oracle.attention_partials(synth.bf16_bits(q), synth.bf16_bits(kv), 4, synth.MLA_SCALE, oracle.BASE_E)
+    assert np.array_equal(o_v, o_f) and np.array_equal(l_v, l_f)
+
+
 def test_full_attention_matches_scipy():
     q, kv = synth.tiny_attention(B=2, hq=4, T=96)
     qb, kb = synth.bf16_bits(q), synth.bf16_bits(kv)
