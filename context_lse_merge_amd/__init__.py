@@ -44,6 +44,8 @@ DCP_DTYPE_FP16 = _C["DCP_DTYPE_FP16"]
 DCP_HEAD_DIM = _C["DCP_HEAD_DIM"]
 DCP_QK_DIM = _C["DCP_QK_DIM"]
 DCP_MAX_CP = _C["DCP_MAX_CP"]
+DCP_KV_CONTIGUOUS = _C["DCP_KV_CONTIGUOUS"]
+DCP_KV_INTERLEAVED = _C["DCP_KV_INTERLEAVED"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -59,11 +61,15 @@ _lib.dcp_lse_combine.argtypes = [_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _i
 _lib.dcp_mla_partial_decode_scratch_size.argtypes = [_i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
 _lib.dcp_mla_partial_decode.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, _i64, _i32, _i32, ctypes.c_float,
                                         _i32, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]
+_lib.dcp_mla_partial_decode_varlen_scratch_size.argtypes = [_i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
+_lib.dcp_mla_partial_decode_varlen.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _i32,
+                                               _i32, ctypes.c_float, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]
 _lib.dcp_last_error.restype = ctypes.c_char_p
 _lib.dcp_status_string.argtypes = [_i32]
 _lib.dcp_status_string.restype = ctypes.c_char_p
 for _f in ("dcp_workspace_create", "dcp_workspace_destroy", "dcp_lse_combine",
-           "dcp_mla_partial_decode_scratch_size", "dcp_mla_partial_decode"):
+           "dcp_mla_partial_decode_scratch_size", "dcp_mla_partial_decode",
+           "dcp_mla_partial_decode_varlen_scratch_size", "dcp_mla_partial_decode_varlen"):
     getattr(_lib, _f).restype = _i32
 
 
@@ -227,4 +233,52 @@ def dcp_mla_partial_decode(q, kv, cp: int, softmax_scale: float, lse_mode: int, 
         _dev_ptr(q, "q"), B, hq, q.stride(0), q.stride(1), _dev_ptr(kv, "kv") if T > 0 else None, T, kv.stride(0),
         dtype, cp, float(softmax_scale), lse_mode, _dev_ptr(o_part, "o_part"), o_part.stride(0), o_part.stride(1),
         _dev_ptr(lse_part, "lse_part"), lse_part.stride(0), _dev_ptr(scratch, "scratch"), nbytes, s))
+    return o_part, lse_part
+
+
+def dcp_mla_partial_decode_varlen_scratch_size(B: int, hq: int, max_seq_len: int, cp: int) -> int:
+    """Bytes of scratch dcp_mla_partial_decode_varlen needs for this shape (0: none)."""
+    n = _sz()
+    _check(_lib.dcp_mla_partial_decode_varlen_scratch_size(B, hq, max_seq_len, cp, ctypes.byref(n)))
+    return n.value
+
+
+def dcp_mla_partial_decode_varlen(q, kv, seq_lens, max_seq_len: int, kv_layout: int, cp: int, softmax_scale: float,
+                                  lse_mode: int, o_part, lse_part, scratch=None, stream=None):
+    """Per-token-length MLA decode partials.  ``q`` [B, hq, 576]; ``kv`` [B, Tmax, 576]
+    (token b's cache) or [Tmax, 576] (one cache shared by every token, kv_sb = 0);
+    ``seq_lens`` int32 [B] on the GPU; ``kv_layout`` DCP_KV_CONTIGUOUS or
+    DCP_KV_INTERLEAVED.  q, kv and o_part all bf16 or all fp16."""
+    import torch
+    if q.dim() != 3 or kv.dim() not in (2, 3) or o_part.dim() != 3 or lse_part.dim() != 2:
+        raise ValueError("q [B,hq,576], kv [B,T,576] or [T,576], o_part [B,cp*hq,512], lse_part [B,cp*hq] expected")
+    if q.dtype not in (torch.bfloat16, torch.float16) or kv.dtype != q.dtype or o_part.dtype != q.dtype:
+        raise ValueError("q, kv and o_part must all be bfloat16 or all float16")
+    if lse_part.dtype != torch.float32 or seq_lens.dtype != torch.int32 or seq_lens.dim() != 1:
+        raise ValueError("lse_part must be float32 and seq_lens a 1-D int32 tensor")
+    dtype = DCP_DTYPE_FP16 if q.dtype == torch.float16 else DCP_DTYPE_BF16
+    B, hq, dqk = q.shape
+    if seq_lens.shape[0] != B:
+        raise ValueError("seq_lens must have B = %d entries" % B)
+    if kv.dim() == 3:
+        if kv.shape[0] != B:
+            raise ValueError("kv [B, T, 576] must have B = %d caches" % B)
+        kv_sb, T = kv.stride(0), kv.shape[1]
+    else:
+        kv_sb, T = 0, kv.shape[0]
+    if max_seq_len > T:
+        raise ValueError("max_seq_len = %d exceeds the %d cache rows" % (max_seq_len, T))
+    if dqk != DCP_QK_DIM or kv.shape[-1] != DCP_QK_DIM:
+        raise ValueError("q and kv rows must have %d columns" % DCP_QK_DIM)
+    if tuple(o_part.shape) != (B, cp * hq, DCP_HEAD_DIM) or tuple(lse_part.shape) != (B, cp * hq):
+        raise ValueError("o_part must be [B, cp*hq, %d] and lse_part [B, cp*hq]" % DCP_HEAD_DIM)
+    if q.stride(2) != 1 or kv.stride(-1) != 1 or o_part.stride(2) != 1 or lse_part.stride(1) != 1:
+        raise ValueError("innermost strides must be 1")
+    nbytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
+    s = _stream_handle(stream)
+    _check(_lib.dcp_mla_partial_decode_varlen(
+        _dev_ptr(q, "q"), B, hq, q.stride(0), q.stride(1), _dev_ptr(kv, "kv") if max_seq_len > 0 else None, kv_sb,
+        kv.stride(-2), max_seq_len, _dev_ptr(seq_lens, "seq_lens"), kv_layout, dtype, cp, float(softmax_scale),
+        lse_mode, _dev_ptr(o_part, "o_part"), o_part.stride(0), o_part.stride(1), _dev_ptr(lse_part, "lse_part"),
+        lse_part.stride(0), _dev_ptr(scratch, "scratch"), nbytes, s))
     return o_part, lse_part

@@ -217,9 +217,11 @@ MergeArgs chunk_args(const MergePlan& plan, int64_t k) {
 // as it merges DCP shards.  The split count aims at about kMlaTargetBlocks
 // workgroups and never gives a split fewer than kMlaMinSplitKeys keys.
 
-void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* split_len, size_t* scratch_bytes) {
+void mla_split(int64_t B, int hq, int64_t T, int cp, bool varlen, int32_t* nsplit, int64_t* split_len,
+               size_t* scratch_bytes) {
     const int64_t rows = B * hq;
-    const int64_t row_blocks = (rows + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
+    const int64_t row_blocks = varlen ? B * ((hq + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock)
+                                      : (rows + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
     const int64_t shard_max = (T + cp - 1) / cp;  // longest shard
     int64_t n = 1;
     if (row_blocks > 0 && shard_max > 0) {
@@ -245,12 +247,15 @@ void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* s
 }
 
 int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv, int64_t T, int64_t kv_st,
-             int dtype, int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb, int64_t o_sh, float* lse,
-             int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan) {
-    const char* fn = "dcp_mla_partial_decode";
+             const MlaVarlen* vl, int dtype, int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb,
+             int64_t o_sh, float* lse, int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan) {
+    const char* fn = vl ? "dcp_mla_partial_decode_varlen" : "dcp_mla_partial_decode";
     if (B < 0 || hq < 1 || T < 0)
-        return fail(DCP_ERR_INVALID_ARG, "%s: need B >= 0, hq >= 1, kv_tokens >= 0 (got %lld, %d, %lld)", fn,
-                    (long long)B, hq, (long long)T);
+        return fail(DCP_ERR_INVALID_ARG, "%s: need B >= 0, hq >= 1, %s >= 0 (got %lld, %d, %lld)", fn,
+                    vl ? "max_seq_len" : "kv_tokens", (long long)B, hq, (long long)T);
+    if (vl && vl->kv_layout != DCP_KV_CONTIGUOUS && vl->kv_layout != DCP_KV_INTERLEAVED)
+        return fail(DCP_ERR_INVALID_ARG, "%s: kv_layout %d is neither DCP_KV_CONTIGUOUS nor DCP_KV_INTERLEAVED", fn,
+                    vl->kv_layout);
     if (cp < 1 || cp > DCP_MAX_CP)
         return fail(DCP_ERR_INVALID_ARG, "%s: cp = %d is outside [1, %d]", fn, cp, DCP_MAX_CP);
     if (lse_mode != DCP_LSE_BASE_E && lse_mode != DCP_LSE_BASE_2)
@@ -267,9 +272,13 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
         return ok();
     }
     if (!q || !o || !lse || (T > 0 && !kv))
-        return fail(DCP_ERR_INVALID_ARG, "%s: q, o_part, lse_part (and kv when kv_tokens > 0) must be non-null", fn);
-    if (q_sb < 0 || q_sh < 0 || kv_st < 0 || o_sb < 0 || o_sh < 0 || lse_sb < 0)
+        return fail(DCP_ERR_INVALID_ARG, "%s: q, o_part, lse_part (and kv when there are keys) must be non-null", fn);
+    if (vl && !vl->seq_lens) return fail(DCP_ERR_INVALID_ARG, "%s: seq_lens must be non-null when B > 0", fn);
+    if (vl && !aligned(vl->seq_lens, 4)) return fail(DCP_ERR_ALIGN, "%s: seq_lens must be 4-byte aligned", fn);
+    const int64_t kv_sb = vl ? vl->kv_sb : 0;
+    if (q_sb < 0 || q_sh < 0 || kv_st < 0 || kv_sb < 0 || o_sb < 0 || o_sh < 0 || lse_sb < 0)
         return fail(DCP_ERR_LAYOUT, "%s: strides must be non-negative", fn);
+    if (kv_sb % 8) return fail(DCP_ERR_ALIGN, "%s: kv_sb must be a multiple of 8 elements", fn);
     const int64_t H = static_cast<int64_t>(cp) * hq;
     if (!rows_disjoint(B, o_sb, H, o_sh, kMlaVDim))
         return fail(DCP_ERR_LAYOUT, "%s: o_part rows overlap (o_sb = %lld, o_sh = %lld)", fn, (long long)o_sb,
@@ -282,22 +291,24 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     if (q_sb % 8 || q_sh % 8 || kv_st % 8 || o_sb % 8 || o_sh % 8)
         return fail(DCP_ERR_ALIGN, "%s: q_sb, q_sh, kv_st, o_sb and o_sh must be multiples of 8 elements", fn);
     if (!aligned(lse, 4)) return fail(DCP_ERR_ALIGN, "%s: lse_part must be 4-byte aligned", fn);
-    // Offsets inside one key tile are 32-bit element counts.
-    if (kv_st > ((int64_t{1} << 31) - kMlaQkDim) / kMlaKeysPerTile)
+    // Offsets inside one key tile are 32-bit element counts; interleaved rows
+    // of a tile are cp rows apart.
+    const int64_t row_step = (vl && vl->kv_layout == DCP_KV_INTERLEAVED) ? cp : 1;
+    if (kv_st * row_step > ((int64_t{1} << 31) - kMlaQkDim) / kMlaKeysPerTile)
         return fail(DCP_ERR_LAYOUT, "%s: kv_st = %lld is too large (at most %lld elements)", fn, (long long)kv_st,
-                    (long long)(((int64_t{1} << 31) - kMlaQkDim) / kMlaKeysPerTile));
+                    (long long)(((int64_t{1} << 31) - kMlaQkDim) / kMlaKeysPerTile / row_step));
 
     int32_t nsplit;
     int64_t split_len;
     size_t need;
-    mla_split(B, hq, T, cp, &nsplit, &split_len, &need);
+    mla_split(B, hq, T, cp, vl != nullptr, &nsplit, &split_len, &need);
     if (need > 0 && (!scratch || scratch_bytes < need))
-        return fail(DCP_ERR_WORKSPACE, "%s: needs %zu bytes of scratch (dcp_mla_partial_decode_scratch_size), got %zu",
-                    fn, need, scratch ? scratch_bytes : size_t{0});
+        return fail(DCP_ERR_WORKSPACE, "%s: needs %zu bytes of scratch (%s_scratch_size), got %zu", fn, need, fn,
+                    scratch ? scratch_bytes : size_t{0});
     if (need > 0 && !aligned(scratch, 16)) return fail(DCP_ERR_ALIGN, "%s: scratch must be 16-byte aligned", fn);
 
     const Extent e_q = extent(q, B, q_sb, hq, q_sh, kMlaQkDim, 2);
-    const Extent e_kv = T > 0 ? extent(kv, T, kv_st, 1, 0, kMlaQkDim, 2) : Extent{0, 0};
+    const Extent e_kv = T > 0 ? extent(kv, vl ? B : 1, kv_sb, T, kv_st, kMlaQkDim, 2) : Extent{0, 0};
     const Extent e_o = extent(o, B, o_sb, H, o_sh, kMlaVDim, 2);
     const Extent e_l = extent(lse, B, lse_sb, 1, 0, H, 4);
     if (overlaps(e_o, e_q) || overlaps(e_o, e_kv) || overlaps(e_l, e_q) || overlaps(e_l, e_kv) ||
@@ -323,6 +334,13 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     a.nsplit = nsplit;
     a.row_blocks = (a.rows + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
     a.dtype = dtype;
+    if (vl) {
+        a.seq_lens = vl->seq_lens;
+        a.kv_sb = vl->kv_sb;
+        a.interleaved = vl->kv_layout == DCP_KV_INTERLEAVED ? 1 : 0;
+        a.rb_per_token = (hq + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
+        a.row_blocks = static_cast<int32_t>(B * a.rb_per_token);
+    }
     a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
     a.lse_scale = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;
     *plan = MlaPlan{};
@@ -363,6 +381,9 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     plan->args = a;
     plan->scratch_bytes = need;
     plan->blocks = static_cast<int64_t>(a.row_blocks) * cp * nsplit;
+    if (plan->blocks >= (int64_t{1} << 31))
+        return fail(DCP_ERR_INVALID_ARG, "%s: %lld workgroups exceed one launch (fewer tokens per call)", fn,
+                    (long long)plan->blocks);
     plan->B = B;
     return ok();
 }
@@ -381,7 +402,22 @@ int dcp_mla_partial_decode_scratch_size(int64_t B, int hq, int64_t kv_tokens, in
         return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_mla_partial_decode_scratch_size: B * hq exceeds 2^30");
     int32_t n;
     int64_t len;
-    dcp::mla_split(B, hq, kv_tokens, cp, &n, &len, bytes);
+    dcp::mla_split(B, hq, kv_tokens, cp, false, &n, &len, bytes);
+    return dcp::ok();
+}
+
+int dcp_mla_partial_decode_varlen_scratch_size(int64_t B, int hq, int64_t max_seq_len, int cp, size_t* bytes) {
+    if (!bytes) return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_mla_partial_decode_varlen_scratch_size: bytes is null");
+    if (B < 0 || hq < 1 || max_seq_len < 0 || cp < 1 || cp > DCP_MAX_CP)
+        return dcp::fail(DCP_ERR_INVALID_ARG,
+                         "dcp_mla_partial_decode_varlen_scratch_size: need B >= 0, hq >= 1, max_seq_len >= 0, "
+                         "1 <= cp <= %d",
+                         DCP_MAX_CP);
+    if (B * static_cast<int64_t>(hq) > (int64_t{1} << 30))
+        return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_mla_partial_decode_varlen_scratch_size: B * hq exceeds 2^30");
+    int32_t n;
+    int64_t len;
+    dcp::mla_split(B, hq, max_seq_len, cp, true, &n, &len, bytes);
     return dcp::ok();
 }
 

@@ -124,6 +124,13 @@ struct MlaArgs {
     float* part_lse;
     int64_t q_sb, q_sh, kv_st, o_sb, o_sh, lse_sb;
     int64_t part_sb;        // nsplit*cp*hq
+    // Variable length (seq_lens != nullptr): token b attends over its own cache
+    // kv + b*kv_sb, rows t < min(max(seq_lens[b], 0), T); a workgroup's rows
+    // never span tokens (rb_per_token blocks of up to 128 heads per token).
+    const int32_t* seq_lens;
+    int64_t kv_sb;
+    int32_t interleaved;    // shard s owns rows t with t mod cp == s (else a contiguous slice)
+    int32_t rb_per_token;
     int64_t T;
     int64_t split_len;      // multiple of kMlaKeysPerTile
     int32_t rows;           // B * hq
@@ -144,12 +151,23 @@ struct MlaPlan {
     int64_t B;
 };
 
-// Split decision and scratch size; pure arithmetic on the shape.
-void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* split_len, size_t* scratch_bytes);
+// Split decision and scratch size; pure arithmetic on the shape.  With
+// varlen the workgroups of one token cover only its heads.
+void mla_split(int64_t B, int hq, int64_t T, int cp, bool varlen, int32_t* nsplit, int64_t* split_len,
+               size_t* scratch_bytes);
 
-// Validate every argument of dcp_mla_partial_decode and build its plan.
+// The variable-length arguments of dcp_mla_partial_decode_varlen.
+struct MlaVarlen {
+    const int32_t* seq_lens;  // device, [B]
+    int64_t kv_sb;            // elements between consecutive tokens' caches (0: one shared cache)
+    int kv_layout;            // DCP_KV_CONTIGUOUS or DCP_KV_INTERLEAVED
+};
+
+// Validate every argument of dcp_mla_partial_decode (vl == nullptr: one cache
+// of T rows shared by every token) or of dcp_mla_partial_decode_varlen (T is
+// then max_seq_len) and build the plan.
 int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv, int64_t T, int64_t kv_st,
-             int dtype, int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb, int64_t o_sh, float* lse,
-             int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan);
+             const MlaVarlen* vl, int dtype, int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb,
+             int64_t o_sh, float* lse, int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan);
 
 }  // namespace dcp

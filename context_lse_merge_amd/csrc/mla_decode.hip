@@ -219,9 +219,17 @@ constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;
 constexpr int kTileSlack = (kDmaPerWave * kWaves - kDmaPerTile) * 64 * 8;  // elements
 constexpr int kTileAlloc = kTileElems + kTileSlack;
 
-__device__ __forceinline__ void dma_tile(const MlaArgs& a, uint16_t* dst, int64_t t0, int64_t k1, int wave,
+// The keys a workgroup visits: logical key j (0, 1, ... within its shard) is
+// cache row rows0 + j * rstride elements (rstride = kv_st, or cp * kv_st when
+// the shard owns every cp-th row).
+struct KeyRows {
+    const uint16_t* rows0;
+    int32_t rstride;
+};
+
+__device__ __forceinline__ void dma_tile(const KeyRows& kr, uint16_t* dst, int64_t t0, int64_t k1, int wave,
                                          int lane_in) {
-    const uint16_t* base = a.kv + t0 * a.kv_st;
+    const uint16_t* base = kr.rows0 + t0 * kr.rstride;
     const int last = static_cast<int>(min(k1 - 1 - t0, static_cast<int64_t>(kKeys - 1)));
     const int lane = opaque(lane_in);
 #pragma unroll
@@ -232,7 +240,7 @@ __device__ __forceinline__ void dma_tile(const MlaArgs& a, uint16_t* dst, int64_
         const int blk = n - h * kHalfBlocks;
         const int key = 16 * h + ((lane & 15) ^ (4 * (blk & 1)));
         const int chunk = 4 * blk + (lane >> 4);
-        const int o = min(key, last) * static_cast<int>(a.kv_st) + 8 * chunk;
+        const int o = min(key, last) * kr.rstride + 8 * chunk;
         lds_dma16(base + o, lds_addr(dst + kBlockElems * copy));
     }
 }
@@ -372,19 +380,54 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     const int g = lane >> 4;    // lane group: keys 4g..4g+3 of each 16-key half
     const Work wk = work_of(a);
 
-    // Key range of this split of this shard.
-    const int64_t s0 = (static_cast<int64_t>(wk.s) * a.T) / a.cp;
-    const int64_t s1 = (static_cast<int64_t>(wk.s + 1) * a.T) / a.cp;
-    const int64_t k0 = s0 + static_cast<int64_t>(wk.p) * a.split_len;
-    const int64_t k1 = min(k0 + a.split_len, s1);
+    // The token(s) and cache of this workgroup.  One shared cache of T rows,
+    // and row blocks of 128 consecutive (token, head) rows; or, with
+    // seq_lens, token b's own cache of min(max(seq_lens[b], 0), T) rows and
+    // row blocks that never span tokens.
+    int64_t L = a.T;
+    const uint16_t* cache = a.kv;
+    int b_tok = 0, h_base = 0;
+    if (a.seq_lens) {
+        b_tok = wk.rb / a.rb_per_token;
+        h_base = (wk.rb - b_tok * a.rb_per_token) * kMlaRowsPerBlock;
+        L = min(max(static_cast<int64_t>(a.seq_lens[b_tok]), int64_t{0}), a.T);
+        cache = a.kv + b_tok * a.kv_sb;
+    }
+    // Shard s: n_s logical keys, key j at cache row start + j * step.
+    int64_t start, n_s;
+    int step;
+    if (a.interleaved) {
+        start = wk.s;
+        step = a.cp;
+        n_s = L > wk.s ? (L - wk.s + a.cp - 1) / a.cp : 0;
+    } else {
+        start = (static_cast<int64_t>(wk.s) * L) / a.cp;
+        step = 1;
+        n_s = (static_cast<int64_t>(wk.s + 1) * L) / a.cp - start;
+    }
+    const KeyRows kr{cache + start * a.kv_st, static_cast<int32_t>(step * a.kv_st)};
+    // Logical key range of this split.
+    const int64_t k0 = static_cast<int64_t>(wk.p) * a.split_len;
+    const int64_t k1 = min(k0 + a.split_len, n_s);
     const int ntiles = k0 < k1 ? static_cast<int>((k1 - k0 + kKeys - 1) / kKeys) : 0;
-    if (ntiles > 0) dma_tile(a, tile0, k0, k1, wave, lane);
+    if (ntiles > 0) dma_tile(kr, tile0, k0, k1, wave, lane);
 
-    // Query row of this lane (rows past the end repeat the last row and are not stored).
-    const int row_raw = wk.rb * kMlaRowsPerBlock + wave * kRowsPerWave + r16;
-    const int row = min(row_raw, a.rows - 1);
-    const int b = row / a.hq;
-    const int h = row - b * a.hq;
+    // Query row (b, h) of this lane; rows past the end repeat the last row and
+    // are not stored.
+    int b, h;
+    bool valid;
+    if (a.seq_lens) {
+        const int h_raw = h_base + wave * kRowsPerWave + r16;
+        valid = h_raw < a.hq;
+        b = b_tok;
+        h = min(h_raw, a.hq - 1);
+    } else {
+        const int row_raw = wk.rb * kMlaRowsPerBlock + wave * kRowsPerWave + r16;
+        valid = row_raw < a.rows;
+        const int row = min(row_raw, a.rows - 1);
+        b = row / a.hq;
+        h = row - b * a.hq;
+    }
 
     // Q fragments: fragment f holds columns 32f + 8g .. +7 of this lane's row.
     typename T::v8 qf[kQSteps];
@@ -424,21 +467,21 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     // Tile it lives in buffer it % 3 and is copied two tiles ahead: while
     // tile it is computed, tiles it+1 and it+2 may be in flight, and the
     // barrier that ends tile it waits only for tile it+1.
-    if (ntiles > 1) dma_tile(a, tile1, k0 + kKeys, k1, wave, lane);
+    if (ntiles > 1) dma_tile(kr, tile1, k0 + kKeys, k1, wave, lane);
     if (ntiles > 0) {
         if (ntiles > 1) older_tile_ready(); else all_tiles_ready();
     }
     for (int it = 0; it < ntiles; it += 3) {
         const int64_t t0 = k0 + static_cast<int64_t>(it) * kKeys;
-        if (it + 2 < ntiles) dma_tile(a, tile2, t0 + 2 * kKeys, k1, wave, lane);
+        if (it + 2 < ntiles) dma_tile(kr, tile2, t0 + 2 * kKeys, k1, wave, lane);
         compute_tile<T>(a, tile0, off, qf, st, t0, k1, g);
         if (it + 1 >= ntiles) break;
         if (it + 2 < ntiles) older_tile_ready(); else all_tiles_ready();
-        if (it + 3 < ntiles) dma_tile(a, tile0, t0 + 3 * kKeys, k1, wave, lane);
+        if (it + 3 < ntiles) dma_tile(kr, tile0, t0 + 3 * kKeys, k1, wave, lane);
         compute_tile<T>(a, tile1, off, qf, st, t0 + kKeys, k1, g);
         if (it + 2 >= ntiles) break;
         if (it + 3 < ntiles) older_tile_ready(); else all_tiles_ready();
-        if (it + 4 < ntiles) dma_tile(a, tile1, t0 + 4 * kKeys, k1, wave, lane);
+        if (it + 4 < ntiles) dma_tile(kr, tile1, t0 + 4 * kKeys, k1, wave, lane);
         compute_tile<T>(a, tile2, off, qf, st, t0 + 2 * kKeys, k1, g);
         if (it + 3 >= ntiles) break;
         if (it + 4 < ntiles) older_tile_ready(); else all_tiles_ready();
@@ -448,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     const float l_run = st.l_run;
     const float m_run = st.m_run;
     const float l_tot = sum_xor32(sum_xor16(l_run));
-    if (row_raw >= a.rows) return;
+    if (!valid) return;
 
     // O / l and the LSE in the caller's base; an empty shard or split gives 0
     // and -inf.  One split: the element type, straight into o_part / lse_part.
@@ -480,34 +523,58 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
 }  // namespace
 }  // namespace dcp
 
-extern "C" int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv,
-                                      int64_t kv_tokens, int64_t kv_st, int dtype, int cp, float softmax_scale,
-                                      int lse_mode,
-                                      void* o_part, int64_t o_sb, int64_t o_sh, float* lse_part, int64_t lse_sb,
-                                      void* scratch, size_t scratch_bytes, void* hip_stream) {
-    dcp::MlaPlan plan;
-    const int rc = dcp::plan_mla(q, B, hq, q_sb, q_sh, kv, kv_tokens, kv_st, dtype, cp, softmax_scale, lse_mode, o_part,
-                                 o_sb, o_sh, lse_part, lse_sb, scratch, scratch_bytes, &plan);
-    if (rc != DCP_OK) return rc;
-    if (plan.blocks == 0) return dcp::ok();
+namespace dcp {
+namespace {
+
+// Enqueue a validated plan: the decode kernel, then (several splits) the
+// merge over splits.
+int run_mla(const MlaPlan& plan, void* hip_stream, const char* fn) {
+    if (plan.blocks == 0) return ok();
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const dim3 grid(static_cast<unsigned>(plan.blocks));
     if (plan.args.dtype == DCP_DTYPE_FP16)
-        dcp::mla_decode_kernel<dcp::F16><<<grid, dim3(dcp::kThreads), 0, stream>>>(plan.args);
+        mla_decode_kernel<F16><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
     else
-        dcp::mla_decode_kernel<dcp::Bf16><<<grid, dim3(dcp::kThreads), 0, stream>>>(plan.args);
+        mla_decode_kernel<Bf16><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && plan.args.nsplit > 1) {
         // The splits of every (token, shard, head) are merged like DCP shards.
         const int64_t H = plan.reduce.h_local;
         int64_t chunk = (int64_t{1} << 30) / H;
-        if (chunk > dcp::kMaxLaunchTokens) chunk = dcp::kMaxLaunchTokens;
+        if (chunk > kMaxLaunchTokens) chunk = kMaxLaunchTokens;
         for (int64_t t0 = 0; t0 < plan.B && e == hipSuccess; t0 += chunk) {
             const int64_t n = plan.B - t0 < chunk ? plan.B - t0 : chunk;
-            e = static_cast<hipError_t>(dcp::merge_launch(dcp::merge_args_at(plan.reduce, t0, n), stream));
+            e = static_cast<hipError_t>(merge_launch(merge_args_at(plan.reduce, t0, n), stream));
         }
     }
-    if (e != hipSuccess)
-        return dcp::fail(DCP_ERR_HIP, "dcp_mla_partial_decode: launch failed: %s", hipGetErrorString(e));
-    return dcp::ok();
+    if (e != hipSuccess) return fail(DCP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+}  // namespace dcp
+
+extern "C" int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv,
+                                      int64_t kv_tokens, int64_t kv_st, int dtype, int cp, float softmax_scale,
+                                      int lse_mode, void* o_part, int64_t o_sb, int64_t o_sh, float* lse_part,
+                                      int64_t lse_sb, void* scratch, size_t scratch_bytes, void* hip_stream) {
+    dcp::MlaPlan plan;
+    const int rc = dcp::plan_mla(q, B, hq, q_sb, q_sh, kv, kv_tokens, kv_st, nullptr, dtype, cp, softmax_scale,
+                                 lse_mode, o_part, o_sb, o_sh, lse_part, lse_sb, scratch, scratch_bytes, &plan);
+    if (rc != DCP_OK) return rc;
+    return dcp::run_mla(plan, hip_stream, "dcp_mla_partial_decode");
+}
+
+extern "C" int dcp_mla_partial_decode_varlen(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh,
+                                             const void* kv, int64_t kv_sb, int64_t kv_st, int64_t max_seq_len,
+                                             const int32_t* seq_lens, int kv_layout, int dtype, int cp,
+                                             float softmax_scale, int lse_mode, void* o_part, int64_t o_sb,
+                                             int64_t o_sh, float* lse_part, int64_t lse_sb, void* scratch,
+                                             size_t scratch_bytes, void* hip_stream) {
+    dcp::MlaPlan plan;
+    const dcp::MlaVarlen vl{seq_lens, kv_sb, kv_layout};
+    const int rc = dcp::plan_mla(q, B, hq, q_sb, q_sh, kv, max_seq_len, kv_st, &vl, dtype, cp, softmax_scale,
+                                 lse_mode, o_part, o_sb, o_sh, lse_part, lse_sb, scratch, scratch_bytes, &plan);
+    if (rc != DCP_OK) return rc;
+    return dcp::run_mla(plan, hip_stream, "dcp_mla_partial_decode_varlen");
 }

@@ -68,6 +68,10 @@ extern "C" {
 #define DCP_QK_DIM 576   /* query/key columns of the MLA decode: 512 latent + 64 rope */
 #define DCP_MAX_CP 64
 
+/* Which cache rows a DCP shard owns (dcp_mla_partial_decode_varlen). */
+#define DCP_KV_CONTIGUOUS 0  /* shard s: rows [floor(s*L/cp), floor((s+1)*L/cp)) of a length-L cache */
+#define DCP_KV_INTERLEAVED 1 /* shard s: rows t < L with t mod cp == s                              */
+
 typedef struct dcp_workspace dcp_workspace;
 
 /*
@@ -178,6 +182,43 @@ int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64
                            int64_t kv_tokens, int64_t kv_st, int dtype, int cp, float softmax_scale, int lse_mode,
                            void* o_part, int64_t o_sb, int64_t o_sh, float* lse_part, int64_t lse_sb, void* scratch,
                            size_t scratch_bytes, void* hip_stream);
+
+/*
+ * MLA decode partials with one cache per query token and per-token lengths:
+ * the producer as a decode batch runs it, each token (request) attending
+ * over its own latent KV rows.  The decode seq_lens decide which shards are
+ * empty ("[Attention] Add direct symmetric-memory DCP A2A", vLLM PR #48897,
+ * amended port commit: the dispatch takes the decode seq_lens and an empty
+ * shard publishes LSE = -inf and no payload); with the latent KV interleaved
+ * across DCP ranks ("[DCP] Optimize shared Output, Query, and Indexer/Top-K
+ * via peer memory", sglang PR #32851, commit log) shard s owns every cp-th
+ * token of each request.
+ *
+ * For query row (b, h) let L = min(max(seq_lens[b], 0), max_seq_len) and
+ * let R_s be the rows shard s owns (kv_layout: DCP_KV_CONTIGUOUS or
+ * DCP_KV_INTERLEAVED, see above); then with z_t = softmax_scale * <q[b,h,:],
+ * cache_b[t,:]> over 576 columns,
+ *     o_part[b, s*hq + h, :] = sum_{t in R_s} softmax(z)_t * cache_b[t, 0:512]
+ *     lse_part[b, s*hq + h]  = log sum_{t in R_s} exp(z_t)  (base of lse_mode)
+ * and a shard with R_s empty gives o_part = 0, lse_part = -inf: exactly the
+ * input dcp_lse_combine expects, whose merge is attention over all L rows.
+ *
+ * kv        token b's cache row t at kv + b*kv_sb + t*kv_st (dtype elements);
+ *           kv_sb = 0 lets every token share one cache.  Rows t >=
+ *           max_seq_len are never read.
+ * seq_lens  device int32 [B]; values outside [0, max_seq_len] are clamped.
+ * max_seq_len  host bound on seq_lens, used to size the key splits.
+ * Other arguments, strides, alignment (kv_sb a multiple of 8 elements too),
+ * arithmetic and errors as dcp_mla_partial_decode.  A workgroup serves the
+ * heads of one token, so hq below 128 leaves part of each workgroup idle.
+ */
+int dcp_mla_partial_decode_varlen_scratch_size(int64_t B, int hq, int64_t max_seq_len, int cp, size_t* bytes);
+
+int dcp_mla_partial_decode_varlen(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv,
+                                  int64_t kv_sb, int64_t kv_st, int64_t max_seq_len, const int32_t* seq_lens,
+                                  int kv_layout, int dtype, int cp, float softmax_scale, int lse_mode, void* o_part,
+                                  int64_t o_sb, int64_t o_sh, float* lse_part, int64_t lse_sb, void* scratch,
+                                  size_t scratch_bytes, void* hip_stream);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char* dcp_last_error(void);

@@ -1,0 +1,186 @@
+"""GPU parity of dcp_mla_partial_decode_varlen against the fp64 oracle.
+
+Each query token attends over its own cache and its own decode length; the
+lengths decide which DCP shards are empty ("[Attention] Add direct
+symmetric-memory DCP A2A", vLLM PR #48897, amended port commit), and shards
+own either a contiguous slice of a token's rows or, with the latent KV
+interleaved across DCP ranks ("[DCP] Optimize shared Output, Query, and
+Indexer/Top-K via peer memory", sglang PR #32851, commit log), every cp-th
+row.  Tolerances as for the fixed-length producer (see test_gpu_mla).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import context_lse_merge_amd as dcp
+import oracle
+import synth
+from tests.merge_helpers import announce, check_against_oracle
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+THREADS = len(os.sched_getaffinity(0))
+OMODE = {dcp.DCP_LSE_BASE_E: oracle.BASE_E, dcp.DCP_LSE_BASE_2: oracle.BASE_2}
+LAYOUTS = {"contiguous": dcp.DCP_KV_CONTIGUOUS, "interleaved": dcp.DCP_KV_INTERLEAVED}
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def run_varlen(q, kv, seq, max_len, layout, cp, mode, kv_dev=None):
+    B, hq, _ = q.shape
+    o = torch.empty((B, cp * hq, 512), dtype=q.dtype, device=DEV)
+    l = torch.empty((B, cp * hq), dtype=torch.float32, device=DEV)
+    nbytes = dcp.dcp_mla_partial_decode_varlen_scratch_size(B, hq, max_len, cp)
+    scratch = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV) if nbytes else None
+    announce("dcp_mla_partial_decode_varlen %s B=%d hq=%d max_len=%d layout=%d cp=%d scratch=%d seq=%s" % (
+        synth.payload_name(q), B, hq, max_len, layout, cp, nbytes, list(seq[:6])))
+    dcp.dcp_mla_partial_decode_varlen(q.to(DEV), kv.to(DEV) if kv_dev is None else kv_dev,
+                                      torch.from_numpy(np.asarray(seq, np.int32)).to(DEV), max_len, layout, cp,
+                                      synth.MLA_SCALE, mode, o, l, scratch)
+    torch.cuda.synchronize()
+    return o, l
+
+
+def check(q, kv, seq, layout, cp, mode, o, l, rows=None):
+    B, hq, _ = q.shape
+    clamped = np.clip(np.asarray(seq, np.int64), 0, kv.shape[-2]).astype(np.int32)
+    o_r, l_r = oracle.attention_partials_varlen(synth.bits16(q), synth.bits16(kv), clamped, cp, synth.MLA_SCALE,
+                                                OMODE[mode], interleaved=(layout == dcp.DCP_KV_INTERLEAVED),
+                                                rows=rows, threads=THREADS, dtype=synth.payload_name(q))
+    rows = np.arange(B * hq) if rows is None else np.asarray(rows)
+    o_g = o.float().cpu().double().numpy().reshape(B, cp, hq, 512)
+    l_g = l.cpu().double().numpy().reshape(B, cp, hq)
+    for i, r in enumerate(rows):
+        b, h = divmod(int(r), hq)
+        for s in range(cp):
+            og, lg, orr, lr = o_g[b, s, h], l_g[b, s, h], o_r[i, s], l_r[i, s]
+            if np.isneginf(lr):
+                assert np.isneginf(lg) and np.all(og == 0), "row %d shard %d: empty shard not (0, -inf)" % (r, s)
+                continue
+            assert abs(lg - lr) <= 1e-5 * max(abs(lr), 1.0), "row %d shard %d: lse %.8g vs %.8g" % (r, s, lg, lr)
+            assert np.abs(og - orr).max() <= 2.0 ** -7 * np.abs(orr).max(), "row %d shard %d" % (r, s)
+    # merged shards (the GPU merge of the GPU partials) against attention over all L rows
+    out = torch.empty((B, hq, 512), dtype=q.dtype, device=DEV)
+    out_lse = torch.empty((B, hq), dtype=torch.float32, device=DEV)
+    ws = dcp.dcp_workspace_create(B, hq, cp,
+                                  dtype=dcp.DCP_DTYPE_FP16 if q.dtype == torch.float16 else dcp.DCP_DTYPE_BF16)
+    dcp.dcp_lse_combine(ws, o, l, dcp.DCP_LSE_BH1, mode, out, out_lse)
+    torch.cuda.synchronize()
+    ws.close()
+    case = synth.MergeCase("varlen output", o.cpu(), l.cpu().reshape(B, cp * hq, 1), cp, "bh1",
+                           "e" if mode == dcp.DCP_LSE_BASE_E else "2")
+    check_against_oracle(case, out, out_lse)
+    o_f, l_f = oracle.attention_partials_varlen(synth.bits16(q), synth.bits16(kv), clamped, 1, synth.MLA_SCALE,
+                                                OMODE[mode], rows=rows, threads=THREADS,
+                                                dtype=synth.payload_name(q))
+    g = out.float().cpu().double().numpy().reshape(B * hq, 512)
+    gl = out_lse.cpu().double().numpy().reshape(B * hq)
+    for i, r in enumerate(rows):
+        if np.isneginf(l_f[i, 0]):
+            assert np.all(g[r] == 0) and np.isneginf(gl[r])
+            continue
+        assert np.abs(g[r] - o_f[i, 0]).max() <= 2.0 ** -7 * np.abs(o_f[i, 0]).max()
+        assert abs(gl[r] - l_f[i, 0]) <= 1e-5 * max(abs(l_f[i, 0]), 1.0)
+
+
+def _caches(seed, B, hq, tmax, dtype=torch.bfloat16):
+    g = synth.gen(seed)
+    q = synth.normal_16((B, hq, 576), g, dtype)
+    kv = synth.normal_16((B, tmax, 576), g, dtype, std=0.5)
+    return q, kv
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "interleaved"])
+@pytest.mark.parametrize("mode", [dcp.DCP_LSE_BASE_E, dcp.DCP_LSE_BASE_2])
+def test_short_and_empty_lengths(layout, mode):
+    """Lengths 0, 1, 3 (fewer rows than shards: empty shards), 150 and 300."""
+    q, kv = _caches(700, 5, 16, 300)
+    seq = [0, 1, 3, 150, 300]
+    o, l = run_varlen(q, kv, seq, 300, LAYOUTS[layout], 4, mode)
+    check(q, kv, seq, LAYOUTS[layout], 4, mode, o, l)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "interleaved"])
+def test_split_path_long_lengths(layout):
+    """Long caches with 128 heads: several key splits per shard, merged by the
+    fp32-input merge kernel; lengths that are not multiples of the tile."""
+    q, kv = _caches(701, 2, 128, 16384)
+    seq = [16384, 9001]
+    o, l = run_varlen(q, kv, seq, 16384, LAYOUTS[layout], 4, dcp.DCP_LSE_BASE_E)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(256)[-8:], np.random.default_rng(7).integers(0, 256, 16)]))
+    check(q, kv, seq, LAYOUTS[layout], 4, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
+
+
+def test_heads_not_a_multiple_of_128_and_odd_cp():
+    q, kv = _caches(702, 3, 160, 700)
+    seq = [700, 2, 333]
+    o, l = run_varlen(q, kv, seq, 700, dcp.DCP_KV_INTERLEAVED, 3, dcp.DCP_LSE_BASE_2)
+    rows = np.unique(np.concatenate([np.arange(0, 480, 7), [159, 160, 319, 320, 479]]))
+    check(q, kv, seq, dcp.DCP_KV_INTERLEAVED, 3, dcp.DCP_LSE_BASE_2, o, l, rows=rows)
+
+
+def test_lengths_outside_the_range_are_clamped():
+    q, kv = _caches(703, 3, 16, 200)
+    seq = [-5, 260, 77]                          # read as 0, 200, 77
+    o, l = run_varlen(q, kv, seq, 200, dcp.DCP_KV_CONTIGUOUS, 4, dcp.DCP_LSE_BASE_E)
+    check(q, kv, seq, dcp.DCP_KV_CONTIGUOUS, 4, dcp.DCP_LSE_BASE_E, o, l)
+    assert torch.all(torch.isneginf(l.cpu()[0]))
+
+
+def test_fp16_varlen():
+    q, kv = _caches(704, 4, 32, 512, dtype=torch.float16)
+    seq = [512, 5, 0, 250]
+    o, l = run_varlen(q, kv, seq, 512, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_E)
+    check(q, kv, seq, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_E, o, l)
+
+
+def test_shared_cache_full_length_matches_fixed_length_bitwise():
+    """Every token sharing one cache at its full length, contiguous ownership:
+    the same tiles in the same order as dcp_mla_partial_decode, so the same bits."""
+    q, kv = synth.mla_decode(2, T=4096, hq=128, seed=705)
+    kv_dev = kv.to(DEV)
+    o_v, l_v = run_varlen(q, kv, [4096, 4096], 4096, dcp.DCP_KV_CONTIGUOUS, 4, dcp.DCP_LSE_BASE_E, kv_dev=kv_dev)
+    o_f = torch.empty_like(o_v)
+    l_f = torch.empty_like(l_v)
+    nbytes = dcp.dcp_mla_partial_decode_scratch_size(2, 128, 4096, 4)
+    scratch = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV) if nbytes else None
+    announce("fixed-length producer on the same shared cache")
+    dcp.dcp_mla_partial_decode(q.to(DEV), kv_dev, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o_f, l_f, scratch)
+    torch.cuda.synchronize()
+    assert torch.equal(o_v.view(torch.int16), o_f.view(torch.int16))
+    assert torch.equal(l_v.view(torch.int32), l_f.view(torch.int32))
+
+
+def test_full_size_shared_cache_random_lengths_interleaved():
+    """64 tokens over one 131072-row cache (kv_sb = 0) with lengths drawn
+    uniformly in [1, 131072], interleaved ownership: sampled rows."""
+    _, kv = synth.mla_decode(1)
+    B = 64
+    q = synth.normal_bf16((B, 128, 576), synth.gen(3300))
+    seq = np.random.default_rng(3300).integers(1, 131073, B).astype(np.int32)
+    seq[:2] = [131072, 3]
+    o, l = run_varlen(q, kv, seq, 131072, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_E)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 128, 129, B * 128 - 1], rng.integers(0, B * 128, 4)]))
+    check(q, kv, seq, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
+
+
+def test_argument_errors():
+    q, kv = _caches(706, 2, 16, 64)
+    o = torch.empty((2, 64, 512), dtype=torch.bfloat16, device=DEV)
+    l = torch.empty((2, 64), dtype=torch.float32, device=DEV)
+    seq = torch.tensor([64, 10], dtype=torch.int32, device=DEV)
+    announce("varlen argument errors (rejected before launch)")
+    with pytest.raises(dcp.DcpError) as e:
+        dcp.dcp_mla_partial_decode_varlen(q.to(DEV), kv.to(DEV), seq, 64, 7, 4, synth.MLA_SCALE,
+                                          dcp.DCP_LSE_BASE_E, o, l, None)
+    assert e.value.status == dcp.DCP_ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        dcp.dcp_mla_partial_decode_varlen(q.to(DEV), kv.to(DEV), seq, 65, dcp.DCP_KV_CONTIGUOUS, 4,
+                                          synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, None)
