@@ -47,7 +47,8 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=600, help="timed layer-merges (a multiple of 60 above 60)")
     p.add_argument("--warmup", type=int, default=120)
-    p.add_argument("--workload", choices=["kimi", "dsv2", "stress"], default="kimi")
+    p.add_argument("--workload", choices=["kimi", "dsv2", "stress", "kimi_f16", "dsv2_f16", "stress_f16"],
+                   default="kimi")
     p.add_argument("--B", type=int, default=128)
     p.add_argument("--no-sweep", action="store_true", help="skip the B = 1..512 sweep")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
@@ -61,19 +62,23 @@ def parse_args():
 
 
 def make_case(workload, B):
+    import torch
     import synth
-    if workload == "kimi":
-        return synth.kimi_merge(B)
-    if workload == "dsv2":
-        return synth.dsv2_merge(B)
-    return synth.stress_merge(B)
+    dtype = torch.float16 if workload.endswith("_f16") else torch.bfloat16
+    base = workload[:-4] if workload.endswith("_f16") else workload
+    if base == "kimi":
+        return synth.kimi_merge(B, dtype=dtype)
+    if base == "dsv2":
+        return synth.dsv2_merge(B, dtype=dtype)
+    return synth.stress_merge(B, dtype=dtype)
 
 
 def workload_name(case, workload):
     desc = {"kimi": "Kimi-K2.5-like merge, [B,H/cp,cp] base-e LSE",
             "dsv2": "DeepSeek-V2-236B-like merge, FlashMLA [B,H,1] base-2 LSE",
-            "stress": "stress merge, 10% empty shards, capacity 128 (ordered chunks)"}[workload]
-    return "%s: B=%d H=%d cp=%d H_local=%d D=512 bf16" % (desc, case.B, case.H, case.cp, case.h_local)
+            "stress": "stress merge, 10% empty shards, capacity 128 (ordered chunks)"}[workload.replace("_f16", "")]
+    return "%s: B=%d H=%d cp=%d H_local=%d D=512 %s" % (desc, case.B, case.H, case.cp, case.h_local,
+                                                         "fp16" if workload.endswith("_f16") else "bf16")
 
 
 def algorithmic_bytes(case):
@@ -106,7 +111,7 @@ class GpuCase:
             attn.copy_(attn0)
             lse = torch.empty_like(lse0)
             lse.copy_(lse0)
-            out = torch.empty((case.B, case.h_local, 512), dtype=torch.bfloat16, device=dev)
+            out = torch.empty((case.B, case.h_local, 512), dtype=case.attn.dtype, device=dev)
             out_lse = torch.empty((case.B, case.h_local), dtype=torch.float32, device=dev)
             self.sets.append((attn, lse, out, out_lse))
         self.capacity = capacity
@@ -121,7 +126,9 @@ class GpuCase:
         """HIP graphs of `calls_per_graph` calls each, together cycling over every set."""
         import torch
         stream = torch.cuda.Stream()
-        ws = self.dcp.dcp_workspace_create(self.capacity, self.case.h_local, self.case.cp, stream=stream)
+        dtype = self.dcp.DCP_DTYPE_FP16 if self.case.attn.dtype == torch.float16 else self.dcp.DCP_DTYPE_BF16
+        ws = self.dcp.dcp_workspace_create(self.capacity, self.case.h_local, self.case.cp, dtype=dtype,
+                                           stream=stream)
         # one eager pass on the capture stream first
         with torch.cuda.stream(stream):
             for k in range(len(self.sets)):
@@ -193,9 +200,13 @@ def parity_check(case, out, out_lse):
     import synth
     olay = oracle.LSE_BHC if case.lse_layout == "bhc" else oracle.LSE_BH1
     omode = oracle.BASE_E if case.lse_mode == "e" else oracle.BASE_2
-    r, rL, A = oracle.merge(synth.bf16_bits(case.attn), case.lse.contiguous().numpy(), case.cp, olay, omode)
+    r, rL, A = oracle.merge(synth.bits16(case.attn), case.lse.contiguous().numpy(), case.cp, olay, omode,
+                            dtype=synth.payload_name(case.attn))
     g = out.float().cpu().double().numpy()
-    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126))) - 7)
+    if synth.payload_name(case.attn) == "f16":
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -14))) - 10)
+    else:
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126))) - 7)
     ok = bool(np.all(np.abs(g - r) <= 2 * ulp + 2.0 ** -16 * A))
     gL = out_lse.cpu().double().numpy()
     fin = np.isfinite(rL)
@@ -208,17 +219,18 @@ def cpu_baseline(case, seconds):
     repeated for about `seconds` (at least 2), all host cores it is allowed."""
     import oracle
     import synth
-    bits = synth.bf16_bits(case.attn)
+    bits = synth.bits16(case.attn)
+    dt = synth.payload_name(case.attn)
     lse = case.lse.contiguous().numpy()
     olay = oracle.LSE_BHC if case.lse_layout == "bhc" else oracle.LSE_BH1
     omode = oracle.BASE_E if case.lse_mode == "e" else oracle.BASE_2
     threads = len(os.sched_getaffinity(0))
-    oracle.merge(bits, lse, case.cp, olay, omode, threads=threads)          # warm-up
+    oracle.merge(bits, lse, case.cp, olay, omode, threads=threads, dtype=dt)          # warm-up
     times = []
     t_end = time.perf_counter() + seconds
     while len(times) < 2 or time.perf_counter() < t_end:
         t0 = time.perf_counter()
-        oracle.merge(bits, lse, case.cp, olay, omode, threads=threads)
+        oracle.merge(bits, lse, case.cp, olay, omode, threads=threads, dtype=dt)
         times.append(time.perf_counter() - t0)
     times.sort()
     med = times[len(times) // 2]
@@ -227,7 +239,7 @@ def cpu_baseline(case, seconds):
     t_end = time.perf_counter() + seconds / 3
     while len(t1) < 2 or time.perf_counter() < t_end:
         t0 = time.perf_counter()
-        oracle.merge(bits, lse, case.cp, olay, omode, threads=1)
+        oracle.merge(bits, lse, case.cp, olay, omode, threads=1, dtype=dt)
         t1.append(time.perf_counter() - t0)
     t1.sort()
     model = ""
@@ -243,6 +255,7 @@ def cpu_baseline(case, seconds):
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16, published
+MFMA_FP16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16, published
 
 
 def producer_flops(B, hq, T):
@@ -250,33 +263,45 @@ def producer_flops(B, hq, T):
     return 2.0 * B * hq * T * (576 + 512)
 
 
-def measure_producer(B, kv_copies, reps=10):
+def measure_producer(B, kv_copies, reps=10, seq_lens=None):
     """dcp_mla_partial_decode (+ the merge of its output) on the full-size MLA
     decode workload: q [B,128,576], one 131072 x 576 cache, 4 shards.  The cache
     is rotated over `kv_copies` device copies (>= 1 GiB together) so every call
-    reads it from HBM.  Returns (producer us, merge us)."""
+    reads it from HBM.  With `seq_lens` (int32 [B] on the GPU) the
+    variable-length entry point runs instead: every token over the shared cache
+    (kv_sb = 0) up to its own length, interleaved ownership.  q, the cache and
+    the outputs take the cache's dtype.  Returns (producer us, merge us)."""
     import torch
     import context_lse_merge_amd as dcp
     import synth
     dev = torch.device("cuda:0")
     hq, cp, T = 128, 4, kv_copies[0].shape[0]
-    q = synth.normal_bf16((B, hq, 576), synth.gen(3000 + B)).to(dev)
-    o = torch.empty((B, cp * hq, 512), dtype=torch.bfloat16, device=dev)
+    dtype = kv_copies[0].dtype
+    q = synth.normal_16((B, hq, 576), synth.gen(3000 + B), dtype).to(dev)
+    o = torch.empty((B, cp * hq, 512), dtype=dtype, device=dev)
     l = torch.empty((B, cp * hq), dtype=torch.float32, device=dev)
-    out = torch.empty((B, hq, 512), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, hq, 512), dtype=dtype, device=dev)
     out_lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
-    nbytes = dcp.dcp_mla_partial_decode_scratch_size(B, hq, T, cp)
+    if seq_lens is None:
+        nbytes = dcp.dcp_mla_partial_decode_scratch_size(B, hq, T, cp)
+    else:
+        nbytes = dcp.dcp_mla_partial_decode_varlen_scratch_size(B, hq, T, cp)
     scratch = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
-    ws = dcp.dcp_workspace_create(B, hq, cp)
+    ws = dcp.dcp_workspace_create(B, hq, cp, dtype=dcp.DCP_DTYPE_FP16 if dtype == torch.float16 else dcp.DCP_DTYPE_BF16)
+
+    def produce(kv):
+        if seq_lens is None:
+            dcp.dcp_mla_partial_decode(q, kv, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, scratch)
+        else:
+            dcp.dcp_mla_partial_decode_varlen(q, kv, seq_lens, T, dcp.DCP_KV_INTERLEAVED, cp, synth.MLA_SCALE,
+                                              dcp.DCP_LSE_BASE_E, o, l, scratch)
     for k in range(2):
-        dcp.dcp_mla_partial_decode(q, kv_copies[k % len(kv_copies)], cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l,
-                                   scratch)
+        produce(kv_copies[k % len(kv_copies)])
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps + 1)]
     ev[0].record()
     for r in range(reps):
-        dcp.dcp_mla_partial_decode(q, kv_copies[r % len(kv_copies)], cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o,
-                                   l, scratch)
+        produce(kv_copies[r % len(kv_copies)])
         ev[2 * r + 1].record()
         dcp.dcp_lse_combine(ws, o, l, dcp.DCP_LSE_BH1, dcp.DCP_LSE_BASE_E, out, out_lse)
         ev[2 * r + 2].record()
@@ -304,7 +329,32 @@ def producer_leg(Bs):
                      "kv_GBps": round(kv_gbs, 1), "flop": fl})
         print("[bench] producer B=%d: %.1f us (%.1f TFLOP/s, %.1f%% of bf16 peak), merge %.2f us"
               % (B, us, tflops, 100 * tflops / MFMA_BF16_PEAK_TFLOPS, us_m), file=sys.stderr, flush=True)
-    del copies, kv_dev
+    # the other payload type and the variable-length entry point, at B = 64
+    import numpy as np
+    seq = np.random.default_rng(64).integers(1, kv.shape[0] + 1, 64).astype(np.int32)
+    seq_dev = torch.from_numpy(seq).to("cuda:0")
+    us, us_m = measure_producer(64, copies, seq_lens=seq_dev)
+    fl = 2.0 * 128 * float(seq.astype(np.int64).sum()) * (576 + 512)
+    tflops = fl / (us * 1e-6) / 1e12
+    rows.append({"B": 64, "variant": "variable length: lengths U[1, 131072] (sum %d), one shared cache, "
+                                     "interleaved ownership" % int(seq.sum()),
+                 "producer_us": round(us, 1), "merge_us": round(us_m, 3), "TFLOPs": round(tflops, 1),
+                 "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "flop": fl})
+    print("[bench] producer varlen B=64 (interleaved, random lengths): %.1f us (%.1f TFLOP/s, %.1f%% of bf16 peak)"
+          % (us, tflops, 100 * tflops / MFMA_BF16_PEAK_TFLOPS), file=sys.stderr, flush=True)
+    del copies
+    copies = [kv_dev.to(torch.float16)]
+    copies += [copies[0].clone() for _ in range(7)]
+    del kv_dev
+    us, us_m = measure_producer(64, copies)
+    fl = producer_flops(64, 128, kv.shape[0])
+    tflops = fl / (us * 1e-6) / 1e12
+    rows.append({"B": 64, "variant": "fp16 q, cache and outputs", "producer_us": round(us, 1),
+                 "merge_us": round(us_m, 3), "TFLOPs": round(tflops, 1),
+                 "mfma_frac": round(tflops / MFMA_FP16_PEAK_TFLOPS, 4), "flop": fl})
+    print("[bench] producer fp16 B=64: %.1f us (%.1f TFLOP/s, %.1f%% of fp16 peak), merge %.2f us"
+          % (us, tflops, 100 * tflops / MFMA_FP16_PEAK_TFLOPS, us_m), file=sys.stderr, flush=True)
+    del copies
     torch.cuda.empty_cache()
     return rows
 
@@ -380,7 +430,7 @@ def main():
     import context_lse_merge_amd  # noqa: F401  (fails loudly if the HIP library is missing)
 
     case = make_case(args.workload, args.B)
-    capacity = 128 if args.workload == "stress" else case.B
+    capacity = 128 if args.workload.startswith("stress") else case.B
     alg = algorithmic_bytes(case)
     print("[bench] %s: %d algorithmic bytes per layer-merge" % (workload_name(case, args.workload), alg),
           file=sys.stderr, flush=True)
@@ -394,10 +444,11 @@ def main():
     sweep = []
     if not args.no_sweep:
         for wl, Bs in (("kimi", [1, 8, 16, 32, 64, 128, 256, 512]), ("dsv2", [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]),
+                       ("kimi_f16", [64, 128, 512]), ("dsv2_f16", [512]),
                        ("stress", [512])):
             for B in Bs:
                 c = make_case(wl, B)
-                cap = 128 if wl == "stress" else B
+                cap = 128 if wl.startswith("stress") else B
                 u, n, fp, _ = measure(c, 120, 60, capacity=cap, cold=True)
                 a = algorithmic_bytes(c)
                 sweep.append({"workload": wl, "B": B, "us": round(u, 3), "GBps": round(a / (u * 1e-6) / 1e9, 1),
