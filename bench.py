@@ -129,6 +129,8 @@ class GpuCase:
         dtype = self.dcp.DCP_DTYPE_FP16 if self.case.attn.dtype == torch.float16 else self.dcp.DCP_DTYPE_BF16
         ws = self.dcp.dcp_workspace_create(self.capacity, self.case.h_local, self.case.cp, dtype=dtype,
                                            stream=stream)
+        if getattr(self, "cached", False):
+            self.dcp.dcp_workspace_set_load_policy(ws, self.dcp.DCP_LOAD_CACHED)
         # one eager pass on the capture stream first
         with torch.cuda.stream(stream):
             for k in range(len(self.sets)):
@@ -172,8 +174,9 @@ def time_graphs(graphs, replays):
     return start.elapsed_time(end)
 
 
-def measure(case, steps, warmup, capacity=None, cold=True):
-    """Returns (us per layer-merge, number of input sets, footprint bytes)."""
+def measure(case, steps, warmup, capacity=None, cold=True, cached=False):
+    """Returns (us per layer-merge, number of input sets, footprint bytes).
+    ``cached``: the workspace's DCP_LOAD_CACHED policy instead of streaming."""
     per_set = case.attn.numel() * 2 + case.lse.numel() * 4 + case.B * case.h_local * (1024 + 4)
     calls = min(GRAPH_CALLS, steps)
     if steps % calls:
@@ -183,6 +186,7 @@ def measure(case, steps, warmup, capacity=None, cold=True):
     ngraphs = max(1, min(1024 // calls, math.ceil(COLD_BYTES / per_set / calls))) if cold else 1
     nsets = ngraphs * calls if cold else 1
     g = GpuCase(case, nsets, capacity or case.B)
+    g.cached = cached
     graphs = g.capture(ngraphs, calls)
     wrep = max(1, math.ceil(warmup / calls))
     time_graphs(graphs, wrep)
@@ -288,6 +292,7 @@ def measure_producer(B, kv_copies, reps=10, seq_lens=None):
         nbytes = dcp.dcp_mla_partial_decode_varlen_scratch_size(B, hq, T, cp)
     scratch = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
     ws = dcp.dcp_workspace_create(B, hq, cp, dtype=dcp.DCP_DTYPE_FP16 if dtype == torch.float16 else dcp.DCP_DTYPE_BF16)
+    dcp.dcp_workspace_set_load_policy(ws, dcp.DCP_LOAD_CACHED)   # the partials were just written
 
     def produce(kv):
         if seq_lens is None:
@@ -437,9 +442,11 @@ def main():
     us, nsets, footprint, first = measure(case, args.steps, args.warmup, capacity=capacity, cold=True)
     ok = parity_check(case, first[2], first[3])
     us_hot = None if args.no_hot else measure(case, args.steps, args.warmup, capacity=capacity, cold=False)[0]
+    us_hot_cached = None if args.no_hot else measure(case, args.steps, args.warmup, capacity=capacity, cold=False,
+                                                     cached=True)[0]
     gbs = alg / (us * 1e-6) / 1e9
-    print("[bench] cold %.3f us (%.1f GB/s), hot %s us, parity %s" % (us, gbs, us_hot, ok), file=sys.stderr,
-          flush=True)
+    print("[bench] cold %.3f us (%.1f GB/s), hot %s us, hot with DCP_LOAD_CACHED %s us, parity %s"
+          % (us, gbs, us_hot, us_hot_cached, ok), file=sys.stderr, flush=True)
 
     sweep = []
     if not args.no_sweep:
@@ -456,6 +463,18 @@ def main():
                               "input_sets": n, "footprint_MB": round(fp / 1e6, 1)})
                 print("[bench] sweep %s B=%d: %.3f us, %.1f GB/s" % (wl, B, u, sweep[-1]["GBps"]), file=sys.stderr,
                       flush=True)
+        # hot inputs (the same buffers every call, as when the partials were just
+        # written): the default streaming policy against DCP_LOAD_CACHED
+        for B in (128, 512):
+            c = make_case("kimi", B)
+            a = algorithmic_bytes(c)
+            for cached in (False, True):
+                u = measure(c, 120, 60, capacity=B, cold=False, cached=cached)[0]
+                sweep.append({"workload": "kimi hot " + ("DCP_LOAD_CACHED" if cached else "DCP_LOAD_STREAMING"),
+                              "B": B, "us": round(u, 3), "GBps": round(a / (u * 1e-6) / 1e9, 1),
+                              "frac_of_peak": round(a / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": a,
+                              "input_sets": 1, "footprint_MB": round(a / 1e6, 1)})
+                print("[bench] sweep %s B=%d: %.3f us" % (sweep[-1]["workload"], B, u), file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -494,6 +513,7 @@ def main():
                    "cache": "cold: each input reused only after >= 1 GiB of other inputs"},
         "us_per_layer_merge": round(us, 3),
         "us_per_layer_merge_hot": None if us_hot is None else round(us_hot, 3),
+        "us_per_layer_merge_hot_cached_policy": None if us_hot_cached is None else round(us_hot_cached, 3),
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "parity_vs_oracle": ok,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -44,6 +44,8 @@ DCP_DTYPE_FP16 = _C["DCP_DTYPE_FP16"]
 DCP_HEAD_DIM = _C["DCP_HEAD_DIM"]
 DCP_QK_DIM = _C["DCP_QK_DIM"]
 DCP_MAX_CP = _C["DCP_MAX_CP"]
+DCP_LOAD_STREAMING = _C["DCP_LOAD_STREAMING"]
+DCP_LOAD_CACHED = _C["DCP_LOAD_CACHED"]
 DCP_KV_CONTIGUOUS = _C["DCP_KV_CONTIGUOUS"]
 DCP_KV_INTERLEAVED = _C["DCP_KV_INTERLEAVED"]
 
@@ -56,6 +58,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
 _lib.dcp_workspace_create.argtypes = [_i64, _i32, _i32, _i32, _i32, _vp, ctypes.POINTER(_vp)]
 _lib.dcp_workspace_destroy.argtypes = [_vp]
+_lib.dcp_workspace_set_load_policy.argtypes = [_vp, _i32]
 _lib.dcp_lse_combine.argtypes = [_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _i64,
                                  _i64, _vp, _i64, _vp]
 _lib.dcp_mla_partial_decode_scratch_size.argtypes = [_i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
@@ -67,7 +70,7 @@ _lib.dcp_mla_partial_decode_varlen.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp,
 _lib.dcp_last_error.restype = ctypes.c_char_p
 _lib.dcp_status_string.argtypes = [_i32]
 _lib.dcp_status_string.restype = ctypes.c_char_p
-for _f in ("dcp_workspace_create", "dcp_workspace_destroy", "dcp_lse_combine",
+for _f in ("dcp_workspace_create", "dcp_workspace_destroy", "dcp_workspace_set_load_policy", "dcp_lse_combine",
            "dcp_mla_partial_decode_scratch_size", "dcp_mla_partial_decode",
            "dcp_mla_partial_decode_varlen_scratch_size", "dcp_mla_partial_decode_varlen"):
     getattr(_lib, _f).restype = _i32
@@ -151,6 +154,12 @@ def dcp_workspace_create(capacity_tokens: int, h_local: int, cp: int, d: int = D
 
 def dcp_workspace_destroy(ws: Workspace):
     ws.close()
+
+
+def dcp_workspace_set_load_policy(ws: Workspace, policy: int):
+    """DCP_LOAD_STREAMING (non-temporal, the default) or DCP_LOAD_CACHED (plain
+    loads and stores, for partials that are still cache-resident)."""
+    _check(_lib.dcp_workspace_set_load_policy(ws.handle, policy))
 
 
 def dcp_lse_combine(ws: Workspace, attn, lse, lse_layout: int, lse_mode: int, out, out_lse=None, stream=None):

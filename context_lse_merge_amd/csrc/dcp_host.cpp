@@ -134,6 +134,7 @@ int plan_merge(const dcp_workspace* ws, const void* attn, int64_t B, int H, int6
     MergeArgs a{};
     a.attn = attn;
     a.in_dtype = ws->dtype;
+    a.cached = ws->load_policy == DCP_LOAD_CACHED ? 1 : 0;
     a.lse = lse;
     a.out = static_cast<uint16_t*>(out);
     a.out_lse = out_lse;
@@ -373,6 +374,7 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
         m.h_local = static_cast<int32_t>(H);
         m.cp = nsplit;
         m.dtype = dtype;
+        m.cached = 1;                  // the partials were written just before
         m.rows = 0;                    // set per token chunk at launch
         m.to_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 1.4426950408889634f;
         m.from_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;
@@ -450,6 +452,7 @@ int dcp_workspace_create(int64_t capacity_tokens, int h_local, int cp, int d, in
     w->cp = cp;
     w->d = d;
     w->dtype = dtype;
+    w->load_policy = DCP_LOAD_STREAMING;
     w->stream = hip_stream;
     w->magic = dcp::kWorkspaceMagic;
     *ws = w;
@@ -462,6 +465,17 @@ int dcp_workspace_destroy(dcp_workspace* ws) {
         return dcp::fail(DCP_ERR_WORKSPACE, "dcp_workspace_destroy: not a workspace (or destroyed twice)");
     ws->magic = 0;
     delete ws;
+    return dcp::ok();
+}
+
+int dcp_workspace_set_load_policy(dcp_workspace* ws, int policy) {
+    if (!ws || ws->magic != dcp::kWorkspaceMagic)
+        return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_workspace_set_load_policy: not a workspace");
+    if (policy != DCP_LOAD_STREAMING && policy != DCP_LOAD_CACHED)
+        return dcp::fail(DCP_ERR_INVALID_ARG,
+                         "dcp_workspace_set_load_policy: policy %d is neither DCP_LOAD_STREAMING nor DCP_LOAD_CACHED",
+                         policy);
+    ws->load_policy = policy;
     return dcp::ok();
 }
 

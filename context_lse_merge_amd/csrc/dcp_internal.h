@@ -32,6 +32,7 @@ struct MergeArgs {
     int32_t cp;
     int32_t in_dtype;   // attn: DCP_DTYPE_BF16, DCP_DTYPE_FP16 or kPayloadF32 (internal)
     int32_t dtype;      // out: DCP_DTYPE_BF16 or DCP_DTYPE_FP16
+    int32_t cached;     // 1: plain loads and stores; 0: non-temporal
     // (lse_s - M) * to_log2 is the exponent of 2 of the weight; log2(S) * from_log2
     // is added to M for the merged LSE.  Base 2: both 1.  Base e: log2 e and ln 2.
     float to_log2;
@@ -68,6 +69,7 @@ struct dcp_workspace {
     int cp;
     int d;
     int dtype;
+    int load_policy;  // DCP_LOAD_STREAMING or DCP_LOAD_CACHED
     void* stream;
     uint64_t magic;
 };

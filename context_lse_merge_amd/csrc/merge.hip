@@ -137,11 +137,19 @@ struct F16 {
 // branch, so the loads stay ahead of their use -- and the all-zero word is +0
 // in every payload type, so an empty shard adds exactly +0 whatever it held
 // (NaN included).
-template <typename T>
+// One 16-byte load, non-temporal (NT) or plain.
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+    if (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+
+template <typename T, bool NT>
 struct Payload16 {
+    static constexpr bool kNT = NT;
     typedef u32x4 row_t;
     static __device__ __forceinline__ row_t load(const void* base, int64_t off) {
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off));
+        return load16<NT>(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off));
     }
     static __device__ __forceinline__ row_t zero_unless(bool use, row_t v) {
         row_t z;
@@ -158,15 +166,17 @@ struct Payload16 {
     }
 };
 
+template <bool NT>
 struct PayloadF32 {
+    static constexpr bool kNT = NT;
     struct row_t {
         u32x4 a, b;
     };
     static __device__ __forceinline__ row_t load(const void* base, int64_t off) {
         const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + off);
         row_t r;
-        r.a = __builtin_nontemporal_load(p);
-        r.b = __builtin_nontemporal_load(p + 1);
+        r.a = load16<NT>(p);
+        r.b = load16<NT>(p + 1);
         return r;
     }
     static __device__ __forceinline__ row_t zero_unless(bool use, row_t v) {
@@ -237,14 +247,18 @@ __device__ __forceinline__ float merged_lse(const MergeArgs& a, float M, float S
     return M + __builtin_amdgcn_logf(S) * a.from_log2;
 }
 
-template <typename T>
+template <typename T, bool NT>
 __device__ __forceinline__ void store_row(const MergeArgs& a, Row r, int lane, const float (&acc)[8], float L) {
     u32x4 packed;
     packed[0] = T::pack(acc[0], acc[1]);
     packed[1] = T::pack(acc[2], acc[3]);
     packed[2] = T::pack(acc[4], acc[5]);
     packed[3] = T::pack(acc[6], acc[7]);
-    __builtin_nontemporal_store(packed, reinterpret_cast<u32x4*>(a.out + r.b * a.o_sb + r.j * a.o_sj + lane * 8));
+    u32x4* dst = reinterpret_cast<u32x4*>(a.out + r.b * a.o_sb + r.j * a.o_sj + lane * 8);
+    if (NT)
+        __builtin_nontemporal_store(packed, dst);
+    else
+        *dst = packed;
     if (a.out_lse && lane == 0) a.out_lse[r.b * a.ol_sb + r.j] = L;
 }
 
@@ -302,7 +316,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
 #pragma unroll
         for (int s = 0; s < CP; ++s) fma8<In>(acc, w[s], v[s]);
     }
-    store_row<Out>(a, r, lane, acc, merged_lse(a, M, S));
+    store_row<Out, In::kNT>(a, r, lane, acc, merged_lse(a, M, S));
 }
 
 // 16 < cp <= 64: the same row algorithm with the shards taken G at a time.
@@ -338,7 +352,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
             fma8<In>(acc, ws, v[i]);
         }
     }
-    store_row<Out>(a, r, lane, acc, merged_lse(a, M, S));
+    store_row<Out, In::kNT>(a, r, lane, acc, merged_lse(a, M, S));
 }
 
 template <int CP, typename In, typename Out>
@@ -369,20 +383,28 @@ void launch_typed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
     }
 }
 
-hipError_t launch(const MergeArgs& a, hipStream_t stream) {
-    const int tokens = a.rows / a.h_local;
-    const dim3 grid((a.h_local + kWavesPerBlock - 1) / kWavesPerBlock, tokens);
+template <bool NT>
+void launch_policy(const MergeArgs& a, dim3 grid, hipStream_t stream) {
     const bool f16_out = a.dtype == DCP_DTYPE_FP16;
     if (a.in_dtype == kPayloadF32) {
         if (f16_out)
-            launch_typed<PayloadF32, F16>(a, grid, stream);
+            launch_typed<PayloadF32<NT>, F16>(a, grid, stream);
         else
-            launch_typed<PayloadF32, Bf16>(a, grid, stream);
+            launch_typed<PayloadF32<NT>, Bf16>(a, grid, stream);
     } else if (f16_out) {
-        launch_typed<Payload16<F16>, F16>(a, grid, stream);
+        launch_typed<Payload16<F16, NT>, F16>(a, grid, stream);
     } else {
-        launch_typed<Payload16<Bf16>, Bf16>(a, grid, stream);
+        launch_typed<Payload16<Bf16, NT>, Bf16>(a, grid, stream);
     }
+}
+
+hipError_t launch(const MergeArgs& a, hipStream_t stream) {
+    const int tokens = a.rows / a.h_local;
+    const dim3 grid((a.h_local + kWavesPerBlock - 1) / kWavesPerBlock, tokens);
+    if (a.cached)
+        launch_policy<false>(a, grid, stream);
+    else
+        launch_policy<true>(a, grid, stream);
     return hipGetLastError();
 }
 

@@ -68,6 +68,11 @@ extern "C" {
 #define DCP_QK_DIM 576   /* query/key columns of the MLA decode: 512 latent + 64 rope */
 #define DCP_MAX_CP 64
 
+/* How dcp_lse_combine reads its partials and writes its output
+ * (dcp_workspace_set_load_policy). */
+#define DCP_LOAD_STREAMING 0 /* non-temporal: partials read from HBM once (default) */
+#define DCP_LOAD_CACHED 1    /* plain loads/stores: partials just written and still cache-resident */
+
 /* Which cache rows a DCP shard owns (dcp_mla_partial_decode_varlen). */
 #define DCP_KV_CONTIGUOUS 0  /* shard s: rows [floor(s*L/cp), floor((s+1)*L/cp)) of a length-L cache */
 #define DCP_KV_INTERLEAVED 1 /* shard s: rows t < L with t mod cp == s                              */
@@ -101,6 +106,18 @@ int dcp_workspace_create(int64_t capacity_tokens, int h_local, int cp, int d, in
 
 /* Release a workspace (host memory only).  NULL is accepted. */
 int dcp_workspace_destroy(dcp_workspace* ws);
+
+/*
+ * Cache policy of every later dcp_lse_combine call on ws.  DCP_LOAD_STREAMING
+ * (the default) reads the partials and writes the output with non-temporal
+ * accesses, which do not displace cached data: fastest when the partials come
+ * from HBM.  DCP_LOAD_CACHED uses plain accesses: fastest when the partials
+ * were written just before (the exchange's receive buffers, or a producer in
+ * the same stream) and still sit in the L2 / Infinity Cache.  Results are
+ * bit-identical under both policies.  Returns DCP_ERR_INVALID_ARG for an
+ * unknown policy or handle.
+ */
+int dcp_workspace_set_load_policy(dcp_workspace* ws, int policy);
 
 /*
  * LSE-weighted merge of cp shard partials, read in place.

@@ -54,6 +54,14 @@ def test_workspace_errors_through_the_binding():
     assert e.value.status == dcp.DCP_ERR_LAYOUT
     ws = dcp.dcp_workspace_create(8, 16, 4, stream=0x1000)
     assert ws.handle
+    dcp.dcp_workspace_set_load_policy(ws, dcp.DCP_LOAD_CACHED)
+    dcp.dcp_workspace_set_load_policy(ws, dcp.DCP_LOAD_STREAMING)
+    with pytest.raises(dcp.DcpError) as e:
+        dcp.dcp_workspace_set_load_policy(ws, 7)
+    assert e.value.status == dcp.DCP_ERR_INVALID_ARG and "policy" in str(e.value)
+    with pytest.raises(dcp.DcpError) as e:
+        dcp.dcp_workspace_create(8, 16, 4, dtype=5, stream=0x1000)
+    assert e.value.status == dcp.DCP_ERR_LAYOUT
     dcp.dcp_workspace_destroy(ws)
     assert ws.handle is None
 

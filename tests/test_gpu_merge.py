@@ -297,6 +297,33 @@ def test_one_workspace_reused_across_batch_sizes():
         ws.close()
 
 
+@pytest.mark.parametrize("which", ["kimi", "dsv2", "stress", "kimi_f16"])
+def test_cached_load_policy_gives_identical_bits(which):
+    """DCP_LOAD_CACHED (plain loads and stores) against the default streaming
+    policy on the same inputs: identical bits, including NaN-filled empty shards."""
+    import context_lse_merge_amd as dcp
+    c = {"kimi": lambda: synth.kimi_merge(96), "dsv2": lambda: synth.dsv2_merge(40),
+         "stress": lambda: synth.stress_merge(300), "kimi_f16": lambda: synth.kimi_merge(96, dtype=torch.float16)}[which]()
+    dtype = dcp.DCP_DTYPE_FP16 if c.attn.dtype == torch.float16 else dcp.DCP_DTYPE_BF16
+    attn, lse = c.attn.to(DEV), c.lse.to(DEV)
+    layout = dcp.DCP_LSE_BHC if c.lse_layout == "bhc" else dcp.DCP_LSE_BH1
+    mode = dcp.DCP_LSE_BASE_E if c.lse_mode == "e" else dcp.DCP_LSE_BASE_2
+    results = []
+    for policy in (dcp.DCP_LOAD_STREAMING, dcp.DCP_LOAD_CACHED):
+        ws = dcp.dcp_workspace_create(c.capacity or c.B, c.h_local, c.cp, dtype=dtype)
+        dcp.dcp_workspace_set_load_policy(ws, policy)
+        out = torch.empty((c.B, c.h_local, synth.D), dtype=c.attn.dtype, device=DEV)
+        L = torch.empty((c.B, c.h_local), dtype=torch.float32, device=DEV)
+        announce("load policy %d on %s" % (policy, c.name))
+        dcp.dcp_lse_combine(ws, attn, lse, layout, mode, out, L)
+        torch.cuda.synchronize()
+        ws.close()
+        results.append((out, L))
+    check_against_oracle(c, results[1][0], results[1][1])
+    assert torch.equal(results[0][0].view(torch.int16), results[1][0].view(torch.int16))
+    assert torch.equal(results[0][1].view(torch.int32), results[1][1].view(torch.int32))
+
+
 # ------------------------------------------------------------ streams and graphs
 
 def test_call_on_another_stream_is_rejected_before_launch():
