@@ -251,3 +251,45 @@ def test_mixed_element_types_are_rejected():
     announce("producer with bf16 q and fp16 o_part (rejected in the binding)")
     with pytest.raises(ValueError):
         dcp.dcp_mla_partial_decode(q.to(DEV), kv.to(DEV), 2, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, None)
+
+
+def test_graph_replays_with_changing_queries_match_eager():
+    """The split path (decode kernel + merge over splits) captured in one HIP
+    graph and replayed with new query contents, interleaved with eager calls:
+    every replay equals the eager call on the same inputs, bit for bit."""
+    B, hq, T, cp = 2, 128, 4096, 4
+    _, kv = synth.mla_decode(B, T=T, hq=hq, seed=4040)
+    kv_dev = kv.to(DEV)
+    q_dev = torch.empty((B, hq, 576), dtype=torch.bfloat16, device=DEV)
+    o = torch.empty((B, cp * hq, 512), dtype=torch.bfloat16, device=DEV)
+    l = torch.empty((B, cp * hq), dtype=torch.float32, device=DEV)
+    nbytes = dcp.dcp_mla_partial_decode_scratch_size(B, hq, T, cp)
+    assert nbytes > 0
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream()
+    q_dev.copy_(synth.normal_bf16((B, hq, 576), synth.gen(4100)).to(DEV))
+    torch.cuda.synchronize()
+    announce("producer graph capture B=%d hq=%d T=%d cp=%d" % (B, hq, T, cp))
+    with torch.cuda.stream(s):
+        dcp.dcp_mla_partial_decode(q_dev, kv_dev, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, scratch, stream=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dcp.dcp_mla_partial_decode(q_dev, kv_dev, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, scratch, stream=s)
+    torch.cuda.synchronize()
+    o_e = torch.empty_like(o)
+    l_e = torch.empty_like(l)
+    for k in range(3):
+        q_dev.copy_(synth.normal_bf16((B, hq, 576), synth.gen(4200 + k)).to(DEV))
+        torch.cuda.synchronize()
+        announce("producer graph replay %d" % k)
+        g.replay()
+        torch.cuda.synchronize()
+        o_g, l_g = o.clone(), l.clone()
+        dcp.dcp_mla_partial_decode(q_dev, kv_dev, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o_e, l_e, scratch)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g.view(torch.int16), o_e.view(torch.int16))
+        assert torch.equal(l_g.view(torch.int32), l_e.view(torch.int32))
+    q = q_dev.cpu()
+    rows = np.arange(0, B * hq, 17)
+    check_partials(q, kv, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o_e, l_e, rows=rows)
