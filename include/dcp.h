@@ -184,9 +184,11 @@ int dcp_lse_combine(dcp_workspace* ws, const void* attn, int64_t B, int H, int64
  * scratch   device buffer of at least dcp_mla_partial_decode_scratch_size()
  *           bytes, 16-byte aligned, for the split-KV partials: when a shard's
  *           keys are split over several workgroups, each split's normalised
- *           output (in dtype) and LSE land here and are merged into o_part /
- *           lse_part by the dcp_lse_combine kernel.  NULL allowed when the
- *           size is 0 (one split per shard).  Contents on entry are ignored.
+ *           output (fp32, so the split reduction adds no 16-bit rounding)
+ *           and LSE land here and are merged into o_part / lse_part by the
+ *           merge kernel of dcp_lse_combine, reading fp32 payloads.  NULL
+ *           allowed when the size is 0 (one split per shard).  Contents on
+ *           entry are ignored.
  * Arithmetic: MFMA products of the 16-bit inputs with fp32 accumulation for
  * q.k and p.v, fp32 online softmax; p is rounded to dtype before the p.v
  * product.
