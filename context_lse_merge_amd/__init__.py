@@ -246,7 +246,7 @@ def dcp_mla_partial_decode(q, kv, cp: int, softmax_scale: float, lse_mode: int, 
 
 
 def dcp_mla_partial_decode_varlen_scratch_size(B: int, hq: int, max_seq_len: int, cp: int) -> int:
-    """Bytes of scratch dcp_mla_partial_decode_varlen needs for this shape (0: none)."""
+    """Bytes of scratch dcp_mla_partial_decode_varlen needs for this shape (0 only when B == 0)."""
     n = _sz()
     _check(_lib.dcp_mla_partial_decode_varlen_scratch_size(B, hq, max_seq_len, cp, ctypes.byref(n)))
     return n.value

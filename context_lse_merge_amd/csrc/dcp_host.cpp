@@ -19,6 +19,7 @@
 // Input checks: the later text of PR #40539 drops the copy of strided or
 // misaligned partials and lets the kernel check its inputs; here an input the
 // kernel cannot read directly is rejected with an error, never copied.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -216,13 +217,13 @@ MergeArgs chunk_args(const MergePlan& plan, int64_t k) {
 // nsplit ranges processed by separate workgroups; each leaves a normalised
 // fp32 partial and its LSE, and the merge kernel reduces the splits exactly
 // as it merges DCP shards.  The split count aims at about kMlaTargetBlocks
-// workgroups and never gives a split fewer than kMlaMinSplitKeys keys.
+// workgroups and never gives a split fewer than kMlaMinSplitKeys keys.  Every
+// token has the same T keys here, so the host decides; with per-token
+// lengths the planning kernel does (varlen_layout sizes its scratch).
 
-void mla_split(int64_t B, int hq, int64_t T, int cp, bool varlen, int32_t* nsplit, int64_t* split_len,
-               size_t* scratch_bytes) {
+void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* split_len, size_t* scratch_bytes) {
     const int64_t rows = B * hq;
-    const int64_t row_blocks = varlen ? B * ((hq + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock)
-                                      : (rows + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
+    const int64_t row_blocks = (rows + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
     const int64_t shard_max = (T + cp - 1) / cp;  // longest shard
     int64_t n = 1;
     if (row_blocks > 0 && shard_max > 0) {
@@ -245,6 +246,24 @@ void mla_split(int64_t B, int hq, int64_t T, int cp, bool varlen, int32_t* nspli
         const int64_t parts = static_cast<int64_t>(cp) * n * rows;  // (token, split, shard, head)
         *scratch_bytes = static_cast<size_t>(parts * kMlaVDim * 4 + parts * 4);
     }
+}
+
+VarlenLayout varlen_layout(int64_t B, int hq, int64_t T, int cp) {
+    VarlenLayout l{};
+    const int64_t rbt = (hq + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
+    l.pairs = B * rbt * cp;
+    l.items = l.pairs + kMlaTargetBlocks;
+    // A pair splits only when it has more than kMlaMinSplitTiles tiles.
+    const int64_t shard_tiles = ((T + cp - 1) / cp + kMlaKeysPerTile - 1) / kMlaKeysPerTile;
+    const int64_t max_n = (shard_tiles + kMlaMinSplitTiles - 1) / kMlaMinSplitTiles;
+    l.slots = max_n > 1 ? std::min<int64_t>(2 * kMlaTargetBlocks, l.pairs * max_n) : 0;
+    const size_t rows = static_cast<size_t>(l.slots) * kMlaRowsPerBlock;
+    l.off_lse = rows * kMlaVDim * sizeof(float);
+    l.off_hdr = (l.off_lse + rows * sizeof(float) + 63) / 64 * 64;
+    l.off_items = l.off_hdr + 64;
+    l.off_split = l.off_items + static_cast<size_t>(l.items) * sizeof(VarlenItem);
+    l.bytes = l.off_split + static_cast<size_t>(kMlaTargetBlocks) * sizeof(VarlenSplit);
+    return l;
 }
 
 int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv, int64_t T, int64_t kv_st,
@@ -299,10 +318,19 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
         return fail(DCP_ERR_LAYOUT, "%s: kv_st = %lld is too large (at most %lld elements)", fn, (long long)kv_st,
                     (long long)(((int64_t{1} << 31) - kMlaQkDim) / kMlaKeysPerTile / row_step));
 
-    int32_t nsplit;
-    int64_t split_len;
+    int32_t nsplit = 1;
+    int64_t split_len = 0;
     size_t need;
-    mla_split(B, hq, T, cp, vl != nullptr, &nsplit, &split_len, &need);
+    VarlenLayout vlay{};
+    if (vl) {
+        vlay = varlen_layout(B, hq, T, cp);
+        if (vlay.items >= (int64_t{1} << 31))
+            return fail(DCP_ERR_INVALID_ARG, "%s: %lld work items exceed one launch (fewer tokens per call)", fn,
+                        (long long)vlay.items);
+        need = vlay.bytes;
+    } else {
+        mla_split(B, hq, T, cp, &nsplit, &split_len, &need);
+    }
     if (need > 0 && (!scratch || scratch_bytes < need))
         return fail(DCP_ERR_WORKSPACE, "%s: needs %zu bytes of scratch (%s_scratch_size), got %zu", fn, need, fn,
                     scratch ? scratch_bytes : size_t{0});
@@ -341,6 +369,13 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
         a.interleaved = vl->kv_layout == DCP_KV_INTERLEAVED ? 1 : 0;
         a.rb_per_token = (hq + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
         a.row_blocks = static_cast<int32_t>(B * a.rb_per_token);
+        char* base = static_cast<char*>(scratch);
+        a.part_o = reinterpret_cast<float*>(base);
+        a.part_lse = reinterpret_cast<float*>(base + vlay.off_lse);
+        a.vl_hdr = reinterpret_cast<VarlenHeader*>(base + vlay.off_hdr);
+        a.vl_items = reinterpret_cast<VarlenItem*>(base + vlay.off_items);
+        a.vl_splits = reinterpret_cast<VarlenSplit*>(base + vlay.off_split);
+        a.slots = vlay.slots;
     }
     a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
     a.lse_scale = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;
@@ -350,7 +385,7 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     a.o_sb = o_sb;
     a.o_sh = o_sh;
     a.lse_sb = lse_sb;
-    if (nsplit > 1) {
+    if (!vl && nsplit > 1) {
         // Per-split fp32 partials in the scratch buffer, then the merge over splits.
         const int64_t heads = static_cast<int64_t>(nsplit) * H;   // per token
         a.part_o = static_cast<float*>(scratch);
@@ -382,7 +417,8 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     }
     plan->args = a;
     plan->scratch_bytes = need;
-    plan->blocks = static_cast<int64_t>(a.row_blocks) * cp * nsplit;
+    plan->blocks = vl ? vlay.items : static_cast<int64_t>(a.row_blocks) * cp * nsplit;
+    plan->varlen = vl != nullptr;
     if (plan->blocks >= (int64_t{1} << 31))
         return fail(DCP_ERR_INVALID_ARG, "%s: %lld workgroups exceed one launch (fewer tokens per call)", fn,
                     (long long)plan->blocks);
@@ -404,7 +440,7 @@ int dcp_mla_partial_decode_scratch_size(int64_t B, int hq, int64_t kv_tokens, in
         return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_mla_partial_decode_scratch_size: B * hq exceeds 2^30");
     int32_t n;
     int64_t len;
-    dcp::mla_split(B, hq, kv_tokens, cp, false, &n, &len, bytes);
+    dcp::mla_split(B, hq, kv_tokens, cp, &n, &len, bytes);
     return dcp::ok();
 }
 
@@ -417,9 +453,7 @@ int dcp_mla_partial_decode_varlen_scratch_size(int64_t B, int hq, int64_t max_se
                          DCP_MAX_CP);
     if (B * static_cast<int64_t>(hq) > (int64_t{1} << 30))
         return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_mla_partial_decode_varlen_scratch_size: B * hq exceeds 2^30");
-    int32_t n;
-    int64_t len;
-    dcp::mla_split(B, hq, max_seq_len, cp, true, &n, &len, bytes);
+    *bytes = B == 0 ? 0 : dcp::varlen_layout(B, hq, max_seq_len, cp).bytes;
     return dcp::ok();
 }
 

@@ -117,6 +117,71 @@ constexpr int kMlaMaxSplits = DCP_MAX_CP;  // ... nor above what the merge kerne
 // part_o [B][nsplit*cp*hq][512] fp32 then part_lse [B][nsplit*cp*hq] fp32,
 // which the merge kernel then reduces over p (an LSE merge with nsplit
 // shards and cp*hq local heads, fp32 input) into o / lse.
+// ------------------------------------------- variable-length work plan
+// With per-token lengths the split length cannot be fixed on the host: a
+// one-workgroup planning kernel reads seq_lens, picks a split length (in key
+// tiles) so that the whole batch makes about kMlaTargetBlocks splits, never
+// fewer than kMlaMinSplitTiles tiles long, and writes the work list -- one
+// item per split of every pair (token, row block, shard), longest first --
+// into the scratch buffer.  Workgroup i of the decode kernel runs item i.  A
+// pair with one split writes its output directly; a pair with n > 1 splits
+// writes n fp32 partials to consecutive slots (kMlaRowsPerBlock rows of 512
+// each), which a reduction kernel merges.  Pair index
+// q = (b * rb_per_token + row block) * cp + s.
+constexpr int kMlaMinSplitTiles = kMlaMinSplitKeys / kMlaKeysPerTile;
+constexpr int kMlaPlanThreads = 1024;  // the planning workgroup; also its number of size bins
+
+struct VarlenHeader {
+    int32_t n_items;      // items in the list; workgroups past it exit
+    int32_t n_split;      // pairs with more than one split
+    int64_t split_tiles;  // key tiles per split
+};
+struct VarlenItem {
+    int32_t pair, p;      // split p of pair q
+    int32_t slot;         // partial slot, or -1: the pair has one split
+    int32_t pad;
+};
+struct VarlenSplit {
+    int32_t pair, first, n, pad;  // the pair's partials are slots first .. first + n - 1
+};
+
+// The plan's arithmetic, shared by the kernels and the host-side checks.
+#if defined(__HIP__)
+#define DCP_HD __host__ __device__
+#else
+#define DCP_HD
+#endif
+
+// Key tiles of shard s of a token with L rows (contiguous slices
+// [floor(s L / cp), floor((s+1) L / cp)) or every cp-th row from row s).
+DCP_HD inline int64_t varlen_shard_tiles(int64_t L, int s, int cp, bool interleaved) {
+    const int64_t n = interleaved ? (L > s ? (L - s + cp - 1) / cp : 0)
+                                  : ((s + 1) * L) / cp - (s * L) / cp;
+    return (n + kMlaKeysPerTile - 1) / kMlaKeysPerTile;
+}
+// Tiles per split for a batch of `total` tiles.
+DCP_HD inline int64_t varlen_split_tiles(int64_t total) {
+    const int64_t st = (total + kMlaTargetBlocks - 1) / kMlaTargetBlocks;
+    return st < kMlaMinSplitTiles ? kMlaMinSplitTiles : st;
+}
+// Splits of a pair of t tiles (an empty pair still has one, to write 0 / -inf).
+DCP_HD inline int64_t varlen_splits(int64_t t, int64_t st) { return t > st ? (t + st - 1) / st : 1; }
+// Size bin of a split of `size` <= st tiles: 0 (empty) .. kMlaPlanThreads - 1 (full).
+DCP_HD inline int varlen_bin(int64_t size, int64_t st) {
+    return static_cast<int>((size * (kMlaPlanThreads - 1)) / st);
+}
+
+// Scratch layout of the variable-length producer: part_o [slots][128][512]
+// fp32, part_lse [slots][128] fp32, the header, the items, the split list.
+// With st >= total / target tiles per split the list holds at most
+// pairs + target items, fewer than target split pairs and fewer than
+// 2 * target partial slots (each split pair has more than st tiles).
+struct VarlenLayout {
+    int64_t pairs, items, slots;
+    size_t off_lse, off_hdr, off_items, off_split, bytes;
+};
+VarlenLayout varlen_layout(int64_t B, int hq, int64_t T, int cp);
+
 struct MlaArgs {
     const uint16_t* q;      // row r at q + b*q_sb + h*q_sh, 576 columns
     const uint16_t* kv;     // token t at kv + t*kv_st, 576 columns
@@ -143,20 +208,30 @@ struct MlaArgs {
     int32_t dtype;          // DCP_DTYPE_BF16 or DCP_DTYPE_FP16 (q, kv, o)
     float scale_log2;       // softmax_scale * log2 e
     float lse_scale;        // lse = log2-domain LSE * lse_scale (1 for base 2, ln 2 for base e)
+    // Variable length: the work list (part_o / part_lse are then the slots).
+    VarlenHeader* vl_hdr;
+    VarlenItem* vl_items;
+    VarlenSplit* vl_splits;
+    int64_t slots;          // partial slots in the scratch (0: no pair may split)
 };
 
 struct MlaPlan {
     MlaArgs args;
     size_t scratch_bytes;   // needed scratch (0 when nsplit == 1)
     int64_t blocks;         // workgroups of the main kernel (0: nothing to do)
+    bool varlen;            // planning kernel, decode over the work list, split reduction
     MergeArgs reduce;       // nsplit > 1: the merge over splits (all B tokens; launched in token chunks)
     int64_t B;
 };
 
-// Split decision and scratch size; pure arithmetic on the shape.  With
-// varlen the workgroups of one token cover only its heads.
-void mla_split(int64_t B, int hq, int64_t T, int cp, bool varlen, int32_t* nsplit, int64_t* split_len,
-               size_t* scratch_bytes);
+// The variable-length producer's planning kernel and split reduction,
+// enqueued on `stream` (a hipStream_t); return the HIP error of the launch.
+int varlen_plan_launch(const MlaArgs& a, void* stream);
+int varlen_reduce_launch(const MlaArgs& a, void* stream);
+
+// Split decision and scratch size of the fixed-length producer; pure
+// arithmetic on the shape.
+void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* split_len, size_t* scratch_bytes);
 
 // The variable-length arguments of dcp_mla_partial_decode_varlen.
 struct MlaVarlen {

@@ -169,6 +169,7 @@ __device__ __forceinline__ uint32_t to_bits(float x) {
 // key range -- are given to blocks of the same XCD.
 struct Work {
     int rb, s, p;
+    int slot;  // variable length: partial slot, or -1 to write o_part directly
 };
 
 __device__ __forceinline__ Work work_of(const MlaArgs& a) {
@@ -180,6 +181,7 @@ __device__ __forceinline__ Work work_of(const MlaArgs& a) {
     const int kc = w / a.row_blocks;
     k.s = kc / a.nsplit;
     k.p = kc - k.s * a.nsplit;
+    k.slot = -1;
     return k;
 }
 
@@ -378,20 +380,36 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15;  // query row of this lane within the wavefront
     const int g = lane >> 4;    // lane group: keys 4g..4g+3 of each 16-key half
-    const Work wk = work_of(a);
-
     // The token(s) and cache of this workgroup.  One shared cache of T rows,
-    // and row blocks of 128 consecutive (token, head) rows; or, with
-    // seq_lens, token b's own cache of min(max(seq_lens[b], 0), T) rows and
-    // row blocks that never span tokens.
+    // row blocks of 128 consecutive (token, head) rows and splits of
+    // a.split_len keys; or, with seq_lens, item blockIdx.x of the planning
+    // kernel's work list: token b's own cache of min(max(seq_lens[b], 0), T)
+    // rows, row blocks that never span tokens, and the plan's split length.
+    Work wk;
     int64_t L = a.T;
+    int64_t split_len = a.split_len;
     const uint16_t* cache = a.kv;
     int b_tok = 0, h_base = 0;
     if (a.seq_lens) {
-        b_tok = wk.rb / a.rb_per_token;
-        h_base = (wk.rb - b_tok * a.rb_per_token) * kMlaRowsPerBlock;
+        // The item is read before the count is checked: entries past the
+        // count are inside the list's capacity (the grid), merely unused.
+        const VarlenItem it = a.vl_items[blockIdx.x];
+        const int n_items = a.vl_hdr->n_items;
+        split_len = a.vl_hdr->split_tiles * kKeys;
+        if (static_cast<int>(blockIdx.x) >= n_items) return;
+        const int per_token = a.rb_per_token * a.cp;
+        b_tok = it.pair / per_token;
+        const int rem = it.pair - b_tok * per_token;
+        const int rbi = rem / a.cp;
+        wk.rb = b_tok * a.rb_per_token + rbi;
+        wk.s = rem - rbi * a.cp;
+        wk.p = it.p;
+        wk.slot = it.slot;
+        h_base = rbi * kMlaRowsPerBlock;
         L = min(max(static_cast<int64_t>(a.seq_lens[b_tok]), int64_t{0}), a.T);
         cache = a.kv + b_tok * a.kv_sb;
+    } else {
+        wk = work_of(a);
     }
     // Shard s: n_s logical keys, key j at cache row start + j * step.
     int64_t start, n_s;
@@ -407,8 +425,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     }
     const KeyRows kr{cache + start * a.kv_st, static_cast<int32_t>(step * a.kv_st)};
     // Logical key range of this split.
-    const int64_t k0 = static_cast<int64_t>(wk.p) * a.split_len;
-    const int64_t k1 = min(k0 + a.split_len, n_s);
+    const int64_t k0 = static_cast<int64_t>(wk.p) * split_len;
+    const int64_t k1 = min(k0 + split_len, n_s);
     const int ntiles = k0 < k1 ? static_cast<int>((k1 - k0 + kKeys - 1) / kKeys) : 0;
     if (ntiles > 0) dma_tile(kr, tile0, k0, k1, wave, lane);
 
@@ -495,11 +513,12 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
 
     // O / l and the LSE in the caller's base; an empty shard or split gives 0
     // and -inf.  One split: the element type, straight into o_part / lse_part.
-    // Several: fp32 into the scratch as head p*cp*hq + s*hq + h, for the merge
-    // kernel to reduce over the splits.
+    // Several: fp32 into the scratch -- as head p*cp*hq + s*hq + h, for the
+    // merge kernel to reduce over the splits, or with seq_lens as row
+    // wave*16 + r16 of the item's slot, for the split reduction.
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * a.lse_scale : -INFINITY;
-    if (a.nsplit == 1) {
+    if (a.seq_lens ? wk.slot < 0 : a.nsplit == 1) {
         const int64_t u = static_cast<int64_t>(wk.s) * a.hq + h;
         uint16_t* orow = a.o + b * a.o_sb + u * a.o_sh + ocol;
 #pragma unroll
@@ -511,12 +530,16 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
         }
         if (g == 0) a.lse[b * a.lse_sb + u] = lse;
     } else {
-        const int64_t u = (static_cast<int64_t>(wk.p) * a.cp + wk.s) * a.hq + h;
-        float* prow = a.part_o + (b * a.part_sb + u) * kDv + ocol;
+        int64_t prow_idx;  // fp32 row of the scratch
+        if (a.seq_lens)
+            prow_idx = static_cast<int64_t>(wk.slot) * kMlaRowsPerBlock + wave * kRowsPerWave + r16;
+        else
+            prow_idx = b * a.part_sb + (static_cast<int64_t>(wk.p) * a.cp + wk.s) * a.hq + h;
+        float* prow = a.part_o + prow_idx * kDv + ocol;
 #pragma unroll
         for (int t = 0; t < kDTiles; ++t)
             *reinterpret_cast<f32x4*>(prow + 64 * (t >> 2) + 8 * (t & 3)) = st.oacc[t] * inv;
-        if (g == 0) a.part_lse[b * a.part_sb + u] = lse;
+        if (g == 0) a.part_lse[prow_idx] = lse;
     }
 }
 
@@ -532,12 +555,19 @@ int run_mla(const MlaPlan& plan, void* hip_stream, const char* fn) {
     if (plan.blocks == 0) return ok();
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const dim3 grid(static_cast<unsigned>(plan.blocks));
+    if (plan.varlen) {
+        const hipError_t e = static_cast<hipError_t>(varlen_plan_launch(plan.args, stream));
+        if (e != hipSuccess) return fail(DCP_ERR_HIP, "%s: launch of the planning kernel failed: %s", fn,
+                                         hipGetErrorString(e));
+    }
     if (plan.args.dtype == DCP_DTYPE_FP16)
         mla_decode_kernel<F16><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
     else
         mla_decode_kernel<Bf16><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && plan.args.nsplit > 1) {
+    if (e == hipSuccess && plan.varlen) {
+        if (plan.args.slots > 0) e = static_cast<hipError_t>(varlen_reduce_launch(plan.args, stream));
+    } else if (e == hipSuccess && plan.args.nsplit > 1) {
         // The splits of every (token, shard, head) are merged like DCP shards.
         const int64_t H = plan.reduce.h_local;
         int64_t chunk = (int64_t{1} << 30) / H;

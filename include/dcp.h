@@ -226,10 +226,19 @@ int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64
  *           kv_sb = 0 lets every token share one cache.  Rows t >=
  *           max_seq_len are never read.
  * seq_lens  device int32 [B]; values outside [0, max_seq_len] are clamped.
- * max_seq_len  host bound on seq_lens, used to size the key splits.
+ * max_seq_len  host bound on seq_lens, used to size the scratch.
+ * scratch   device buffer of at least
+ *           dcp_mla_partial_decode_varlen_scratch_size() bytes (never 0 when
+ *           B > 0), 16-byte aligned.  The key splits are sized on the device
+ *           from the actual lengths: a planning kernel writes a work list
+ *           (longest split first) into the scratch, and splits of a (token,
+ *           shard) leave fp32 partials there that a reduction kernel merges
+ *           into o_part / lse_part.  Contents on entry are ignored.
  * Other arguments, strides, alignment (kv_sb a multiple of 8 elements too),
  * arithmetic and errors as dcp_mla_partial_decode.  A workgroup serves the
  * heads of one token, so hq below 128 leaves part of each workgroup idle.
+ * How the keys are split depends on the lengths of the whole batch, so a
+ * token's results can differ in the last bits between batches.
  */
 int dcp_mla_partial_decode_varlen_scratch_size(int64_t B, int hq, int64_t max_seq_len, int cp, size_t* bytes);
 

@@ -7,6 +7,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <random>
+#include <vector>
 
 #include "dcp_internal.h"
 
@@ -20,6 +22,100 @@ static int g_failures = 0;
     } while (0)
 
 static void* fake(uintptr_t a) { return reinterpret_cast<void*>(a); }
+
+// The variable-length work plan, run sequentially with the planning kernel's
+// arithmetic, against the capacities varlen_layout gives the scratch: the
+// list fits, the slots fit, every pair's tiles are covered once by splits of
+// at most st tiles, and the list runs longest split first.
+static void check_varlen_plan(const std::vector<int64_t>& lens, int hq, int64_t T, int cp, bool il) {
+    const int64_t B = static_cast<int64_t>(lens.size());
+    const dcp::VarlenLayout lay = dcp::varlen_layout(B, hq, T, cp);
+    const int rbt = (hq + dcp::kMlaRowsPerBlock - 1) / dcp::kMlaRowsPerBlock;
+    int64_t total = 0;
+    for (int64_t L : lens)
+        for (int s = 0; s < cp; ++s) total += rbt * dcp::varlen_shard_tiles(L < 0 ? 0 : (L > T ? T : L), s, cp, il);
+    const int64_t st = dcp::varlen_split_tiles(total);
+    CHECK(st >= dcp::kMlaMinSplitTiles && st * dcp::kMlaTargetBlocks >= total);
+    int64_t items = 0, slots = 0, split_pairs = 0, covered = 0;
+    std::vector<int64_t> bins(dcp::kMlaPlanThreads, 0);
+    for (int64_t L : lens) {
+        const int64_t Lc = L < 0 ? 0 : (L > T ? T : L);
+        int64_t keys = 0;
+        for (int s = 0; s < cp; ++s) {
+            const int64_t t = dcp::varlen_shard_tiles(Lc, s, cp, il);
+            keys += t;
+            const int64_t n = dcp::varlen_splits(t, st);
+            CHECK(n >= 1 && (n - 1) * st < t + (t == 0) && n * st >= t);
+            for (int64_t p = 0; p < n; ++p) {
+                const int64_t size = (p + 1) * st < t ? st : t - p * st;
+                CHECK(size >= 0 && size <= st && (size > 0 || t == 0));
+                ++bins[dcp::varlen_bin(size, st)];
+                covered += size;
+            }
+            items += rbt * n;
+            if (n > 1) {
+                slots += rbt * n;
+                split_pairs += rbt;
+            }
+        }
+        // Every key of the token is in exactly one shard.
+        CHECK(keys * dcp::kMlaKeysPerTile >= Lc && (keys - cp) * dcp::kMlaKeysPerTile < Lc + 1);
+    }
+    CHECK(covered * rbt == total);
+    CHECK(items <= lay.items);
+    CHECK(slots <= lay.slots);
+    CHECK(split_pairs < dcp::kMlaTargetBlocks || split_pairs == 0);
+    CHECK(bins[dcp::kMlaPlanThreads - 1] == 0 || dcp::varlen_bin(st, st) == dcp::kMlaPlanThreads - 1);
+    CHECK(lay.pairs == B * rbt * cp && lay.items == lay.pairs + dcp::kMlaTargetBlocks);
+    CHECK(lay.off_hdr % 64 == 0 && lay.off_items % 16 == 0 && lay.off_split % 16 == 0);
+    CHECK(lay.bytes == lay.off_split + dcp::kMlaTargetBlocks * sizeof(dcp::VarlenSplit));
+}
+
+static void varlen_plan_checks() {
+    std::mt19937_64 rng(20261202);
+    const int64_t T = 131072;
+    for (int trial = 0; trial < 200; ++trial) {
+        const int64_t B = 1 + static_cast<int64_t>(rng() % 300);
+        const int cp = 1 + static_cast<int>(rng() % 8);
+        const int hq = (trial % 3 == 0) ? 200 : 128;
+        std::vector<int64_t> lens(B);
+        for (auto& L : lens) {
+            switch (trial % 4) {
+                case 0: L = 1 + static_cast<int64_t>(rng() % T); break;             // uniform
+                case 1: L = T; break;                                               // all full
+                case 2: L = (rng() % 10 == 0) ? T : static_cast<int64_t>(rng() % 4096);  // skewed
+                default: L = static_cast<int64_t>(rng() % 600) - 100;               // short, some clamped
+            }
+        }
+        check_varlen_plan(lens, hq, T, cp, trial % 2 == 0);
+    }
+    check_varlen_plan({T}, 128, T, 4, true);           // one long token: many splits per pair
+    check_varlen_plan({0, 0, 0}, 16, T, 4, false);     // nothing to attend to
+    check_varlen_plan({5}, 16, 0, 1, false);           // max_seq_len 0
+    CHECK(dcp::varlen_layout(4, 16, 100, 4).slots == 0);  // no pair can exceed 8 tiles
+
+    // Scratch size query and the plan's pointers into the scratch.
+    size_t bytes = 0;
+    CHECK(dcp_mla_partial_decode_varlen_scratch_size(64, 128, T, 4, &bytes) == DCP_OK);
+    CHECK(bytes == dcp::varlen_layout(64, 128, T, 4).bytes);
+    CHECK(dcp_mla_partial_decode_varlen_scratch_size(0, 128, T, 4, &bytes) == DCP_OK && bytes == 0);
+    const uintptr_t q = uintptr_t{1} << 40, kv = uintptr_t{2} << 40, o = uintptr_t{3} << 40,
+                    l = uintptr_t{4} << 40, seq = uintptr_t{5} << 40, scr = uintptr_t{6} << 40;
+    const dcp::VarlenLayout lay = dcp::varlen_layout(64, 128, T, 4);
+    const dcp::MlaVarlen vl{reinterpret_cast<const int32_t*>(seq), 0, DCP_KV_INTERLEAVED};
+    dcp::MlaPlan plan;
+    CHECK(dcp::plan_mla(fake(q), 64, 128, 128 * 576, 576, fake(kv), T, 576, &vl, DCP_DTYPE_BF16, 4, 0.07f,
+                        DCP_LSE_BASE_E, fake(o), 512 * 512, 512, reinterpret_cast<float*>(l), 512, fake(scr),
+                        lay.bytes, &plan) == DCP_OK);
+    CHECK(plan.varlen && plan.blocks == lay.items && plan.args.slots == lay.slots);
+    CHECK(reinterpret_cast<uintptr_t>(plan.args.part_lse) == scr + lay.off_lse);
+    CHECK(reinterpret_cast<uintptr_t>(plan.args.vl_hdr) == scr + lay.off_hdr);
+    CHECK(reinterpret_cast<uintptr_t>(plan.args.vl_items) == scr + lay.off_items);
+    CHECK(reinterpret_cast<uintptr_t>(plan.args.vl_splits) == scr + lay.off_split);
+    CHECK(dcp::plan_mla(fake(q), 64, 128, 128 * 576, 576, fake(kv), T, 576, &vl, DCP_DTYPE_BF16, 4, 0.07f,
+                        DCP_LSE_BASE_E, fake(o), 512 * 512, 512, reinterpret_cast<float*>(l), 512, fake(scr),
+                        lay.bytes - 1, &plan) == DCP_ERR_WORKSPACE);
+}
 
 int main() {
     void* stream = fake(0x5000);
@@ -141,6 +237,8 @@ int main() {
     CHECK(dcp_workspace_destroy(ws6) == DCP_OK);
     CHECK(dcp_workspace_destroy(nullptr) == DCP_OK);
     CHECK(std::strcmp(dcp_status_string(DCP_ERR_ALIGN), "DCP_ERR_ALIGN") == 0);
+
+    varlen_plan_checks();
 
     if (g_failures) {
         std::fprintf(stderr, "%d check(s) failed\n", g_failures);

@@ -109,7 +109,7 @@ def test_short_and_empty_lengths(layout, mode):
 @pytest.mark.parametrize("layout", ["contiguous", "interleaved"])
 def test_split_path_long_lengths(layout):
     """Long caches with 128 heads: several key splits per shard, merged by the
-    fp32-input merge kernel; lengths that are not multiples of the tile."""
+    split reduction; lengths that are not multiples of the tile."""
     q, kv = _caches(701, 2, 128, 16384)
     seq = [16384, 9001]
     o, l = run_varlen(q, kv, seq, 16384, LAYOUTS[layout], 4, dcp.DCP_LSE_BASE_E)
@@ -141,8 +141,11 @@ def test_fp16_varlen():
 
 
 def test_shared_cache_full_length_matches_fixed_length_bitwise():
-    """Every token sharing one cache at its full length, contiguous ownership:
-    the same tiles in the same order as dcp_mla_partial_decode, so the same bits."""
+    """Every token sharing one cache at its full length, contiguous ownership.
+    At this shape the planning kernel picks the fixed-length path's split
+    length (256 keys: 4 splits per shard), so every split runs the same tiles
+    in the same order, and the split reduction forms the weights exactly as
+    the merge kernel does: the same bits."""
     q, kv = synth.mla_decode(2, T=4096, hq=128, seed=705)
     kv_dev = kv.to(DEV)
     o_v, l_v = run_varlen(q, kv, [4096, 4096], 4096, dcp.DCP_KV_CONTIGUOUS, 4, dcp.DCP_LSE_BASE_E, kv_dev=kv_dev)
@@ -184,3 +187,115 @@ def test_argument_errors():
     with pytest.raises(ValueError):
         dcp.dcp_mla_partial_decode_varlen(q.to(DEV), kv.to(DEV), seq, 65, dcp.DCP_KV_CONTIGUOUS, 4,
                                           synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, None)
+
+
+# The split length is chosen on the device from the batch's actual lengths
+# (about 256 splits over the whole batch, none under 256 keys), so the cases
+# below aim at its regimes: a batch dominated by a few long tokens, a single
+# long token split many times per shard, row blocks of a token with more
+# than 128 heads, the scratch reused by calls with other lengths, and the
+# plan rebuilt on every replay of a captured graph.
+
+
+def test_skewed_lengths_few_long_tokens():
+    """Per-token caches, 3 long tokens among 29 short ones: the long pairs are
+    split, the short ones run unsplit, all in one list."""
+    B, T = 32, 6144
+    q, kv = _caches(707, B, 128, T)
+    rng = np.random.default_rng(707)
+    seq = rng.integers(0, 300, B).astype(np.int32)
+    seq[[3, 17, 30]] = [T, 5000, 4097]
+    o, l = run_varlen(q, kv, seq, T, dcp.DCP_KV_CONTIGUOUS, 4, dcp.DCP_LSE_BASE_E)
+    rows = np.unique(np.concatenate([np.arange(3 * 128, 4 * 128, 9), np.arange(17 * 128, 18 * 128, 13),
+                                     [30 * 128, 30 * 128 + 127, 0, 1, 5 * 128 + 64, B * 128 - 1]]))
+    check(q, kv, seq, dcp.DCP_KV_CONTIGUOUS, 4, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
+
+
+def test_one_long_token_many_splits_per_shard():
+    """B = 1 over the full 131072-row cache: 4096 tiles, 16-tile splits, so
+    64 partials per (shard, head) for the reduction."""
+    _, kv = synth.mla_decode(1)
+    q = synth.normal_bf16((1, 128, 576), synth.gen(708))
+    o, l = run_varlen(q, kv, [131072], 131072, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_2)
+    check(q, kv, [131072], dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_2, o, l, rows=[0, 1, 63, 64, 126, 127])
+
+
+def test_more_than_128_heads_with_splits():
+    """hq = 200: two row blocks per token, the second with 72 live rows, and
+    pairs split several times."""
+    q, kv = _caches(709, 3, 200, 9000)
+    seq = [9000, 5, 7001]
+    o, l = run_varlen(q, kv, seq, 9000, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_E)
+    rows = np.unique(np.concatenate([[0, 127, 128, 199, 200, 327, 328, 399, 400, 527, 528, 599],
+                                     np.arange(0, 600, 37)]))
+    check(q, kv, seq, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
+
+
+def test_scratch_reused_with_other_lengths_and_repeatable():
+    """One scratch buffer, a long-token call, then a call whose plan is
+    smaller: the second is right whatever the first left behind, and running
+    it again gives the same bits (the list order may differ; the arithmetic
+    of each split does not)."""
+    B, T = 6, 4096
+    q, kv = _caches(710, B, 128, T)
+    qd, kvd = q.to(DEV), kv.to(DEV)
+    nbytes = dcp.dcp_mla_partial_decode_varlen_scratch_size(B, 128, T, 4)
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    outs = []
+    for k, seq in enumerate([[4096] * B, [4096, 0, 77, 1000, 2049, 3], [4096, 0, 77, 1000, 2049, 3]]):
+        o = torch.empty((B, 4 * 128, 512), dtype=torch.bfloat16, device=DEV)
+        l = torch.empty((B, 4 * 128), dtype=torch.float32, device=DEV)
+        announce("varlen scratch reuse call %d seq=%s" % (k, seq))
+        dcp.dcp_mla_partial_decode_varlen(qd, kvd, torch.tensor(seq, dtype=torch.int32, device=DEV), T,
+                                          dcp.DCP_KV_CONTIGUOUS, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l,
+                                          scratch)
+        torch.cuda.synchronize()
+        outs.append((o, l))
+    (o1, l1), (o2, l2) = outs[1], outs[2]
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    rows = np.unique(np.concatenate([np.arange(0, B * 128, 23), [128, 255, 5 * 128 + 127]]))
+    check(q, kv, [4096, 0, 77, 1000, 2049, 3], dcp.DCP_KV_CONTIGUOUS, 4, dcp.DCP_LSE_BASE_E, o1, l1, rows=rows)
+
+
+def test_graph_replays_with_changing_lengths_match_eager():
+    """The planning kernel, the decode over its list and the split reduction
+    captured in one HIP graph; each replay with new seq_lens (and so a new
+    plan) equals the eager call on the same inputs, bit for bit."""
+    B, T = 4, 4096
+    q, kv = _caches(711, B, 128, T)
+    qd, kvd = q.to(DEV), kv.to(DEV)
+    seq_dev = torch.tensor([4096, 10, 2000, 0], dtype=torch.int32, device=DEV)
+    o = torch.empty((B, 4 * 128, 512), dtype=torch.bfloat16, device=DEV)
+    l = torch.empty((B, 4 * 128), dtype=torch.float32, device=DEV)
+    nbytes = dcp.dcp_mla_partial_decode_varlen_scratch_size(B, 128, T, 4)
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream()
+
+    def call(o_, l_, stream=None):
+        dcp.dcp_mla_partial_decode_varlen(qd, kvd, seq_dev, T, dcp.DCP_KV_INTERLEAVED, 4, synth.MLA_SCALE,
+                                          dcp.DCP_LSE_BASE_E, o_, l_, scratch, stream=stream)
+    announce("varlen graph capture B=%d T=%d" % (B, T))
+    with torch.cuda.stream(s):
+        call(o, l, stream=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(o, l, stream=s)
+    torch.cuda.synchronize()
+    o_e, l_e = torch.empty_like(o), torch.empty_like(l)
+    for k, seq in enumerate([[4096, 4096, 4096, 4096], [1, 0, 3000, 4095], [0, 0, 0, 0]]):
+        seq_dev.copy_(torch.tensor(seq, dtype=torch.int32))
+        torch.cuda.synchronize()
+        announce("varlen graph replay %d seq=%s" % (k, seq))
+        g.replay()
+        torch.cuda.synchronize()
+        o_g, l_g = o.clone(), l.clone()
+        call(o_e, l_e)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g.view(torch.int16), o_e.view(torch.int16))
+        assert torch.equal(l_g.view(torch.int32), l_e.view(torch.int32))
+        if k == 1:
+            rows = np.unique(np.concatenate([np.arange(0, B * 128, 29), [B * 128 - 1]]))
+            check(q, kv, seq, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_E, o_e, l_e, rows=rows)
+    assert torch.all(torch.isneginf(l_e)) and torch.all(o_e == 0)
