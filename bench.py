@@ -272,14 +272,15 @@ def measure_producer(B, kv_copies, reps=10, seq_lens=None):
     decode workload: q [B,128,576], one 131072 x 576 cache, 4 shards.  The cache
     is rotated over `kv_copies` device copies (>= 1 GiB together) so every call
     reads it from HBM.  With `seq_lens` (int32 [B] on the GPU) the
-    variable-length entry point runs instead: every token over the shared cache
-    (kv_sb = 0) up to its own length, interleaved ownership.  q, the cache and
-    the outputs take the cache's dtype.  Returns (producer us, merge us)."""
+    variable-length entry point runs instead: every token up to its own length,
+    interleaved ownership, over the shared cache (kv_sb = 0) or, when the
+    copies are [B, T, 576], over its own cache.  q, the cache and the outputs
+    take the cache's dtype.  Returns (producer us, merge us)."""
     import torch
     import context_lse_merge_amd as dcp
     import synth
     dev = torch.device("cuda:0")
-    hq, cp, T = 128, 4, kv_copies[0].shape[0]
+    hq, cp, T = 128, 4, kv_copies[0].shape[-2]
     dtype = kv_copies[0].dtype
     q = synth.normal_16((B, hq, 576), synth.gen(3000 + B), dtype).to(dev)
     o = torch.empty((B, cp * hq, 512), dtype=dtype, device=dev)
@@ -346,6 +347,21 @@ def producer_leg(Bs):
                  "producer_us": round(us, 1), "merge_us": round(us_m, 3), "TFLOPs": round(tflops, 1),
                  "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "flop": fl})
     print("[bench] producer varlen B=64 (interleaved, random lengths): %.1f us (%.1f TFLOP/s, %.1f%% of bf16 peak)"
+          % (us, tflops, 100 * tflops / MFMA_BF16_PEAK_TFLOPS), file=sys.stderr, flush=True)
+    # the same lengths over one cache per token (64 x 131072 rows, 9.7 GB: every row from HBM)
+    own = torch.empty((64,) + tuple(kv.shape), dtype=torch.bfloat16, device="cuda:0")
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(6400)
+    for b in range(64):
+        own[b].normal_(0.0, 0.5, generator=gen)
+    us, us_m = measure_producer(64, [own], seq_lens=seq_dev)
+    del own
+    tflops = fl / (us * 1e-6) / 1e12
+    rows.append({"B": 64, "variant": "variable length: the same lengths, one cache per token (kv_sb = 131072 rows), "
+                                     "interleaved ownership",
+                 "producer_us": round(us, 1), "merge_us": round(us_m, 3), "TFLOPs": round(tflops, 1),
+                 "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "flop": fl})
+    print("[bench] producer varlen B=64, per-token caches: %.1f us (%.1f TFLOP/s, %.1f%% of bf16 peak)"
           % (us, tflops, 100 * tflops / MFMA_BF16_PEAK_TFLOPS), file=sys.stderr, flush=True)
     del copies
     copies = [kv_dev.to(torch.float16)]
