@@ -24,6 +24,11 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
     "--offload-arch=" + ARCH,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Kernel-argument preloading: the leading scalar arguments of a kernel
+    # (up to 16 dwords) arrive in SGPRs when the wavefront starts.  The merge
+    # kernels lead with what their first loads need; kernels whose first
+    # argument is a struct are unaffected.
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
 

@@ -182,6 +182,12 @@ int plan_merge(const dcp_workspace* ws, const void* attn, int64_t B, int H, int6
             return fail(DCP_ERR_INVALID_ARG, "dcp_lse_combine: out_lse overlaps attn, lse or out");
     }
 
+    if (!merge_strides_fit(a))
+        return fail(DCP_ERR_LAYOUT,
+                    "dcp_lse_combine: attn and lse strides must be below 2^31 elements (attn_sb = %lld, attn_sh = %lld, "
+                    "lse strides %lld, %lld, %lld)",
+                    (long long)attn_sb, (long long)attn_sh, (long long)l0, (long long)l1, (long long)l2);
+
     plan->args = a;
     plan->B = B;
     // Tokens are the second grid dimension, which holds at most kMaxLaunchTokens
@@ -413,6 +419,9 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
         m.rows = 0;                    // set per token chunk at launch
         m.to_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 1.4426950408889634f;
         m.from_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;
+        if (!merge_strides_fit(m))
+            return fail(DCP_ERR_INVALID_ARG, "%s: %lld split partials per token are too many (fewer heads per call)",
+                        fn, (long long)heads);
         plan->reduce = m;
     }
     plan->args = a;

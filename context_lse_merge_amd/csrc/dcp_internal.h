@@ -92,6 +92,17 @@ int plan_merge(const dcp_workspace* ws, const void* attn, int64_t B, int H, int6
 // Arguments of chunk k of a plan (token range [k*chunk, min((k+1)*chunk, B))).
 MergeArgs chunk_args(const MergePlan& plan, int64_t k);
 
+// The merge kernels take the payload and LSE strides as 32-bit values (so
+// that they fit the SGPRs the hardware preloads): true when every one of
+// them is below 2^31 in magnitude.
+inline bool merge_strides_fit(const MergeArgs& a) {
+    const int64_t lim = int64_t{1} << 31;
+    const int64_t v[6] = {a.a_sb, a.a_sj, a.a_ss, a.l_sb, a.l_sj, a.l_ss};
+    for (int64_t x : v)
+        if (x >= lim || x <= -lim) return false;
+    return true;
+}
+
 // Enqueue one merge launch of already validated arguments (rows = tokens *
 // h_local with at most kMaxLaunchTokens tokens) on `stream` (a hipStream_t).
 // Returns the HIP error code of the launch (0 = success).

@@ -217,12 +217,32 @@ struct Row {
     int b, j;
 };
 
-__device__ __forceinline__ Row row_of(const MergeArgs& a) {
+__device__ __forceinline__ Row row_of(int h_local) {
     Row r;
     r.b = blockIdx.y;
     const int j = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-    r.j = j < a.h_local ? j : a.h_local - 1;
+    r.j = j < h_local ? j : h_local - 1;
     return r;
+}
+
+// Kernel arguments.  What the first loads need leads the parameter list as
+// scalars -- the payload and LSE pointers, their 32-bit element strides and
+// h_local -- so that the hardware preloads them into SGPRs before the
+// wavefront starts (gfx950 kernel-argument preloading, switched on by the
+// build): the addresses are formed and the loads issued without first
+// waiting on a scalar load of the argument block, one memory latency less per
+// launch.  The rest is needed only once the loads are in flight and comes in
+// one struct, read with ordinary scalar loads meanwhile.
+struct MergeTail {
+    uint16_t* out;
+    float* out_lse;
+    int64_t o_sb, o_sj, ol_sb;
+    float to_log2, from_log2;
+    int32_t cp;
+};
+
+MergeTail tail_of(const MergeArgs& a) {
+    return MergeTail{a.out, a.out_lse, a.o_sb, a.o_sj, a.ol_sb, a.to_log2, a.from_log2, a.cp};
 }
 
 // Weights of one row from the LSE held by lane s (lanes >= cp hold -inf).
@@ -234,32 +254,32 @@ __device__ __forceinline__ Row row_of(const MergeArgs& a) {
 // exponents below -126 flush the weight to 0, i.e. a shard whose weight is
 // under 2^-126 of the largest is skipped.
 template <int MaxCp>
-__device__ __forceinline__ float row_weights(const MergeArgs& a, float x, int cp, float& M, float& S) {
+__device__ __forceinline__ float row_weights(float to_log2, float x, int cp, float& M, float& S) {
     M = wave_max<MaxCp>(x, cp);
-    const float w = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x - M) * a.to_log2);
+    const float w = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x - M) * to_log2);
     S = wave_sum<MaxCp>(w, cp);
     const float inv = (S > 0.0f) ? __builtin_amdgcn_rcpf(S) : 0.0f;
     return w * inv;
 }
 
-__device__ __forceinline__ float merged_lse(const MergeArgs& a, float M, float S) {
+__device__ __forceinline__ float merged_lse(const MergeTail& t, float M, float S) {
     // S = 0 (all shards empty) gives log2(0) = -inf and M = -inf: L = -inf.
-    return M + __builtin_amdgcn_logf(S) * a.from_log2;
+    return M + __builtin_amdgcn_logf(S) * t.from_log2;
 }
 
 template <typename T, bool NT>
-__device__ __forceinline__ void store_row(const MergeArgs& a, Row r, int lane, const float (&acc)[8], float L) {
+__device__ __forceinline__ void store_row(const MergeTail& t, Row r, int lane, const float (&acc)[8], float L) {
     u32x4 packed;
     packed[0] = T::pack(acc[0], acc[1]);
     packed[1] = T::pack(acc[2], acc[3]);
     packed[2] = T::pack(acc[4], acc[5]);
     packed[3] = T::pack(acc[6], acc[7]);
-    u32x4* dst = reinterpret_cast<u32x4*>(a.out + r.b * a.o_sb + r.j * a.o_sj + lane * 8);
+    u32x4* dst = reinterpret_cast<u32x4*>(t.out + r.b * t.o_sb + r.j * t.o_sj + lane * 8);
     if (NT)
         __builtin_nontemporal_store(packed, dst);
     else
         *dst = packed;
-    if (a.out_lse && lane == 0) a.out_lse[r.b * a.ol_sb + r.j] = L;
+    if (t.out_lse && lane == 0) t.out_lse[r.b * t.ol_sb + r.j] = L;
 }
 
 // cp = CP <= 16 shards, known at compile time; In is the payload reader,
@@ -270,22 +290,25 @@ __device__ __forceinline__ void store_row(const MergeArgs& a, Row r, int lane, c
 // Rows whose every weight is nonzero (the common case) take the plain FMA
 // path; a row with an empty shard zeroes that shard's payload first.
 template <int CP, typename In, typename Out>
-__global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(kBlock) void merge_kernel(const void* attn, const float* lse, int32_t a_sb, int32_t a_sj,
+                                                       int32_t a_ss, int32_t l_sb, int32_t l_sj, int32_t l_ss,
+                                                       int32_t h_local, MergeTail t) {
     const int lane = threadIdx.x & 63;
-    const Row r = row_of(a);
+    const Row r = row_of(h_local);
 
-    const int64_t orow = r.b * a.a_sb + r.j * a.a_sj + lane * 8;  // elements of the payload
-    const float* lrow = a.lse + r.b * a.l_sb + r.j * a.l_sj;
+    // elements of the payload
+    const int64_t orow = static_cast<int64_t>(r.b) * a_sb + static_cast<int64_t>(r.j) * a_sj + lane * 8;
+    const float* lrow = lse + static_cast<int64_t>(r.b) * l_sb + static_cast<int64_t>(r.j) * l_sj;
     // Every kernel argument the addresses need is read above this point, in
     // one batch of scalar loads, rather than a second batch after the
     // payload loads are issued.
     __builtin_amdgcn_sched_barrier(0);
     float x[CP];
 #pragma unroll
-    for (int s = 0; s < CP; ++s) x[s] = lrow[s * a.l_ss];
+    for (int s = 0; s < CP; ++s) x[s] = lrow[static_cast<int64_t>(s) * l_ss];
     typename In::row_t v[CP];
 #pragma unroll
-    for (int s = 0; s < CP; ++s) v[s] = In::load(a.attn, orow + s * a.a_ss);
+    for (int s = 0; s < CP; ++s) v[s] = In::load(attn, orow + static_cast<int64_t>(s) * a_ss);
     // Keep every load above this point: nothing that waits on them may be
     // scheduled before the last one is issued.
     __builtin_amdgcn_sched_barrier(0);
@@ -297,7 +320,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
     float S = 0.0f;
 #pragma unroll
     for (int s = 0; s < CP; ++s) {
-        w[s] = (x[s] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x[s] - M) * a.to_log2);
+        w[s] = (x[s] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x[s] - M) * t.to_log2);
         S += w[s];
     }
     const float inv = (S > 0.0f) ? __builtin_amdgcn_rcpf(S) : 0.0f;
@@ -316,35 +339,39 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(MergeArgs a) {
 #pragma unroll
         for (int s = 0; s < CP; ++s) fma8<In>(acc, w[s], v[s]);
     }
-    store_row<Out, In::kNT>(a, r, lane, acc, merged_lse(a, M, S));
+    store_row<Out, In::kNT>(t, r, lane, acc, merged_lse(t, M, S));
 }
 
 // 16 < cp <= 64: the same row algorithm with the shards taken G at a time.
 // Loads past the last shard re-read shard cp-1 (an address already being
 // fetched) and get weight 0.
 template <int G, typename In, typename Out>
-__global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
+__global__ __launch_bounds__(kBlock) void merge_kernel_wide(const void* attn, const float* lse, int32_t a_sb,
+                                                            int32_t a_sj, int32_t a_ss, int32_t l_sb, int32_t l_sj,
+                                                            int32_t l_ss, int32_t h_local, MergeTail t) {
     const int lane = threadIdx.x & 63;
-    const Row r = row_of(a);
-    const int cp = a.cp;
+    const Row r = row_of(h_local);
+    const int cp = t.cp;
 
     const int ls = lane < cp ? lane : cp - 1;
-    const float xl = a.lse[r.b * a.l_sb + r.j * a.l_sj + ls * a.l_ss];
-    const int64_t orow = r.b * a.a_sb + r.j * a.a_sj + lane * 8;
+    const float xl = lse[static_cast<int64_t>(r.b) * l_sb + static_cast<int64_t>(r.j) * l_sj +
+                         static_cast<int64_t>(ls) * l_ss];
+    const int64_t orow = static_cast<int64_t>(r.b) * a_sb + static_cast<int64_t>(r.j) * a_sj + lane * 8;
     typename In::row_t v[G];
 #pragma unroll
-    for (int i = 0; i < G; ++i) v[i] = In::load(a.attn, orow + min(i, cp - 1) * a.a_ss);
+    for (int i = 0; i < G; ++i) v[i] = In::load(attn, orow + static_cast<int64_t>(min(i, cp - 1)) * a_ss);
     __builtin_amdgcn_sched_barrier(0);
 
     const float x = lane < cp ? xl : -INFINITY;
     float M, S;
-    const float wn = row_weights<64>(a, x, cp, M, S);
+    const float wn = row_weights<64>(t.to_log2, x, cp, M, S);
 
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < cp; s0 += G) {
         if (s0 > 0) {
 #pragma unroll
-            for (int i = 0; i < G; ++i) v[i] = In::load(a.attn, orow + min(s0 + i, cp - 1) * a.a_ss);
+            for (int i = 0; i < G; ++i)
+                v[i] = In::load(attn, orow + static_cast<int64_t>(min(s0 + i, cp - 1)) * a_ss);
         }
 #pragma unroll
         for (int i = 0; i < G; ++i) {
@@ -352,12 +379,24 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_wide(MergeArgs a) {
             fma8<In>(acc, ws, v[i]);
         }
     }
-    store_row<Out, In::kNT>(a, r, lane, acc, merged_lse(a, M, S));
+    store_row<Out, In::kNT>(t, r, lane, acc, merged_lse(t, M, S));
+}
+
+typedef void (*MergeKernel)(const void*, const float*, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
+                            MergeTail);
+
+// The strides go to the kernel as 32-bit values: the planners check them
+// with merge_strides_fit before anything is enqueued.
+void launch_merge(MergeKernel k, const MergeArgs& a, dim3 grid, hipStream_t stream) {
+    k<<<grid, dim3(kBlock), 0, stream>>>(a.attn, a.lse, static_cast<int32_t>(a.a_sb), static_cast<int32_t>(a.a_sj),
+                                         static_cast<int32_t>(a.a_ss), static_cast<int32_t>(a.l_sb),
+                                         static_cast<int32_t>(a.l_sj), static_cast<int32_t>(a.l_ss), a.h_local,
+                                         tail_of(a));
 }
 
 template <int CP, typename In, typename Out>
 void launch_fixed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
-    merge_kernel<CP, In, Out><<<grid, dim3(kBlock), 0, stream>>>(a);
+    launch_merge(merge_kernel<CP, In, Out>, a, grid, stream);
 }
 
 template <typename In, typename Out>
@@ -379,7 +418,7 @@ void launch_typed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
         case 14: launch_fixed<14, In, Out>(a, grid, stream); break;
         case 15: launch_fixed<15, In, Out>(a, grid, stream); break;
         case 16: launch_fixed<16, In, Out>(a, grid, stream); break;
-        default: merge_kernel_wide<16, In, Out><<<grid, dim3(kBlock), 0, stream>>>(a); break;
+        default: launch_merge(merge_kernel_wide<16, In, Out>, a, grid, stream); break;
     }
 }
 

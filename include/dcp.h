@@ -145,7 +145,10 @@ int dcp_workspace_set_load_policy(dcp_workspace* ws, int policy);
  * consecutive token ranges, in order, on hip_stream (PR #40539, Modifications).
  *
  * Alignment: attn and out 16-byte aligned; attn_sb, attn_sh, out_sb, out_sh
- * multiples of 8 elements; lse and out_lse 4-byte aligned.
+ * multiples of 8 elements; lse and out_lse 4-byte aligned.  The strides of
+ * attn and lse (attn_sb, attn_sh, l0, l1, l2, and h_local times the shard
+ * stride) must be below 2^31 elements (DCP_ERR_LAYOUT otherwise): the kernel
+ * takes them as 32-bit values.
  */
 int dcp_lse_combine(dcp_workspace* ws, const void* attn, int64_t B, int H, int64_t attn_sb, int64_t attn_sh,
                     const float* lse, int lse_layout, int64_t l0, int64_t l1, int64_t l2, int lse_mode, void* out,

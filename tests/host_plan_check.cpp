@@ -220,6 +220,13 @@ int main() {
           DCP_ERR_INVALID_ARG);  // out inside attn
     CHECK(call(ws, fake(attn), 4, 64, sb, sh, lse, 0, 64, 4, 1, 0, fake(out), 16 * D, D, lse + 16, 16, stream) ==
           DCP_ERR_INVALID_ARG);  // out_lse inside lse
+    // Strides the kernel cannot take as 32-bit values are rejected.
+    CHECK(call(ws, fake(attn), 2, 64, int64_t{1} << 31, sh, lse, 0, 64, 4, 1, 0, fake(uintptr_t{1} << 45), 16 * D, D,
+               0, 0, stream) == DCP_ERR_LAYOUT);
+    CHECK(call(ws, fake(attn), 2, 64, (int64_t{1} << 31) - 8, sh, lse, 0, 64, 4, 1, 0, fake(uintptr_t{1} << 45),
+               16 * D, D, 0, 0, stream) == DCP_OK);
+    CHECK(call(ws, fake(attn), 2, 64, sb, sh, lse, 0, int64_t{1} << 31, 4, 1, 0, fake(uintptr_t{1} << 45), 16 * D,
+               D, 0, 0, stream) == DCP_ERR_LAYOUT);
     // A transposed but non-overlapping out ([h_local, B, D] storage) is fine.
     CHECK(call(ws, fake(attn), 4, 64, sb, sh, lse, 0, 64, 4, 1, 0, fake(out), D, 4 * D, 0, 0, stream) == DCP_OK);
 
