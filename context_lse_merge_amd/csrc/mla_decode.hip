@@ -25,14 +25,19 @@
 //    staging; each barrier waits only for the older tile.
 //  * LDS layout of a tile: 36 blocks of 1 KiB, block (h, b) holding the 16-byte
 //    chunks 4b..4b+3 of keys 16h..16h+15, chunk c of key k at slot
-//    16 (c % 4) + ((k % 16) ^ 4 (b % 2)).  Measured on gfx950, a 16-byte LDS
+//    16 (c % 4) + ((k % 16) ^ 8 (b % 2)).  Measured on gfx950, a 16-byte LDS
 //    read runs at the full 256 B/clk only when every 16-lane group of the
 //    wavefront reads one 256-byte row in the same lane order, and the
 //    transpose read only when each half-wavefront touches all 64 banks; in
 //    this layout the q.k operand read of a 32-column step is exactly one
-//    block read in one order, and the p.v operand pairs chunk c (XOR 0) with
-//    chunk c + 4 (XOR 4), which fall on complementary banks.  One direct copy
-//    fills one block.
+//    block read in one order (XOR-permuted alike in every group), and the
+//    p.v operand pairs chunk c (XOR 0) with chunk c + 4 (XOR 8): the eight
+//    keys a half-wavefront reads from the even block land on banks 0-31 and
+//    those from the odd block on banks 32-63 (or the reverse), so every
+//    transpose read is free of bank conflicts (counted: 0 conflict cycles;
+//    XOR 4 left the two 16-lane groups of a half-wavefront on the same 32
+//    banks, 1.28 conflict cycles per LDS instruction).  One direct copy fills
+//    one block.
 //  * The wavefront computes S^T = K Q^T (A = K, B = Q^T) and O^T += V^T P^T
 //    (A = V^T, B = P^T).  In this orientation a lane holds eight scores of
 //    query row lane % 16 and, with the k index of p.v permuted the same way in
@@ -195,7 +200,7 @@ __device__ __forceinline__ int opaque(int v) {
 
 // Copy the K tile of keys [t0, t0 + 32) into LDS tile `dst` with direct
 // loads: copy n = w + 8 i of wavefront w fills block n = 18 h + b, its lane l
-// slot l, i.e. chunk 4b + l / 16 of key 16 h + ((l % 16) ^ 4 (b % 2)).  In a
+// slot l, i.e. chunk 4b + l / 16 of key 16 h + ((l % 16) ^ 8 (b % 2)).  In a
 // ragged last tile, keys at or past k1 re-read key k1 - 1 (their scores are
 // masked).
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS
@@ -240,7 +245,7 @@ __device__ __forceinline__ void dma_tile(const KeyRows& kr, uint16_t* dst, int64
         const int n = min(copy, kDmaPerTile - 1);  // slack copies repeat the last block's source
         const int h = n >= kHalfBlocks ? 1 : 0;
         const int blk = n - h * kHalfBlocks;
-        const int key = 16 * h + ((lane & 15) ^ (4 * (blk & 1)));
+        const int key = 16 * h + ((lane & 15) ^ (8 * (blk & 1)));
         const int chunk = 4 * blk + (lane >> 4);
         const int o = min(key, last) * kr.rstride + 8 * chunk;
         lds_dma16(base + o, lds_addr(dst + kBlockElems * copy));
@@ -459,17 +464,17 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     }
 
     // Operand offsets.  q.k step f: key r16, chunk 4f + g, in block f at slot
-    // 16 g + (r16 ^ 4 (f % 2)).  p.v tile t = 4j + u: key k = 4g + r16/4 and
+    // 16 g + (r16 ^ 8 (f % 2)).  p.v tile t = 4j + u: key k = 4g + r16/4 and
     // quarter qq = r16 % 4 of the tile's 16 columns: chunk c = 8j + u (qq < 2)
-    // or c + 4 (qq >= 2), i.e. block 2j + qq/2 at slot 16u + (k ^ 4 (qq/2)),
+    // or c + 4 (qq >= 2), i.e. block 2j + qq/2 at slot 16u + (k ^ 8 (qq/2)),
     // plus 4 elements for the odd quarters.
     LaneOffsets off;
     {
         off.s_even = 8 * (16 * g + r16);
-        off.s_odd = 8 * (16 * g + (r16 ^ 4));
+        off.s_odd = 8 * (16 * g + (r16 ^ 8));
         const int key = 4 * g + (r16 >> 2);
         const int qh = (r16 & 3) >> 1;
-        const int tr0 = kBlockElems * qh + 8 * (key ^ (4 * qh)) + 4 * (r16 & 1);
+        const int tr0 = kBlockElems * qh + 8 * (key ^ (8 * qh)) + 4 * (r16 & 1);
 #pragma unroll
         for (int u = 0; u < 4; ++u) off.tr[u] = tr0 + 128 * u;
     }
