@@ -258,17 +258,17 @@ VarlenLayout varlen_layout(int64_t B, int hq, int64_t T, int cp) {
     VarlenLayout l{};
     const int64_t rbt = (hq + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
     l.pairs = B * rbt * cp;
-    l.items = l.pairs + kMlaTargetBlocks;
+    l.items = l.pairs + kVarlenTarget;
     // A pair splits only when it has more than kMlaMinSplitTiles tiles.
     const int64_t shard_tiles = ((T + cp - 1) / cp + kMlaKeysPerTile - 1) / kMlaKeysPerTile;
     const int64_t max_n = (shard_tiles + kMlaMinSplitTiles - 1) / kMlaMinSplitTiles;
-    l.slots = max_n > 1 ? std::min<int64_t>(2 * kMlaTargetBlocks, l.pairs * max_n) : 0;
+    l.slots = max_n > 1 ? std::min<int64_t>(2 * kVarlenTarget, l.pairs * max_n) : 0;
     const size_t rows = static_cast<size_t>(l.slots) * kMlaRowsPerBlock;
     l.off_lse = rows * kMlaVDim * sizeof(float);
     l.off_hdr = (l.off_lse + rows * sizeof(float) + 63) / 64 * 64;
     l.off_items = l.off_hdr + 64;
     l.off_split = l.off_items + static_cast<size_t>(l.items) * sizeof(VarlenItem);
-    l.bytes = l.off_split + static_cast<size_t>(kMlaTargetBlocks) * sizeof(VarlenSplit);
+    l.bytes = l.off_split + static_cast<size_t>(kVarlenTarget) * sizeof(VarlenSplit);
     return l;
 }
 

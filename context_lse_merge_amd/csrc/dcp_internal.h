@@ -131,7 +131,7 @@ constexpr int kMlaMaxSplits = DCP_MAX_CP;  // ... nor above what the merge kerne
 // ------------------------------------------- variable-length work plan
 // With per-token lengths the split length cannot be fixed on the host: a
 // one-workgroup planning kernel reads seq_lens, picks a split length (in key
-// tiles) so that the whole batch makes about kMlaTargetBlocks splits, never
+// tiles) so that the whole batch makes about kVarlenTarget splits, never
 // fewer than kMlaMinSplitTiles tiles long, and writes the work list -- one
 // item per split of every pair (token, row block, shard), longest first --
 // into the scratch buffer.  Workgroup i of the decode kernel runs item i.  A
@@ -139,7 +139,8 @@ constexpr int kMlaMaxSplits = DCP_MAX_CP;  // ... nor above what the merge kerne
 // writes n fp32 partials to consecutive slots (kMlaRowsPerBlock rows of 512
 // each), which a reduction kernel merges.  Pair index
 // q = (b * rb_per_token + row block) * cp + s.
-constexpr int kMlaMinSplitTiles = kMlaMinSplitKeys / kMlaKeysPerTile;
+constexpr int kVarlenTarget = 256;       // splits over the whole batch (about one per compute unit)
+constexpr int kMlaMinSplitTiles = kMlaMinSplitKeys / kMlaKeysPerTile;  // shortest split
 constexpr int kMlaPlanThreads = 1024;  // the planning workgroup; also its number of size bins
 
 struct VarlenHeader {
@@ -172,7 +173,7 @@ DCP_HD inline int64_t varlen_shard_tiles(int64_t L, int s, int cp, bool interlea
 }
 // Tiles per split for a batch of `total` tiles.
 DCP_HD inline int64_t varlen_split_tiles(int64_t total) {
-    const int64_t st = (total + kMlaTargetBlocks - 1) / kMlaTargetBlocks;
+    const int64_t st = (total + kVarlenTarget - 1) / kVarlenTarget;
     return st < kMlaMinSplitTiles ? kMlaMinSplitTiles : st;
 }
 // Splits of a pair of t tiles (an empty pair still has one, to write 0 / -inf).

@@ -145,7 +145,7 @@ __device__ __forceinline__ uint32_t pack2<_Float16>(float x, float y) {
            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(y))) << 16);
 }
 
-// Grid (kMlaRowsPerBlock / kReduceWaves, kMlaTargetBlocks): block (x, y)
+// Grid (kMlaRowsPerBlock / kReduceWaves, kVarlenTarget): block (x, y)
 // merges rows 4x .. 4x + 3 of split pair y, one row per wavefront; lane l
 // owns columns 8l .. 8l + 7.  Pairs past n_split exit.
 template <typename E>
@@ -223,7 +223,7 @@ int varlen_reduce_launch(const MlaArgs& a, void* stream) {
     const bool base2 = a.lse_scale == 1.0f;
     const float to_log2 = base2 ? 1.0f : 1.4426950408889634f;
     const float from_log2 = base2 ? 1.0f : 0.6931471805599453f;
-    const dim3 grid(kMlaRowsPerBlock / kReduceWaves, kMlaTargetBlocks);
+    const dim3 grid(kMlaRowsPerBlock / kReduceWaves, kVarlenTarget);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (a.dtype == DCP_DTYPE_FP16)
         varlen_reduce_kernel<_Float16><<<grid, dim3(64 * kReduceWaves), 0, s>>>(a, to_log2, from_log2);

@@ -35,7 +35,7 @@ static void check_varlen_plan(const std::vector<int64_t>& lens, int hq, int64_t 
     for (int64_t L : lens)
         for (int s = 0; s < cp; ++s) total += rbt * dcp::varlen_shard_tiles(L < 0 ? 0 : (L > T ? T : L), s, cp, il);
     const int64_t st = dcp::varlen_split_tiles(total);
-    CHECK(st >= dcp::kMlaMinSplitTiles && st * dcp::kMlaTargetBlocks >= total);
+    CHECK(st >= dcp::kMlaMinSplitTiles && st * dcp::kVarlenTarget >= total);
     int64_t items = 0, slots = 0, split_pairs = 0, covered = 0;
     std::vector<int64_t> bins(dcp::kMlaPlanThreads, 0);
     for (int64_t L : lens) {
@@ -64,11 +64,11 @@ static void check_varlen_plan(const std::vector<int64_t>& lens, int hq, int64_t 
     CHECK(covered * rbt == total);
     CHECK(items <= lay.items);
     CHECK(slots <= lay.slots);
-    CHECK(split_pairs < dcp::kMlaTargetBlocks || split_pairs == 0);
+    CHECK(split_pairs < dcp::kVarlenTarget || split_pairs == 0);
     CHECK(bins[dcp::kMlaPlanThreads - 1] == 0 || dcp::varlen_bin(st, st) == dcp::kMlaPlanThreads - 1);
-    CHECK(lay.pairs == B * rbt * cp && lay.items == lay.pairs + dcp::kMlaTargetBlocks);
+    CHECK(lay.pairs == B * rbt * cp && lay.items == lay.pairs + dcp::kVarlenTarget);
     CHECK(lay.off_hdr % 64 == 0 && lay.off_items % 16 == 0 && lay.off_split % 16 == 0);
-    CHECK(lay.bytes == lay.off_split + dcp::kMlaTargetBlocks * sizeof(dcp::VarlenSplit));
+    CHECK(lay.bytes == lay.off_split + dcp::kVarlenTarget * sizeof(dcp::VarlenSplit));
 }
 
 static void varlen_plan_checks() {
