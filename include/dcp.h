@@ -191,7 +191,9 @@ int dcp_lse_combine(dcp_workspace* ws, const void* attn, int64_t B, int H, int64
  *           and LSE land here and are merged into o_part / lse_part by the
  *           merge kernel of dcp_lse_combine, reading fp32 payloads.  NULL
  *           allowed when the size is 0 (one split per shard).  Contents on
- *           entry are ignored.
+ *           entry are ignored.  A scratch buffer serves one call at a time:
+ *           calls that may overlap (on other streams) need buffers of their
+ *           own.
  * Arithmetic: MFMA products of the 16-bit inputs with fp32 accumulation for
  * q.k and p.v, fp32 online softmax; p is rounded to dtype before the p.v
  * product.
@@ -236,7 +238,8 @@ int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64
  *           from the actual lengths: a planning kernel writes a work list
  *           (longest split first) into the scratch, and splits of a (token,
  *           shard) leave fp32 partials there that a reduction kernel merges
- *           into o_part / lse_part.  Contents on entry are ignored.
+ *           into o_part / lse_part.  Contents on entry are ignored; one
+ *           call at a time per buffer, as for dcp_mla_partial_decode.
  * Other arguments, strides, alignment (kv_sb a multiple of 8 elements too),
  * arithmetic and errors as dcp_mla_partial_decode.  A workgroup serves the
  * heads of one token, so hq below 128 leaves part of each workgroup idle.
