@@ -259,6 +259,34 @@ def test_without_merged_lse():
     check_against_oracle(c, out, None)
 
 
+def test_element_offsets_beyond_2_31():
+    """40000 tokens of 128 heads at cp 8 (a 5.2 GB input): token b starts at
+    element b * 65536, past 2^31 from token 32768 on.  The kernel takes the
+    strides as 32-bit values and forms every offset in 64 bits; sampled tokens
+    on both sides of 2^30 and 2^31, and the last one, against the oracle run
+    on just those tokens."""
+    import context_lse_merge_amd as dcp
+    B, H, cp = 40000, 128, 8
+    hl = H // cp
+    announce("merge with element offsets past 2^31: B=%d H=%d cp=%d (5.2 GB input)" % (B, H, cp))
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7777)
+    attn = torch.empty((B, H, synth.D), dtype=torch.bfloat16, device=DEV)
+    for t0 in range(0, B, 4000):
+        attn[t0:t0 + 4000] = torch.randn((4000, H, synth.D), generator=gen, device=DEV).to(torch.bfloat16)
+    lse = torch.randn((B, H, 1), generator=gen, device=DEV) * 2.0 + 10.0
+    out = torch.empty((B, hl, synth.D), dtype=torch.bfloat16, device=DEV)
+    out_lse = torch.empty((B, hl), dtype=torch.float32, device=DEV)
+    ws = dcp.dcp_workspace_create(B, hl, cp)
+    dcp.dcp_lse_combine(ws, attn, lse, dcp.DCP_LSE_BH1, dcp.DCP_LSE_BASE_2, out, out_lse)
+    torch.cuda.synchronize()
+    ws.close()
+    for b in (0, 16383, 16384, 32767, 32768, 32769, B - 1):
+        case = synth.MergeCase("token %d of %d" % (b, B), attn[b:b + 1].cpu(), lse[b:b + 1].cpu(), cp, "bh1", "2")
+        check_against_oracle(case, out[b:b + 1], out_lse[b:b + 1])
+    del attn
+
+
 def test_zero_tokens_is_a_no_op():
     import context_lse_merge_amd as dcp
     ws = dcp.dcp_workspace_create(4, 16, 4)
