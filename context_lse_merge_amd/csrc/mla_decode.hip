@@ -59,7 +59,9 @@
 //    normalised fp32 output and LSE in the scratch buffer, and the merge
 //    kernel of dcp_lse_combine (its fp32-input instance) reduces the splits
 //    of each (token, shard, head) exactly as it merges DCP shards.  With a
-//    single split the kernel writes the final output and LSE itself.
+//    single split the kernel writes the final output and LSE itself.  With
+//    per-token lengths (seq_lens) the splits are sized on the device instead
+//    and the workgroup runs one item of a work list (mla_varlen.hip).
 //  * Workgroups that share a key range are placed on the same XCD (block ids
 //    are dealt round-robin over the 8 XCDs), so a KV tile is fetched from HBM
 //    about once per XCD-L2 rather than once per workgroup.
