@@ -197,6 +197,25 @@ def measure(case, steps, warmup, capacity=None, cold=True, cached=False):
     return us, nsets, nsets * per_set, first
 
 
+def launch_floor(steps, warmup):
+    """us per launch of a one-element fill kernel (one workgroup) in the same
+    harness -- graphs of GRAPH_CALLS launches on one stream: the fixed cost
+    every layer-merge pays before moving any bytes."""
+    import torch
+    buf = torch.zeros(1, device="cuda:0")
+    calls = min(GRAPH_CALLS, steps)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        buf.fill_(1.0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(calls):
+            buf.fill_(1.0)
+    time_graphs([g], max(1, math.ceil(warmup / calls)))
+    return time_graphs([g], steps // calls) * 1000.0 / steps
+
+
 def parity_check(case, out, out_lse):
     """The bench's own sanity check of its first input set against the oracle."""
     import numpy as np
@@ -509,6 +528,9 @@ def main():
     if args.calibrate:
         calibration_copy()
     traffic = counters_traffic()
+    floor_us = launch_floor(args.steps, args.warmup)
+    print("[bench] launch floor: a one-element fill kernel in the same graph harness takes %.3f us per launch"
+          % floor_us, file=sys.stderr, flush=True)
     line = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -531,6 +553,9 @@ def main():
         "us_per_layer_merge_hot": None if us_hot is None else round(us_hot, 3),
         "us_per_layer_merge_hot_cached_policy": None if us_hot_cached is None else round(us_hot_cached, 3),
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "launch_floor_us": {"us": round(floor_us, 3),
+                            "kernel": "one-element fill (one workgroup) in the same graphs of %d launches"
+                                      % GRAPH_CALLS},
         "parity_vs_oracle": ok,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
