@@ -217,8 +217,11 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
         reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)(p)));
 }
 
+// The LDS address goes in M0, bound as an input operand so that the compiler
+// writes M0 itself and knows it is in use; the s_nop keeps one wait state
+// between that write and the copy that reads it.
 __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
 
 constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;
