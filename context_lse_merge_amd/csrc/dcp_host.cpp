@@ -13,8 +13,8 @@
 // Chunk planner (PR #40539, Modifications and Coordination): batches wider
 // than the workspace run as several launches over consecutive token ranges,
 // in order, on the workspace's stream.  A call on any other stream is rejected
-// before anything is enqueued (PR #40539, Accuracy Tests: a third stream is
-// rejected before the collective).
+// before anything is enqueued (PR #40539, Accuracy Tests: a call from a third
+// stream is refused before any exchange starts).
 //
 // Input checks: the later text of PR #40539 drops the copy of strided or
 // misaligned partials and lets the kernel check its inputs; here an input the

@@ -4,8 +4,8 @@
 // What it computes: for every token b and local head j, the LSE-weighted merge
 // of the cp shard partials of that head ("[DCP] Run fi_a2a on FlashInfer's
 // fused all-to-all + LSE reduce", sglang PR #40539, Motivation/Modifications;
-// "[Attention] Add direct symmetric-memory DCP A2A", vLLM PR #48897: FP32 LSE
-// weighting, empty shards publish -inf and their payload is skipped):
+// "[Attention] Add direct symmetric-memory DCP A2A", vLLM PR #48897: weights
+// formed in fp32, empty shards publish -inf and their payload is skipped):
 //     M = max_s lse_s, w_s = 2^((lse_s - M) * c), S = sum_s w_s,
 //     out = sum_s (w_s / S) O_s, L = M + log2(S) / c,
 // with c = 1 for base-2 LSEs and c = log2 e for natural-log LSEs.

@@ -7,8 +7,8 @@
  * (token, head).  The exact attention output is the LSE-weighted merge of the
  * shards' partials ("[DCP] Run fi_a2a on FlashInfer's fused all-to-all + LSE
  * reduce", sglang PR #40539, Motivation; "[Attention] Add direct
- * symmetric-memory DCP A2A", vLLM PR #48897, commit message: states are
- * combined with FP32 LSE weighting):
+ * symmetric-memory DCP A2A", vLLM PR #48897, commit message: the merge
+ * weights are formed in fp32):
  *
  *     M = max_s lse_s,  w_s = base^(lse_s - M),  S = sum_s w_s
  *     out = sum_s (w_s / S) O_s,                 L = M + log_base S
@@ -213,10 +213,10 @@ int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64
  * over its own latent KV rows.  The decode seq_lens decide which shards are
  * empty ("[Attention] Add direct symmetric-memory DCP A2A", vLLM PR #48897,
  * amended port commit: the dispatch takes the decode seq_lens and an empty
- * shard publishes LSE = -inf and no payload); with the latent KV interleaved
- * across DCP ranks ("[DCP] Optimize shared Output, Query, and Indexer/Top-K
- * via peer memory", sglang PR #32851, commit log) shard s owns every cp-th
- * token of each request.
+ * shard publishes LSE = -inf and no payload); with the latent KV spread over
+ * the DCP ranks in interleaved order ("[DCP] Optimize shared Output, Query,
+ * and Indexer/Top-K via peer memory", sglang PR #32851, commit log) shard s
+ * owns every cp-th token of each request.
  *
  * For query row (b, h) let L = min(max(seq_lens[b], 0), max_seq_len) and
  * let R_s be the rows shard s owns (kv_layout: DCP_KV_CONTIGUOUS or

@@ -28,8 +28,8 @@
  *            LSE = -inf, its payload is not written, and zero-weight sources
  *            are skipped.  "[DCP] Optimize shared Output, Query, and
  *            Indexer/Top-K via peer memory" (sglang PR #32851), commit log:
- *            zero-count rows contribute exp2(-inf) = 0, and rows with no
- *            selected tokens must give 0, not NaN.
+ *            a row that selected no token weighs in with exp2 of -inf, i.e.
+ *            zero, and its merged result must be zero rather than NaN.
  *            The pages name the merge but never print its formula; it is the
  *            split-softmax identity
  *                M   = max_s lse_s
@@ -57,8 +57,8 @@
  *            symmetric-memory DCP A2A", vLLM PR #48897, amended port commit:
  *            the decode seq_lens decide which KV shards are empty; an empty
  *            shard publishes -inf).  Shard s owns either a contiguous slice
- *            [floor(s L/cp), floor((s+1) L/cp)) or, with the latent KV
- *            interleaved across DCP ranks ("[DCP] Optimize shared Output,
+ *            [floor(s L/cp), floor((s+1) L/cp)) or, with the latent KV spread
+ *            over the DCP ranks in interleaved order ("[DCP] Optimize shared Output,
  *            Query, and Indexer/Top-K via peer memory", sglang PR #32851,
  *            commit log), the tokens t < L with t mod cp = s.
  */

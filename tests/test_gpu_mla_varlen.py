@@ -3,8 +3,8 @@
 Each query token attends over its own cache and its own decode length; the
 lengths decide which DCP shards are empty ("[Attention] Add direct
 symmetric-memory DCP A2A", vLLM PR #48897, amended port commit), and shards
-own either a contiguous slice of a token's rows or, with the latent KV
-interleaved across DCP ranks ("[DCP] Optimize shared Output, Query, and
+own either a contiguous slice of a token's rows or, with the latent KV spread
+over the DCP ranks in interleaved order ("[DCP] Optimize shared Output, Query, and
 Indexer/Top-K via peer memory", sglang PR #32851, commit log), every cp-th
 row.  Tolerances as for the fixed-length producer (see test_gpu_mla).
 """
