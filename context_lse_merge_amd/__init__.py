@@ -157,8 +157,9 @@ def dcp_workspace_destroy(ws: Workspace):
 
 
 def dcp_workspace_set_load_policy(ws: Workspace, policy: int):
-    """DCP_LOAD_STREAMING (non-temporal, the default) or DCP_LOAD_CACHED (plain
-    loads and stores, for partials that are still cache-resident)."""
+    """DCP_LOAD_STREAMING (non-temporal loads, the default) or DCP_LOAD_CACHED
+    (plain loads, for partials that are still cache-resident); the output is
+    written with non-temporal stores under both."""
     _check(_lib.dcp_workspace_set_load_policy(ws.handle, policy))
 
 

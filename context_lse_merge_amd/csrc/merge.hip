@@ -146,7 +146,6 @@ __device__ __forceinline__ u32x4 load16(const u32x4* p) {
 
 template <typename T, bool NT>
 struct Payload16 {
-    static constexpr bool kNT = NT;
     typedef u32x4 row_t;
     static __device__ __forceinline__ row_t load(const void* base, int64_t off) {
         return load16<NT>(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off));
@@ -168,7 +167,6 @@ struct Payload16 {
 
 template <bool NT>
 struct PayloadF32 {
-    static constexpr bool kNT = NT;
     struct row_t {
         u32x4 a, b;
     };
@@ -267,7 +265,11 @@ __device__ __forceinline__ float merged_lse(const MergeTail& t, float M, float S
     return M + __builtin_amdgcn_logf(S) * t.from_log2;
 }
 
-template <typename T, bool NT>
+// The output row always leaves with a non-temporal store, under either load
+// policy: measured, that is the faster store both when the partials stream in
+// from HBM and when they are read from the caches (B = 512 hot: 5.05 us
+// against 5.79 us with plain stores).
+template <typename T>
 __device__ __forceinline__ void store_row(const MergeTail& t, Row r, int lane, const float (&acc)[8], float L) {
     u32x4 packed;
     packed[0] = T::pack(acc[0], acc[1]);
@@ -275,10 +277,7 @@ __device__ __forceinline__ void store_row(const MergeTail& t, Row r, int lane, c
     packed[2] = T::pack(acc[4], acc[5]);
     packed[3] = T::pack(acc[6], acc[7]);
     u32x4* dst = reinterpret_cast<u32x4*>(t.out + r.b * t.o_sb + r.j * t.o_sj + lane * 8);
-    if (NT)
-        __builtin_nontemporal_store(packed, dst);
-    else
-        *dst = packed;
+    __builtin_nontemporal_store(packed, dst);
     if (t.out_lse && lane == 0) t.out_lse[r.b * t.ol_sb + r.j] = L;
 }
 
@@ -339,7 +338,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const void* attn, const f
 #pragma unroll
         for (int s = 0; s < CP; ++s) fma8<In>(acc, w[s], v[s]);
     }
-    store_row<Out, In::kNT>(t, r, lane, acc, merged_lse(t, M, S));
+    store_row<Out>(t, r, lane, acc, merged_lse(t, M, S));
 }
 
 // 16 < cp <= 64: the same row algorithm with the shards taken G at a time.
@@ -379,7 +378,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_wide(const void* attn, co
             fma8<In>(acc, ws, v[i]);
         }
     }
-    store_row<Out, In::kNT>(t, r, lane, acc, merged_lse(t, M, S));
+    store_row<Out>(t, r, lane, acc, merged_lse(t, M, S));
 }
 
 typedef void (*MergeKernel)(const void*, const float*, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,

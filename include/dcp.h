@@ -71,7 +71,7 @@ extern "C" {
 /* How dcp_lse_combine reads its partials and writes its output
  * (dcp_workspace_set_load_policy). */
 #define DCP_LOAD_STREAMING 0 /* non-temporal: partials read from HBM once (default) */
-#define DCP_LOAD_CACHED 1    /* plain loads/stores: partials just written and still cache-resident */
+#define DCP_LOAD_CACHED 1    /* plain loads: partials just written and still cache-resident */
 
 /* Which cache rows a DCP shard owns (dcp_mla_partial_decode_varlen). */
 #define DCP_KV_CONTIGUOUS 0  /* shard s: rows [floor(s*L/cp), floor((s+1)*L/cp)) of a length-L cache */
@@ -108,13 +108,14 @@ int dcp_workspace_create(int64_t capacity_tokens, int h_local, int cp, int d, in
 int dcp_workspace_destroy(dcp_workspace* ws);
 
 /*
- * Cache policy of every later dcp_lse_combine call on ws.  DCP_LOAD_STREAMING
- * (the default) reads the partials and writes the output with non-temporal
- * accesses, which do not displace cached data: fastest when the partials come
- * from HBM.  DCP_LOAD_CACHED uses plain accesses: fastest when the partials
- * were written just before (the exchange's receive buffers, or a producer in
- * the same stream) and still sit in the L2 / Infinity Cache.  Results are
- * bit-identical under both policies.  Returns DCP_ERR_INVALID_ARG for an
+ * Cache policy of every later dcp_lse_combine call on ws: how the partials are
+ * read.  DCP_LOAD_STREAMING (the default) reads them with non-temporal loads,
+ * which do not displace cached data: fastest when the partials come from HBM.
+ * DCP_LOAD_CACHED reads them with plain loads: fastest when they were written
+ * just before (the exchange's receive buffers, or a producer in the same
+ * stream) and still sit in the L2 / Infinity Cache.  The output is written
+ * with non-temporal stores under both (measured faster in both cases).
+ * Results are bit-identical under both policies.  Returns DCP_ERR_INVALID_ARG for an
  * unknown policy or handle.
  */
 int dcp_workspace_set_load_policy(dcp_workspace* ws, int policy);
