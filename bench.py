@@ -216,6 +216,38 @@ def launch_floor(steps, warmup):
     return time_graphs([g], steps // calls) * 1000.0 / steps
 
 
+def copy_ceiling(headline_bytes):
+    """Cold device-to-device copies (torch copy_) in the same harness: graphs of
+    GRAPH_CALLS copies cycling over >= 1 GiB of buffers.  Returns GB/s (bytes
+    read + written) for 256 MiB copies, and us per copy that reads and writes
+    half of `headline_bytes` each (the same total bytes as one layer-merge)."""
+    import torch
+    res = {}
+    for label, nbytes in (("256MiB", 256 << 20), ("headline", headline_bytes // 2)):
+        n = max(1, nbytes // 2)
+        sets = max(2, math.ceil((1 << 30) / (2 * n * 2)))
+        src = [torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0) for _ in range(sets)]
+        dst = [torch.empty_like(x) for x in src]
+        calls = min(GRAPH_CALLS, 4 * sets)
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            dst[0].copy_(src[0])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(calls):
+                dst[i % sets].copy_(src[i % sets])
+        time_graphs([g], 2)
+        us = time_graphs([g], 5) * 1000.0 / (5 * calls)
+        res[label] = (us, 2.0 * n * 2 / (us * 1e-6) / 1e9)
+        del src, dst, g
+        torch.cuda.empty_cache()
+    return {"GBps_256MiB": round(res["256MiB"][1], 1),
+            "us_at_headline_bytes": round(res["headline"][0], 3),
+            "kernel": "torch copy_ of bf16 buffers, cold (>= 1 GiB cycled), graphs of %d copies; GB/s counts "
+                      "bytes read plus bytes written" % GRAPH_CALLS}
+
+
 def parity_check(case, out, out_lse):
     """The bench's own sanity check of its first input set against the oracle."""
     import numpy as np
@@ -531,6 +563,10 @@ def main():
     floor_us = launch_floor(args.steps, args.warmup)
     print("[bench] launch floor: a one-element fill kernel in the same graph harness takes %.3f us per launch"
           % floor_us, file=sys.stderr, flush=True)
+    copy = copy_ceiling(alg)
+    print("[bench] copy ceiling: torch copy_ moves 256 MiB at %.1f GB/s (read + write); a copy of the headline's "
+          "%d bytes takes %.3f us" % (copy["GBps_256MiB"], alg, copy["us_at_headline_bytes"]), file=sys.stderr,
+          flush=True)
     line = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -556,6 +592,7 @@ def main():
         "launch_floor_us": {"us": round(floor_us, 3),
                             "kernel": "one-element fill (one workgroup) in the same graphs of %d launches"
                                       % GRAPH_CALLS},
+        "copy_ceiling": copy,
         "parity_vs_oracle": ok,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
