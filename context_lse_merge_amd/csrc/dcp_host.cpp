@@ -300,6 +300,8 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     if (!q || !o || !lse || (T > 0 && !kv))
         return fail(DCP_ERR_INVALID_ARG, "%s: q, o_part, lse_part (and kv when there are keys) must be non-null", fn);
     if (vl && !vl->seq_lens) return fail(DCP_ERR_INVALID_ARG, "%s: seq_lens must be non-null when B > 0", fn);
+    if (vl && T > kVarlenMaxLen)
+        return fail(DCP_ERR_INVALID_ARG, "%s: max_seq_len = %lld exceeds %d", fn, (long long)T, kVarlenMaxLen);
     if (vl && !aligned(vl->seq_lens, 4)) return fail(DCP_ERR_ALIGN, "%s: seq_lens must be 4-byte aligned", fn);
     const int64_t kv_sb = vl ? vl->kv_sb : 0;
     if (q_sb < 0 || q_sh < 0 || kv_st < 0 || kv_sb < 0 || o_sb < 0 || o_sh < 0 || lse_sb < 0)
@@ -462,6 +464,9 @@ int dcp_mla_partial_decode_varlen_scratch_size(int64_t B, int hq, int64_t max_se
                          DCP_MAX_CP);
     if (B * static_cast<int64_t>(hq) > (int64_t{1} << 30))
         return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_mla_partial_decode_varlen_scratch_size: B * hq exceeds 2^30");
+    if (max_seq_len > dcp::kVarlenMaxLen)
+        return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_mla_partial_decode_varlen_scratch_size: max_seq_len = %lld exceeds %d",
+                         (long long)max_seq_len, dcp::kVarlenMaxLen);
     *bytes = B == 0 ? 0 : dcp::varlen_layout(B, hq, max_seq_len, cp).bytes;
     return dcp::ok();
 }

@@ -146,7 +146,7 @@ constexpr int kMlaPlanThreads = 1024;  // the planning workgroup; also its numbe
 struct VarlenHeader {
     int32_t n_items;      // items in the list; workgroups past it exit
     int32_t n_split;      // pairs with more than one split
-    int64_t split_tiles;  // key tiles per split
+    int64_t split_tiles;  // key tiles per split (at most kVarlenMaxLen)
 };
 struct VarlenItem {
     int32_t pair, p;      // split p of pair q
@@ -164,23 +164,40 @@ struct VarlenSplit {
 #define DCP_HD
 #endif
 
+// Token lengths are at most kVarlenMaxLen (checked on the host), so the
+// per-pair arithmetic below is exact in 32 bits: the GPU has no integer
+// divide, and a 64-bit division costs several times a 32-bit one.
+constexpr int32_t kVarlenMaxLen = int32_t{1} << 30;
+
 // Key tiles of shard s of a token with L rows (contiguous slices
 // [floor(s L / cp), floor((s+1) L / cp)) or every cp-th row from row s).
-DCP_HD inline int64_t varlen_shard_tiles(int64_t L, int s, int cp, bool interleaved) {
-    const int64_t n = interleaved ? (L > s ? (L - s + cp - 1) / cp : 0)
-                                  : ((s + 1) * L) / cp - (s * L) / cp;
+// With L = q cp + r, floor(k L / cp) = k q + floor(k r / cp).
+DCP_HD inline int32_t varlen_shard_tiles(int32_t L, int32_t s, int32_t cp, bool interleaved) {
+    int32_t n;
+    if (interleaved) {
+        n = L > s ? (L - s + cp - 1) / cp : 0;
+    } else {
+        const int32_t q = L / cp, r = L - q * cp;
+        n = q + ((s + 1) * r) / cp - (s * r) / cp;
+    }
     return (n + kMlaKeysPerTile - 1) / kMlaKeysPerTile;
 }
-// Tiles per split for a batch of `total` tiles.
-DCP_HD inline int64_t varlen_split_tiles(int64_t total) {
-    const int64_t st = (total + kVarlenTarget - 1) / kVarlenTarget;
-    return st < kMlaMinSplitTiles ? kMlaMinSplitTiles : st;
+// Tiles per split for a batch of `total` tiles.  Capped at kVarlenMaxLen: a
+// split that long already holds any shard whole (no pair splits).
+DCP_HD inline int32_t varlen_split_tiles(int64_t total) {
+    int64_t st = (total + kVarlenTarget - 1) / kVarlenTarget;
+    if (st < kMlaMinSplitTiles) st = kMlaMinSplitTiles;
+    return st > kVarlenMaxLen ? kVarlenMaxLen : static_cast<int32_t>(st);
 }
 // Splits of a pair of t tiles (an empty pair still has one, to write 0 / -inf).
-DCP_HD inline int64_t varlen_splits(int64_t t, int64_t st) { return t > st ? (t + st - 1) / st : 1; }
-// Size bin of a split of `size` <= st tiles: 0 (empty) .. kMlaPlanThreads - 1 (full).
-DCP_HD inline int varlen_bin(int64_t size, int64_t st) {
-    return static_cast<int>((size * (kMlaPlanThreads - 1)) / st);
+DCP_HD inline int32_t varlen_splits(int32_t t, int32_t st) { return t > st ? (t + st - 1) / st : 1; }
+// Size bin of a split of `size` <= st tiles: 0 (empty) .. kMlaPlanThreads - 1
+// (full), rounded from size / st in fp32 (the bins only order the work list;
+// both passes of the plan compute them identically).
+DCP_HD inline int varlen_bin(int32_t size, int32_t st) {
+    const float x = static_cast<float>(size) * static_cast<float>(kMlaPlanThreads - 1) / static_cast<float>(st);
+    const int b = static_cast<int>(x + 0.5f);
+    return b < kMlaPlanThreads - 1 ? b : kMlaPlanThreads - 1;
 }
 
 // Scratch layout of the variable-length producer: part_o [slots][128][512]

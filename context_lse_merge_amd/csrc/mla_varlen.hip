@@ -8,8 +8,9 @@
 // key splits: a split length fixed from the longest possible token leaves
 // most of the chip idle while the few long tokens finish.  Here a planning
 // kernel sizes the splits from the actual lengths instead:
-//  * one workgroup sums the key tiles of every pair (token, row block,
-//    shard), picks st = max(ceil(total / 256), 8) tiles per split -- about
+//  * one workgroup (its threads spread over the (token, shard) pairs, all
+//    in exact 32-bit arithmetic) sums the key tiles of every pair (token, row
+//    block, shard), picks st = max(ceil(total / 256), 8) tiles per split -- about
 //    one split per compute unit over the whole batch, none shorter than 256
 //    keys -- and gives each pair ceil(tiles / st) splits (one if it has at
 //    most st tiles, including the empty pairs, which still write 0 / -inf);
@@ -42,22 +43,25 @@ constexpr int kReduceWaves = 4;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int64_t token_len(const MlaArgs& a, int64_t b) {
-    const int64_t L = a.seq_lens[b];
-    return L < 0 ? 0 : (L > a.T ? a.T : L);
+__device__ __forceinline__ int32_t token_len(const MlaArgs& a, int32_t b) {
+    const int32_t L = a.seq_lens[b];
+    const int32_t T = static_cast<int32_t>(a.T);  // at most kVarlenMaxLen
+    return L < 0 ? 0 : (L > T ? T : L);
 }
 
-// One workgroup of kMlaPlanThreads threads.  Pass 1 sums the tiles, pass 2
-// counts the splits per size bin, a scan turns the counts into the first
-// list position of each bin (largest bin first), pass 3 places the splits.
+// One workgroup of kMlaPlanThreads threads; thread i takes the (token,
+// shard) pairs i, i + kMlaPlanThreads, ... (all row blocks of a token share
+// them).  Pass 1 sums the tiles, pass 2 counts the splits per size bin, a
+// scan turns the counts into the first list position of each bin (largest
+// bin first), pass 3 places the splits.
 __global__ __launch_bounds__(kMlaPlanThreads) void varlen_plan_kernel(MlaArgs a) {
     __shared__ unsigned long long s_total;
     __shared__ int32_t s_pos[kBins];
     __shared__ int32_t s_scan[2][kBins];
     __shared__ int32_t s_slots, s_split;
     const int tid = threadIdx.x;
-    const int64_t B = a.rows / a.hq;
-    const int cp = a.cp, rbt = a.rb_per_token;
+    const int32_t cp = a.cp, rbt = a.rb_per_token;
+    const int32_t n_ts = (a.rows / a.hq) * cp;  // (token, shard) pairs
     const bool il = a.interleaved != 0;
     if (tid == 0) {
         s_total = 0;
@@ -68,22 +72,20 @@ __global__ __launch_bounds__(kMlaPlanThreads) void varlen_plan_kernel(MlaArgs a)
     __syncthreads();
 
     unsigned long long mine = 0;
-    for (int64_t b = tid; b < B; b += kMlaPlanThreads) {
-        const int64_t L = token_len(a, b);
-        for (int s = 0; s < cp; ++s) mine += varlen_shard_tiles(L, s, cp, il);
+    for (int32_t i = tid; i < n_ts; i += kMlaPlanThreads) {
+        const int32_t b = i / cp;
+        mine += varlen_shard_tiles(token_len(a, b), i - b * cp, cp, il);
     }
     if (mine) atomicAdd(&s_total, mine * rbt);
     __syncthreads();
-    const int64_t st = varlen_split_tiles(static_cast<int64_t>(s_total));
+    const int32_t st = varlen_split_tiles(static_cast<int64_t>(s_total));
 
-    for (int64_t b = tid; b < B; b += kMlaPlanThreads) {
-        const int64_t L = token_len(a, b);
-        for (int s = 0; s < cp; ++s) {
-            const int64_t t = varlen_shard_tiles(L, s, cp, il);
-            const int64_t n = varlen_splits(t, st);
-            if (n > 1) atomicAdd(&s_pos[kBins - 1], static_cast<int32_t>((n - 1) * rbt));
-            atomicAdd(&s_pos[varlen_bin(t - (n - 1) * st, st)], rbt);
-        }
+    for (int32_t i = tid; i < n_ts; i += kMlaPlanThreads) {
+        const int32_t b = i / cp;
+        const int32_t t = varlen_shard_tiles(token_len(a, b), i - b * cp, cp, il);
+        const int32_t n = varlen_splits(t, st);
+        if (n > 1) atomicAdd(&s_pos[kBins - 1], (n - 1) * rbt);
+        atomicAdd(&s_pos[varlen_bin(t - (n - 1) * st, st)], rbt);
     }
     __syncthreads();
 
@@ -103,24 +105,22 @@ __global__ __launch_bounds__(kMlaPlanThreads) void varlen_plan_kernel(MlaArgs a)
     s_pos[kBins - 1 - tid] = inclusive - count;
     __syncthreads();
 
-    for (int64_t b = tid; b < B; b += kMlaPlanThreads) {
-        const int64_t L = token_len(a, b);
-        for (int s = 0; s < cp; ++s) {
-            const int64_t t = varlen_shard_tiles(L, s, cp, il);
-            const int32_t n = static_cast<int32_t>(varlen_splits(t, st));
-            const int bin = varlen_bin(t - static_cast<int64_t>(n - 1) * st, st);
-            for (int r = 0; r < rbt; ++r) {
-                const int32_t q = static_cast<int32_t>((b * rbt + r) * cp + s);
-                int32_t first = -1;
-                if (n > 1) {
-                    first = atomicAdd(&s_slots, n);
-                    a.vl_splits[atomicAdd(&s_split, 1)] = VarlenSplit{q, first, n, 0};
-                    const int32_t pos = atomicAdd(&s_pos[kBins - 1], n - 1);
-                    for (int32_t p = 0; p < n - 1; ++p) a.vl_items[pos + p] = VarlenItem{q, p, first + p, 0};
-                }
-                const int32_t pos = atomicAdd(&s_pos[bin], 1);
-                a.vl_items[pos] = VarlenItem{q, n - 1, first < 0 ? -1 : first + n - 1, 0};
+    for (int32_t i = tid; i < n_ts; i += kMlaPlanThreads) {
+        const int32_t b = i / cp, s = i - b * cp;
+        const int32_t t = varlen_shard_tiles(token_len(a, b), s, cp, il);
+        const int32_t n = varlen_splits(t, st);
+        const int bin = varlen_bin(t - (n - 1) * st, st);
+        for (int32_t r = 0; r < rbt; ++r) {
+            const int32_t q = (b * rbt + r) * cp + s;
+            int32_t first = -1;
+            if (n > 1) {
+                first = atomicAdd(&s_slots, n);
+                a.vl_splits[atomicAdd(&s_split, 1)] = VarlenSplit{q, first, n, 0};
+                const int32_t pos = atomicAdd(&s_pos[kBins - 1], n - 1);
+                for (int32_t p = 0; p < n - 1; ++p) a.vl_items[pos + p] = VarlenItem{q, p, first + p, 0};
             }
+            const int32_t pos = atomicAdd(&s_pos[bin], 1);
+            a.vl_items[pos] = VarlenItem{q, n - 1, first < 0 ? -1 : first + n - 1, 0};
         }
     }
     if (tid == kBins - 1) {

@@ -232,7 +232,9 @@ int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64
  *           kv_sb = 0 lets every token share one cache.  Rows t >=
  *           max_seq_len are never read.
  * seq_lens  device int32 [B]; values outside [0, max_seq_len] are clamped.
- * max_seq_len  host bound on seq_lens, used to size the scratch.
+ * max_seq_len  host bound on seq_lens, used to size the scratch; at most
+ *           2^30 (DCP_ERR_INVALID_ARG beyond), so that the device plan
+ *           counts keys and tiles exactly in 32 bits.
  * scratch   device buffer of at least
  *           dcp_mla_partial_decode_varlen_scratch_size() bytes (never 0 when
  *           B > 0), 16-byte aligned.  The key splits are sized on the device

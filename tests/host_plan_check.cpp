@@ -71,7 +71,36 @@ static void check_varlen_plan(const std::vector<int64_t>& lens, int hq, int64_t 
     CHECK(lay.bytes == lay.off_split + dcp::kVarlenTarget * sizeof(dcp::VarlenSplit));
 }
 
+// The plan's 32-bit shard sizes against their plain 64-bit definition.
+static void shard_formula_checks() {
+    std::mt19937_64 rng(7);
+    for (int trial = 0; trial < 200000; ++trial) {
+        const int32_t cp = 1 + static_cast<int32_t>(rng() % 64);
+        const int32_t s = static_cast<int32_t>(rng() % cp);
+        const int64_t L = (trial % 2) ? static_cast<int64_t>(rng() % 5000)
+                                      : static_cast<int64_t>(rng() % (int64_t{dcp::kVarlenMaxLen} + 1));
+        const int64_t n_c = ((s + 1) * L) / cp - (s * L) / cp;
+        const int64_t n_i = L > s ? (L - s + cp - 1) / cp : 0;
+        CHECK(dcp::varlen_shard_tiles(static_cast<int32_t>(L), s, cp, false) == (n_c + 31) / 32);
+        CHECK(dcp::varlen_shard_tiles(static_cast<int32_t>(L), s, cp, true) == (n_i + 31) / 32);
+    }
+    // Size bins: 0 for an empty split, the top bin for a full one, monotone in between.
+    for (int32_t st : {8, 9, 100, 549, 4096, 1 << 20, dcp::kVarlenMaxLen}) {
+        CHECK(dcp::varlen_bin(0, st) == 0);
+        CHECK(dcp::varlen_bin(st, st) == dcp::kMlaPlanThreads - 1);
+        int prev = 0;
+        for (int32_t k = 1; k <= 64; ++k) {
+            const int32_t size = static_cast<int32_t>((static_cast<int64_t>(st) * k) / 64);
+            const int b = dcp::varlen_bin(size, st);
+            CHECK(b >= prev && b < dcp::kMlaPlanThreads);
+            prev = b;
+        }
+    }
+    CHECK(dcp::varlen_split_tiles(int64_t{1} << 50) == dcp::kVarlenMaxLen);
+}
+
 static void varlen_plan_checks() {
+    shard_formula_checks();
     std::mt19937_64 rng(20261202);
     const int64_t T = 131072;
     for (int trial = 0; trial < 200; ++trial) {

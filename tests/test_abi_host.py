@@ -66,6 +66,18 @@ def test_workspace_errors_through_the_binding():
     assert ws.handle is None
 
 
+def test_varlen_scratch_size_limits_through_the_binding():
+    import context_lse_merge_amd as dcp
+    assert dcp.dcp_mla_partial_decode_varlen_scratch_size(0, 128, 1 << 30, 4) == 0
+    assert dcp.dcp_mla_partial_decode_varlen_scratch_size(4, 128, 1 << 30, 4) > 0
+    with pytest.raises(dcp.DcpError) as e:
+        dcp.dcp_mla_partial_decode_varlen_scratch_size(4, 128, (1 << 30) + 1, 4)
+    assert e.value.status == dcp.DCP_ERR_INVALID_ARG and "max_seq_len" in str(e.value)
+    with pytest.raises(dcp.DcpError) as e:
+        dcp.dcp_mla_partial_decode_varlen_scratch_size(1 << 24, 128, 4096, 4)
+    assert e.value.status == dcp.DCP_ERR_INVALID_ARG
+
+
 def test_host_planner_under_sanitizers(tmp_path):
     exe = tmp_path / "host_plan_check"
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
