@@ -221,8 +221,8 @@ MergeArgs chunk_args(const MergePlan& plan, int64_t k) {
 // ceil(B*hq/128)*cp units of work -- 4 at B = 1 with 128 heads and cp = 4, far
 // too few for 256 compute units.  Each shard's keys are therefore split into
 // nsplit ranges processed by separate workgroups; each leaves a normalised
-// fp32 partial and its LSE, and the merge kernel reduces the splits exactly
-// as it merges DCP shards.  The split count aims at about kMlaTargetBlocks
+// partial (fp16 rows scaled by a power of two) and its LSE, and the merge
+// kernel reduces the splits exactly as it merges DCP shards.  The split count aims at about kMlaTargetBlocks
 // workgroups and never gives a split fewer than kMlaMinSplitKeys keys.  Every
 // token has the same T keys here, so the host decides; with per-token
 // lengths the planning kernel does (varlen_layout sizes its scratch).
@@ -250,7 +250,7 @@ void mla_split(int64_t B, int hq, int64_t T, int cp, int32_t* nsplit, int64_t* s
         *scratch_bytes = 0;
     } else {
         const int64_t parts = static_cast<int64_t>(cp) * n * rows;  // (token, split, shard, head)
-        *scratch_bytes = static_cast<size_t>(parts * kMlaVDim * 4 + parts * 4);
+        *scratch_bytes = static_cast<size_t>(parts * kMlaVDim * 2 + parts * 4 * 2);  // rows, LSEs, scales
     }
 }
 
@@ -264,8 +264,9 @@ VarlenLayout varlen_layout(int64_t B, int hq, int64_t T, int cp) {
     const int64_t max_n = (shard_tiles + kMlaMinSplitTiles - 1) / kMlaMinSplitTiles;
     l.slots = max_n > 1 ? std::min<int64_t>(2 * kVarlenTarget, l.pairs * max_n) : 0;
     const size_t rows = static_cast<size_t>(l.slots) * kMlaRowsPerBlock;
-    l.off_lse = rows * kMlaVDim * sizeof(float);
-    l.off_hdr = (l.off_lse + rows * sizeof(float) + 63) / 64 * 64;
+    l.off_lse = rows * kMlaVDim * sizeof(uint16_t);
+    l.off_scale = l.off_lse + rows * sizeof(float);
+    l.off_hdr = (l.off_scale + rows * sizeof(float) + 63) / 64 * 64;
     l.off_items = l.off_hdr + 64;
     l.off_split = l.off_items + static_cast<size_t>(l.items) * sizeof(VarlenItem);
     l.bytes = l.off_split + static_cast<size_t>(kVarlenTarget) * sizeof(VarlenSplit);
@@ -378,8 +379,9 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
         a.rb_per_token = (hq + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
         a.row_blocks = static_cast<int32_t>(B * a.rb_per_token);
         char* base = static_cast<char*>(scratch);
-        a.part_o = reinterpret_cast<float*>(base);
+        a.part_o = reinterpret_cast<uint16_t*>(base);
         a.part_lse = reinterpret_cast<float*>(base + vlay.off_lse);
+        a.part_scale = reinterpret_cast<float*>(base + vlay.off_scale);
         a.vl_hdr = reinterpret_cast<VarlenHeader*>(base + vlay.off_hdr);
         a.vl_items = reinterpret_cast<VarlenItem*>(base + vlay.off_items);
         a.vl_splits = reinterpret_cast<VarlenSplit*>(base + vlay.off_split);
@@ -394,15 +396,17 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     a.o_sh = o_sh;
     a.lse_sb = lse_sb;
     if (!vl && nsplit > 1) {
-        // Per-split fp32 partials in the scratch buffer, then the merge over splits.
+        // Per-split scaled fp16 partials in the scratch buffer, then the merge over splits.
         const int64_t heads = static_cast<int64_t>(nsplit) * H;   // per token
-        a.part_o = static_cast<float*>(scratch);
-        a.part_lse = static_cast<float*>(scratch) + B * heads * kMlaVDim;
+        a.part_o = static_cast<uint16_t*>(scratch);
+        a.part_lse = reinterpret_cast<float*>(a.part_o + B * heads * kMlaVDim);
+        a.part_scale = a.part_lse + B * heads;
         a.part_sb = heads;
         MergeArgs m{};
         m.attn = a.part_o;
-        m.in_dtype = kPayloadF32;
+        m.in_dtype = kPayloadF16Scaled;
         m.lse = a.part_lse;
+        m.sc_off = B * heads;          // part_scale sits right after part_lse
         m.out = static_cast<uint16_t*>(o);
         m.out_lse = lse;
         m.a_sb = heads * kMlaVDim;

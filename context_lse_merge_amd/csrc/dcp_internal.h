@@ -30,24 +30,31 @@ struct MergeArgs {
     int32_t rows;
     int32_t h_local;
     int32_t cp;
-    int32_t in_dtype;   // attn: DCP_DTYPE_BF16, DCP_DTYPE_FP16 or kPayloadF32 (internal)
+    int32_t in_dtype;   // attn: DCP_DTYPE_BF16, DCP_DTYPE_FP16 or kPayloadF16Scaled (internal)
     int32_t dtype;      // out: DCP_DTYPE_BF16 or DCP_DTYPE_FP16
     int32_t cached;     // 1: plain loads and stores; 0: non-temporal
     // (lse_s - M) * to_log2 is the exponent of 2 of the weight; log2(S) * from_log2
     // is added to M for the merged LSE.  Base 2: both 1.  Base e: log2 e and ln 2.
     float to_log2;
     float from_log2;
+    // kPayloadF16Scaled: shard s of a row is scaled by the float sc_off
+    // elements after its LSE (lse + b*l_sb + j*l_sj + s*l_ss + sc_off).
+    int64_t sc_off;
 };
 
 // Most tokens one merge launch covers (the grid's second dimension).
 constexpr int64_t kMaxLaunchTokens = 65535;
 
-// Payload type of the merge input used only inside the library: fp32
-// partials (the MLA decode's split partials).  Never accepted from callers.
-constexpr int32_t kPayloadF32 = 100;
+// Payload type of the merge input used only inside the library: the MLA
+// decode's split partials, each row stored in fp16 after multiplication by
+// an exact power of two (chosen so that the row's largest magnitude lies in
+// [2^14, 2^15)), with the inverse factor stored beside the row's LSE.  The
+// merge multiplies a split's normalised weight by that factor.  Never
+// accepted from callers.
+constexpr int32_t kPayloadF16Scaled = 100;
 
-// Bytes of one payload element of a merge input type.
-inline int64_t payload_bytes(int32_t in_dtype) { return in_dtype == kPayloadF32 ? 4 : 2; }
+// Bytes of one payload element of a merge input type (every type is 16-bit).
+inline int64_t payload_bytes(int32_t) { return 2; }
 
 // The arguments `a` moved to start at token t0 and cover `tokens` tokens.
 MergeArgs merge_args_at(const MergeArgs& a, int64_t t0, int64_t tokens);
@@ -124,10 +131,10 @@ constexpr int kMlaMaxSplits = DCP_MAX_CP;  // ... nor above what the merge kerne
 // With one split the kernel writes the output of (b, shard s, head h) in the
 // element type to o + b*o_sb + (s*hq + h)*o_sh and its LSE to
 // lse + b*lse_sb + s*hq + h.  With several, split p writes its normalised
-// fp32 output and LSE as head u = p*cp*hq + s*hq + h of the scratch buffer,
-// part_o [B][nsplit*cp*hq][512] fp32 then part_lse [B][nsplit*cp*hq] fp32,
-// which the merge kernel then reduces over p (an LSE merge with nsplit
-// shards and cp*hq local heads, fp32 input) into o / lse.
+// output (kPayloadF16Scaled), LSE and scale as head u = p*cp*hq + s*hq + h of
+// the scratch buffer: part_o [B][nsplit*cp*hq][512] fp16, then part_lse and
+// part_scale [B][nsplit*cp*hq] fp32, which the merge kernel then reduces over
+// p (an LSE merge with nsplit shards and cp*hq local heads) into o / lse.
 // ------------------------------------------- variable-length work plan
 // With per-token lengths the split length cannot be fixed on the host: a
 // one-workgroup planning kernel reads seq_lens, picks a split length (in key
@@ -136,8 +143,9 @@ constexpr int kMlaMaxSplits = DCP_MAX_CP;  // ... nor above what the merge kerne
 // item per split of every pair (token, row block, shard), longest first --
 // into the scratch buffer.  Workgroup i of the decode kernel runs item i.  A
 // pair with one split writes its output directly; a pair with n > 1 splits
-// writes n fp32 partials to consecutive slots (kMlaRowsPerBlock rows of 512
-// each), which a reduction kernel merges.  Pair index
+// writes n scaled fp16 partials to consecutive slots (kMlaRowsPerBlock rows
+// of 512 each, with an LSE and a scale per row), which a reduction kernel
+// merges.  Pair index
 // q = (b * rb_per_token + row block) * cp + s.
 constexpr int kVarlenTarget = 256;       // splits over the whole batch (about one per compute unit)
 constexpr int kMlaMinSplitTiles = kMlaMinSplitKeys / kMlaKeysPerTile;  // shortest split
@@ -201,13 +209,14 @@ DCP_HD inline int varlen_bin(int32_t size, int32_t st) {
 }
 
 // Scratch layout of the variable-length producer: part_o [slots][128][512]
-// fp32, part_lse [slots][128] fp32, the header, the items, the split list.
+// fp16 (kPayloadF16Scaled), part_lse and part_scale [slots][128] fp32, the
+// header, the items, the split list.
 // With st >= total / target tiles per split the list holds at most
 // pairs + target items, fewer than target split pairs and fewer than
 // 2 * target partial slots (each split pair has more than st tiles).
 struct VarlenLayout {
     int64_t pairs, items, slots;
-    size_t off_lse, off_hdr, off_items, off_split, bytes;
+    size_t off_lse, off_scale, off_hdr, off_items, off_split, bytes;
 };
 VarlenLayout varlen_layout(int64_t B, int hq, int64_t T, int cp);
 
@@ -216,8 +225,9 @@ struct MlaArgs {
     const uint16_t* kv;     // token t at kv + t*kv_st, 576 columns
     uint16_t* o;
     float* lse;
-    float* part_o;          // nsplit > 1
+    uint16_t* part_o;       // nsplit > 1: kPayloadF16Scaled rows
     float* part_lse;
+    float* part_scale;      // the factor that undoes a partial row's scaling
     int64_t q_sb, q_sh, kv_st, o_sb, o_sh, lse_sb;
     int64_t part_sb;        // nsplit*cp*hq
     // Variable length (seq_lens != nullptr): token b attends over its own cache

@@ -130,9 +130,10 @@ struct F16 {
     }
 };
 
-// How a lane reads its 8 columns of one shard row and accumulates them.
-// 16-bit payloads (bf16, fp16): one 16-byte load.  fp32 payloads (the MLA
-// decode's split partials, inside the library only): two 16-byte loads.
+// How a lane reads its 8 columns of one shard row and accumulates them: one
+// 16-byte load.  kScaled: the row was stored multiplied by a power of two
+// (the MLA decode's split partials, fp16, inside the library only) and its
+// weight is multiplied by the factor stored sc_off floats after its LSE.
 // `zero` replaces the row by zeros -- a select on the loaded words, not a
 // branch, so the loads stay ahead of their use -- and the all-zero word is +0
 // in every payload type, so an empty shard adds exactly +0 whatever it held
@@ -144,8 +145,9 @@ __device__ __forceinline__ u32x4 load16(const u32x4* p) {
     return *p;
 }
 
-template <typename T, bool NT>
+template <typename T, bool NT, bool Scaled = false>
 struct Payload16 {
+    static constexpr bool kScaled = Scaled;
     typedef u32x4 row_t;
     static __device__ __forceinline__ row_t load(const void* base, int64_t off) {
         return load16<NT>(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off));
@@ -161,36 +163,6 @@ struct Payload16 {
         for (int i = 0; i < 4; ++i) {
             acc[2 * i] = fmaf(w, T::lo(v[i]), acc[2 * i]);
             acc[2 * i + 1] = fmaf(w, T::hi(v[i]), acc[2 * i + 1]);
-        }
-    }
-};
-
-template <bool NT>
-struct PayloadF32 {
-    struct row_t {
-        u32x4 a, b;
-    };
-    static __device__ __forceinline__ row_t load(const void* base, int64_t off) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + off);
-        row_t r;
-        r.a = load16<NT>(p);
-        r.b = load16<NT>(p + 1);
-        return r;
-    }
-    static __device__ __forceinline__ row_t zero_unless(bool use, row_t v) {
-        row_t z;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            z.a[i] = use ? v.a[i] : 0u;
-            z.b[i] = use ? v.b[i] : 0u;
-        }
-        return z;
-    }
-    static __device__ __forceinline__ void fma(float (&acc)[8], float w, row_t v) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[i] = fmaf(w, __uint_as_float(v.a[i]), acc[i]);
-            acc[4 + i] = fmaf(w, __uint_as_float(v.b[i]), acc[4 + i]);
         }
     }
 };
@@ -235,12 +207,13 @@ struct MergeTail {
     uint16_t* out;
     float* out_lse;
     int64_t o_sb, o_sj, ol_sb;
+    int64_t sc_off;  // scaled payloads: the factors, in floats after the LSEs
     float to_log2, from_log2;
     int32_t cp;
 };
 
 MergeTail tail_of(const MergeArgs& a) {
-    return MergeTail{a.out, a.out_lse, a.o_sb, a.o_sj, a.ol_sb, a.to_log2, a.from_log2, a.cp};
+    return MergeTail{a.out, a.out_lse, a.o_sb, a.o_sj, a.ol_sb, a.sc_off, a.to_log2, a.from_log2, a.cp};
 }
 
 // Weights of one row from the LSE held by lane s (lanes >= cp hold -inf).
@@ -302,9 +275,12 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const void* attn, const f
     // one batch of scalar loads, rather than a second batch after the
     // payload loads are issued.
     __builtin_amdgcn_sched_barrier(0);
-    float x[CP];
+    float x[CP], sc[CP];
 #pragma unroll
-    for (int s = 0; s < CP; ++s) x[s] = lrow[static_cast<int64_t>(s) * l_ss];
+    for (int s = 0; s < CP; ++s) {
+        x[s] = lrow[static_cast<int64_t>(s) * l_ss];
+        if (In::kScaled) sc[s] = lrow[static_cast<int64_t>(s) * l_ss + t.sc_off];
+    }
     typename In::row_t v[CP];
 #pragma unroll
     for (int s = 0; s < CP; ++s) v[s] = In::load(attn, orow + static_cast<int64_t>(s) * a_ss);
@@ -327,6 +303,7 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const void* attn, const f
 #pragma unroll
     for (int s = 0; s < CP; ++s) {
         w[s] *= inv;
+        if (In::kScaled) w[s] *= sc[s];
         dense = dense && (w[s] != 0.0f);
     }
 
@@ -353,8 +330,10 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_wide(const void* attn, co
     const int cp = t.cp;
 
     const int ls = lane < cp ? lane : cp - 1;
-    const float xl = lse[static_cast<int64_t>(r.b) * l_sb + static_cast<int64_t>(r.j) * l_sj +
-                         static_cast<int64_t>(ls) * l_ss];
+    const float* ll = lse + static_cast<int64_t>(r.b) * l_sb + static_cast<int64_t>(r.j) * l_sj +
+                      static_cast<int64_t>(ls) * l_ss;
+    const float xl = ll[0];
+    const float scl = In::kScaled ? ll[t.sc_off] : 1.0f;
     const int64_t orow = static_cast<int64_t>(r.b) * a_sb + static_cast<int64_t>(r.j) * a_sj + lane * 8;
     typename In::row_t v[G];
 #pragma unroll
@@ -363,7 +342,8 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_wide(const void* attn, co
 
     const float x = lane < cp ? xl : -INFINITY;
     float M, S;
-    const float wn = row_weights<64>(t.to_log2, x, cp, M, S);
+    float wn = row_weights<64>(t.to_log2, x, cp, M, S);
+    if (In::kScaled) wn *= scl;
 
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < cp; s0 += G) {
@@ -424,11 +404,11 @@ void launch_typed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
 template <bool NT>
 void launch_policy(const MergeArgs& a, dim3 grid, hipStream_t stream) {
     const bool f16_out = a.dtype == DCP_DTYPE_FP16;
-    if (a.in_dtype == kPayloadF32) {
+    if (a.in_dtype == kPayloadF16Scaled) {
         if (f16_out)
-            launch_typed<PayloadF32<NT>, F16>(a, grid, stream);
+            launch_typed<Payload16<F16, NT, true>, F16>(a, grid, stream);
         else
-            launch_typed<PayloadF32<NT>, Bf16>(a, grid, stream);
+            launch_typed<Payload16<F16, NT, true>, Bf16>(a, grid, stream);
     } else if (f16_out) {
         launch_typed<Payload16<F16, NT>, F16>(a, grid, stream);
     } else {

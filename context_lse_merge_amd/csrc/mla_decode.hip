@@ -56,9 +56,10 @@
 //    the sum uses the fp32 p.
 //  * Split-KV: shards are split into key ranges so that about 256 workgroups
 //    (one per compute unit) exist even at B = 1; each split leaves its
-//    normalised fp32 output and LSE in the scratch buffer, and the merge
-//    kernel of dcp_lse_combine (its fp32-input instance) reduces the splits
-//    of each (token, shard, head) exactly as it merges DCP shards.  With a
+//    normalised output (fp16, scaled per row by a power of two, the inverse
+//    factor stored with the LSE) and its LSE in the scratch buffer, and the
+//    merge kernel of dcp_lse_combine (its scaled-fp16 instance) reduces the
+//    splits of each (token, shard, head) exactly as it merges DCP shards.  With a
 //    single split the kernel writes the final output and LSE itself.  With
 //    per-token lengths (seq_lens) the splits are sized on the device instead
 //    and the workgroup runs one item of a work list (mla_varlen.hip).
@@ -519,16 +520,28 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     const float l_run = st.l_run;
     const float m_run = st.m_run;
     const float l_tot = sum_xor32(sum_xor16(l_run));
+    const bool direct = a.seq_lens ? wk.slot < 0 : a.nsplit == 1;
+    float amax = 0.0f;  // several splits: the row's largest accumulator magnitude
+    if (!direct) {
+#pragma unroll
+        for (int t = 0; t < kDTiles; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st.oacc[t][i]));
+        amax = max_xor32(max_xor16(amax));
+    }
     if (!valid) return;
 
     // O / l and the LSE in the caller's base; an empty shard or split gives 0
     // and -inf.  One split: the element type, straight into o_part / lse_part.
-    // Several: fp32 into the scratch -- as head p*cp*hq + s*hq + h, for the
-    // merge kernel to reduce over the splits, or with seq_lens as row
-    // wave*16 + r16 of the item's slot, for the split reduction.
+    // Several: into the scratch -- as head p*cp*hq + s*hq + h, for the merge
+    // kernel to reduce over the splits, or with seq_lens as row wave*16 + r16
+    // of the item's slot, for the split reduction -- in fp16, the row
+    // multiplied by 2^k so that its largest magnitude lies in [2^14, 2^15)
+    // (fp16 then carries 11 significant bits relative to the row's largest
+    // value), with 2^-k stored beside the LSE.
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * a.lse_scale : -INFINITY;
-    if (a.seq_lens ? wk.slot < 0 : a.nsplit == 1) {
+    if (direct) {
         const int64_t u = static_cast<int64_t>(wk.s) * a.hq + h;
         uint16_t* orow = a.o + b * a.o_sb + u * a.o_sh + ocol;
 #pragma unroll
@@ -540,16 +553,28 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
         }
         if (g == 0) a.lse[b * a.lse_sb + u] = lse;
     } else {
-        int64_t prow_idx;  // fp32 row of the scratch
+        int64_t prow_idx;  // partial row of the scratch
         if (a.seq_lens)
             prow_idx = static_cast<int64_t>(wk.slot) * kMlaRowsPerBlock + wave * kRowsPerWave + r16;
         else
             prow_idx = b * a.part_sb + (static_cast<int64_t>(wk.p) * a.cp + wk.s) * a.hq + h;
-        float* prow = a.part_o + prow_idx * kDv + ocol;
+        // amax * inv = m 2^e with m in [0.5, 1): k = 15 - e.  Capped at 100
+        // so that 2^-k stays a normal float (rows below 2^-85 keep fewer bits;
+        // an all-zero row gets k = 15).  1/l <= 1, so inv * 2^k stays finite.
+        const int k = min(15 - __builtin_amdgcn_frexp_expf(amax * inv), 100);
+        const float mul = __builtin_amdgcn_ldexpf(inv, k);
+        uint16_t* prow = a.part_o + prow_idx * kDv + ocol;
 #pragma unroll
-        for (int t = 0; t < kDTiles; ++t)
-            *reinterpret_cast<f32x4*>(prow + 64 * (t >> 2) + 8 * (t & 3)) = st.oacc[t] * inv;
-        if (g == 0) a.part_lse[prow_idx] = lse;
+        for (int t = 0; t < kDTiles; ++t) {
+            const f32x4 v = st.oacc[t];
+            const uint32_t lo = to_bits<F16>(v[0] * mul) | (to_bits<F16>(v[1] * mul) << 16);
+            const uint32_t hi = to_bits<F16>(v[2] * mul) | (to_bits<F16>(v[3] * mul) << 16);
+            *reinterpret_cast<uint2*>(prow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
+        }
+        if (g == 0) {
+            a.part_lse[prow_idx] = lse;
+            a.part_scale[prow_idx] = __builtin_amdgcn_ldexpf(1.0f, -k);
+        }
     }
 }
 

@@ -19,12 +19,15 @@
 //    splits start first and the short ones fill in behind them, the
 //    longest-processing-time-first order of list scheduling;
 //  * a pair with a single split writes its output straight into o_part /
-//    lse_part; a pair with several leaves one normalised fp32 partial per
-//    split in consecutive slots, and the reduction kernel below merges them.
+//    lse_part; a pair with several leaves one normalised partial per split
+//    in consecutive slots (fp16, each row scaled by a power of two whose
+//    inverse is stored beside its LSE), and the reduction kernel below
+//    merges them.
 // The reduction forms the weights exactly as the merge kernel of
 // dcp_lse_combine does (sequential maximum and sum in ascending split order,
-// normalised weights, fp32 FMAs in ascending split order), so a pair split
-// at the same boundaries gives the same bits on either path.  Which
+// normalised weights times the rows' scale factors, fp32 FMAs in ascending
+// split order), so a pair split at the same boundaries gives the same bits
+// on either path.  Which
 // workgroup runs which split, and which slots a pair gets, depend on the
 // order of LDS atomics; the arithmetic of a split does not, so the results
 // are deterministic.
@@ -40,7 +43,6 @@ namespace {
 
 constexpr int kBins = kMlaPlanThreads;
 constexpr int kReduceWaves = 4;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int32_t token_len(const MlaArgs& a, int32_t b) {
@@ -132,6 +134,14 @@ __global__ __launch_bounds__(kMlaPlanThreads) void varlen_plan_kernel(MlaArgs a)
     if (tid == 0) a.vl_hdr->n_split = s_split;
 }
 
+// The two fp16 halves of a 32-bit word, widened (exactly) to fp32.
+__device__ __forceinline__ float half_lo(uint32_t w) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float x, float y);
 template <>
@@ -166,7 +176,8 @@ __global__ __launch_bounds__(64 * kReduceWaves) void varlen_reduce_kernel(MlaArg
 
     const int64_t row0 = static_cast<int64_t>(sp.first) * kMlaRowsPerBlock + r;  // slot `first`, row r
     const float* lse = a.part_lse + row0;                                          // split p at p * 128
-    const float* po = a.part_o + row0 * kMlaVDim + 8 * lane;                       // split p at p * 128 * 512
+    const float* scl = a.part_scale + row0;
+    const uint16_t* po = a.part_o + row0 * kMlaVDim + 8 * lane;                    // split p at p * 128 * 512
     const int64_t o_step = static_cast<int64_t>(kMlaRowsPerBlock) * kMlaVDim;
     const int n = sp.n;
 
@@ -180,26 +191,25 @@ __global__ __launch_bounds__(64 * kReduceWaves) void varlen_reduce_kernel(MlaArg
     const float inv = (S > 0.0f) ? __builtin_amdgcn_rcpf(S) : 0.0f;
 
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    constexpr int kBatch = 4;  // splits whose loads are in flight together
+    constexpr int kBatch = 8;  // splits whose loads are in flight together
     for (int p0 = 0; p0 < n; p0 += kBatch) {
-        f32x4 v[kBatch][2];
+        u32x4 v[kBatch];
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             const int p = p0 + i < n ? p0 + i : n - 1;
-            const f32x4* src = reinterpret_cast<const f32x4*>(po + p * o_step);
-            v[i][0] = src[0];
-            v[i][1] = src[1];
+            v[i] = *reinterpret_cast<const u32x4*>(po + p * o_step);
         }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             if (p0 + i >= n) break;
             const float x = lse[(p0 + i) * kMlaRowsPerBlock];
-            const float w = ((x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x - M) * to_log2)) * inv;
+            float w = ((x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x - M) * to_log2)) * inv;
+            w *= scl[(p0 + i) * kMlaRowsPerBlock];  // undoes the row's power-of-two scaling
             if (w == 0.0f) continue;  // an empty split adds +0 whatever its slot holds
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                acc[k] = fmaf(w, v[i][0][k], acc[k]);
-                acc[4 + k] = fmaf(w, v[i][1][k], acc[4 + k]);
+                acc[2 * k] = fmaf(w, half_lo(v[i][k]), acc[2 * k]);
+                acc[2 * k + 1] = fmaf(w, half_hi(v[i][k]), acc[2 * k + 1]);
             }
         }
     }

@@ -188,10 +188,13 @@ int dcp_lse_combine(dcp_workspace* ws, const void* attn, int64_t B, int H, int64
  * scratch   device buffer of at least dcp_mla_partial_decode_scratch_size()
  *           bytes, 16-byte aligned, for the split-KV partials: when a shard's
  *           keys are split over several workgroups, each split's normalised
- *           output (fp32, so the split reduction adds no 16-bit rounding)
- *           and LSE land here and are merged into o_part / lse_part by the
- *           merge kernel of dcp_lse_combine, reading fp32 payloads.  NULL
- *           allowed when the size is 0 (one split per shard).  Contents on
+ *           output and LSE land here and are merged into o_part / lse_part
+ *           by the merge kernel of dcp_lse_combine.  A partial row is stored
+ *           in fp16 after multiplication by a power of two that puts its
+ *           largest magnitude in [2^14, 2^15), with the inverse factor beside
+ *           its LSE, so it keeps 11 significant bits relative to the row's
+ *           largest value whatever the values' range (1032 bytes per row).
+ *           NULL allowed when the size is 0 (one split per shard).  Contents on
  *           entry are ignored.  A scratch buffer serves one call at a time:
  *           calls that may overlap (on other streams) need buffers of their
  *           own.
@@ -240,8 +243,8 @@ int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64
  *           B > 0), 16-byte aligned.  The key splits are sized on the device
  *           from the actual lengths: a planning kernel writes a work list
  *           (longest split first) into the scratch, and splits of a (token,
- *           shard) leave fp32 partials there that a reduction kernel merges
- *           into o_part / lse_part.  Contents on entry are ignored; one
+ *           shard) leave partials there (scaled fp16 rows, as above) that a
+ *           reduction kernel merges into o_part / lse_part.  Contents on entry are ignored; one
  *           call at a time per buffer, as for dcp_mla_partial_decode.
  * Other arguments, strides, alignment (kv_sb a multiple of 8 elements too),
  * arithmetic and errors as dcp_mla_partial_decode.  A workgroup serves the

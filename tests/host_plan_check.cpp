@@ -69,6 +69,41 @@ static void check_varlen_plan(const std::vector<int64_t>& lens, int hq, int64_t 
     CHECK(lay.pairs == B * rbt * cp && lay.items == lay.pairs + dcp::kVarlenTarget);
     CHECK(lay.off_hdr % 64 == 0 && lay.off_items % 16 == 0 && lay.off_split % 16 == 0);
     CHECK(lay.bytes == lay.off_split + dcp::kVarlenTarget * sizeof(dcp::VarlenSplit));
+    // fp16 partial rows, then one LSE and one scale per row, then the plan.
+    const size_t rows = static_cast<size_t>(lay.slots) * dcp::kMlaRowsPerBlock;
+    CHECK(lay.off_lse == rows * dcp::kMlaVDim * 2 && lay.off_scale == lay.off_lse + rows * 4);
+    CHECK(lay.off_hdr >= lay.off_scale + rows * 4);
+}
+
+// The fixed-length producer's split scratch: fp16 rows [B][nsplit*cp*hq][512],
+// then part_lse and part_scale [B][nsplit*cp*hq], and the merge over splits
+// reading them as a scaled-fp16 payload.
+static void fixed_split_checks() {
+    const int64_t B = 3, T = 131072;
+    const int hq = 128, cp = 4;
+    int32_t nsplit;
+    int64_t split_len;
+    size_t need;
+    dcp::mla_split(B, hq, T, cp, &nsplit, &split_len, &need);
+    CHECK(nsplit > 1);
+    const int64_t heads = static_cast<int64_t>(nsplit) * cp * hq;
+    CHECK(need == static_cast<size_t>(B * heads) * (dcp::kMlaVDim * 2 + 8));
+    const uintptr_t q = uintptr_t{1} << 40, kv = uintptr_t{2} << 40, o = uintptr_t{3} << 40,
+                    l = uintptr_t{4} << 40, scr = uintptr_t{6} << 40;
+    dcp::MlaPlan plan;
+    CHECK(dcp::plan_mla(fake(q), B, hq, hq * 576, 576, fake(kv), T, 576, nullptr, DCP_DTYPE_BF16, cp, 0.07f,
+                        DCP_LSE_BASE_E, fake(o), cp * hq * 512, 512, reinterpret_cast<float*>(l), cp * hq, fake(scr),
+                        need, &plan) == DCP_OK);
+    CHECK(reinterpret_cast<uintptr_t>(plan.args.part_o) == scr);
+    CHECK(reinterpret_cast<uintptr_t>(plan.args.part_lse) == scr + B * heads * dcp::kMlaVDim * 2);
+    CHECK(plan.args.part_scale == plan.args.part_lse + B * heads);
+    CHECK(reinterpret_cast<uintptr_t>(plan.args.part_scale + B * heads) == scr + need);
+    CHECK(plan.reduce.in_dtype == dcp::kPayloadF16Scaled && plan.reduce.sc_off == B * heads);
+    CHECK(plan.reduce.attn == plan.args.part_o && plan.reduce.lse == plan.args.part_lse);
+    CHECK(plan.reduce.cp == nsplit && plan.reduce.h_local == cp * hq && plan.reduce.a_sb == heads * dcp::kMlaVDim);
+    CHECK(dcp::plan_mla(fake(q), B, hq, hq * 576, 576, fake(kv), T, 576, nullptr, DCP_DTYPE_BF16, cp, 0.07f,
+                        DCP_LSE_BASE_E, fake(o), cp * hq * 512, 512, reinterpret_cast<float*>(l), cp * hq, fake(scr),
+                        need - 1, &plan) == DCP_ERR_WORKSPACE);
 }
 
 // The plan's 32-bit shard sizes against their plain 64-bit definition.
@@ -138,6 +173,7 @@ static void varlen_plan_checks() {
                         lay.bytes, &plan) == DCP_OK);
     CHECK(plan.varlen && plan.blocks == lay.items && plan.args.slots == lay.slots);
     CHECK(reinterpret_cast<uintptr_t>(plan.args.part_lse) == scr + lay.off_lse);
+    CHECK(reinterpret_cast<uintptr_t>(plan.args.part_scale) == scr + lay.off_scale);
     CHECK(reinterpret_cast<uintptr_t>(plan.args.vl_hdr) == scr + lay.off_hdr);
     CHECK(reinterpret_cast<uintptr_t>(plan.args.vl_items) == scr + lay.off_items);
     CHECK(reinterpret_cast<uintptr_t>(plan.args.vl_splits) == scr + lay.off_split);
@@ -275,6 +311,7 @@ int main() {
     CHECK(std::strcmp(dcp_status_string(DCP_ERR_ALIGN), "DCP_ERR_ALIGN") == 0);
 
     varlen_plan_checks();
+    fixed_split_checks();
 
     if (g_failures) {
         std::fprintf(stderr, "%d check(s) failed\n", g_failures);

@@ -116,7 +116,7 @@ def test_tiny_two_shards_of_64_rows(mode):
 
 @pytest.mark.parametrize("B,hq,T,cp", [(2, 128, 4096, 4), (1, 128, 16384, 4), (3, 16, 1000, 4), (5, 24, 777, 3)])
 def test_split_kv_shapes(B, hq, T, cp):
-    """Several splits per shard (fp32 partials + reduction), ragged T, row counts that
+    """Several splits per shard (scaled fp16 partials + reduction), ragged T, row counts that
     are not a multiple of 64, odd cp."""
     q, kv = synth.mla_decode(B, T=T, hq=hq, seed=2000 + T)
     o, l = run_producer(q, kv, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E)
