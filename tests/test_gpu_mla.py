@@ -126,6 +126,31 @@ def test_split_kv_shapes(B, hq, T, cp):
     check_end_to_end(q, kv, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
 
 
+def _rescaled(q, kv, s):
+    """q * 2^-s and kv * 2^s: exact in bf16 (an exponent shift), and every score q.k is unchanged."""
+    q2 = (q.float() * 2.0 ** -s).to(q.dtype)
+    kv2 = (kv.float() * 2.0 ** s).to(kv.dtype)
+    assert torch.equal(q2.float() * 2.0 ** s, q.float()) and torch.equal(kv2.float() * 2.0 ** -s, kv.float())
+    return q2, kv2
+
+
+@pytest.mark.parametrize("s", [20, -20, 60, -60])
+def test_split_partials_keep_their_bits_under_power_of_two_rescaling(s):
+    """With the cache scaled by 2^s and the queries by 2^-s every score is unchanged and every value is 2^s times
+    larger, so o_part must be exactly 2^s times the unscaled result and lse_part identical, bit for bit -- including
+    |s| = 60, where the split partials' values (about 2^60 or 2^-60) lie far outside fp16's range: each partial row
+    is stored with its own power-of-two factor."""
+    B, hq, T, cp = 1, 128, 16384, 4      # 16 splits of 256 keys per shard
+    assert dcp.dcp_mla_partial_decode_scratch_size(B, hq, T, cp) > 0
+    q, kv = synth.mla_decode(B, T=T, hq=hq, seed=2400)
+    o1, l1 = run_producer(q, kv, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E)
+    q2, kv2 = _rescaled(q, kv, s)
+    o2, l2 = run_producer(q2, kv2, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E)
+    assert torch.equal(l1, l2)
+    assert torch.equal(o2.float() * 2.0 ** -s, o1.float())
+    assert torch.isfinite(o2.float()).all()
+
+
 def test_empty_shards_give_zero_and_minus_inf():
     q, kv = synth.mla_decode(2, T=3, hq=16, seed=77)   # 3 keys over 4 shards: shard 0 is empty
     o, l = run_producer(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_2)

@@ -174,6 +174,27 @@ def test_full_size_shared_cache_random_lengths_interleaved():
     check(q, kv, seq, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
 
 
+def test_split_partials_keep_their_bits_under_power_of_two_rescaling():
+    """Per-token caches scaled by 2^s_b (s_b = 40, -40, 0; queries by 2^-s_b): scores are unchanged, so each token's
+    o_part rows must be exactly 2^s_b times the unscaled ones and lse_part identical, bit for bit, through the split
+    path (scaled fp16 partials in slots, then the split reduction), whatever the values' range."""
+    B, hq, T, cp = 3, 128, 12000, 4
+    q, kv = _caches(2500, B, hq, T)
+    seq = [12000, 9000, 11000]
+    assert dcp.dcp_mla_partial_decode_varlen_scratch_size(B, hq, T, cp) > 0
+    o1, l1 = run_varlen(q, kv, seq, T, dcp.DCP_KV_INTERLEAVED, cp, dcp.DCP_LSE_BASE_E)
+    sh = [40, -40, 0]
+    q2 = torch.stack([(q[b].float() * 2.0 ** -sh[b]).to(q.dtype) for b in range(B)])
+    kv2 = torch.stack([(kv[b].float() * 2.0 ** sh[b]).to(kv.dtype) for b in range(B)])
+    for b in range(B):
+        assert torch.equal(kv2[b].float() * 2.0 ** -sh[b], kv[b].float())
+        assert torch.equal(q2[b].float() * 2.0 ** sh[b], q[b].float())
+    o2, l2 = run_varlen(q2, kv2, seq, T, dcp.DCP_KV_INTERLEAVED, cp, dcp.DCP_LSE_BASE_E)
+    assert torch.equal(l1, l2)
+    for b in range(B):
+        assert torch.equal(o2[b].float() * 2.0 ** -sh[b], o1[b].float())
+
+
 def test_argument_errors():
     q, kv = _caches(706, 2, 16, 64)
     o = torch.empty((2, 64, 512), dtype=torch.bfloat16, device=DEV)
