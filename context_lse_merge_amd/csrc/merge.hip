@@ -29,7 +29,10 @@
 //  * fp32 FMAs in ascending shard order, then the hardware round-to-nearest-
 //    even convert to the payload type and one 16-byte store per lane.  The
 //    payload is bf16 or fp16 (both are the pages' payload types); one kernel
-//    instance per type, differing only in the widening and narrowing.
+//    instance per type, differing only in the widening and narrowing.  A
+//    third instance, inside the library only, reduces the MLA decode's split
+//    partials: fp16 rows stored multiplied by a power of two, whose inverse
+//    factor (read beside the LSE) multiplies the split's normalised weight.
 // The per-element arithmetic does not depend on B, on the chunking or on the
 // grid, so chunked and unchunked calls give identical bits.
 #include <hip/hip_runtime.h>
