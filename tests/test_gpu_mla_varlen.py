@@ -195,6 +195,24 @@ def test_split_partials_keep_their_bits_under_power_of_two_rescaling():
         assert torch.equal(o2[b].float() * 2.0 ** -sh[b], o1[b].float())
 
 
+def test_large_batch_of_short_tokens_with_a_few_long_ones():
+    """3000 tokens over one 131072-row cache: most lengths in [0, 2000] (some empty), ten full-length tokens whose
+    shards are split; 12000 (token, shard) pairs, so every thread of the planning workgroup loops over many pairs and
+    the work list holds over 12000 items.  Sampled rows against the oracle, every row through the merge."""
+    _, kv = synth.mla_decode(1)
+    B, hq, cp = 3000, 16, 4
+    q = synth.normal_bf16((B, hq, 576), synth.gen(3400))
+    rng = np.random.default_rng(3400)
+    seq = rng.integers(0, 2001, B).astype(np.int32)
+    long_tokens = rng.choice(B, 10, replace=False)
+    seq[long_tokens] = 131072
+    seq[:3] = [0, 1, 2000]
+    o, l = run_varlen(q, kv, seq, 131072, dcp.DCP_KV_INTERLEAVED, cp, dcp.DCP_LSE_BASE_E)
+    rows = np.unique(np.concatenate([[0, 1, 16, 32, 47, B * hq - 1], long_tokens[:4] * hq + 5,
+                                     rng.integers(0, B * hq, 12)]))
+    check(q, kv, seq, dcp.DCP_KV_INTERLEAVED, cp, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
+
+
 def test_argument_errors():
     q, kv = _caches(706, 2, 16, 64)
     o = torch.empty((2, 64, 512), dtype=torch.bfloat16, device=DEV)
