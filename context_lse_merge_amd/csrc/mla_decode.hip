@@ -51,9 +51,10 @@
 //    V[key][d0 + 4(j%4)] of four keys receive a column of V^T.
 //  * Online softmax in base 2 (scale * log2 e folded into one multiply); the
 //    row max is a 4-lane reduction per tile, the row sum stays lane-partial
-//    until the end, and the output accumulators are rescaled only on tiles
-//    where some row's maximum grew.  p is rounded to bf16 for the p.v MFMA;
-//    the sum uses the fp32 p.
+//    until the end, and the reference maximum moves (rescaling the output
+//    accumulators) only when some row's score exceeds it by more than 8
+//    (log2 units), so p stays at most 256.  p is rounded to bf16 for the p.v MFMA; the sum
+//    uses the fp32 p.
 //  * Split-KV: shards are split into key ranges so that about 256 workgroups
 //    (one per compute unit) exist even at B = 1; each split leaves its
 //    normalised output (fp16, scaled per row by a power of two, the inverse
@@ -285,6 +286,10 @@ struct RowState {
     float m_run, l_run;
 };
 
+// The running maximum of the online softmax lags the true one by at most
+// this much (log2 units): p <= 2^8.
+constexpr float kLazyLog2 = 8.0f;
+
 // One 32-key tile: scores, online softmax, p.v.
 template <typename T>
 __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* kt, const LaneOffsets& off,
@@ -331,21 +336,27 @@ __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* k
     float tmax = z[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
-    tmax = max_xor32(max_xor16(tmax));
-    const float m_new = fmaxf(st.m_run, tmax);  // finite: the tile has a valid key
-    if (__any(m_new > st.m_run)) {
-        // Some row's maximum grew: rescale the accumulators (alpha = 1 for the others).
-        const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);  // 0 on the first tile
+    tmax = max_xor32(max_xor16(tmax));  // finite: the tile has a valid key
+    // Lazy rescaling: the running maximum m_run (the reference of the
+    // exponentials) moves only when some row's tile maximum exceeds it by
+    // more than kLazyLog2; otherwise the tile's p = 2^(z - m_run) stay below
+    // 2^kLazyLog2 (safe in the 16-bit p and the fp32 sums), and O / l and
+    // m_run + log2 l do not depend on which reference was used.  Rescaling
+    // the 128 accumulators then happens on the first tile of a split and
+    // rarely after, instead of on every tile where some row's maximum grows.
+    if (__any(tmax > st.m_run + kLazyLog2)) {
+        const float m_new = fmaxf(st.m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);  // 0 on the first tile, 1 for unchanged rows
         st.l_run *= alpha;
 #pragma unroll
         for (int t = 0; t < kDTiles; ++t) st.oacc[t] *= alpha;
+        st.m_run = m_new;
     }
-    st.m_run = m_new;
     float psum = 0.0f;
     typename T::v8 pb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(z[i] - m_new);
+        const float p = __builtin_amdgcn_exp2f(z[i] - st.m_run);
         psum += p;
         pb[i] = static_cast<typename T::elem>(p);
     }
