@@ -318,7 +318,7 @@ def producer_flops(B, hq, T):
     return 2.0 * B * hq * T * (576 + 512)
 
 
-def measure_producer(B, kv_copies, reps=10, seq_lens=None):
+def measure_producer(B, kv_copies, reps=8, seq_lens=None, replays=5):
     """dcp_mla_partial_decode (+ the merge of its output) on the full-size MLA
     decode workload: q [B,128,576], one 131072 x 576 cache, 4 shards.  The cache
     is rotated over `kv_copies` device copies (>= 1 GiB together) so every call
@@ -326,7 +326,12 @@ def measure_producer(B, kv_copies, reps=10, seq_lens=None):
     variable-length entry point runs instead: every token up to its own length,
     interleaved ownership, over the shared cache (kv_sb = 0) or, when the
     copies are [B, T, 576], over its own cache.  q, the cache and the outputs
-    take the cache's dtype.  Returns (producer us, merge us)."""
+    take the cache's dtype.  Both steps are timed as a serving decode loop runs
+    them, captured in HIP graphs: one graph of `reps` producer calls (each cache
+    copy in turn) and one of `reps` merges of its output, each replayed
+    `replays` times with HIP events around every replay on the stream it is
+    launched on.
+    Returns (producer us, merge us) per call, medians over the replays."""
     import torch
     import context_lse_merge_amd as dcp
     import synth
@@ -343,7 +348,9 @@ def measure_producer(B, kv_copies, reps=10, seq_lens=None):
     else:
         nbytes = dcp.dcp_mla_partial_decode_varlen_scratch_size(B, hq, T, cp)
     scratch = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
-    ws = dcp.dcp_workspace_create(B, hq, cp, dtype=dcp.DCP_DTYPE_FP16 if dtype == torch.float16 else dcp.DCP_DTYPE_BF16)
+    stream = torch.cuda.Stream()
+    ws = dcp.dcp_workspace_create(B, hq, cp, dtype=dcp.DCP_DTYPE_FP16 if dtype == torch.float16 else dcp.DCP_DTYPE_BF16,
+                                  stream=stream)
     dcp.dcp_workspace_set_load_policy(ws, dcp.DCP_LOAD_CACHED)   # the partials were just written
 
     def produce(kv):
@@ -352,21 +359,41 @@ def measure_producer(B, kv_copies, reps=10, seq_lens=None):
         else:
             dcp.dcp_mla_partial_decode_varlen(q, kv, seq_lens, T, dcp.DCP_KV_INTERLEAVED, cp, synth.MLA_SCALE,
                                               dcp.DCP_LSE_BASE_E, o, l, scratch)
-    for k in range(2):
-        produce(kv_copies[k % len(kv_copies)])
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps + 1)]
-    ev[0].record()
-    for r in range(reps):
-        produce(kv_copies[r % len(kv_copies)])
-        ev[2 * r + 1].record()
+
+    def merge():
         dcp.dcp_lse_combine(ws, o, l, dcp.DCP_LSE_BH1, dcp.DCP_LSE_BASE_E, out, out_lse)
-        ev[2 * r + 2].record()
+
+    with torch.cuda.stream(stream):       # eager passes on the capture stream first
+        for k in range(2):
+            produce(kv_copies[k % len(kv_copies)])
+            merge()
     torch.cuda.synchronize()
-    prod = sorted(ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(reps))
-    merge = sorted(ev[2 * r + 1].elapsed_time(ev[2 * r + 2]) for r in range(reps))
+    g_prod, g_merge = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_prod, stream=stream):
+        for r in range(reps):
+            produce(kv_copies[r % len(kv_copies)])
+    with torch.cuda.graph(g_merge, stream=stream):
+        for r in range(reps):
+            merge()
+    torch.cuda.synchronize()
+
+    def per_call_us(g):
+        g.replay()                        # warm-up replay
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(replays):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()                   # a replay runs on the current stream
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[replays // 2] * 1000.0 / reps
+
+    prod, mrg = per_call_us(g_prod), per_call_us(g_merge)
+    del g_prod, g_merge
     ws.close()
-    return prod[reps // 2] * 1000.0, merge[reps // 2] * 1000.0
+    return prod, mrg
 
 
 def producer_leg(Bs):
