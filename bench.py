@@ -328,9 +328,10 @@ def measure_producer(B, kv_copies, reps=8, seq_lens=None, replays=5):
     copies are [B, T, 576], over its own cache.  q, the cache and the outputs
     take the cache's dtype.  Both steps are timed as a serving decode loop runs
     them, captured in HIP graphs: one graph of `reps` producer calls (each cache
-    copy in turn) and one of `reps` merges of its output, each replayed
-    `replays` times with HIP events around every replay on the stream it is
-    launched on.
+    copy in turn) and one of `reps` merges of its output, each warmed up for
+    about 50 ms and then replayed at least `replays` times (and for at least
+    20 ms) with HIP events around every replay on the stream it is launched
+    on.
     Returns (producer us, merge us) per call, medians over the replays."""
     import torch
     import context_lse_merge_amd as dcp
@@ -378,17 +379,26 @@ def measure_producer(B, kv_copies, reps=8, seq_lens=None, replays=5):
     torch.cuda.synchronize()
 
     def per_call_us(g):
-        g.replay()                        # warm-up replay
+        # Warm up for about 50 ms of this work: the first ~20 ms of sustained
+        # load run measurably slower (seen in eager and graph runs alike).
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        once_ms = max(e0.elapsed_time(e1), 1e-3)
+        for _ in range(int(math.ceil(50.0 / once_ms))):
+            g.replay()
         torch.cuda.synchronize()
         ts = []
-        for _ in range(replays):
+        for _ in range(max(replays, int(math.ceil(20.0 / once_ms)))):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()                   # a replay runs on the current stream
             g.replay()
             e1.record()
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
-        return sorted(ts)[replays // 2] * 1000.0 / reps
+        return sorted(ts)[len(ts) // 2] * 1000.0 / reps
 
     prod, mrg = per_call_us(g_prod), per_call_us(g_merge)
     del g_prod, g_merge
