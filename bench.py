@@ -639,6 +639,8 @@ def main():
         "producer": {"workload": "MLA split-KV decode, q [B,128,576] bf16, latent KV cache 131072 x 576 bf16 in "
                                  "4 contiguous shards, scale 1/sqrt(192), then the merge of its partials",
                      "bound": "mfma (B >= 2), hbm (B = 1)", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                     "timing": "HIP graphs of 8 calls (each of 8 cache copies once) and of 8 merges, replayed "
+                               "for ~50 ms of warm-up, then timed per replay; median replay / 8",
                      "rows": producer, "cpu_baseline": producer_cpu},
     }
     print(json.dumps(line), flush=True)
