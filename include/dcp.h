@@ -199,8 +199,9 @@ int dcp_lse_combine(dcp_workspace* ws, const void* attn, int64_t B, int H, int64
  *           calls that may overlap (on other streams) need buffers of their
  *           own.
  * Arithmetic: MFMA products of the 16-bit inputs with fp32 accumulation for
- * q.k and p.v, fp32 online softmax; p is rounded to dtype before the p.v
- * product.
+ * q.k and p.v, fp32 online softmax whose reference maximum is moved only when
+ * a score exceeds it by more than 8 (log2 units), so p <= 256; p is rounded
+ * to dtype before the p.v product.
  * Alignment: q, kv, o_part 16-byte aligned; q_sb, q_sh, kv_st, o_sb, o_sh
  * multiples of 8 elements; lse_part 4-byte aligned.
  */
