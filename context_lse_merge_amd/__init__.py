@@ -48,6 +48,7 @@ DCP_LOAD_STREAMING = _C["DCP_LOAD_STREAMING"]
 DCP_LOAD_CACHED = _C["DCP_LOAD_CACHED"]
 DCP_KV_CONTIGUOUS = _C["DCP_KV_CONTIGUOUS"]
 DCP_KV_INTERLEAVED = _C["DCP_KV_INTERLEAVED"]
+DCP_NOALLOC_SCRATCH_BYTES = _C["DCP_NOALLOC_SCRATCH_BYTES"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -64,6 +65,8 @@ _lib.dcp_lse_combine.argtypes = [_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _i
 _lib.dcp_mla_partial_decode_scratch_size.argtypes = [_i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
 _lib.dcp_mla_partial_decode.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, _i64, _i32, _i32, ctypes.c_float,
                                         _i32, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]
+_lib.dcp_mla_partial_decode_noalloc.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, _i64, _i32, _i32,
+                                                ctypes.c_float, _i32, _vp, _i64, _i64, _vp, _i64, _vp]
 _lib.dcp_mla_partial_decode_varlen_scratch_size.argtypes = [_i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
 _lib.dcp_mla_partial_decode_varlen.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _i32,
                                                _i32, ctypes.c_float, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]
@@ -71,7 +74,7 @@ _lib.dcp_last_error.restype = ctypes.c_char_p
 _lib.dcp_status_string.argtypes = [_i32]
 _lib.dcp_status_string.restype = ctypes.c_char_p
 for _f in ("dcp_workspace_create", "dcp_workspace_destroy", "dcp_workspace_set_load_policy", "dcp_lse_combine",
-           "dcp_mla_partial_decode_scratch_size", "dcp_mla_partial_decode",
+           "dcp_mla_partial_decode_scratch_size", "dcp_mla_partial_decode", "dcp_mla_partial_decode_noalloc",
            "dcp_mla_partial_decode_varlen_scratch_size", "dcp_mla_partial_decode_varlen"):
     getattr(_lib, _f).restype = _i32
 
@@ -243,6 +246,39 @@ def dcp_mla_partial_decode(q, kv, cp: int, softmax_scale: float, lse_mode: int, 
         _dev_ptr(q, "q"), B, hq, q.stride(0), q.stride(1), _dev_ptr(kv, "kv") if T > 0 else None, T, kv.stride(0),
         dtype, cp, float(softmax_scale), lse_mode, _dev_ptr(o_part, "o_part"), o_part.stride(0), o_part.stride(1),
         _dev_ptr(lse_part, "lse_part"), lse_part.stride(0), _dev_ptr(scratch, "scratch"), nbytes, s))
+    return o_part, lse_part
+
+
+def _producer_args(q, kv, cp, o_part, lse_part):
+    """Shape and dtype checks shared by the fixed-length producer entry points;
+    returns (B, hq, T, dtype code)."""
+    import torch
+    if q.dim() != 3 or kv.dim() != 2 or o_part.dim() != 3 or lse_part.dim() != 2:
+        raise ValueError("q [B,hq,576], kv [T,576], o_part [B,cp*hq,512], lse_part [B,cp*hq] expected")
+    if q.dtype not in (torch.bfloat16, torch.float16) or kv.dtype != q.dtype or o_part.dtype != q.dtype:
+        raise ValueError("q, kv and o_part must all be bfloat16 or all float16")
+    if lse_part.dtype != torch.float32:
+        raise ValueError("lse_part must be float32")
+    B, hq, dqk = q.shape
+    if dqk != DCP_QK_DIM or kv.shape[1] != DCP_QK_DIM:
+        raise ValueError("q and kv rows must have %d columns" % DCP_QK_DIM)
+    if tuple(o_part.shape) != (B, cp * hq, DCP_HEAD_DIM) or tuple(lse_part.shape) != (B, cp * hq):
+        raise ValueError("o_part must be [B, cp*hq, %d] and lse_part [B, cp*hq]" % DCP_HEAD_DIM)
+    if q.stride(2) != 1 or kv.stride(1) != 1 or o_part.stride(2) != 1 or lse_part.stride(1) != 1:
+        raise ValueError("innermost strides must be 1")
+    return B, hq, kv.shape[0], (DCP_DTYPE_FP16 if q.dtype == torch.float16 else DCP_DTYPE_BF16)
+
+
+def dcp_mla_partial_decode_noalloc(q, kv, cp: int, softmax_scale: float, lse_mode: int, o_part, lse_part,
+                                   stream=None):
+    """dcp_mla_partial_decode with the split partials in the library's static
+    device array (no scratch argument; the C entry point allocates nothing)."""
+    B, hq, T, dtype = _producer_args(q, kv, cp, o_part, lse_part)
+    s = _stream_handle(stream)
+    _check(_lib.dcp_mla_partial_decode_noalloc(
+        _dev_ptr(q, "q"), B, hq, q.stride(0), q.stride(1), _dev_ptr(kv, "kv") if T > 0 else None, T, kv.stride(0),
+        dtype, cp, float(softmax_scale), lse_mode, _dev_ptr(o_part, "o_part"), o_part.stride(0), o_part.stride(1),
+        _dev_ptr(lse_part, "lse_part"), lse_part.stride(0), s))
     return o_part, lse_part
 
 

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdcp.so")
 ARCH = "gfx950"
 
-SOURCES = ["dcp_host.cpp", "merge.hip", "mla_decode.hip", "mla_varlen.hip"]
+SOURCES = ["dcp_host.cpp", "merge.hip", "mla_decode.hip", "mla_varlen.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",

@@ -286,4 +286,9 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
              const MlaVarlen* vl, int dtype, int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb,
              int64_t o_sh, float* lse, int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan);
 
+// Enqueue a validated plan on `stream` (a hipStream_t): the planning kernel
+// (variable length), the decode kernel and the split reduction.  Returns a
+// DCP status; `fn` names the entry point in error messages.
+int run_mla(const MlaPlan& plan, void* stream, const char* fn);
+
 }  // namespace dcp

@@ -593,7 +593,6 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
 }  // namespace dcp
 
 namespace dcp {
-namespace {
 
 // Enqueue a validated plan: the decode kernel, then (several splits) the
 // merge over splits.
@@ -627,7 +626,6 @@ int run_mla(const MlaPlan& plan, void* hip_stream, const char* fn) {
     return ok();
 }
 
-}  // namespace
 }  // namespace dcp
 
 extern "C" int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv,

@@ -213,6 +213,32 @@ int dcp_mla_partial_decode(const void* q, int64_t B, int hq, int64_t q_sb, int64
                            size_t scratch_bytes, void* hip_stream);
 
 /*
+ * dcp_mla_partial_decode without a scratch argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results (bit for bit), errors
+ * and alignment are those of dcp_mla_partial_decode; the split partials go to
+ * a static device array of DCP_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends, which fits the
+ * partials of every shape this entry point accepts (a shape needing more is
+ * rejected with DCP_ERR_WORKSPACE before anything is enqueued).
+ *  - The kernels run on hip_stream's device, which must be the current device
+ *    (DCP_ERR_STREAM otherwise).  The first call on a device looks up the
+ *    array's address there (hipGetSymbolAddress, no allocation), so make that
+ *    first call outside graph capture; later calls, captured or not, only
+ *    launch kernels.
+ *  - Every call on one GPU shares that GPU's array: calls that may overlap on
+ *    one GPU (on different streams, or in graphs replayed concurrently) race
+ *    and give wrong results.  Calls ordered on one stream are safe; nothing in
+ *    the array needs to be cleared between them.
+ */
+#define DCP_NOALLOC_SCRATCH_BYTES 67368960 /* 510 units x 128 rows x 1032 bytes */
+
+int dcp_mla_partial_decode_noalloc(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv,
+                                   int64_t kv_tokens, int64_t kv_st, int dtype, int cp, float softmax_scale,
+                                   int lse_mode, void* o_part, int64_t o_sb, int64_t o_sh, float* lse_part,
+                                   int64_t lse_sb, void* hip_stream);
+
+/*
  * MLA decode partials with one cache per query token and per-token lengths:
  * the producer as a decode batch runs it, each token (request) attending
  * over its own latent KV rows.  The decode seq_lens decide which shards are

@@ -90,3 +90,18 @@ def test_host_planner_under_sanitizers(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, env=env)
     assert r.returncode == 0, r.stderr + r.stdout
     assert "host plan checks passed" in r.stdout
+
+
+def test_noalloc_static_scratch_covers_every_fixed_length_shape():
+    """dcp_mla_partial_decode_noalloc keeps the split partials in a static array of DCP_NOALLOC_SCRATCH_BYTES:
+    over a grid of shapes that includes the largest case (255 row-block x shard units, two splits each), the
+    scratch dcp_mla_partial_decode needs never exceeds it, and the largest case needs exactly that much."""
+    import context_lse_merge_amd as dcp
+    cap = dcp.DCP_NOALLOC_SCRATCH_BYTES
+    worst = 0
+    for cp in (1, 2, 3, 4, 5, 7, 8, 13, 16, 31, 64):
+        for hq in (1, 7, 16, 100, 128, 129, 200, 256):
+            for B in list(range(1, 40)) + [51, 63, 64, 65, 127, 128, 255, 256, 257, 1000]:
+                for T in (0, 1, 31, 255, 256, 257, 511, 2560, 4097, 32768, 131072, 1 << 20):
+                    worst = max(worst, dcp.dcp_mla_partial_decode_scratch_size(B, hq, T, cp))
+    assert worst == cap == dcp.dcp_mla_partial_decode_scratch_size(51, 128, 2560, 5)
