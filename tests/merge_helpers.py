@@ -8,7 +8,10 @@ were summed,
 for fp16 payloads the same with ulp_f16(r) = 2^(max(floor(log2 |r|), -14) - 10).
 The second term only matters under cancellation (|r| << A), where fp32
 accumulation error of order cp * 2^-24 A can exceed 2 ulp(r) although every
-step is correctly rounded.  The merged LSE must satisfy
+step is correctly rounded.  Every check reports how many elements needed that
+term (the "floor") and asserts that each of them is a cancellation: |r| <
+2^-8 A (without cancellation |r| is close to A and 2 ulp(r) alone covers the
+fp32 error many times over).  The merged LSE must satisfy
 |L_g - L_r| <= 1e-5 max(|L_r|, 1), and -inf must match exactly.
 """
 import sys
@@ -97,7 +100,12 @@ def check_against_oracle(case, out, out_lse, ref=None):
     assert not bad.any(), "%s: %d elements out of tolerance; worst |g-r| = %.4g at %s (r = %.6g, tol %.3g)" % (
         case.name, int(bad.sum()), err.max(), np.unravel_index(np.argmax(err - tol), err.shape),
         r.flat[np.argmax(err - tol)], tol.flat[np.argmax(err - tol)])
-    report = {"max_err_ulps": float(np.max(err / ulp)), "needed_floor": int((err > ulp_tol).sum())}
+    floored = err > ulp_tol
+    not_cancel = floored & (np.abs(r) >= 2.0 ** -8 * A)
+    assert not not_cancel.any(), "%s: %d elements needed the 2^-16 A floor without cancellation (|r| >= 2^-8 A)" % (
+        case.name, int(not_cancel.sum()))
+    report = {"max_err_ulps": float(np.max(err / ulp)), "needed_floor": int(floored.sum()), "elements": int(err.size),
+              "max_err_over_A": float(np.max(err / np.maximum(A, 1e-300)))}
     if out_lse is not None:
         gL = out_lse.cpu().double().numpy()
         inf = np.isneginf(rL)
@@ -107,4 +115,7 @@ def check_against_oracle(case, out, out_lse, ref=None):
         assert np.all(d <= lim), "%s: merged LSE off by %.3g (limit %.3g)" % (case.name, d.max(),
                                                                               lim[np.argmax(d - lim)])
         report["max_lse_rel"] = float(np.max(d / np.maximum(np.abs(rL[~inf]), 1.0))) if d.size else 0.0
+    announce("%s: %d elements, max error %.3f ulp, %d needed the cancellation floor (all with |r| < 2^-8 A)%s" % (
+        case.name, report["elements"], report["max_err_ulps"], report["needed_floor"],
+        ", merged LSE max rel err %.2e" % report["max_lse_rel"] if "max_lse_rel" in report else ""))
     return report

@@ -10,8 +10,10 @@ Tolerances (the pages fix none for the producer; see the oracle's notes):
   merge tolerance against the oracle merge of those same partials;
 * end to end: the merged output within 2^-7 of the row max of fp64 full
   attention over all T keys.
-Full-size runs (T = 131072, 128 heads, cp = 4) check sampled rows, which the
-oracle computes one by one.
+Full-size runs (T = 131072, 128 heads, cp = 4) check every row of the first
+and the last token -- each a whole 128-row workgroup, all eight wavefronts and
+all sixteen rows of each -- plus sampled rows, which the oracle computes one by
+one.
 """
 import os
 
@@ -209,17 +211,23 @@ def _full_kv():
     return _KV_CACHE["kv"]
 
 
+def whole_token_rows(B, hq, seed):
+    """Every row of the first and of the last token, plus six random rows."""
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(hq), np.arange((B - 1) * hq, B * hq), rng.integers(0, B * hq, 6)]))
+
+
 @pytest.mark.parametrize("B", [1, 8, 32, 64])
-def test_full_size_config_sampled_rows(B):
+def test_full_size_config_whole_tokens(B):
     """q [B,128,576], one 131072 x 576 cache in 4 contiguous shards of 32768,
-    scale 1/sqrt(192): sampled rows against the oracle, partials and merged."""
+    scale 1/sqrt(192): all 128 rows of tokens 0 and B-1 (and sampled rows)
+    against the oracle, partials and merged."""
     kv = _full_kv()
     q = synth.normal_bf16((B, 128, 576), synth.gen(3000 + B))
     o, l = run_producer(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E)
-    rng = np.random.default_rng(B)
-    rows = np.unique(np.concatenate([[0, B * 128 - 1], rng.integers(0, B * 128, 6)]))
+    rows = whole_token_rows(B, 128, B)
     worst = check_partials(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
-    announce("full size B=%d: worst partial row error %.3g of row max" % (B, worst))
+    announce("full size B=%d: %d rows checked, worst partial row error %.3g of row max" % (B, len(rows), worst))
     check_end_to_end(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
 
 
@@ -257,15 +265,14 @@ def test_empty_shards_f16():
     assert torch.all(torch.isneginf(l.cpu().reshape(2, 4, 16)[:, 0]))
 
 
-@pytest.mark.parametrize("B", [1, 64])
-def test_full_size_config_sampled_rows_f16(B):
+@pytest.mark.parametrize("B", [1, 8, 32, 64])
+def test_full_size_config_whole_tokens_f16(B):
     _, kv = synth.mla_decode(1, dtype=F16)
     q = synth.normal_16((B, 128, 576), synth.gen(3100 + B), F16)
     o, l = run_producer(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E)
-    rng = np.random.default_rng(100 + B)
-    rows = np.unique(np.concatenate([[0, B * 128 - 1], rng.integers(0, B * 128, 6)]))
+    rows = whole_token_rows(B, 128, 100 + B)
     worst = check_partials(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
-    announce("full size fp16 B=%d: worst partial row error %.3g of row max" % (B, worst))
+    announce("full size fp16 B=%d: %d rows checked, worst partial row error %.3g of row max" % (B, len(rows), worst))
     check_end_to_end(q, kv, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
 
 

@@ -162,7 +162,8 @@ def test_shared_cache_full_length_matches_fixed_length_bitwise():
 
 def test_full_size_shared_cache_random_lengths_interleaved():
     """64 tokens over one 131072-row cache (kv_sb = 0) with lengths drawn
-    uniformly in [1, 131072], interleaved ownership: sampled rows."""
+    uniformly in [1, 131072], interleaved ownership: every row of two whole
+    tokens (the full-length token 0 and the last token) and sampled rows."""
     _, kv = synth.mla_decode(1)
     B = 64
     q = synth.normal_bf16((B, 128, 576), synth.gen(3300))
@@ -170,7 +171,10 @@ def test_full_size_shared_cache_random_lengths_interleaved():
     seq[:2] = [131072, 3]
     o, l = run_varlen(q, kv, seq, 131072, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_E)
     rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, 128, 129, B * 128 - 1], rng.integers(0, B * 128, 4)]))
+    rows = np.unique(np.concatenate([np.arange(128), [128, 129], np.arange((B - 1) * 128, B * 128),
+                                     rng.integers(0, B * 128, 4)]))
+    announce("varlen full size: checking %d rows (tokens 0 and %d whole, lengths %d and %d)" % (
+        len(rows), B - 1, seq[0], seq[B - 1]))
     check(q, kv, seq, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_E, o, l, rows=rows)
 
 
