@@ -57,7 +57,10 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
-_lib.dcp_workspace_create.argtypes = [_i64, _i32, _i32, _i32, _i32, _vp, ctypes.POINTER(_vp)]
+_lib.dcp_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
+_lib.dcp_workspace_create.argtypes = [_vp, _sz, _i64, _i32, _i32, _i32, _i32, _vp, ctypes.POINTER(_vp)]
+_lib.dcp_workspace_recv.argtypes = [_vp, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                                    ctypes.POINTER(_vp), ctypes.POINTER(_i64)]
 _lib.dcp_workspace_destroy.argtypes = [_vp]
 _lib.dcp_workspace_set_load_policy.argtypes = [_vp, _i32]
 _lib.dcp_lse_combine.argtypes = [_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _i64,
@@ -73,7 +76,7 @@ _lib.dcp_mla_partial_decode_varlen.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp,
 _lib.dcp_last_error.restype = ctypes.c_char_p
 _lib.dcp_status_string.argtypes = [_i32]
 _lib.dcp_status_string.restype = ctypes.c_char_p
-for _f in ("dcp_workspace_create", "dcp_workspace_destroy", "dcp_workspace_set_load_policy", "dcp_lse_combine",
+for _f in ("dcp_workspace_size", "dcp_workspace_create", "dcp_workspace_recv", "dcp_workspace_destroy", "dcp_workspace_set_load_policy", "dcp_lse_combine",
            "dcp_mla_partial_decode_scratch_size", "dcp_mla_partial_decode", "dcp_mla_partial_decode_noalloc",
            "dcp_mla_partial_decode_varlen_scratch_size", "dcp_mla_partial_decode_varlen"):
     getattr(_lib, _f).restype = _i32
@@ -117,20 +120,23 @@ def _dev_ptr(t, name):
 
 
 class Workspace:
-    """Owns a dcp_workspace handle; ``handle`` is what the C calls take."""
+    """Owns a dcp_workspace handle; ``handle`` is what the C calls take.  ``buf``
+    is the device buffer it was created over (kept alive with it)."""
 
-    def __init__(self, handle: int, capacity: int, h_local: int, cp: int, stream: int, dtype: int):
+    def __init__(self, handle: int, capacity: int, h_local: int, cp: int, stream: int, dtype: int, buf=None):
         self.handle = handle
         self.capacity = capacity
         self.h_local = h_local
         self.cp = cp
         self.stream = stream
         self.dtype = dtype
+        self.buf = buf
 
     def close(self):
         if self.handle:
             _check(_lib.dcp_workspace_destroy(self.handle))
             self.handle = None
+        self.buf = None
 
     def __del__(self):
         try:
@@ -145,14 +151,55 @@ class Workspace:
         self.close()
 
 
+def dcp_workspace_size(capacity_tokens: int, h_local: int, cp: int, d: int = DCP_HEAD_DIM,
+                       dtype: int = DCP_DTYPE_BF16) -> int:
+    """Bytes of device memory a workspace of this geometry needs."""
+    n = _sz()
+    _check(_lib.dcp_workspace_size(capacity_tokens, h_local, cp, d, dtype, ctypes.byref(n)))
+    return n.value
+
+
 def dcp_workspace_create(capacity_tokens: int, h_local: int, cp: int, d: int = DCP_HEAD_DIM,
-                         dtype: int = DCP_DTYPE_BF16, stream=None) -> Workspace:
+                         dtype: int = DCP_DTYPE_BF16, stream=None, buf=None, buf_bytes=None) -> Workspace:
     """Create a workspace bound to ``stream`` (default: torch's current stream).
-    ``dtype`` is DCP_DTYPE_BF16 or DCP_DTYPE_FP16, the payload type of every call."""
+    ``dtype`` is DCP_DTYPE_BF16 or DCP_DTYPE_FP16, the payload type of every call.
+    ``buf`` is its device buffer: a GPU tensor, a raw device address (with
+    ``buf_bytes``), or None to allocate dcp_workspace_size() bytes with torch on
+    the current device."""
     s = _stream_handle(stream)
+    if buf is None:
+        import torch
+        n = dcp_workspace_size(capacity_tokens, h_local, cp, d, dtype)
+        buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    if isinstance(buf, int):
+        ptr, nbytes = buf, int(buf_bytes or 0)
+    else:
+        ptr, nbytes = _dev_ptr(buf, "buf"), buf.numel() * buf.element_size()
     h = _vp()
-    _check(_lib.dcp_workspace_create(capacity_tokens, h_local, cp, d, dtype, s, ctypes.byref(h)))
-    return Workspace(h.value, capacity_tokens, h_local, cp, s, dtype)
+    _check(_lib.dcp_workspace_create(ptr, nbytes, capacity_tokens, h_local, cp, d, dtype, s, ctypes.byref(h)))
+    return Workspace(h.value, capacity_tokens, h_local, cp, s, dtype, buf)
+
+
+def dcp_workspace_recv(ws: Workspace):
+    """The workspace's landing zone as torch views of its buffer: ``attn``
+    [capacity, cp*h_local, D] in the workspace's dtype (head s*h_local + j holds
+    shard s of local head j) and ``lse`` [capacity, cp*h_local] fp32 (FlashMLA
+    layout: merge with DCP_LSE_BH1)."""
+    import torch
+    a, lp = _vp(), _vp()
+    sb, sh, lsb = _i64(), _i64(), _i64()
+    _check(_lib.dcp_workspace_recv(ws.handle, ctypes.byref(a), ctypes.byref(sb), ctypes.byref(sh), ctypes.byref(lp),
+                                   ctypes.byref(lsb)))
+    if not isinstance(ws.buf, torch.Tensor):
+        raise ValueError("dcp_workspace_recv: the workspace was created over a raw address, not a tensor")
+    base = ws.buf.data_ptr()
+    H = ws.cp * ws.h_local
+    dt = torch.float16 if ws.dtype == DCP_DTYPE_FP16 else torch.bfloat16
+    n_attn = ws.capacity * sb.value
+    attn = ws.buf[a.value - base:a.value - base + 2 * n_attn].view(dt).view(ws.capacity, H, DCP_HEAD_DIM)
+    lse = ws.buf[lp.value - base:lp.value - base + 4 * ws.capacity * lsb.value].view(torch.float32)
+    assert sh.value == DCP_HEAD_DIM and sb.value == H * DCP_HEAD_DIM and lsb.value == H
+    return attn, lse.view(ws.capacity, H)
 
 
 def dcp_workspace_destroy(ws: Workspace):
@@ -222,22 +269,7 @@ def dcp_mla_partial_decode(q, kv, cp: int, softmax_scale: float, lse_mode: int, 
     ``o_part`` [B, cp*hq, 512] all bf16 or all fp16 (the element type passed on),
     ``lse_part`` [B, cp*hq] fp32, ``scratch`` a GPU tensor of at least
     dcp_mla_partial_decode_scratch_size() bytes (or None when 0)."""
-    import torch
-    if q.dim() != 3 or kv.dim() != 2 or o_part.dim() != 3 or lse_part.dim() != 2:
-        raise ValueError("q [B,hq,576], kv [T,576], o_part [B,cp*hq,512], lse_part [B,cp*hq] expected")
-    if q.dtype not in (torch.bfloat16, torch.float16) or kv.dtype != q.dtype or o_part.dtype != q.dtype:
-        raise ValueError("q, kv and o_part must all be bfloat16 or all float16")
-    dtype = DCP_DTYPE_FP16 if q.dtype == torch.float16 else DCP_DTYPE_BF16
-    if lse_part.dtype != torch.float32:
-        raise ValueError("lse_part must be float32")
-    B, hq, dqk = q.shape
-    T = kv.shape[0]
-    if dqk != DCP_QK_DIM or kv.shape[1] != DCP_QK_DIM:
-        raise ValueError("q and kv rows must have %d columns" % DCP_QK_DIM)
-    if tuple(o_part.shape) != (B, cp * hq, DCP_HEAD_DIM) or tuple(lse_part.shape) != (B, cp * hq):
-        raise ValueError("o_part must be [B, cp*hq, %d] and lse_part [B, cp*hq]" % DCP_HEAD_DIM)
-    if q.stride(2) != 1 or kv.stride(1) != 1 or o_part.stride(2) != 1 or lse_part.stride(1) != 1:
-        raise ValueError("innermost strides must be 1")
+    B, hq, T, dtype = _producer_args(q, kv, cp, o_part, lse_part)
     nbytes = 0
     if scratch is not None:
         nbytes = scratch.numel() * scratch.element_size()

@@ -441,6 +441,26 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     return ok();
 }
 
+namespace {
+// The checks dcp_workspace_size and dcp_workspace_create share.
+int check_geometry(const char* fn, int64_t capacity_tokens, int h_local, int cp, int d, int dtype) {
+    if (capacity_tokens < 1)
+        return fail(DCP_ERR_INVALID_ARG, "%s: capacity_tokens = %lld must be >= 1", fn, (long long)capacity_tokens);
+    if (h_local < 1 || cp < 1 || cp > DCP_MAX_CP)
+        return fail(DCP_ERR_INVALID_ARG, "%s: need h_local >= 1 and 1 <= cp <= %d (got %d, %d)", fn, DCP_MAX_CP,
+                    h_local, cp);
+    if (d != DCP_HEAD_DIM)
+        return fail(DCP_ERR_LAYOUT, "%s: head dimension %d is not supported (only %d)", fn, d, DCP_HEAD_DIM);
+    if (dtype != DCP_DTYPE_BF16 && dtype != DCP_DTYPE_FP16)
+        return fail(DCP_ERR_LAYOUT, "%s: dtype %d is not supported (DCP_DTYPE_BF16 or DCP_DTYPE_FP16)", fn, dtype);
+    // One launch covers capacity * h_local rows, counted in 32 bits.
+    if (capacity_tokens * static_cast<int64_t>(h_local) > (int64_t{1} << 30))
+        return fail(DCP_ERR_INVALID_ARG, "%s: capacity_tokens * h_local = %lld exceeds 2^30 rows per launch", fn,
+                    (long long)(capacity_tokens * h_local));
+    return DCP_OK;
+}
+}  // namespace
+
 }  // namespace dcp
 
 extern "C" {
@@ -475,30 +495,32 @@ int dcp_mla_partial_decode_varlen_scratch_size(int64_t B, int hq, int64_t max_se
     return dcp::ok();
 }
 
-int dcp_workspace_create(int64_t capacity_tokens, int h_local, int cp, int d, int dtype, void* hip_stream,
-                         dcp_workspace** ws) {
-    if (!ws) return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_workspace_create: ws (the output handle) is null");
+
+int dcp_workspace_size(int64_t capacity_tokens, int h_local, int cp, int d, int dtype, size_t* bytes) {
+    if (!bytes) return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_workspace_size: bytes (the output) is null");
+    const int rc = dcp::check_geometry("dcp_workspace_size", capacity_tokens, h_local, cp, d, dtype);
+    if (rc != DCP_OK) return rc;
+    *bytes = dcp::workspace_layout(capacity_tokens, h_local, cp, d).bytes;
+    return dcp::ok();
+}
+
+int dcp_workspace_create(void* dev_buf, size_t bytes, int64_t capacity_tokens, int h_local, int cp, int d, int dtype,
+                         void* hip_stream, dcp_workspace** ws) {
+    const char* fn = "dcp_workspace_create";
+    if (!ws) return dcp::fail(DCP_ERR_INVALID_ARG, "%s: ws (the output handle) is null", fn);
     *ws = nullptr;
-    if (capacity_tokens < 1)
-        return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_workspace_create: capacity_tokens = %lld must be >= 1",
-                         (long long)capacity_tokens);
-    if (h_local < 1 || cp < 1 || cp > DCP_MAX_CP)
-        return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_workspace_create: need h_local >= 1 and 1 <= cp <= %d (got %d, %d)",
-                         DCP_MAX_CP, h_local, cp);
-    if (d != DCP_HEAD_DIM)
-        return dcp::fail(DCP_ERR_LAYOUT, "dcp_workspace_create: head dimension %d is not supported (only %d)", d,
-                         DCP_HEAD_DIM);
-    if (dtype != DCP_DTYPE_BF16 && dtype != DCP_DTYPE_FP16)
-        return dcp::fail(DCP_ERR_LAYOUT,
-                         "dcp_workspace_create: dtype %d is not supported (DCP_DTYPE_BF16 or DCP_DTYPE_FP16)",
-                         dtype);
-    // One launch covers capacity * h_local rows, counted in 32 bits.
-    if (capacity_tokens * static_cast<int64_t>(h_local) > (int64_t{1} << 30))
-        return dcp::fail(DCP_ERR_INVALID_ARG,
-                         "dcp_workspace_create: capacity_tokens * h_local = %lld exceeds 2^30 rows per launch",
-                         (long long)(capacity_tokens * h_local));
+    const int rc = dcp::check_geometry(fn, capacity_tokens, h_local, cp, d, dtype);
+    if (rc != DCP_OK) return rc;
+    const size_t need = dcp::workspace_layout(capacity_tokens, h_local, cp, d).bytes;
+    if (!dev_buf || bytes < need)
+        return dcp::fail(DCP_ERR_WORKSPACE,
+                         "%s: the device buffer must hold %zu bytes for capacity %lld x %d local heads x %d shards "
+                         "(dcp_workspace_size); got %zu bytes at %p",
+                         fn, need, (long long)capacity_tokens, h_local, cp, dev_buf ? bytes : size_t{0}, dev_buf);
+    if (reinterpret_cast<uintptr_t>(dev_buf) % 16)
+        return dcp::fail(DCP_ERR_ALIGN, "%s: the device buffer (%p) must be 16-byte aligned", fn, dev_buf);
     dcp_workspace* w = new (std::nothrow) dcp_workspace;
-    if (!w) return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_workspace_create: out of host memory");
+    if (!w) return dcp::fail(DCP_ERR_INVALID_ARG, "%s: out of host memory", fn);
     w->capacity = capacity_tokens;
     w->h_local = h_local;
     w->cp = cp;
@@ -506,8 +528,26 @@ int dcp_workspace_create(int64_t capacity_tokens, int h_local, int cp, int d, in
     w->dtype = dtype;
     w->load_policy = DCP_LOAD_STREAMING;
     w->stream = hip_stream;
+    w->buf = dev_buf;
+    w->bytes = bytes;
     w->magic = dcp::kWorkspaceMagic;
     *ws = w;
+    return dcp::ok();
+}
+
+int dcp_workspace_recv(const dcp_workspace* ws, void** attn, int64_t* attn_sb, int64_t* attn_sh, float** lse,
+                       int64_t* lse_sb) {
+    if (!ws || ws->magic != dcp::kWorkspaceMagic)
+        return dcp::fail(DCP_ERR_WORKSPACE, "dcp_workspace_recv: not a workspace (or destroyed)");
+    if (!attn || !attn_sb || !attn_sh || !lse || !lse_sb)
+        return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_workspace_recv: every output pointer must be non-null");
+    const int64_t H = static_cast<int64_t>(ws->cp) * ws->h_local;
+    const dcp::WorkspaceLayout l = dcp::workspace_layout(ws->capacity, ws->h_local, ws->cp, ws->d);
+    *attn = ws->buf;
+    *attn_sh = ws->d;
+    *attn_sb = H * ws->d;
+    *lse = reinterpret_cast<float*>(static_cast<char*>(ws->buf) + l.lse_off);
+    *lse_sb = H;
     return dcp::ok();
 }
 

@@ -78,12 +78,32 @@ struct dcp_workspace {
     int dtype;
     int load_policy;  // DCP_LOAD_STREAMING or DCP_LOAD_CACHED
     void* stream;
+    void* buf;        // the caller's device buffer: the landing zone
+    size_t bytes;
     uint64_t magic;
 };
 
 namespace dcp {
 
-constexpr uint64_t kWorkspaceMagic = 0x64637077736b7631ull;  // "dcpwskv1"
+constexpr uint64_t kWorkspaceMagic = 0x64637077736b7632ull;  // "dcpwskv2"
+
+// The workspace's device buffer: the receive-buffer landing zone of up to
+// `capacity` tokens, laid out as the [B, H, D] attention output that
+// dcp_lse_combine reads (H = cp * h_local, head s*h_local + j holding shard
+// s of local head j, rows of D elements back to back), then the LSEs in the
+// FlashMLA [B, H] layout, each region starting on a 256-byte boundary.
+struct WorkspaceLayout {
+    size_t lse_off;  // bytes from the buffer's start to the LSE region
+    size_t bytes;    // total
+};
+inline WorkspaceLayout workspace_layout(int64_t capacity, int h_local, int cp, int d) {
+    const size_t rows = static_cast<size_t>(capacity) * static_cast<size_t>(h_local) * static_cast<size_t>(cp);
+    const size_t payload = rows * static_cast<size_t>(d) * 2;
+    WorkspaceLayout l;
+    l.lse_off = (payload + 255) / 256 * 256;
+    l.bytes = l.lse_off + (rows * 4 + 255) / 256 * 256;
+    return l;
+}
 
 // Record a message for dcp_last_error() and return `status`.
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

@@ -21,7 +21,8 @@
  *  - All pointers to tensors are DEVICE pointers owned by the caller; the
  *    library never allocates, frees, synchronises or prints, so every call may
  *    be captured into a HIP graph.  Host-side objects (a workspace) are the
- *    only memory the library allocates, and only in dcp_workspace_create.
+ *    only memory the library allocates, and only in dcp_workspace_create;
+ *    device buffers (a workspace's, a producer's scratch) are the caller's.
  *  - Sizes and strides are in ELEMENTS, not bytes.  The innermost (D) stride
  *    of every tensor is 1.
  *  - Every argument is checked before anything is enqueued: on any error the
@@ -48,7 +49,7 @@ extern "C" {
 #define DCP_ERR_LAYOUT 2      /* unsupported D or dtype, negative or overlapping strides         */
 #define DCP_ERR_ALIGN 3       /* a pointer or row stride breaks the 16-byte alignment rule      */
 #define DCP_ERR_STREAM 4      /* called on a stream other than the workspace's                  */
-#define DCP_ERR_WORKSPACE 5   /* geometry differs from the workspace's, or no workspace given    */
+#define DCP_ERR_WORKSPACE 5   /* no workspace, other geometry, or a device buffer too small        */
 #define DCP_ERR_HIP 6         /* the HIP runtime refused a launch                               */
 
 /* LSE base: the attention backend decides which one its LSE is in
@@ -80,14 +81,38 @@ extern "C" {
 typedef struct dcp_workspace dcp_workspace;
 
 /*
- * Create a merge workspace: a host-side object that fixes the geometry
- * (h_local = H/cp local heads, cp shards, head dimension d, dtype), the token
- * capacity and the ONE stream it serves.  Mirrors the pages' workspaces: one
- * per ordered stream, sized by the widest decode batch (PR #40539,
- * Modifications and Coordination), created once before graph capture.
+ * Bytes of device memory a merge workspace needs (dcp_workspace_create's
+ * dev_buf): its receive-buffer landing zone for up to capacity_tokens tokens,
+ * i.e. capacity_tokens * h_local * cp rows of d payload elements plus one fp32
+ * LSE per row, each region rounded up to 256 bytes.  The pages size their
+ * fused-reduce workspaces with such a function, by the widest decode batch
+ * times the local heads ("[DCP] Run fi_a2a on FlashInfer's fused all-to-all +
+ * LSE reduce", sglang PR #40539, Coordination, and Speed Tests and Profiling,
+ * memory), from the geometry a caller holds at initialisation (maximum
+ * tokens, heads per rank, head dimension, dtype: "[Attention] Add direct
+ * symmetric-memory DCP A2A", vLLM PR #48897, review thread).  Arguments and
+ * errors as dcp_workspace_create; *bytes receives the size.
+ */
+int dcp_workspace_size(int64_t capacity_tokens, int h_local, int cp, int d, int dtype, size_t* bytes);
+
+/*
+ * Create a merge workspace over a caller-owned device buffer.  It fixes the
+ * geometry (h_local = H/cp local heads, cp shards, head dimension d, dtype),
+ * the token capacity and the ONE stream it serves, as the pages' workspaces
+ * do: one per ordered stream, sized by the widest decode batch and created
+ * once, before graph capture (PR #40539, Modifications).
  *
+ * dev_buf, bytes   device buffer of at least dcp_workspace_size() bytes,
+ *                  16-byte aligned, owned by the caller (allocate it with
+ *                  PyTorch or hipMalloc; it must outlive the workspace).  It is
+ *                  the landing zone: dcp_workspace_recv says where a caller may
+ *                  stage the shard partials of up to capacity_tokens tokens to
+ *                  merge them with dcp_lse_combine.  The library never reads
+ *                  or writes it by itself.  NULL or too small gives
+ *                  DCP_ERR_WORKSPACE, misaligned DCP_ERR_ALIGN.
  * capacity_tokens  >= 1; dcp_lse_combine splits wider batches into ordered
- *                  chunks of at most this many tokens.
+ *                  chunks of at most this many tokens (PR #40539,
+ *                  Modifications and Coordination).
  * h_local, cp      >= 1; cp <= DCP_MAX_CP.
  * d                DCP_HEAD_DIM.
  * dtype            DCP_DTYPE_BF16 or DCP_DTYPE_FP16: the element type of the
@@ -98,13 +123,27 @@ typedef struct dcp_workspace dcp_workspace;
  *                  must use (opaque value, compared, never dereferenced).
  * ws               receives the handle; release it with dcp_workspace_destroy.
  *
- * On one GPU the shards' receive buffers are the caller's resident attention
- * output, so the workspace holds no device memory.
+ * On one GPU the shards' partials are usually the caller's resident attention
+ * output, which dcp_lse_combine reads in place; the landing zone serves a
+ * caller that gathers them first (as an exchange would).
  */
-int dcp_workspace_create(int64_t capacity_tokens, int h_local, int cp, int d, int dtype, void* hip_stream,
-                         dcp_workspace** ws);
+int dcp_workspace_create(void* dev_buf, size_t bytes, int64_t capacity_tokens, int h_local, int cp, int d, int dtype,
+                         void* hip_stream, dcp_workspace** ws);
 
-/* Release a workspace (host memory only).  NULL is accepted. */
+/*
+ * The landing zone of ws: shard s of local head j of token b (b < capacity)
+ * goes to attn + b*attn_sb + (s*h_local + j)*attn_sh, D elements of the
+ * workspace's dtype, and its LSE to lse[b*lse_sb + s*h_local + j], so that
+ *     dcp_lse_combine(ws, attn, B, cp*h_local, attn_sb, attn_sh, lse,
+ *                     DCP_LSE_BH1, lse_sb, 1, 0, ...)
+ * merges the first B staged tokens (head h of the [B, H, D] view belongs to
+ * shard h / h_local, PR #40539, Modifications).  attn_sh = D, attn_sb = H*D,
+ * lse_sb = H.  Pointers are device pointers inside dev_buf.
+ */
+int dcp_workspace_recv(const dcp_workspace* ws, void** attn, int64_t* attn_sb, int64_t* attn_sh, float** lse,
+                       int64_t* lse_sb);
+
+/* Release a workspace (its host object; the device buffer stays the caller's).  NULL is accepted. */
 int dcp_workspace_destroy(dcp_workspace* ws);
 
 /*
@@ -287,10 +326,19 @@ int dcp_mla_partial_decode_varlen(const void* q, int64_t B, int hq, int64_t q_sb
                                   int64_t o_sb, int64_t o_sh, float* lse_part, int64_t lse_sb, void* scratch,
                                   size_t scratch_bytes, void* hip_stream);
 
-/* Message for the last failing call on this thread ("" if none). */
+/*
+ * Message for the last failing call on this thread ("" if none): it names the
+ * argument at fault and what to change.  The pages report a workspace that
+ * cannot be created, or is given a bad configuration, together with the fix
+ * ("[DCP] Run fi_a2a on FlashInfer's fused all-to-all + LSE reduce", sglang PR
+ * #40539, commit log; "[Attention] Add direct symmetric-memory DCP A2A", vLLM
+ * PR #48897, commit messages on the staging-slot count).  The string is owned
+ * by the library and stays valid until the next call on the same thread.
+ */
 const char* dcp_last_error(void);
 
-/* Name of a status code. */
+/* Name of a status code ("DCP_ERR_WORKSPACE", ...; "DCP_ERR_UNKNOWN" for any
+ * other value), for the same error reports.  A static string. */
 const char* dcp_status_string(int status);
 
 #ifdef __cplusplus

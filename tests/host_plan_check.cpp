@@ -182,10 +182,20 @@ static void varlen_plan_checks() {
                         lay.bytes - 1, &plan) == DCP_ERR_WORKSPACE);
 }
 
+// A fake, 256-byte aligned device address for workspace buffers (never dereferenced).
+constexpr uintptr_t kWsBuf = uintptr_t{0x7} << 40;
+
+size_t ws_bytes(int64_t capacity, int h_local, int cp) {
+    size_t n = 0;
+    CHECK(dcp_workspace_size(capacity, h_local, cp, 512, DCP_DTYPE_BF16, &n) == DCP_OK);
+    return n;
+}
+
 int main() {
     void* stream = fake(0x5000);
     dcp_workspace* ws = nullptr;
-    CHECK(dcp_workspace_create(128, 16, 4, 512, DCP_DTYPE_BF16, stream, &ws) == DCP_OK);
+    CHECK(dcp_workspace_create(fake(kWsBuf), ws_bytes(128, 16, 4), 128, 16, 4, 512, DCP_DTYPE_BF16, stream, &ws) ==
+          DCP_OK);
     CHECK(ws != nullptr);
 
     const int64_t B = 500, H = 64, D = 512;
@@ -222,7 +232,7 @@ int main() {
 
     // 24 heads viewed out of a 128-head backing buffer (padded token stride).
     dcp_workspace* ws6 = nullptr;
-    CHECK(dcp_workspace_create(8, 6, 4, 512, DCP_DTYPE_BF16, stream, &ws6) == DCP_OK);
+    CHECK(dcp_workspace_create(fake(kWsBuf), ws_bytes(8, 6, 4), 8, 6, 4, 512, DCP_DTYPE_BF16, stream, &ws6) == DCP_OK);
     rc = dcp::plan_merge(ws6, fake(attn), 5, 24, 128 * D, D, reinterpret_cast<const float*>(lse), DCP_LSE_BH1, 24, 1,
                          0, DCP_LSE_BASE_E, fake(out), 6 * D, D, nullptr, 0, stream, &plan);
     CHECK(rc == DCP_OK && plan.n_chunks == 1 && plan.args.rows == 30 && plan.args.a_ss == 6 * D);
@@ -230,7 +240,8 @@ int main() {
     // A capacity above the per-launch token limit is split further: 70000
     // tokens with capacity 100000 run as 65535 + 4465.
     dcp_workspace* wsw = nullptr;
-    CHECK(dcp_workspace_create(100000, 16, 4, 512, DCP_DTYPE_BF16, stream, &wsw) == DCP_OK);
+    CHECK(dcp_workspace_create(fake(kWsBuf), ws_bytes(100000, 16, 4), 100000, 16, 4, 512, DCP_DTYPE_BF16, stream,
+                               &wsw) == DCP_OK);
     const uintptr_t wattn = uintptr_t{1} << 44, wlse = uintptr_t{2} << 44, wout = uintptr_t{3} << 44;
     rc = dcp::plan_merge(wsw, fake(wattn), 70000, H, H * D, D, reinterpret_cast<const float*>(wlse), DCP_LSE_BHC,
                          16 * 4, 4, 1, DCP_LSE_BASE_E, fake(wout), 16 * D, D, nullptr, 0, stream, &plan);
@@ -297,13 +308,44 @@ int main() {
 
     // Workspace creation errors.
     dcp_workspace* bad = nullptr;
-    CHECK(dcp_workspace_create(0, 16, 4, 512, 0, stream, &bad) == DCP_ERR_INVALID_ARG && bad == nullptr);
-    CHECK(dcp_workspace_create(8, 0, 4, 512, 0, stream, &bad) == DCP_ERR_INVALID_ARG);
-    CHECK(dcp_workspace_create(8, 16, 65, 512, 0, stream, &bad) == DCP_ERR_INVALID_ARG);
-    CHECK(dcp_workspace_create(8, 16, 4, 256, 0, stream, &bad) == DCP_ERR_LAYOUT);
-    CHECK(dcp_workspace_create(8, 16, 4, 512, 3, stream, &bad) == DCP_ERR_LAYOUT);
-    CHECK(dcp_workspace_create(8, 16, 4, 512, 0, stream, nullptr) == DCP_ERR_INVALID_ARG);
-    CHECK(dcp_workspace_create(int64_t{1} << 27, 16, 4, 512, 0, stream, &bad) == DCP_ERR_INVALID_ARG);
+    void* wb = fake(kWsBuf);
+    const size_t big = size_t{1} << 40;
+    CHECK(dcp_workspace_create(wb, big, 0, 16, 4, 512, 0, stream, &bad) == DCP_ERR_INVALID_ARG && bad == nullptr);
+    CHECK(dcp_workspace_create(wb, big, 8, 0, 4, 512, 0, stream, &bad) == DCP_ERR_INVALID_ARG);
+    CHECK(dcp_workspace_create(wb, big, 8, 16, 65, 512, 0, stream, &bad) == DCP_ERR_INVALID_ARG);
+    CHECK(dcp_workspace_create(wb, big, 8, 16, 4, 256, 0, stream, &bad) == DCP_ERR_LAYOUT);
+    CHECK(dcp_workspace_create(wb, big, 8, 16, 4, 512, 3, stream, &bad) == DCP_ERR_LAYOUT);
+    CHECK(dcp_workspace_create(wb, big, 8, 16, 4, 512, 0, stream, nullptr) == DCP_ERR_INVALID_ARG);
+    CHECK(dcp_workspace_create(wb, big, int64_t{1} << 27, 16, 4, 512, 0, stream, &bad) == DCP_ERR_INVALID_ARG);
+    // The device buffer: its size, too small or missing, misaligned.
+    size_t need = 0;
+    CHECK(dcp_workspace_size(8, 16, 4, 512, 0, &need) == DCP_OK);
+    CHECK(need == size_t{8} * 16 * 4 * 1024 + size_t{8} * 16 * 4 * 4);  // both regions already multiples of 256
+    CHECK(dcp_workspace_size(3, 5, 3, 512, 1, &need) == DCP_OK);
+    CHECK(need == (size_t{45} * 1024 + 255) / 256 * 256 + (size_t{45} * 4 + 255) / 256 * 256);
+    CHECK(dcp_workspace_size(0, 16, 4, 512, 0, &need) == DCP_ERR_INVALID_ARG);
+    CHECK(dcp_workspace_size(8, 16, 4, 512, 0, nullptr) == DCP_ERR_INVALID_ARG);
+    CHECK(dcp_workspace_create(wb, ws_bytes(8, 16, 4) - 1, 8, 16, 4, 512, 0, stream, &bad) == DCP_ERR_WORKSPACE &&
+          bad == nullptr);
+    CHECK(std::strstr(dcp_last_error(), "dcp_workspace_size") != nullptr);
+    CHECK(dcp_workspace_create(nullptr, big, 8, 16, 4, 512, 0, stream, &bad) == DCP_ERR_WORKSPACE);
+    CHECK(dcp_workspace_create(fake(kWsBuf + 8), big, 8, 16, 4, 512, 0, stream, &bad) == DCP_ERR_ALIGN);
+    // The landing zone: [capacity, H, D] payload at the buffer's start, the [capacity, H] LSEs after it.
+    dcp_workspace* wz = nullptr;
+    CHECK(dcp_workspace_create(fake(kWsBuf), ws_bytes(3, 5, 3), 3, 5, 3, 512, 0, stream, &wz) == DCP_OK);
+    void* ra = nullptr;
+    float* rl = nullptr;
+    int64_t rsb = 0, rsh = 0, rlsb = 0;
+    CHECK(dcp_workspace_recv(wz, &ra, &rsb, &rsh, &rl, &rlsb) == DCP_OK);
+    CHECK(reinterpret_cast<uintptr_t>(ra) == kWsBuf && rsb == 15 * 512 && rsh == 512 && rlsb == 15);
+    CHECK(reinterpret_cast<uintptr_t>(rl) == kWsBuf + (45 * 1024 + 255) / 256 * 256);
+    CHECK(dcp_workspace_recv(wz, &ra, &rsb, nullptr, &rl, &rlsb) == DCP_ERR_INVALID_ARG);
+    // A staged merge over the landing zone plans like any other.
+    rc = dcp::plan_merge(wz, ra, 3, 15, rsb, rsh, rl, DCP_LSE_BH1, rlsb, 1, 0, DCP_LSE_BASE_E, fake(out), 5 * D, D,
+                         nullptr, 0, stream, &plan);
+    CHECK(rc == DCP_OK && plan.args.a_ss == 5 * D && plan.args.l_ss == 5 && plan.n_chunks == 1);
+    CHECK(dcp_workspace_destroy(wz) == DCP_OK);
+    CHECK(dcp_workspace_recv(nullptr, &ra, &rsb, &rsh, &rl, &rlsb) == DCP_ERR_WORKSPACE);
 
     CHECK(dcp_workspace_destroy(ws) == DCP_OK);
     CHECK(dcp_workspace_destroy(ws6) == DCP_OK);

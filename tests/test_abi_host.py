@@ -52,7 +52,8 @@ def test_workspace_errors_through_the_binding():
     with pytest.raises(dcp.DcpError) as e:
         dcp.dcp_workspace_create(8, 16, 4, d=128, stream=0x1000)
     assert e.value.status == dcp.DCP_ERR_LAYOUT
-    ws = dcp.dcp_workspace_create(8, 16, 4, stream=0x1000)
+    fake = 0x7 << 40          # a device address the library stores but never touches
+    ws = dcp.dcp_workspace_create(8, 16, 4, stream=0x1000, buf=fake, buf_bytes=dcp.dcp_workspace_size(8, 16, 4))
     assert ws.handle
     dcp.dcp_workspace_set_load_policy(ws, dcp.DCP_LOAD_CACHED)
     dcp.dcp_workspace_set_load_policy(ws, dcp.DCP_LOAD_STREAMING)
@@ -64,6 +65,31 @@ def test_workspace_errors_through_the_binding():
     assert e.value.status == dcp.DCP_ERR_LAYOUT
     dcp.dcp_workspace_destroy(ws)
     assert ws.handle is None
+
+
+def test_workspace_buffer_size_and_rejection_through_the_binding():
+    """dcp_workspace_size is the landing zone's size (capacity x h_local x cp rows of D bf16/fp16 values plus one
+    fp32 LSE each, regions rounded to 256 bytes); create rejects a missing, smaller or misaligned buffer before
+    making anything."""
+    import context_lse_merge_amd as dcp
+    fake = 0x7 << 40
+    for cap, hl, cp, dt in ((128, 16, 4, dcp.DCP_DTYPE_BF16), (3, 5, 3, dcp.DCP_DTYPE_FP16), (1, 1, 1, 0)):
+        rows = cap * hl * cp
+        want = (rows * 1024 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+        n = dcp.dcp_workspace_size(cap, hl, cp, dtype=dt)
+        assert n == want
+        ws = dcp.dcp_workspace_create(cap, hl, cp, dtype=dt, stream=0x1000, buf=fake, buf_bytes=n)
+        ws.close()
+        with pytest.raises(dcp.DcpError) as e:
+            dcp.dcp_workspace_create(cap, hl, cp, dtype=dt, stream=0x1000, buf=fake, buf_bytes=n - 1)
+        assert e.value.status == dcp.DCP_ERR_WORKSPACE and "dcp_workspace_size" in str(e.value)
+    with pytest.raises(dcp.DcpError) as e:
+        dcp.dcp_workspace_create(8, 16, 4, stream=0x1000, buf=0, buf_bytes=1 << 30)
+    assert e.value.status == dcp.DCP_ERR_WORKSPACE
+    with pytest.raises(dcp.DcpError) as e:
+        dcp.dcp_workspace_create(8, 16, 4, stream=0x1000, buf=fake + 8, buf_bytes=1 << 30)
+    assert e.value.status == dcp.DCP_ERR_ALIGN
+    assert dcp.dcp_workspace_size(128, 16, 4) == 128 * 16 * 4 * (1024 + 4)
 
 
 def test_varlen_scratch_size_limits_through_the_binding():

@@ -428,3 +428,39 @@ def test_graph_replays_with_changing_inputs_interleaved_with_eager():
         torch.cuda.synchronize()
     ws_graph.close()
     ws_eager.close()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_staged_merge_in_the_workspace_landing_zone(dtype):
+    """A caller gathers the shards into the workspace's landing zone -- each shard's [B, h_local, D] head slice and
+    its LSEs copied in from a buffer of its own, as an exchange would deliver them -- and merges them there.  A batch
+    wider than the capacity is staged and merged chunk by chunk.  The result meets the oracle and equals the in-place
+    merge of the same values bit for bit."""
+    import context_lse_merge_amd as dcp
+    B, cap = 150, 64
+    c = synth.kimi_merge(B, dtype=dtype)
+    hl, cp = c.h_local, c.cp
+    ref_out, ref_lse = gpu_merge(c)                      # in place, one launch
+    shards = [c.attn[:, s * hl:(s + 1) * hl].contiguous().to(DEV) for s in range(cp)]
+    shard_lse = [c.lse[:, :, s].contiguous().to(DEV) for s in range(cp)]     # BHC [B, hl, cp] -> per shard [B, hl]
+    wdt = dcp.DCP_DTYPE_FP16 if dtype == torch.float16 else dcp.DCP_DTYPE_BF16
+    ws = dcp.dcp_workspace_create(cap, hl, cp, dtype=wdt)
+    assert ws.buf.numel() == dcp.dcp_workspace_size(cap, hl, cp, dtype=wdt)
+    r_attn, r_lse = dcp.dcp_workspace_recv(ws)
+    assert tuple(r_attn.shape) == (cap, cp * hl, synth.D) and tuple(r_lse.shape) == (cap, cp * hl)
+    out = torch.empty((B, hl, synth.D), dtype=dtype, device=DEV)
+    out_lse = torch.empty((B, hl), dtype=torch.float32, device=DEV)
+    announce("staged merge through the landing zone: %s B=%d capacity=%d" % (synth.payload_name(c.attn), B, cap))
+    for t0 in range(0, B, cap):
+        n = min(cap, B - t0)
+        r_attn[:n].fill_(float("nan"))                   # stale contents are overwritten by the staging below
+        for s in range(cp):
+            r_attn[:n, s * hl:(s + 1) * hl].copy_(shards[s][t0:t0 + n])
+            r_lse[:n, s * hl:(s + 1) * hl].copy_(shard_lse[s][t0:t0 + n])
+        dcp.dcp_lse_combine(ws, r_attn[:n], r_lse[:n], dcp.DCP_LSE_BH1, dcp.DCP_LSE_BASE_E, out[t0:t0 + n],
+                            out_lse[t0:t0 + n])
+    torch.cuda.synchronize()
+    ws.close()
+    check_against_oracle(c, out, out_lse)
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(out_lse.view(torch.int32), ref_lse.view(torch.int32))
