@@ -6,13 +6,17 @@ synthetic batch (every chunk included), i.e. the whole hot path -- layout
 adapter, chunk planner, LSE reduction, weighted accumulation, store.
 
 Timing.  Inputs are resident in HBM before the timed region starts.  Calls
-are captured into HIP graphs of 60 calls each (one per MLA layer of a decode
-step), cycling over enough copies of the input that consecutive uses of the
-same bytes are at least 1 GiB apart -- more than the 256 MB Infinity Cache --
-so the figure is an HBM (cold-cache) figure.  The timed region is bracketed by
-a barrier and torch.cuda.synchronize(), and measured with HIP events on the
-stream the graphs are launched on.  A hot-cache figure (same buffers every
-call) is reported beside it.
+are captured into HIP graphs of min(60, steps) calls each (60: one per MLA
+layer of a decode step).  The timed calls read input sets of their own: all
+distinct when they fit in 1 GiB, else cycled so that the same bytes come back
+only after at least 1 GiB of other inputs -- more than the 256 MB Infinity
+Cache.  Warm-up calls run on a separate set in a separate graph; then 1 GiB of
+unrelated data is read, so every timed input comes from HBM (a cold-cache
+figure).  A bounded spin kernel queued before the start event keeps the GPU
+busy while the host submits the timed graph launches, so the region holds GPU
+work only.  The region is bracketed by a barrier and torch.cuda.synchronize()
+and measured with HIP events on the stream the graphs are launched on.  A
+hot-cache figure (same buffers every call) is reported beside it.
 
 Output: one JSON line (rank 0).  ``value`` is achieved HBM throughput in GB/s
 = algorithmic bytes per layer-merge / time per layer-merge, where algorithmic
@@ -119,11 +123,11 @@ class GpuCase:
         self.mode = dcp.DCP_LSE_BASE_E if case.lse_mode == "e" else dcp.DCP_LSE_BASE_2
 
     def call(self, ws, k, stream):
-        attn, lse, out, out_lse = self.sets[k % len(self.sets)]
+        attn, lse, out, out_lse = self.sets[k]
         self.dcp.dcp_lse_combine(ws, attn, lse, self.layout, self.mode, out, out_lse, stream=stream)
 
-    def capture(self, ngraphs, calls_per_graph):
-        """HIP graphs of `calls_per_graph` calls each, together cycling over every set."""
+    def capture(self, set_lists):
+        """One HIP graph per list of set indices, calling the sets in that order."""
         import torch
         stream = torch.cuda.Stream()
         dtype = self.dcp.DCP_DTYPE_FP16 if self.case.attn.dtype == torch.float16 else self.dcp.DCP_DTYPE_BF16
@@ -137,13 +141,11 @@ class GpuCase:
                 self.call(ws, k, stream)
         torch.cuda.synchronize()
         graphs = []
-        k = 0
-        for _ in range(ngraphs):
+        for ks in set_lists:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
-                for _ in range(calls_per_graph):
+                for k in ks:
                     self.call(ws, k, stream)
-                    k += 1
             graphs.append(g)
         torch.cuda.synchronize()
         self.ws = ws
@@ -156,15 +158,51 @@ def barrier():
         dist.barrier()
 
 
-def time_graphs(graphs, replays):
-    """Replay graphs round-robin `replays` times; returns elapsed ms (HIP events on
-    the stream the replays are launched on)."""
+_SLEEP_CYCLES_PER_MS = []
+
+
+def gpu_delay(ms):
+    """Queue a spin kernel of about `ms` milliseconds on the current stream (torch's bounded sleep kernel,
+    calibrated once with HIP events).  Queued ahead of a start event, it keeps the GPU busy while the host submits
+    the graph launches that follow, so the timed region holds GPU work only, not host submission."""
+    import torch
+    if not _SLEEP_CYCLES_PER_MS:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        torch.cuda._sleep(1 << 20)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS.append((1 << 20) / max(e0.elapsed_time(e1), 1e-3))
+    torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS[0]))
+
+
+_SCRUB = []
+
+
+def evict_caches():
+    """Read 1 GiB that no measurement uses: every cached byte of earlier work (L2, Infinity Cache) is displaced,
+    and dirty lines are written back before the timed region, not during it."""
+    import torch
+    if not _SCRUB:
+        _SCRUB.append(torch.ones(COLD_BYTES // 2, dtype=torch.bfloat16, device="cuda:0"))
+    torch.sum(_SCRUB[0])
+
+
+def time_graphs(graphs, replays, evict=False):
+    """Replay graphs round-robin from graphs[0], `replays` times; returns elapsed ms, HIP events on the stream the
+    replays are launched on, bracketed by a barrier and a synchronize on both sides.  A spin kernel queued before
+    the start event covers the host's submission of the replays; with `evict`, 1 GiB of unrelated data is read
+    between the spin kernel and the start event."""
     import torch
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     barrier()
     torch.cuda.synchronize()
+    gpu_delay(1.0 + 0.05 * replays)
+    if evict:
+        evict_caches()          # runs right before the start event: the GPU is not idle when timing starts
     start.record(stream)
     for r in range(replays):
         graphs[r % len(graphs)].replay()
@@ -174,33 +212,62 @@ def time_graphs(graphs, replays):
     return start.elapsed_time(end)
 
 
-def measure(case, steps, warmup, capacity=None, cold=True, cached=False):
-    """Returns (us per layer-merge, number of input sets, footprint bytes).
-    ``cached``: the workspace's DCP_LOAD_CACHED policy instead of streaming."""
-    per_set = case.attn.numel() * 2 + case.lse.numel() * 4 + case.B * case.h_local * (1024 + 4)
+def warm_up(graph, calls, warmup):
+    """Replay a warm-up graph of `calls` calls until at least `warmup` calls ran; returns how many ran."""
+    import torch
+    if warmup <= 0:
+        return 0
+    n = math.ceil(warmup / calls)
+    for _ in range(n):
+        graph.replay()
+    torch.cuda.synchronize()
+    return n * calls
+
+
+def plan_sets(per_set, steps, cold):
+    """Which input set each timed call reads.  Returns (calls per graph, timed sets, one list of set indices per
+    timed graph, the warm-up set).  The timed region replays the graphs in order, round-robin, steps / calls times.
+    cold: the timed calls read sets [0, n) -- every call a different one when steps fit in the reuse distance, else
+    n >= 1 GiB / per_set sets cycled in order -- and the warm-up reads set n, which no timed call reads.  hot: set 0
+    throughout."""
     calls = min(GRAPH_CALLS, steps)
-    if steps % calls:
-        raise SystemExit("--steps must be a multiple of %d" % calls)
-    # The graphs together call every set exactly once, round-robin, so the same
-    # bytes come back only after all the other sets (>= 1 GiB, or 1020 sets).
-    ngraphs = max(1, min(1024 // calls, math.ceil(COLD_BYTES / per_set / calls))) if cold else 1
-    nsets = ngraphs * calls if cold else 1
-    g = GpuCase(case, nsets, capacity or case.B)
+    if steps <= 0 or steps % calls:
+        raise SystemExit("--steps must be a positive multiple of %d" % calls)
+    if not cold:
+        return calls, 1, [[0] * calls], 0
+    reuse = math.ceil(COLD_BYTES / per_set)
+    n_sets = min(steps, math.ceil(reuse / calls) * calls)
+    timed = [list(range(g * calls, (g + 1) * calls)) for g in range(n_sets // calls)]
+    return calls, n_sets, timed, n_sets
+
+
+def measure(case, steps, warmup, capacity=None, cold=True, cached=False):
+    """Time `steps` layer-merges in HIP graphs of `calls` calls each.
+
+    cold: the timed calls use input sets of their own, all distinct when they fit in the reuse distance, else
+    cycled so that the same bytes come back only after >= 1 GiB of other inputs; warm-up runs on a separate set
+    and separate graphs; then 1 GiB of unrelated data is read, so every timed input comes from HBM.  hot: every
+    call (warm-up and timed) uses one set.  ``cached``: the workspace's DCP_LOAD_CACHED policy.
+    Returns a dict: us per layer-merge, calls per graph, timed input sets, warm-up calls, footprint, first set."""
+    per_set = case.attn.numel() * 2 + case.lse.numel() * 4 + case.B * case.h_local * (1024 + 4)
+    calls, n_sets, timed, warm_set = plan_sets(per_set, steps, cold)
+    g = GpuCase(case, max(n_sets, warm_set + 1), capacity or case.B)
     g.cached = cached
-    graphs = g.capture(ngraphs, calls)
-    wrep = max(1, math.ceil(warmup / calls))
-    time_graphs(graphs, wrep)
-    ms = time_graphs(graphs, steps // calls)
+    w_calls = max(1, min(warmup, calls))
+    graphs = g.capture(timed + [[warm_set] * w_calls])
+    warm_calls = warm_up(graphs[-1], w_calls, warmup)
+    ms = time_graphs(graphs[:-1], steps // calls, evict=cold)
     us = ms * 1000.0 / steps
     first = g.sets[0]
     g.ws.close()
-    return us, nsets, nsets * per_set, first
+    return {"us": us, "calls": calls, "sets": n_sets, "warm_calls": warm_calls, "footprint": n_sets * per_set,
+            "first": first, "reuse_distance_bytes": (n_sets * per_set if steps > n_sets else None)}
 
 
 def launch_floor(steps, warmup):
-    """us per launch of a one-element fill kernel (one workgroup) in the same
-    harness -- graphs of GRAPH_CALLS launches on one stream: the fixed cost
-    every layer-merge pays before moving any bytes."""
+    """us per launch of a one-element fill kernel (one workgroup) in the same harness -- graphs of GRAPH_CALLS
+    launches on one stream, warmed up, a spin kernel ahead of the start event: the fixed cost every layer-merge
+    pays before moving any bytes."""
     import torch
     buf = torch.zeros(1, device="cuda:0")
     calls = min(GRAPH_CALLS, steps)
@@ -212,7 +279,7 @@ def launch_floor(steps, warmup):
     with torch.cuda.graph(g, stream=stream):
         for _ in range(calls):
             buf.fill_(1.0)
-    time_graphs([g], max(1, math.ceil(warmup / calls)))
+    warm_up(g, calls, warmup)
     return time_graphs([g], steps // calls) * 1000.0 / steps
 
 
@@ -237,8 +304,8 @@ def copy_ceiling(headline_bytes):
         with torch.cuda.graph(g, stream=stream):
             for i in range(calls):
                 dst[i % sets].copy_(src[i % sets])
-        time_graphs([g], 2)
-        us = time_graphs([g], 5) * 1000.0 / (5 * calls)
+        warm_up(g, calls, 2 * calls)
+        us = time_graphs([g], 5, evict=True) * 1000.0 / (5 * calls)
         res[label] = (us, 2.0 * n * 2 / (us * 1e-6) / 1e9)
         del src, dst, g
         torch.cuda.empty_cache()
@@ -393,6 +460,7 @@ def measure_producer(B, kv_copies, reps=8, seq_lens=None, replays=5):
         ts = []
         for _ in range(max(replays, int(math.ceil(20.0 / once_ms)))):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gpu_delay(0.2)                # covers the host's submission of the replay
             e0.record()                   # a replay runs on the current stream
             g.replay()
             e1.record()
@@ -526,6 +594,16 @@ def counters_traffic():
         return None
 
 
+def cache_note(m):
+    if m["reuse_distance_bytes"] is None:
+        reuse = "each timed call reads an input set no other timed call uses"
+    else:
+        reuse = "the timed calls cycle over %d input sets, so the same bytes come back only after %.2f GB of " \
+                "other inputs" % (m["sets"], m["reuse_distance_bytes"] / 1e9)
+    return ("cold: %s; warm-up ran on a separate set and separate graphs, then 1 GiB of unrelated data was read "
+            "before the timed region" % reuse)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -543,11 +621,12 @@ def main():
     alg = algorithmic_bytes(case)
     print("[bench] %s: %d algorithmic bytes per layer-merge" % (workload_name(case, args.workload), alg),
           file=sys.stderr, flush=True)
-    us, nsets, footprint, first = measure(case, args.steps, args.warmup, capacity=capacity, cold=True)
-    ok = parity_check(case, first[2], first[3])
-    us_hot = None if args.no_hot else measure(case, args.steps, args.warmup, capacity=capacity, cold=False)[0]
+    head = measure(case, args.steps, args.warmup, capacity=capacity, cold=True)
+    us = head["us"]
+    ok = parity_check(case, head["first"][2], head["first"][3])
+    us_hot = None if args.no_hot else measure(case, args.steps, args.warmup, capacity=capacity, cold=False)["us"]
     us_hot_cached = None if args.no_hot else measure(case, args.steps, args.warmup, capacity=capacity, cold=False,
-                                                     cached=True)[0]
+                                                     cached=True)["us"]
     gbs = alg / (us * 1e-6) / 1e9
     print("[bench] cold %.3f us (%.1f GB/s), hot %s us, hot with DCP_LOAD_CACHED %s us, parity %s"
           % (us, gbs, us_hot, us_hot_cached, ok), file=sys.stderr, flush=True)
@@ -560,11 +639,12 @@ def main():
             for B in Bs:
                 c = make_case(wl, B)
                 cap = 128 if wl.startswith("stress") else B
-                u, n, fp, _ = measure(c, 120, 60, capacity=cap, cold=True)
+                m = measure(c, 120, 60, capacity=cap, cold=True)
+                u = m["us"]
                 a = algorithmic_bytes(c)
                 sweep.append({"workload": wl, "B": B, "us": round(u, 3), "GBps": round(a / (u * 1e-6) / 1e9, 1),
                               "frac_of_peak": round(a / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": a,
-                              "input_sets": n, "footprint_MB": round(fp / 1e6, 1)})
+                              "input_sets": m["sets"], "footprint_MB": round(m["footprint"] / 1e6, 1)})
                 print("[bench] sweep %s B=%d: %.3f us, %.1f GB/s" % (wl, B, u, sweep[-1]["GBps"]), file=sys.stderr,
                       flush=True)
         # hot inputs (the same buffers every call, as when the partials were just
@@ -573,7 +653,7 @@ def main():
             c = make_case("kimi", B)
             a = algorithmic_bytes(c)
             for cached in (False, True):
-                u = measure(c, 120, 60, capacity=B, cold=False, cached=cached)[0]
+                u = measure(c, 120, 60, capacity=B, cold=False, cached=cached)["us"]
                 sweep.append({"workload": "kimi hot " + ("DCP_LOAD_CACHED" if cached else "DCP_LOAD_STREAMING"),
                               "B": B, "us": round(u, 3), "GBps": round(a / (u * 1e-6) / 1e9, 1),
                               "frac_of_peak": round(a / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": a,
@@ -620,8 +700,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_name(case, args.workload), "B": case.B, "H": case.H, "cp": case.cp,
                    "D": 512, "lse_layout": case.lse_layout, "lse_mode": case.lse_mode, "capacity": capacity,
-                   "graph_calls": GRAPH_CALLS, "input_sets": nsets, "footprint_MB": round(footprint / 1e6, 1),
-                   "cache": "cold: each input reused only after >= 1 GiB of other inputs"},
+                   "graph_calls": head["calls"], "timed_graph_replays": args.steps // head["calls"],
+                   "input_sets": head["sets"], "footprint_MB": round(head["footprint"] / 1e6, 1),
+                   "warmup_calls_run": head["warm_calls"],
+                   "cache": cache_note(head)},
         "us_per_layer_merge": round(us, 3),
         "us_per_layer_merge_hot": None if us_hot is None else round(us_hot, 3),
         "us_per_layer_merge_hot_cached_policy": None if us_hot_cached is None else round(us_hot_cached, 3),

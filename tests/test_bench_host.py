@@ -19,3 +19,25 @@ def test_help_lists_the_contract_options():
     assert r.returncode == 0
     for opt in ("--gpus", "--steps", "--warmup"):
         assert opt in r.stdout
+
+
+def test_cold_set_plan_meets_its_stated_conditions():
+    """The timed calls of a cold measurement read each input set either once, or again only after >= 1 GiB of other
+    sets; the warm-up set is never read by a timed call; the graphs hold the calls the line reports."""
+    sys.path.insert(0, ROOT)
+    import bench
+    for per_set in (82_240 + 1024, 10_526_720 + 4096, 75_800_000, 300_000_000):
+        for steps in (20, 60, 120, 600, 1200):
+            calls, n, timed, warm = bench.plan_sets(per_set, steps, cold=True)
+            assert calls == min(60, steps) and all(len(g) == calls for g in timed)
+            order = [k for r in range(steps // calls) for k in timed[r % len(timed)]]
+            assert len(order) == steps and warm not in order
+            last = {}
+            for i, k in enumerate(order):
+                if k in last:
+                    assert (i - last[k]) * per_set >= bench.COLD_BYTES, (per_set, steps)
+                last[k] = i
+            if steps * per_set <= bench.COLD_BYTES:
+                assert len(set(order)) == steps
+    calls, n, timed, warm = bench.plan_sets(10_530_816, 20, cold=False)
+    assert (calls, n, warm) == (20, 1, 0) and timed == [[0] * 20]
