@@ -24,8 +24,10 @@
 //    with no cross-lane step; a row whose weights are all nonzero takes a
 //    plain FMA path, a row with an empty shard (weight exactly 0, which covers
 //    lse = -inf) zeroes that shard's payload first, so it is never used;
-//  * cp > 16: lane s holds lse_s and the max and the sum over shards are
-//    wavefront DPP reductions inside 16-lane rows plus lane reads across rows;
+//  * cp > 16: lane s holds lse_s; the maximum and the sum run over the lanes
+//    in ascending shard order (the same order as for cp <= 16), and the
+//    payloads stream in 16 shards at a time, each group's loads issued before
+//    the previous group's FMAs;
 //  * fp32 FMAs in ascending shard order, then the hardware round-to-nearest-
 //    even convert to the payload type and one 16-byte store per lane.  The
 //    payload is bf16 or fp16 (both are the pages' payload types); one kernel
@@ -34,147 +36,26 @@
 //    partials: fp16 rows stored multiplied by a power of two, whose inverse
 //    factor (read beside the LSE) multiplies the split's normalised weight.
 // The per-element arithmetic does not depend on B, on the chunking or on the
-// grid, so chunked and unchunked calls give identical bits.
+// grid, so chunked and unchunked calls give identical bits; it is the one in
+// merge_row.h, which every merge of partials in the library uses.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 
 #include "dcp_internal.h"
+#include "merge_row.h"
 
 namespace dcp {
 namespace {
 
+using mrow::Bf16;
+using mrow::F16;
+using mrow::Payload16;
+using mrow::u32x4;
+
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = 64 * kWavesPerBlock;
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// DPP controls (gfx9 encoding): quad_perm [1,0,3,2] and [2,3,0,1], then
-// row_half_mirror and row_mirror.  Applied in that order they combine all 16
-// lanes of a row, and every lane of the row ends up holding the result.
-constexpr int kDppQuadXor1 = 0xB1;
-constexpr int kDppQuadXor2 = 0x4E;
-constexpr int kDppRowHalfMirror = 0x141;
-constexpr int kDppRowMirror = 0x140;
-
-template <int Ctrl>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float row_max16(float v) {
-    v = fmaxf(v, dpp<kDppQuadXor1>(v));
-    v = fmaxf(v, dpp<kDppQuadXor2>(v));
-    v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
-    v = fmaxf(v, dpp<kDppRowMirror>(v));
-    return v;
-}
-
-__device__ __forceinline__ float row_sum16(float v) {
-    v = v + dpp<kDppQuadXor1>(v);
-    v = v + dpp<kDppQuadXor2>(v);
-    v = v + dpp<kDppRowHalfMirror>(v);
-    v = v + dpp<kDppRowMirror>(v);
-    return v;
-}
-
-__device__ __forceinline__ float lane_value(float v, int lane) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-// Reduce over the first `cp` lanes (cp <= 64) and return the result in a
-// scalar register.  Lanes >= cp must hold the identity of the reduction.
-template <int MaxCp>
-__device__ __forceinline__ float wave_max(float v, int cp) {
-    v = row_max16(v);
-    float m = lane_value(v, 0);
-    if (MaxCp > 16) {
-        if (cp > 16) m = fmaxf(m, lane_value(v, 16));
-        if (cp > 32) m = fmaxf(fmaxf(m, lane_value(v, 32)), lane_value(v, 48));
-    }
-    return m;
-}
-
-template <int MaxCp>
-__device__ __forceinline__ float wave_sum(float v, int cp) {
-    v = row_sum16(v);
-    float s = lane_value(v, 0);
-    if (MaxCp > 16) {
-        if (cp > 16) s = s + lane_value(v, 16);
-        if (cp > 32) s = s + (lane_value(v, 32) + lane_value(v, 48));
-    }
-    return s;
-}
-
-// The two 16-bit payload types.  A 32-bit word holds two elements, the
-// lower-addressed one in the low half; widening to fp32 is exact for both,
-// narrowing rounds to nearest even.
-struct Bf16 {
-    // bf16 is the high half of an fp32: shifting or masking widens it.
-    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
-    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-    static __device__ __forceinline__ uint32_t pack(float a, float b) {
-        return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
-               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
-    }
-};
-
-struct F16 {
-    static __device__ __forceinline__ float lo(uint32_t w) {
-        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
-    }
-    static __device__ __forceinline__ float hi(uint32_t w) {
-        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
-    }
-    static __device__ __forceinline__ uint32_t pack(float a, float b) {
-        return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(a))) |
-               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(b))) << 16);
-    }
-};
-
-// How a lane reads its 8 columns of one shard row and accumulates them: one
-// 16-byte load.  kScaled: the row was stored multiplied by a power of two
-// (the MLA decode's split partials, fp16, inside the library only) and its
-// weight is multiplied by the factor stored sc_off floats after its LSE.
-// `zero` replaces the row by zeros -- a select on the loaded words, not a
-// branch, so the loads stay ahead of their use -- and the all-zero word is +0
-// in every payload type, so an empty shard adds exactly +0 whatever it held
-// (NaN included).
-// One 16-byte load, non-temporal (NT) or plain.
-template <bool NT>
-__device__ __forceinline__ u32x4 load16(const u32x4* p) {
-    if (NT) return __builtin_nontemporal_load(p);
-    return *p;
-}
-
-template <typename T, bool NT, bool Scaled = false>
-struct Payload16 {
-    static constexpr bool kScaled = Scaled;
-    typedef u32x4 row_t;
-    static __device__ __forceinline__ row_t load(const void* base, int64_t off) {
-        return load16<NT>(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off));
-    }
-    static __device__ __forceinline__ row_t zero_unless(bool use, row_t v) {
-        row_t z;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] = use ? v[i] : 0u;
-        return z;
-    }
-    static __device__ __forceinline__ void fma(float (&acc)[8], float w, row_t v) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = fmaf(w, T::lo(v[i]), acc[2 * i]);
-            acc[2 * i + 1] = fmaf(w, T::hi(v[i]), acc[2 * i + 1]);
-        }
-    }
-};
-
-// acc += w * v; a shard with weight exactly 0 (an empty one) adds +0.
-template <typename In>
-__device__ __forceinline__ void fma8(float (&acc)[8], float w, typename In::row_t v) {
-    In::fma(acc, w, In::zero_unless(w != 0.0f, v));
-}
 
 // Grid: x = group g of kWavesPerBlock local heads, y = token b of the chunk;
 // wavefront w of block (g, b) merges local head j = g * kWavesPerBlock + w.
@@ -219,39 +100,13 @@ MergeTail tail_of(const MergeArgs& a) {
     return MergeTail{a.out, a.out_lse, a.o_sb, a.o_sj, a.ol_sb, a.sc_off, a.to_log2, a.from_log2, a.cp};
 }
 
-// Weights of one row from the LSE held by lane s (lanes >= cp hold -inf).
-// Returns the normalised weight of the lane's shard; S receives the sum of
-// the unnormalised weights (0 when every shard is empty) and M the maximum.
-// An all-empty row needs no branch: every weight is 0, S = 0, the guarded
-// reciprocal is 0, and the merged LSE M + log2(0) is -inf.
-// v_exp_f32 / v_log_f32 / v_rcp_f32 are the hardware's 1-ulp instructions;
-// exponents below -126 flush the weight to 0, i.e. a shard whose weight is
-// under 2^-126 of the largest is skipped.
-template <int MaxCp>
-__device__ __forceinline__ float row_weights(float to_log2, float x, int cp, float& M, float& S) {
-    M = wave_max<MaxCp>(x, cp);
-    const float w = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x - M) * to_log2);
-    S = wave_sum<MaxCp>(w, cp);
-    const float inv = (S > 0.0f) ? __builtin_amdgcn_rcpf(S) : 0.0f;
-    return w * inv;
-}
-
-__device__ __forceinline__ float merged_lse(const MergeTail& t, float M, float S) {
-    // S = 0 (all shards empty) gives log2(0) = -inf and M = -inf: L = -inf.
-    return M + __builtin_amdgcn_logf(S) * t.from_log2;
-}
-
 // The output row always leaves with a non-temporal store, under either load
 // policy: measured, that is the faster store both when the partials stream in
 // from HBM and when they are read from the caches (B = 512 hot: 5.05 us
 // against 5.79 us with plain stores).
 template <typename T>
 __device__ __forceinline__ void store_row(const MergeTail& t, Row r, int lane, const float (&acc)[8], float L) {
-    u32x4 packed;
-    packed[0] = T::pack(acc[0], acc[1]);
-    packed[1] = T::pack(acc[2], acc[3]);
-    packed[2] = T::pack(acc[4], acc[5]);
-    packed[3] = T::pack(acc[6], acc[7]);
+    const u32x4 packed = mrow::pack8<T>(acc);
     u32x4* dst = reinterpret_cast<u32x4*>(t.out + r.b * t.o_sb + r.j * t.o_sj + lane * 8);
     __builtin_nontemporal_store(packed, dst);
     if (t.out_lse && lane == 0) t.out_lse[r.b * t.ol_sb + r.j] = L;
@@ -298,10 +153,10 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const void* attn, const f
     float S = 0.0f;
 #pragma unroll
     for (int s = 0; s < CP; ++s) {
-        w[s] = (x[s] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x[s] - M) * t.to_log2);
+        w[s] = mrow::shard_weight(x[s], M, t.to_log2);
         S += w[s];
     }
-    const float inv = (S > 0.0f) ? __builtin_amdgcn_rcpf(S) : 0.0f;
+    const float inv = mrow::inv_sum(S);
     bool dense = true;
 #pragma unroll
     for (int s = 0; s < CP; ++s) {
@@ -316,52 +171,24 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const void* attn, const f
         for (int s = 0; s < CP; ++s) In::fma(acc, w[s], v[s]);
     } else {
 #pragma unroll
-        for (int s = 0; s < CP; ++s) fma8<In>(acc, w[s], v[s]);
+        for (int s = 0; s < CP; ++s) mrow::fma8<In>(acc, w[s], v[s]);
     }
-    store_row<Out>(t, r, lane, acc, merged_lse(t, M, S));
+    store_row<Out>(t, r, lane, acc, mrow::merged_lse(M, S, t.from_log2));
 }
 
-// 16 < cp <= 64: the same row algorithm with the shards taken G at a time.
-// Loads past the last shard re-read shard cp-1 (an address already being
-// fetched) and get weight 0.
+// 16 < cp <= 64: the same row arithmetic with the shards taken G at a time
+// (mrow::merge_row_any).
 template <int G, typename In, typename Out>
 __global__ __launch_bounds__(kBlock) void merge_kernel_wide(const void* attn, const float* lse, int32_t a_sb,
                                                             int32_t a_sj, int32_t a_ss, int32_t l_sb, int32_t l_sj,
                                                             int32_t l_ss, int32_t h_local, MergeTail t) {
     const int lane = threadIdx.x & 63;
     const Row r = row_of(h_local);
-    const int cp = t.cp;
-
-    const int ls = lane < cp ? lane : cp - 1;
-    const float* ll = lse + static_cast<int64_t>(r.b) * l_sb + static_cast<int64_t>(r.j) * l_sj +
-                      static_cast<int64_t>(ls) * l_ss;
-    const float xl = ll[0];
-    const float scl = In::kScaled ? ll[t.sc_off] : 1.0f;
     const int64_t orow = static_cast<int64_t>(r.b) * a_sb + static_cast<int64_t>(r.j) * a_sj + lane * 8;
-    typename In::row_t v[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) v[i] = In::load(attn, orow + static_cast<int64_t>(min(i, cp - 1)) * a_ss);
-    __builtin_amdgcn_sched_barrier(0);
-
-    const float x = lane < cp ? xl : -INFINITY;
-    float M, S;
-    float wn = row_weights<64>(t.to_log2, x, cp, M, S);
-    if (In::kScaled) wn *= scl;
-
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < cp; s0 += G) {
-        if (s0 > 0) {
-#pragma unroll
-            for (int i = 0; i < G; ++i)
-                v[i] = In::load(attn, orow + static_cast<int64_t>(min(s0 + i, cp - 1)) * a_ss);
-        }
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const float ws = (s0 + i < cp) ? lane_value(wn, min(s0 + i, 63)) : 0.0f;
-            fma8<In>(acc, ws, v[i]);
-        }
-    }
-    store_row<Out>(t, r, lane, acc, merged_lse(t, M, S));
+    const float* lrow = lse + static_cast<int64_t>(r.b) * l_sb + static_cast<int64_t>(r.j) * l_sj;
+    float acc[8], M, S;
+    mrow::merge_row_any<G, In>(attn, orow, a_ss, lrow, l_ss, t.sc_off, t.cp, t.to_log2, acc, M, S);
+    store_row<Out>(t, r, lane, acc, mrow::merged_lse(M, S, t.from_log2));
 }
 
 typedef void (*MergeKernel)(const void*, const float*, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
@@ -434,6 +261,7 @@ hipError_t launch(const MergeArgs& a, hipStream_t stream) {
 int merge_launch(const MergeArgs& a, void* stream) {
     return static_cast<int>(launch(a, static_cast<hipStream_t>(stream)));
 }
+
 
 }  // namespace dcp
 

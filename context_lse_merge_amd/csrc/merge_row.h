@@ -1,0 +1,192 @@
+// merge_row.h -- the per-row arithmetic of the DCP LSE merge, in one place.
+//
+// Every kernel that merges LSE-weighted partials -- the merge of DCP shards
+// (merge.hip), the reduction of the MLA decode's key splits (the same merge
+// kernel over scratch partials, the variable-length reducer in mla_varlen.hip,
+// and the fused epilogue of mla_decode.hip) -- forms one row's result with the
+// functions below, so they all give the same bits for the same inputs:
+//     M = max over s, ascending;   w_s = 2^((lse_s - M) * c), 0 for lse_s = -inf;
+//     S = sum of w_s, ascending from 0;   inv = 1/S (0 when S = 0);
+//     w^_s = w_s * inv (* the row's scale factor, for scaled partials);
+//     acc = sum of w^_s * O_s, ascending, fp32 FMA, a shard of weight 0 adding +0;
+//     L = M + log2(S) / c.
+// ("[DCP] Run fi_a2a on FlashInfer's fused all-to-all + LSE reduce", sglang PR
+// #40539, Motivation; "[Attention] Add direct symmetric-memory DCP A2A", vLLM
+// PR #48897: weights formed in fp32, empty shards publish -inf and their
+// payload is skipped.)  c = 1 for base-2 LSEs and log2 e for natural ones.
+// A lane owns 8 consecutive columns of the row: one 16-byte load per shard.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+namespace dcp {
+namespace mrow {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The two 16-bit payload types.  A 32-bit word holds two elements, the
+// lower-addressed one in the low half; widening to fp32 is exact for both,
+// narrowing rounds to nearest even.
+struct Bf16 {
+    // bf16 is the high half of an fp32: shifting or masking widens it.
+    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+    }
+};
+
+struct F16 {
+    static __device__ __forceinline__ float lo(uint32_t w) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+    }
+    static __device__ __forceinline__ float hi(uint32_t w) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+    }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) {
+        return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(a))) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(b))) << 16);
+    }
+};
+
+// One 16-byte load, non-temporal (NT) or plain.
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+    if (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+
+// How a lane reads its 8 columns of one shard row and accumulates them.
+// Scaled: the row was stored multiplied by a power of two (the MLA decode's
+// split partials, fp16, inside the library only); its weight is multiplied
+// by the factor stored sc_off floats after its LSE.  zero_unless replaces the
+// row by zeros -- a select on the loaded words, not a branch, so the loads
+// stay ahead of their use -- and the all-zero word is +0 in every payload
+// type, so an empty shard adds exactly +0 whatever it held (NaN included).
+template <typename T, bool NT, bool Scaled = false>
+struct Payload16 {
+    static constexpr bool kScaled = Scaled;
+    typedef u32x4 row_t;
+    static __device__ __forceinline__ row_t load(const void* base, int64_t off) {
+        return load16<NT>(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off));
+    }
+    static __device__ __forceinline__ row_t zero_unless(bool use, row_t v) {
+        row_t z;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = use ? v[i] : 0u;
+        return z;
+    }
+    static __device__ __forceinline__ void fma(float (&acc)[8], float w, row_t v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(w, T::lo(v[i]), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(w, T::hi(v[i]), acc[2 * i + 1]);
+        }
+    }
+};
+
+// acc += w * v; a shard with weight exactly 0 (an empty one) adds +0.  For a
+// nonzero w this is In::fma(acc, w, v) exactly.
+template <typename In>
+__device__ __forceinline__ void fma8(float (&acc)[8], float w, typename In::row_t v) {
+    In::fma(acc, w, In::zero_unless(w != 0.0f, v));
+}
+
+// Unnormalised weight of a shard with LSE x against the row maximum M.
+// v_exp_f32 is the hardware's 1-ulp exp2; an exponent below -126 flushes
+// the weight to 0, i.e. a shard under 2^-126 of the largest is skipped.
+__device__ __forceinline__ float shard_weight(float x, float M, float to_log2) {
+    return (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x - M) * to_log2);
+}
+
+// 1/S, or 0 when every shard is empty (S = 0).
+__device__ __forceinline__ float inv_sum(float S) { return (S > 0.0f) ? __builtin_amdgcn_rcpf(S) : 0.0f; }
+
+// The merged LSE in the input's base; S = 0 (all shards empty, M = -inf)
+// gives -inf.
+__device__ __forceinline__ float merged_lse(float M, float S, float from_log2) {
+    return M + __builtin_amdgcn_logf(S) * from_log2;
+}
+
+// The lane's 8 accumulators rounded to the output type, as one 16-byte word.
+template <typename T>
+__device__ __forceinline__ u32x4 pack8(const float (&acc)[8]) {
+    u32x4 p;
+    p[0] = T::pack(acc[0], acc[1]);
+    p[1] = T::pack(acc[2], acc[3]);
+    p[2] = T::pack(acc[4], acc[5]);
+    p[3] = T::pack(acc[6], acc[7]);
+    return p;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Merge of one row over a runtime number n >= 1 of shards, called by all 64
+// lanes of a wavefront with wave-uniform arguments.  Shard s's 8 columns of
+// this lane are In elements at attn + o0 + s*a_ss (o0 includes the lane's
+// column offset); its LSE is lrow[s*l_ss] and, for scaled payloads, its
+// factor lrow[s*l_ss + sc_off].  The LSEs come in 64 at a time, shard c0 + l
+// in lane l, and the sequential maximum and sum read them lane by lane; the
+// payloads come G shards at a time, the next group's loads issued before the
+// current group's FMAs.  Returns the accumulators, M and S.
+template <int G, typename In>
+__device__ __forceinline__ void merge_row_any(const void* attn, int64_t o0, int64_t a_ss, const float* lrow,
+                                              int64_t l_ss, int64_t sc_off, int n, float to_log2, float (&acc)[8],
+                                              float& M, float& S) {
+    const int lane = threadIdx.x & 63;
+    typedef typename In::row_t row_t;
+    row_t cur[G], nxt[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) cur[i] = In::load(attn, o0 + static_cast<int64_t>(min(i, n - 1)) * a_ss);
+
+    M = 0.0f;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+        const int m = min(64, n - c0);
+        const float x = lane < m ? lrow[static_cast<int64_t>(c0 + lane) * l_ss] : -INFINITY;
+        for (int i = 0; i < m; ++i) {
+            const float xi = lane_value(x, i);
+            M = (c0 + i == 0) ? xi : fmaxf(M, xi);
+        }
+    }
+    S = 0.0f;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+        const int m = min(64, n - c0);
+        const float x = lane < m ? lrow[static_cast<int64_t>(c0 + lane) * l_ss] : -INFINITY;
+        const float w = shard_weight(x, M, to_log2);
+        for (int i = 0; i < m; ++i) S += lane_value(w, i);
+    }
+    const float inv = inv_sum(S);
+
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+        const int m = min(64, n - c0);
+        const int64_t ls = static_cast<int64_t>(c0 + (lane < m ? lane : 0)) * l_ss;
+        float wl = shard_weight(lane < m ? lrow[ls] : -INFINITY, M, to_log2) * inv;
+        if (In::kScaled) wl *= lrow[ls + sc_off];
+        for (int g0 = 0; g0 < m; g0 += G) {
+            const int s_next = c0 + g0 + G;  // first shard of the next group
+            if (s_next < n) {
+#pragma unroll
+                for (int i = 0; i < G; ++i)
+                    nxt[i] = In::load(attn, o0 + static_cast<int64_t>(min(s_next + i, n - 1)) * a_ss);
+            }
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+                if (g0 + i < m) fma8<In>(acc, lane_value(wl, g0 + i), cur[i]);
+            if (s_next < n) {
+#pragma unroll
+                for (int i = 0; i < G; ++i) cur[i] = nxt[i];
+            }
+        }
+    }
+}
+
+}  // namespace mrow
+}  // namespace dcp

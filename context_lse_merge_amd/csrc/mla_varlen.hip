@@ -23,11 +23,10 @@
 //    in consecutive slots (fp16, each row scaled by a power of two whose
 //    inverse is stored beside its LSE), and the reduction kernel below
 //    merges them.
-// The reduction forms the weights exactly as the merge kernel of
-// dcp_lse_combine does (sequential maximum and sum in ascending split order,
-// normalised weights times the rows' scale factors, fp32 FMAs in ascending
-// split order), so a pair split at the same boundaries gives the same bits
-// on either path.  Which
+// The reduction is the merge's own row arithmetic (merge_row.h: sequential
+// maximum and sum in ascending split order, normalised weights times the
+// rows' scale factors, fp32 FMAs in ascending split order), so a pair split
+// at the same boundaries gives the same bits on either path.  Which
 // workgroup runs which split, and which slots a pair gets, depend on the
 // order of LDS atomics; the arithmetic of a split does not, so the results
 // are deterministic.
@@ -37,13 +36,13 @@
 #include <cstdint>
 
 #include "dcp_internal.h"
+#include "merge_row.h"
 
 namespace dcp {
 namespace {
 
 constexpr int kBins = kMlaPlanThreads;
 constexpr int kReduceWaves = 4;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int32_t token_len(const MlaArgs& a, int32_t b) {
     const int32_t L = a.seq_lens[b];
@@ -134,31 +133,12 @@ __global__ __launch_bounds__(kMlaPlanThreads) void varlen_plan_kernel(MlaArgs a)
     if (tid == 0) a.vl_hdr->n_split = s_split;
 }
 
-// The two fp16 halves of a 32-bit word, widened (exactly) to fp32.
-__device__ __forceinline__ float half_lo(uint32_t w) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
-}
-__device__ __forceinline__ float half_hi(uint32_t w) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
-}
-
-template <typename T>
-__device__ __forceinline__ uint32_t pack2(float x, float y);
-template <>
-__device__ __forceinline__ uint32_t pack2<__bf16>(float x, float y) {
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x))) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(y))) << 16);
-}
-template <>
-__device__ __forceinline__ uint32_t pack2<_Float16>(float x, float y) {
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x))) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(y))) << 16);
-}
-
 // Grid (kMlaRowsPerBlock / kReduceWaves, kVarlenTarget): block (x, y)
 // merges rows 4x .. 4x + 3 of split pair y, one row per wavefront; lane l
-// owns columns 8l .. 8l + 7.  Pairs past n_split exit.
-template <typename E>
+// owns columns 8l .. 8l + 7.  Pairs past n_split exit.  Split p of row r sits
+// in slot first + p: its fp16 row at part_o + ((first + p) * 128 + r) * 512,
+// its LSE and scale at part_lse / part_scale + (first + p) * 128 + r.
+template <typename Out>
 __global__ __launch_bounds__(64 * kReduceWaves) void varlen_reduce_kernel(MlaArgs a, float to_log2,
                                                                            float from_log2) {
     const VarlenHeader* hdr = a.vl_hdr;
@@ -175,50 +155,14 @@ __global__ __launch_bounds__(64 * kReduceWaves) void varlen_reduce_kernel(MlaArg
     if (h >= a.hq) return;
 
     const int64_t row0 = static_cast<int64_t>(sp.first) * kMlaRowsPerBlock + r;  // slot `first`, row r
-    const float* lse = a.part_lse + row0;                                          // split p at p * 128
-    const float* scl = a.part_scale + row0;
-    const uint16_t* po = a.part_o + row0 * kMlaVDim + 8 * lane;                    // split p at p * 128 * 512
-    const int64_t o_step = static_cast<int64_t>(kMlaRowsPerBlock) * kMlaVDim;
-    const int n = sp.n;
-
-    float M = lse[0];
-    for (int p = 1; p < n; ++p) M = fmaxf(M, lse[p * kMlaRowsPerBlock]);
-    float S = 0.0f;
-    for (int p = 0; p < n; ++p) {
-        const float x = lse[p * kMlaRowsPerBlock];
-        S += (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x - M) * to_log2);
-    }
-    const float inv = (S > 0.0f) ? __builtin_amdgcn_rcpf(S) : 0.0f;
-
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    constexpr int kBatch = 8;  // splits whose loads are in flight together
-    for (int p0 = 0; p0 < n; p0 += kBatch) {
-        u32x4 v[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            const int p = p0 + i < n ? p0 + i : n - 1;
-            v[i] = *reinterpret_cast<const u32x4*>(po + p * o_step);
-        }
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            if (p0 + i >= n) break;
-            const float x = lse[(p0 + i) * kMlaRowsPerBlock];
-            float w = ((x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((x - M) * to_log2)) * inv;
-            w *= scl[(p0 + i) * kMlaRowsPerBlock];  // undoes the row's power-of-two scaling
-            if (w == 0.0f) continue;  // an empty split adds +0 whatever its slot holds
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                acc[2 * k] = fmaf(w, half_lo(v[i][k]), acc[2 * k]);
-                acc[2 * k + 1] = fmaf(w, half_hi(v[i][k]), acc[2 * k + 1]);
-            }
-        }
-    }
-    u32x4 packed;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) packed[k] = pack2<E>(acc[2 * k], acc[2 * k + 1]);
+    const int64_t sc_off = a.part_scale - a.part_lse;
+    float acc[8], M, S;
+    mrow::merge_row_any<8, mrow::Payload16<mrow::F16, false, true>>(
+        a.part_o, row0 * kMlaVDim + 8 * lane, static_cast<int64_t>(kMlaRowsPerBlock) * kMlaVDim, a.part_lse + row0,
+        kMlaRowsPerBlock, sc_off, sp.n, to_log2, acc, M, S);
     const int64_t u = static_cast<int64_t>(s) * a.hq + h;
-    *reinterpret_cast<u32x4*>(a.o + b * a.o_sb + u * a.o_sh + 8 * lane) = packed;
-    if (lane == 0) a.lse[b * a.lse_sb + u] = M + __builtin_amdgcn_logf(S) * from_log2;
+    *reinterpret_cast<mrow::u32x4*>(a.o + b * a.o_sb + u * a.o_sh + 8 * lane) = mrow::pack8<Out>(acc);
+    if (lane == 0) a.lse[b * a.lse_sb + u] = mrow::merged_lse(M, S, from_log2);
 }
 
 }  // namespace
@@ -236,9 +180,9 @@ int varlen_reduce_launch(const MlaArgs& a, void* stream) {
     const dim3 grid(kMlaRowsPerBlock / kReduceWaves, kVarlenTarget);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (a.dtype == DCP_DTYPE_FP16)
-        varlen_reduce_kernel<_Float16><<<grid, dim3(64 * kReduceWaves), 0, s>>>(a, to_log2, from_log2);
+        varlen_reduce_kernel<mrow::F16><<<grid, dim3(64 * kReduceWaves), 0, s>>>(a, to_log2, from_log2);
     else
-        varlen_reduce_kernel<__bf16><<<grid, dim3(64 * kReduceWaves), 0, s>>>(a, to_log2, from_log2);
+        varlen_reduce_kernel<mrow::Bf16><<<grid, dim3(64 * kReduceWaves), 0, s>>>(a, to_log2, from_log2);
     return static_cast<int>(hipGetLastError());
 }
 
