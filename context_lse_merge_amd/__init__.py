@@ -49,11 +49,20 @@ DCP_LOAD_CACHED = _C["DCP_LOAD_CACHED"]
 DCP_KV_CONTIGUOUS = _C["DCP_KV_CONTIGUOUS"]
 DCP_KV_INTERLEAVED = _C["DCP_KV_INTERLEAVED"]
 DCP_NOALLOC_SCRATCH_BYTES = _C["DCP_NOALLOC_SCRATCH_BYTES"]
+DCP_FUSE_NONE = _C["DCP_FUSE_NONE"]
+DCP_FUSE_EPILOGUE = _C["DCP_FUSE_EPILOGUE"]
+DCP_FUSE_AUTO = _C["DCP_FUSE_AUTO"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         "context_lse_merge_amd: %s is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
         "(or python context_lse_merge_amd/_build.py) first" % LIB_PATH)
+
+# torch ships its own HIP runtime.  Loading it first makes libdcp.so bind to
+# that same runtime (the sonames match); loaded the other way round, the
+# process would hold two HIP runtimes and kernels launched through one would
+# not see the device state of the other.
+import torch  # noqa: E402,F401
 
 _lib = ctypes.CDLL(LIB_PATH)
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
@@ -70,6 +79,9 @@ _lib.dcp_mla_partial_decode.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, 
                                         _i32, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]
 _lib.dcp_mla_partial_decode_noalloc.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, _i64, _i32, _i32,
                                                 ctypes.c_float, _i32, _vp, _i64, _i64, _vp, _i64, _vp]
+_lib.dcp_mla_decode_merged_scratch_size.argtypes = [_i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
+_lib.dcp_mla_decode_merged.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, _i64, _i32, _i32, ctypes.c_float, _i32,
+                                       _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _sz, _vp]
 _lib.dcp_mla_partial_decode_varlen_scratch_size.argtypes = [_i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
 _lib.dcp_mla_partial_decode_varlen.argtypes = [_vp, _i64, _i32, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i32, _i32,
                                                _i32, ctypes.c_float, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]
@@ -78,6 +90,7 @@ _lib.dcp_status_string.argtypes = [_i32]
 _lib.dcp_status_string.restype = ctypes.c_char_p
 for _f in ("dcp_workspace_size", "dcp_workspace_create", "dcp_workspace_recv", "dcp_workspace_destroy", "dcp_workspace_set_load_policy", "dcp_lse_combine",
            "dcp_mla_partial_decode_scratch_size", "dcp_mla_partial_decode", "dcp_mla_partial_decode_noalloc",
+           "dcp_mla_decode_merged_scratch_size", "dcp_mla_decode_merged",
            "dcp_mla_partial_decode_varlen_scratch_size", "dcp_mla_partial_decode_varlen"):
     getattr(_lib, _f).restype = _i32
 
@@ -312,6 +325,40 @@ def dcp_mla_partial_decode_noalloc(q, kv, cp: int, softmax_scale: float, lse_mod
         dtype, cp, float(softmax_scale), lse_mode, _dev_ptr(o_part, "o_part"), o_part.stride(0), o_part.stride(1),
         _dev_ptr(lse_part, "lse_part"), lse_part.stride(0), s))
     return o_part, lse_part
+
+
+def dcp_mla_decode_merged_scratch_size(B: int, hq: int, kv_tokens: int, cp: int) -> int:
+    """Bytes of zero-filled scratch dcp_mla_decode_merged needs for this shape."""
+    n = _sz()
+    _check(_lib.dcp_mla_decode_merged_scratch_size(B, hq, kv_tokens, cp, ctypes.byref(n)))
+    return n.value
+
+
+def dcp_mla_decode_merged(q, kv, cp: int, softmax_scale: float, lse_mode: int, o_part, lse_part, out, out_lse=None,
+                          fuse: int = DCP_FUSE_AUTO, scratch=None, stream=None):
+    """The producer's per-shard partials and their LSE merge in one call.  ``out`` [B, hq, 512] in the
+    element type of q, ``out_lse`` [B, hq] fp32 or None; ``fuse`` DCP_FUSE_NONE / _EPILOGUE / _AUTO.
+    ``scratch``: a GPU tensor of dcp_mla_decode_merged_scratch_size() bytes that was zero-filled before its
+    first use (every call leaves its counters at zero); None allocates a zeroed one for this call."""
+    import torch
+    B, hq, T, dtype = _producer_args(q, kv, cp, o_part, lse_part)
+    if out.dim() != 3 or tuple(out.shape) != (B, hq, DCP_HEAD_DIM) or out.dtype != q.dtype or out.stride(2) != 1:
+        raise ValueError("out must be [B, hq, %d] of q's dtype with unit innermost stride" % DCP_HEAD_DIM)
+    if out_lse is not None and (tuple(out_lse.shape) != (B, hq) or out_lse.dtype != torch.float32
+                                or out_lse.stride(1) != 1):
+        raise ValueError("out_lse must be [B, hq] float32 with unit head stride")
+    if scratch is None:
+        n = dcp_mla_decode_merged_scratch_size(B, hq, T, cp)
+        scratch = torch.zeros(max(n, 16), dtype=torch.uint8, device=q.device)
+    nbytes = scratch.numel() * scratch.element_size()
+    s = _stream_handle(stream)
+    _check(_lib.dcp_mla_decode_merged(
+        _dev_ptr(q, "q"), B, hq, q.stride(0), q.stride(1), _dev_ptr(kv, "kv") if T > 0 else None, T, kv.stride(0),
+        dtype, cp, float(softmax_scale), lse_mode, _dev_ptr(o_part, "o_part"), o_part.stride(0), o_part.stride(1),
+        _dev_ptr(lse_part, "lse_part"), lse_part.stride(0), _dev_ptr(out, "out"), out.stride(0), out.stride(1),
+        _dev_ptr(out_lse, "out_lse"), out_lse.stride(0) if out_lse is not None else 0, fuse,
+        _dev_ptr(scratch, "scratch"), nbytes, s))
+    return out, out_lse
 
 
 def dcp_mla_partial_decode_varlen_scratch_size(B: int, hq: int, max_seq_len: int, cp: int) -> int:

@@ -24,6 +24,10 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
     "--offload-arch=" + ARCH,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Every rounding is the one the source writes: no implicit contraction of
+    # a multiply and an add into an FMA, so that kernels sharing an
+    # arithmetic give the same bits however they are inlined or unrolled.
+    "-ffp-contract=off",
     # Kernel-argument preloading: the leading scalar arguments of a kernel
     # (up to 16 dwords) arrive in SGPRs when the wavefront starts.  The merge
     # kernels lead with what their first loads need; kernels whose first

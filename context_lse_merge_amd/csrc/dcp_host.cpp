@@ -275,8 +275,9 @@ VarlenLayout varlen_layout(int64_t B, int hq, int64_t T, int cp) {
 
 int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv, int64_t T, int64_t kv_st,
              const MlaVarlen* vl, int dtype, int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb,
-             int64_t o_sh, float* lse, int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan) {
-    const char* fn = vl ? "dcp_mla_partial_decode_varlen" : "dcp_mla_partial_decode";
+             int64_t o_sh, float* lse, int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan,
+             const char* fn_name) {
+    const char* fn = fn_name ? fn_name : (vl ? "dcp_mla_partial_decode_varlen" : "dcp_mla_partial_decode");
     if (B < 0 || hq < 1 || T < 0)
         return fail(DCP_ERR_INVALID_ARG, "%s: need B >= 0, hq >= 1, %s >= 0 (got %lld, %d, %lld)", fn,
                     vl ? "max_seq_len" : "kv_tokens", (long long)B, hq, (long long)T);
@@ -461,9 +462,133 @@ int check_geometry(const char* fn, int64_t capacity_tokens, int h_local, int cp,
 }
 }  // namespace
 
+size_t merged_counter_bytes(int64_t B, int hq, int cp) {
+    const int64_t row_blocks = (B * hq + kMlaRowsPerBlock - 1) / kMlaRowsPerBlock;
+    return static_cast<size_t>((row_blocks * (cp + 1) * 4 + 255) / 256 * 256);
+}
+
+// dcp_mla_decode_merged: the producer's plan with the split partials placed
+// after the arrival counters, plus the shard merge (fused into the decode
+// kernel's epilogue, or as its own launches).
+int plan_mla_merged(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv, int64_t T,
+                    int64_t kv_st, int dtype, int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb,
+                    int64_t o_sh, float* lse, int64_t lse_sb, void* out, int64_t out_sb, int64_t out_sh,
+                    float* out_lse, int64_t out_lse_sb, int fuse, void* scratch, size_t scratch_bytes,
+                    MlaPlan* plan) {
+    const char* fn = "dcp_mla_decode_merged";
+    if (fuse != DCP_FUSE_NONE && fuse != DCP_FUSE_EPILOGUE && fuse != DCP_FUSE_AUTO)
+        return fail(DCP_ERR_INVALID_ARG, "%s: fuse %d is not DCP_FUSE_NONE, DCP_FUSE_EPILOGUE or DCP_FUSE_AUTO", fn,
+                    fuse);
+    if (B < 0 || hq < 1 || T < 0 || cp < 1 || cp > DCP_MAX_CP || B * static_cast<int64_t>(hq) > (int64_t{1} << 30))
+        return fail(DCP_ERR_INVALID_ARG, "%s: need B >= 0, hq >= 1, kv_tokens >= 0, 1 <= cp <= %d and B * hq <= 2^30",
+                    fn, DCP_MAX_CP);
+    const size_t cnt = merged_counter_bytes(B, hq, cp);
+    int32_t nsplit;
+    int64_t split_len;
+    size_t part;
+    mla_split(B, hq, T, cp, &nsplit, &split_len, &part);
+    if (B > 0 && (!scratch || scratch_bytes < cnt + part))
+        return fail(DCP_ERR_WORKSPACE, "%s: needs %zu bytes of zero-filled scratch (%s_scratch_size), got %zu", fn,
+                    cnt + part, fn, scratch ? scratch_bytes : size_t{0});
+    char* parts = scratch ? static_cast<char*>(scratch) + cnt : nullptr;
+    const int rc = plan_mla(q, B, hq, q_sb, q_sh, kv, T, kv_st, nullptr, dtype, cp, softmax_scale, lse_mode, o, o_sb,
+                            o_sh, lse, lse_sb, parts, scratch ? scratch_bytes - cnt : 0, plan, fn);
+    if (rc != DCP_OK) return rc;
+    plan->merge_shards = false;
+    if (B == 0) return ok();
+    if (!out) return fail(DCP_ERR_INVALID_ARG, "%s: out must be non-null when B > 0", fn);
+    if (out_sb < 0 || out_sh < 0 || out_lse_sb < 0) return fail(DCP_ERR_LAYOUT, "%s: strides must be non-negative", fn);
+    if (!rows_disjoint(B, out_sb, hq, out_sh, kMlaVDim))
+        return fail(DCP_ERR_LAYOUT, "%s: out rows overlap (out_sb = %lld, out_sh = %lld)", fn, (long long)out_sb,
+                    (long long)out_sh);
+    if (out_lse && !rows_disjoint(B, out_lse_sb, hq, 1, 1))
+        return fail(DCP_ERR_LAYOUT, "%s: out_lse_sb = %lld < hq = %d makes out_lse rows overlap", fn,
+                    (long long)out_lse_sb, hq);
+    if (!aligned(out, 16) || out_sb % 8 || out_sh % 8)
+        return fail(DCP_ERR_ALIGN, "%s: out must be 16-byte aligned with out_sb, out_sh multiples of 8 elements", fn);
+    if (out_lse && !aligned(out_lse, 4)) return fail(DCP_ERR_ALIGN, "%s: out_lse must be 4-byte aligned", fn);
+    if (!aligned(scratch, 16)) return fail(DCP_ERR_ALIGN, "%s: scratch must be 16-byte aligned", fn);
+    const int64_t H = static_cast<int64_t>(cp) * hq;
+    const Extent e_q = extent(q, B, q_sb, hq, q_sh, kMlaQkDim, 2);
+    const Extent e_kv = T > 0 ? extent(kv, 1, 0, T, kv_st, kMlaQkDim, 2) : Extent{0, 0};
+    const Extent e_o = extent(o, B, o_sb, H, o_sh, kMlaVDim, 2);
+    const Extent e_l = extent(lse, B, lse_sb, 1, 0, H, 4);
+    const Extent e_s{reinterpret_cast<uintptr_t>(scratch), reinterpret_cast<uintptr_t>(scratch) + cnt + part};
+    const Extent e_out = extent(out, B, out_sb, hq, out_sh, kMlaVDim, 2);
+    if (overlaps(e_out, e_q) || overlaps(e_out, e_kv) || overlaps(e_out, e_o) || overlaps(e_out, e_l) ||
+        overlaps(e_out, e_s))
+        return fail(DCP_ERR_INVALID_ARG, "%s: out overlaps an input, o_part, lse_part or the scratch", fn);
+    if (out_lse) {
+        const Extent e_ol = extent(out_lse, B, out_lse_sb, 1, 0, hq, 4);
+        if (overlaps(e_ol, e_q) || overlaps(e_ol, e_kv) || overlaps(e_ol, e_o) || overlaps(e_ol, e_l) ||
+            overlaps(e_ol, e_s) || overlaps(e_ol, e_out))
+            return fail(DCP_ERR_INVALID_ARG, "%s: out_lse overlaps another buffer", fn);
+    }
+
+    MlaArgs& a = plan->args;
+    // DCP_FUSE_AUTO takes the separate launches: measured faster at every
+    // shape (the agent-scope publication of each workgroup's part costs more
+    // than the launches the epilogue saves).
+    a.fused = fuse == DCP_FUSE_EPILOGUE ? 1 : 0;
+    a.split_cnt = static_cast<int32_t*>(scratch);
+    a.rb_cnt = a.split_cnt + static_cast<int64_t>(a.row_blocks) * cp;
+    a.out = static_cast<uint16_t*>(out);
+    a.out_lse = out_lse;
+    a.out_sb = out_sb;
+    a.out_sh = out_sh;
+    a.out_lse_sb = out_lse_sb;
+    a.to_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 1.4426950408889634f;
+    a.from_log2 = lse_mode == DCP_LSE_BASE_2 ? 1.0f : 0.6931471805599453f;
+    if (!a.fused) {
+        // The shard merge as dcp_lse_combine runs it over (o, lse) in the
+        // FlashMLA layout, the partials read with plain loads (just written).
+        MergeArgs m{};
+        m.attn = o;
+        m.in_dtype = dtype;
+        m.lse = lse;
+        m.out = static_cast<uint16_t*>(out);
+        m.out_lse = out_lse;
+        m.a_sb = o_sb;
+        m.a_sj = o_sh;
+        m.a_ss = static_cast<int64_t>(hq) * o_sh;
+        m.l_sb = lse_sb;
+        m.l_sj = 1;
+        m.l_ss = hq;
+        m.o_sb = out_sb;
+        m.o_sj = out_sh;
+        m.ol_sb = out_lse_sb;
+        m.h_local = hq;
+        m.cp = cp;
+        m.dtype = dtype;
+        m.cached = 1;
+        m.to_log2 = a.to_log2;
+        m.from_log2 = a.from_log2;
+        if (!merge_strides_fit(m))
+            return fail(DCP_ERR_LAYOUT, "%s: o_part / lse_part strides must be below 2^31 elements", fn);
+        plan->merge_shards = true;
+        plan->shard_merge = m;
+    }
+    return ok();
+}
+
 }  // namespace dcp
 
 extern "C" {
+
+int dcp_mla_decode_merged_scratch_size(int64_t B, int hq, int64_t kv_tokens, int cp, size_t* bytes) {
+    if (!bytes) return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_mla_decode_merged_scratch_size: bytes is null");
+    if (B < 0 || hq < 1 || kv_tokens < 0 || cp < 1 || cp > DCP_MAX_CP || B * static_cast<int64_t>(hq) > (int64_t{1} << 30))
+        return dcp::fail(DCP_ERR_INVALID_ARG,
+                         "dcp_mla_decode_merged_scratch_size: need B >= 0, hq >= 1, kv_tokens >= 0, 1 <= cp <= %d, "
+                         "B * hq <= 2^30",
+                         DCP_MAX_CP);
+    int32_t n;
+    int64_t len;
+    size_t part;
+    dcp::mla_split(B, hq, kv_tokens, cp, &n, &len, &part);
+    *bytes = B == 0 ? 0 : dcp::merged_counter_bytes(B, hq, cp) + part;
+    return dcp::ok();
+}
 
 int dcp_mla_partial_decode_scratch_size(int64_t B, int hq, int64_t kv_tokens, int cp, size_t* bytes) {
     if (!bytes) return dcp::fail(DCP_ERR_INVALID_ARG, "dcp_mla_partial_decode_scratch_size: bytes is null");

@@ -272,6 +272,18 @@ struct MlaArgs {
     VarlenItem* vl_items;
     VarlenSplit* vl_splits;
     int64_t slots;          // partial slots in the scratch (0: no pair may split)
+    // Fused epilogue (fixed length only): arrival counters (zero between
+    // calls) and the merged output.  The last workgroup of (row block rb,
+    // shard s) to count itself into split_cnt[rb*cp + s] reduces the shard's
+    // splits into o / lse; the last shard of rb to count itself into
+    // rb_cnt[rb] merges the cp shards of its rows into out / out_lse.
+    int32_t fused;
+    int32_t* split_cnt;
+    int32_t* rb_cnt;
+    uint16_t* out;
+    float* out_lse;
+    int64_t out_sb, out_sh, out_lse_sb;
+    float to_log2, from_log2;  // the merges' base constants (as in MergeArgs)
 };
 
 struct MlaPlan {
@@ -281,7 +293,27 @@ struct MlaPlan {
     bool varlen;            // planning kernel, decode over the work list, split reduction
     MergeArgs reduce;       // nsplit > 1: the merge over splits (all B tokens; launched in token chunks)
     int64_t B;
+    // dcp_mla_decode_merged without the fused epilogue: the shard merge of
+    // o / lse into out / out_lse (all B tokens; launched in token chunks).
+    bool merge_shards;
+    MergeArgs shard_merge;
 };
+
+// Launch a merge over all B tokens of `m` in chunks of at most
+// kMaxLaunchTokens tokens and 2^30 rows; returns the first HIP error.
+int merge_launch_all(const MergeArgs& m, int64_t B, void* stream);
+
+// Scratch of dcp_mla_decode_merged: the arrival counters (row_blocks * (cp + 1)
+// int32, rounded to 256 bytes), then the split partials as for
+// dcp_mla_partial_decode.
+size_t merged_counter_bytes(int64_t B, int hq, int cp);
+
+// Validate every argument of dcp_mla_decode_merged and build the plan.
+int plan_mla_merged(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv, int64_t T,
+                    int64_t kv_st, int dtype, int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb,
+                    int64_t o_sh, float* lse, int64_t lse_sb, void* out, int64_t out_sb, int64_t out_sh,
+                    float* out_lse, int64_t out_lse_sb, int fuse, void* scratch, size_t scratch_bytes,
+                    MlaPlan* plan);
 
 // The variable-length producer's planning kernel and split reduction,
 // enqueued on `stream` (a hipStream_t); return the HIP error of the launch.
@@ -304,7 +336,8 @@ struct MlaVarlen {
 // then max_seq_len) and build the plan.
 int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv, int64_t T, int64_t kv_st,
              const MlaVarlen* vl, int dtype, int cp, float softmax_scale, int lse_mode, void* o, int64_t o_sb,
-             int64_t o_sh, float* lse, int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan);
+             int64_t o_sh, float* lse, int64_t lse_sb, void* scratch, size_t scratch_bytes, MlaPlan* plan,
+             const char* fn_name = nullptr);
 
 // Enqueue a validated plan on `stream` (a hipStream_t): the planning kernel
 // (variable length), the decode kernel and the split reduction.  Returns a

@@ -262,6 +262,16 @@ int merge_launch(const MergeArgs& a, void* stream) {
     return static_cast<int>(launch(a, static_cast<hipStream_t>(stream)));
 }
 
+int merge_launch_all(const MergeArgs& m, int64_t B, void* stream) {
+    int64_t chunk = (int64_t{1} << 30) / m.h_local;
+    if (chunk > kMaxLaunchTokens) chunk = kMaxLaunchTokens;
+    for (int64_t t0 = 0; t0 < B; t0 += chunk) {
+        const int64_t n = B - t0 < chunk ? B - t0 : chunk;
+        const hipError_t e = launch(merge_args_at(m, t0, n), static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return static_cast<int>(e);
+    }
+    return 0;
+}
 
 }  // namespace dcp
 

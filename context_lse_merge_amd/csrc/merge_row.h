@@ -31,6 +31,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // lower-addressed one in the low half; widening to fp32 is exact for both,
 // narrowing rounds to nearest even.
 struct Bf16 {
+    static constexpr bool kFoldsIntoFma = false;
     // bf16 is the high half of an fp32: shifting or masking widens it.
     static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
     static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -41,6 +42,10 @@ struct Bf16 {
 };
 
 struct F16 {
+    // The compiler may fold the last FMA of a sum and its conversion to fp16
+    // into one mixed-precision FMA that rounds once; pack8 keeps the two
+    // roundings the arithmetic states (fp32, then fp16) on every path.
+    static constexpr bool kFoldsIntoFma = true;
     static __device__ __forceinline__ float lo(uint32_t w) {
         return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
     }
@@ -113,8 +118,16 @@ __device__ __forceinline__ float merged_lse(float M, float S, float from_log2) {
 }
 
 // The lane's 8 accumulators rounded to the output type, as one 16-byte word.
+// For fp16 the fp32 sums pass through an empty asm first, so the conversion
+// cannot be merged with the FMA that produced them.
 template <typename T>
-__device__ __forceinline__ u32x4 pack8(const float (&acc)[8]) {
+__device__ __forceinline__ u32x4 pack8(const float (&acc_in)[8]) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        acc[i] = acc_in[i];
+        if (T::kFoldsIntoFma) asm volatile("" : "+v"(acc[i]));
+    }
     u32x4 p;
     p[0] = T::pack(acc[0], acc[1]);
     p[1] = T::pack(acc[2], acc[3]);
@@ -185,6 +198,45 @@ __device__ __forceinline__ void merge_row_any(const void* attn, int64_t o0, int6
                 for (int i = 0; i < G; ++i) cur[i] = nxt[i];
             }
         }
+    }
+}
+
+// R rows of N shards each (N known at compile time), all R * N payload loads
+// issued before any arithmetic: for a wavefront that merges several rows in
+// turn, the rows' memory latencies overlap instead of adding up.  Row r's
+// shard s is at attn + o0[r] + s*a_ss and its LSE at lrow[r][s*l_ss] (wave-
+// uniform).  The arithmetic of each row is merge_row_any's, step for step.
+template <int R, int N, typename In>
+__device__ __forceinline__ void merge_rows_batch(const void* attn, const int64_t (&o0)[R], int64_t a_ss,
+                                                 const float* const (&lrow)[R], int64_t l_ss, int64_t sc_off,
+                                                 float to_log2, float (&acc)[R][8], float (&M)[R], float (&S)[R]) {
+    typename In::row_t v[R][N];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int s = 0; s < N; ++s) v[r][s] = In::load(attn, o0[r] + static_cast<int64_t>(s) * a_ss);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float x[N];
+#pragma unroll
+        for (int s = 0; s < N; ++s) x[s] = lrow[r][static_cast<int64_t>(s) * l_ss];
+        float m = x[0];
+#pragma unroll
+        for (int s = 1; s < N; ++s) m = fmaxf(m, x[s]);
+        float sum = 0.0f;
+#pragma unroll
+        for (int s = 0; s < N; ++s) sum += shard_weight(x[s], m, to_log2);
+        const float inv = inv_sum(sum);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[r][i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < N; ++s) {
+            float w = shard_weight(x[s], m, to_log2) * inv;
+            if (In::kScaled) w *= lrow[r][static_cast<int64_t>(s) * l_ss + sc_off];
+            fma8<In>(acc[r], w, v[r][s]);
+        }
+        M[r] = m;
+        S[r] = sum;
     }
 }
 

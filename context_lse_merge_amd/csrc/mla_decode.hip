@@ -73,6 +73,7 @@
 #include <cstdint>
 
 #include "dcp_internal.h"
+#include "merge_row.h"
 
 namespace dcp {
 namespace {
@@ -138,6 +139,7 @@ struct Bf16 {
     typedef __bf16 elem;
     typedef bf16x8 v8;
     typedef bf16x4 v4;
+    typedef mrow::Bf16 merge_t;  // the same element type for the merges of the fused epilogue
     static __device__ __forceinline__ f32x4 mfma(v8 a, v8 b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
@@ -150,6 +152,7 @@ struct F16 {
     typedef _Float16 elem;
     typedef f16x8 v8;
     typedef f16x4 v4;
+    typedef mrow::F16 merge_t;
     static __device__ __forceinline__ f32x4 mfma(v8 a, v8 b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
@@ -392,7 +395,216 @@ __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* k
     }
 }
 
+// The epilogue's stores of a lane's row: O / l and the LSE in the caller's
+// base; an empty shard or split gives 0 and -inf.  One split: the element
+// type, straight into o_part / lse_part.  Several: into the scratch -- as
+// head p*cp*hq + s*hq + h, for the merge kernel to reduce over the splits, or
+// with seq_lens as row wave*16 + r16 of the item's slot, for the split
+// reduction -- in fp16, the row multiplied by 2^k so that its largest
+// magnitude lies in [2^14, 2^15) (fp16 then carries 11 significant bits
+// relative to the row's largest value), with 2^-k stored beside the LSE.
 template <typename T>
+__device__ __forceinline__ void store_rows(const MlaArgs& a, const Work& wk, int b, int h, int wave, int r16, int g,
+                                           int ocol, const RowState& st, float m_run, float l_tot, float amax,
+                                           bool direct) {
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * a.lse_scale : -INFINITY;
+    if (direct) {
+        const int64_t u = static_cast<int64_t>(wk.s) * a.hq + h;
+        uint16_t* orow = a.o + b * a.o_sb + u * a.o_sh + ocol;
+#pragma unroll
+        for (int t = 0; t < kDTiles; ++t) {
+            const f32x4 v = st.oacc[t];
+            const uint32_t lo = to_bits<T>(v[0] * inv) | (to_bits<T>(v[1] * inv) << 16);
+            const uint32_t hi = to_bits<T>(v[2] * inv) | (to_bits<T>(v[3] * inv) << 16);
+            *reinterpret_cast<uint2*>(orow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
+        }
+        if (g == 0) a.lse[b * a.lse_sb + u] = lse;
+    } else {
+        int64_t prow_idx;  // partial row of the scratch
+        if (a.seq_lens)
+            prow_idx = static_cast<int64_t>(wk.slot) * kMlaRowsPerBlock + wave * kRowsPerWave + r16;
+        else
+            prow_idx = b * a.part_sb + (static_cast<int64_t>(wk.p) * a.cp + wk.s) * a.hq + h;
+        // amax * inv = m 2^e with m in [0.5, 1): k = 15 - e.  Capped at 100
+        // so that 2^-k stays a normal float (rows below 2^-85 keep fewer bits;
+        // an all-zero row gets k = 15).  1/l <= 1, so inv * 2^k stays finite.
+        const int k = min(15 - __builtin_amdgcn_frexp_expf(amax * inv), 100);
+        const float mul = __builtin_amdgcn_ldexpf(inv, k);
+        uint16_t* prow = a.part_o + prow_idx * kDv + ocol;
+#pragma unroll
+        for (int t = 0; t < kDTiles; ++t) {
+            const f32x4 v = st.oacc[t];
+            const uint32_t lo = to_bits<F16>(v[0] * mul) | (to_bits<F16>(v[1] * mul) << 16);
+            const uint32_t hi = to_bits<F16>(v[2] * mul) | (to_bits<F16>(v[3] * mul) << 16);
+            *reinterpret_cast<uint2*>(prow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
+        }
+        if (g == 0) {
+            a.part_lse[prow_idx] = lse;
+            a.part_scale[prow_idx] = __builtin_amdgcn_ldexpf(1.0f, -k);
+        }
+    }
+}
+
+
+// Count this workgroup into *cnt, one of n arrivals, and tell whether it was
+// the last.  Each wavefront first waits until its own stores have completed
+// (vmcnt counts stores too), the workgroup synchronises, and one thread then
+// releases them all at agent scope -- a write-back of this XCD's L2, which
+// every store of the workgroup has reached -- before the count.  An
+// agent-scope fence per wavefront would write the L2 back eight times.  The
+// last workgroup acquires (one invalidation serves the whole workgroup: its
+// wavefronts share the compute unit's L1 and the XCD's L2) before anyone
+// reads what the others published, and puts the counter back to zero for the
+// next call (all n arrivals of this call have happened).  No workgroup waits
+// for another.
+__device__ __forceinline__ bool arrive_last(int32_t* cnt, int n, int* flag) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        const int old = atomicAdd(cnt, 1);
+        const bool last = old == n - 1;
+        if (last) {
+            atomicExch(cnt, 0);
+            __threadfence();
+        }
+        *flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    return *flag != 0;
+}
+
+// One tail of the fused epilogue: the wavefront merges rows wave, wave + 8,
+// ... of row block rb, each over n parts (key splits or shards) of `In`
+// payload.  addr(row, &o0, &lrow) places a row's first part and its LSE,
+// store(row, acc, M, S) writes the result.  For n <= 8 four rows are merged
+// at once (merge_rows_batch: their loads all in flight together); beyond
+// that one row at a time.  The arithmetic is the same either way.
+template <typename In, int N, typename Addr, typename Store>
+__device__ __forceinline__ void tail_batched(int rb, int rows, int wave, const void* src, int64_t a_ss, int64_t l_ss,
+                                             int64_t sc_off, float to_log2, Addr addr, Store store) {
+    constexpr int R = 4;
+    for (int k0 = 0; k0 < kRowsPerWave; k0 += R) {
+        int64_t o0[R];
+        const float* lr[R];
+        int row[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            row[r] = rb * kMlaRowsPerBlock + wave + kWaves * (k0 + r);
+            addr(min(row[r], rows - 1), o0[r], lr[r]);  // rows past the end repeat the last one, unstored
+        }
+        float acc[R][8], M[R], S[R];
+        mrow::merge_rows_batch<R, N, In>(src, o0, a_ss, lr, l_ss, sc_off, to_log2, acc, M, S);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (row[r] < rows) store(row[r], acc[r], M[r], S[r]);
+    }
+}
+
+template <typename In, typename Addr, typename Store>
+__device__ __forceinline__ void tail_rows(int n, int rb, int rows, int wave, const void* src, int64_t a_ss,
+                                          int64_t l_ss, int64_t sc_off, float to_log2, Addr addr, Store store) {
+    switch (n) {
+#define DCP_TAIL_CASE(k) \
+    case k: tail_batched<In, k>(rb, rows, wave, src, a_ss, l_ss, sc_off, to_log2, addr, store); return;
+        DCP_TAIL_CASE(1)
+        DCP_TAIL_CASE(2)
+        DCP_TAIL_CASE(3)
+        DCP_TAIL_CASE(4)
+        DCP_TAIL_CASE(5)
+        DCP_TAIL_CASE(6)
+        DCP_TAIL_CASE(7)
+        DCP_TAIL_CASE(8)
+#undef DCP_TAIL_CASE
+        default: break;
+    }
+    for (int k = 0; k < kRowsPerWave; ++k) {
+        const int row = rb * kMlaRowsPerBlock + wave + kWaves * k;
+        if (row >= rows) break;
+        int64_t o0;
+        const float* lr;
+        addr(row, o0, lr);
+        float acc[8], M, S;
+        mrow::merge_row_any<8, In>(src, o0, a_ss, lr, l_ss, sc_off, n, to_log2, acc, M, S);
+        store(row, acc, M, S);
+    }
+}
+
+typedef __attribute__((address_space(4))) const MlaArgs KernArgs;
+
+// The fused epilogue (fixed length): once this workgroup's rows are stored,
+// (1) with several splits per shard, the last workgroup of (row block, shard)
+// to arrive reduces the shard's splits into o_part / lse_part, and (2) the
+// last shard of the row block to complete merges the cp shards of every row
+// into out / out_lse.  Both reductions are the merge's own row arithmetic
+// (merge_row.h), one wavefront per row, so the results equal those of the
+// split-reduction launch and of dcp_lse_combine over o_part / lse_part.
+template <typename T>
+__device__ __forceinline__ void fused_epilogue(const int* work) {
+    __shared__ int flag;
+    typedef typename T::merge_t Out;
+    // The arguments (the kernel's only one, at the start of its argument
+    // segment) are read through a pointer the compiler cannot see through,
+    // so their loads stay here instead of being hoisted above the key loop
+    // and held in registers across it.  The work item comes back from LDS
+    // for the same reason.
+    KernArgs* ap = (KernArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
+    asm volatile("" : "+s"(ap));
+    KernArgs& a = *ap;
+    const int rb = __builtin_amdgcn_readfirstlane(work[0]);
+    const int s = __builtin_amdgcn_readfirstlane(work[1]);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int hq = a.hq;
+    if (a.nsplit > 1) {
+        if (!arrive_last(a.split_cnt + rb * a.cp + s, a.nsplit, &flag)) return;
+        uint16_t* const o = a.o;
+        float* const lse = a.lse;
+        const uint16_t* const part_o = a.part_o;
+        const float* const part_lse = a.part_lse;
+        const int64_t part_sb = a.part_sb, o_sb = a.o_sb, o_sh = a.o_sh, lse_sb = a.lse_sb;
+        const float from_log2 = a.from_log2;
+        auto addr = [&](int row, int64_t& o0, const float*& lr) {
+            const int b = row / hq, h = row - b * hq;
+            const int64_t prow = b * part_sb + static_cast<int64_t>(s) * hq + h;  // split 0's partial row
+            o0 = prow * kDv + 8 * lane;
+            lr = part_lse + prow;
+        };
+        auto store = [&](int row, const float (&acc)[8], float M, float S) {
+            const int b = row / hq, h = row - b * hq;
+            const int64_t u = static_cast<int64_t>(s) * hq + h;
+            *reinterpret_cast<mrow::u32x4*>(o + b * o_sb + u * o_sh + 8 * lane) = mrow::pack8<Out>(acc);
+            if (lane == 0) lse[b * lse_sb + u] = mrow::merged_lse(M, S, from_log2);
+        };
+        tail_rows<mrow::Payload16<mrow::F16, false, true>>(a.nsplit, rb, a.rows, wave, part_o,
+                                                           static_cast<int64_t>(a.cp) * hq * kDv,
+                                                           static_cast<int64_t>(a.cp) * hq, a.part_scale - a.part_lse,
+                                                           a.to_log2, addr, store);
+    }
+    if (!arrive_last(a.rb_cnt + rb, a.cp, &flag)) return;
+    uint16_t* const out = a.out;
+    float* const out_lse = a.out_lse;
+    const float* const lse = a.lse;
+    const int64_t o_sb = a.o_sb, o_sh = a.o_sh, lse_sb = a.lse_sb, out_sb = a.out_sb, out_sh = a.out_sh,
+                  out_lse_sb = a.out_lse_sb;
+    const float from_log2 = a.from_log2;
+    auto addr = [&](int row, int64_t& o0, const float*& lr) {
+        const int b = row / hq, h = row - b * hq;
+        o0 = b * o_sb + h * o_sh + 8 * lane;
+        lr = lse + b * lse_sb + h;
+    };
+    auto store = [&](int row, const float (&acc)[8], float M, float S) {
+        const int b = row / hq, h = row - b * hq;
+        __builtin_nontemporal_store(mrow::pack8<Out>(acc),
+                                    reinterpret_cast<mrow::u32x4*>(out + b * out_sb + h * out_sh + 8 * lane));
+        if (lane == 0 && out_lse) out_lse[b * out_lse_sb + h] = mrow::merged_lse(M, S, from_log2);
+    };
+    tail_rows<mrow::Payload16<Out, false>>(a.cp, rb, a.rows, wave, a.o, static_cast<int64_t>(hq) * o_sh, hq, 0,
+                                           a.to_log2, addr, store);
+}
+
+template <typename T, bool Fused>
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t tile0[kTileAlloc];
     __shared__ __attribute__((aligned(16))) uint16_t tile1[kTileAlloc];
@@ -432,6 +644,11 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
         cache = a.kv + b_tok * a.kv_sb;
     } else {
         wk = work_of(a);
+    }
+    __shared__ int fused_work[2];  // (row block, shard) for the fused epilogue
+    if (Fused && tid == 0) {
+        fused_work[0] = wk.rb;
+        fused_work[1] = wk.s;
     }
     // Shard s: n_s logical keys, key j at cache row start + j * step.
     int64_t start, n_s;
@@ -540,53 +757,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
             for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st.oacc[t][i]));
         amax = max_xor32(max_xor16(amax));
     }
-    if (!valid) return;
-
-    // O / l and the LSE in the caller's base; an empty shard or split gives 0
-    // and -inf.  One split: the element type, straight into o_part / lse_part.
-    // Several: into the scratch -- as head p*cp*hq + s*hq + h, for the merge
-    // kernel to reduce over the splits, or with seq_lens as row wave*16 + r16
-    // of the item's slot, for the split reduction -- in fp16, the row
-    // multiplied by 2^k so that its largest magnitude lies in [2^14, 2^15)
-    // (fp16 then carries 11 significant bits relative to the row's largest
-    // value), with 2^-k stored beside the LSE.
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * a.lse_scale : -INFINITY;
-    if (direct) {
-        const int64_t u = static_cast<int64_t>(wk.s) * a.hq + h;
-        uint16_t* orow = a.o + b * a.o_sb + u * a.o_sh + ocol;
-#pragma unroll
-        for (int t = 0; t < kDTiles; ++t) {
-            const f32x4 v = st.oacc[t];
-            const uint32_t lo = to_bits<T>(v[0] * inv) | (to_bits<T>(v[1] * inv) << 16);
-            const uint32_t hi = to_bits<T>(v[2] * inv) | (to_bits<T>(v[3] * inv) << 16);
-            *reinterpret_cast<uint2*>(orow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
-        }
-        if (g == 0) a.lse[b * a.lse_sb + u] = lse;
-    } else {
-        int64_t prow_idx;  // partial row of the scratch
-        if (a.seq_lens)
-            prow_idx = static_cast<int64_t>(wk.slot) * kMlaRowsPerBlock + wave * kRowsPerWave + r16;
-        else
-            prow_idx = b * a.part_sb + (static_cast<int64_t>(wk.p) * a.cp + wk.s) * a.hq + h;
-        // amax * inv = m 2^e with m in [0.5, 1): k = 15 - e.  Capped at 100
-        // so that 2^-k stays a normal float (rows below 2^-85 keep fewer bits;
-        // an all-zero row gets k = 15).  1/l <= 1, so inv * 2^k stays finite.
-        const int k = min(15 - __builtin_amdgcn_frexp_expf(amax * inv), 100);
-        const float mul = __builtin_amdgcn_ldexpf(inv, k);
-        uint16_t* prow = a.part_o + prow_idx * kDv + ocol;
-#pragma unroll
-        for (int t = 0; t < kDTiles; ++t) {
-            const f32x4 v = st.oacc[t];
-            const uint32_t lo = to_bits<F16>(v[0] * mul) | (to_bits<F16>(v[1] * mul) << 16);
-            const uint32_t hi = to_bits<F16>(v[2] * mul) | (to_bits<F16>(v[3] * mul) << 16);
-            *reinterpret_cast<uint2*>(prow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
-        }
-        if (g == 0) {
-            a.part_lse[prow_idx] = lse;
-            a.part_scale[prow_idx] = __builtin_amdgcn_ldexpf(1.0f, -k);
-        }
-    }
+    if (valid) store_rows<T>(a, wk, b, h, wave, r16, g, ocol, st, m_run, l_tot, amax, direct);
+    if (Fused) fused_epilogue<T>(fused_work);
 }
 
 }  // namespace
@@ -605,23 +777,26 @@ int run_mla(const MlaPlan& plan, void* hip_stream, const char* fn) {
         if (e != hipSuccess) return fail(DCP_ERR_HIP, "%s: launch of the planning kernel failed: %s", fn,
                                          hipGetErrorString(e));
     }
-    if (plan.args.dtype == DCP_DTYPE_FP16)
-        mla_decode_kernel<F16><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
-    else
-        mla_decode_kernel<Bf16><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
+    const bool f16 = plan.args.dtype == DCP_DTYPE_FP16;
+    if (plan.args.fused) {
+        if (f16)
+            mla_decode_kernel<F16, true><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
+        else
+            mla_decode_kernel<Bf16, true><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
+    } else if (f16) {
+        mla_decode_kernel<F16, false><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
+    } else {
+        mla_decode_kernel<Bf16, false><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
+    }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && plan.varlen) {
         if (plan.args.slots > 0) e = static_cast<hipError_t>(varlen_reduce_launch(plan.args, stream));
-    } else if (e == hipSuccess && plan.args.nsplit > 1) {
+    } else if (e == hipSuccess && plan.args.nsplit > 1 && !plan.args.fused) {
         // The splits of every (token, shard, head) are merged like DCP shards.
-        const int64_t H = plan.reduce.h_local;
-        int64_t chunk = (int64_t{1} << 30) / H;
-        if (chunk > kMaxLaunchTokens) chunk = kMaxLaunchTokens;
-        for (int64_t t0 = 0; t0 < plan.B && e == hipSuccess; t0 += chunk) {
-            const int64_t n = plan.B - t0 < chunk ? plan.B - t0 : chunk;
-            e = static_cast<hipError_t>(merge_launch(merge_args_at(plan.reduce, t0, n), stream));
-        }
+        e = static_cast<hipError_t>(merge_launch_all(plan.reduce, plan.B, stream));
     }
+    if (e == hipSuccess && plan.merge_shards)
+        e = static_cast<hipError_t>(merge_launch_all(plan.shard_merge, plan.B, stream));
     if (e != hipSuccess) return fail(DCP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }
@@ -651,4 +826,18 @@ extern "C" int dcp_mla_partial_decode_varlen(const void* q, int64_t B, int hq, i
                                  lse_mode, o_part, o_sb, o_sh, lse_part, lse_sb, scratch, scratch_bytes, &plan);
     if (rc != DCP_OK) return rc;
     return dcp::run_mla(plan, hip_stream, "dcp_mla_partial_decode_varlen");
+}
+
+extern "C" int dcp_mla_decode_merged(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv,
+                                     int64_t kv_tokens, int64_t kv_st, int dtype, int cp, float softmax_scale,
+                                     int lse_mode, void* o_part, int64_t o_sb, int64_t o_sh, float* lse_part,
+                                     int64_t lse_sb, void* out, int64_t out_sb, int64_t out_sh, float* out_lse,
+                                     int64_t out_lse_sb, int fuse, void* scratch, size_t scratch_bytes,
+                                     void* hip_stream) {
+    dcp::MlaPlan plan;
+    const int rc = dcp::plan_mla_merged(q, B, hq, q_sb, q_sh, kv, kv_tokens, kv_st, dtype, cp, softmax_scale,
+                                        lse_mode, o_part, o_sb, o_sh, lse_part, lse_sb, out, out_sb, out_sh, out_lse,
+                                        out_lse_sb, fuse, scratch, scratch_bytes, &plan);
+    if (rc != DCP_OK) return rc;
+    return dcp::run_mla(plan, hip_stream, "dcp_mla_decode_merged");
 }

@@ -277,6 +277,57 @@ int dcp_mla_partial_decode_noalloc(const void* q, int64_t B, int hq, int64_t q_s
                                    int lse_mode, void* o_part, int64_t o_sb, int64_t o_sh, float* lse_part,
                                    int64_t lse_sb, void* hip_stream);
 
+/* How dcp_mla_decode_merged reduces the key splits and merges the shards. */
+#define DCP_FUSE_NONE 0     /* separate launches: decode, split reduction, shard merge             */
+#define DCP_FUSE_EPILOGUE 1 /* one launch: the decode kernel's last arrivals reduce and merge      */
+#define DCP_FUSE_AUTO 2     /* whichever measured faster on MI355X: NONE at every shape measured   */
+
+/*
+ * MLA decode over cp shards followed by the LSE merge of the shards: the
+ * per-shard partials of dcp_mla_partial_decode AND their merge, which
+ * dcp_lse_combine would compute from them, in one call.  On the pages the
+ * merge runs after the partials have made a round trip through global memory
+ * and costs a launch per layer; fusing it removes both ("[DCP] Run fi_a2a on
+ * FlashInfer's fused all-to-all + LSE reduce", sglang PR #40539, Motivation
+ * and commit log).  On one GPU the shards need no exchange, so the merge can
+ * run in the decode kernel's epilogue:
+ *  - DCP_FUSE_EPILOGUE: every workgroup publishes its part (a split's partial,
+ *    or its shard's output) and counts itself in with a device-scope atomic;
+ *    the last workgroup of a (row block, shard) to arrive reduces that
+ *    shard's key splits, and the last shard of a row block to complete merges
+ *    the cp shards into out / out_lse.  No workgroup waits for another.
+ *  - DCP_FUSE_NONE: the decode kernel, the split reduction and the shard
+ *    merge as separate launches (what dcp_mla_partial_decode followed by
+ *    dcp_lse_combine does).
+ *  - DCP_FUSE_AUTO: the faster of the two as measured on MI355X, which is
+ *    NONE at every shape measured (128 heads, 4 shards, 131072 keys, B = 1,
+ *    8, 32, 64): publishing a workgroup's part at agent scope writes back
+ *    the L2 of its XCD, and that costs more than the launches it saves.
+ * Every mode gives the same bits: o_part / lse_part equal
+ * dcp_mla_partial_decode's, and out / out_lse equal dcp_lse_combine over them
+ * (DCP_LSE_BH1, the same lse_mode).
+ *
+ * q, kv, dtype, cp, softmax_scale, lse_mode, o_part, lse_part: as
+ * dcp_mla_partial_decode (o_part / lse_part are outputs here too).
+ * out       [B, hq, 512] in dtype, row (b, h) at out + b*out_sb + h*out_sh.
+ * out_lse   [B, hq] fp32 at out_lse + b*out_lse_sb + h, or NULL.
+ * scratch   device buffer of at least dcp_mla_decode_merged_scratch_size()
+ *           bytes, 16-byte aligned, ZERO-FILLED before its first use: it
+ *           holds the arrival counters (which every complete call leaves at
+ *           zero again, so later calls and graph replays need no clearing)
+ *           and the split partials.  One call at a time per buffer.
+ * Alignment of out as o_part (16 bytes; strides multiples of 8 elements);
+ * out / out_lse must not overlap any other buffer.  Errors as
+ * dcp_mla_partial_decode, plus DCP_ERR_INVALID_ARG for an unknown fuse mode.
+ */
+int dcp_mla_decode_merged_scratch_size(int64_t B, int hq, int64_t kv_tokens, int cp, size_t* bytes);
+
+int dcp_mla_decode_merged(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const void* kv,
+                          int64_t kv_tokens, int64_t kv_st, int dtype, int cp, float softmax_scale, int lse_mode,
+                          void* o_part, int64_t o_sb, int64_t o_sh, float* lse_part, int64_t lse_sb, void* out,
+                          int64_t out_sb, int64_t out_sh, float* out_lse, int64_t out_lse_sb, int fuse,
+                          void* scratch, size_t scratch_bytes, void* hip_stream);
+
 /*
  * MLA decode partials with one cache per query token and per-token lengths:
  * the producer as a decode batch runs it, each token (request) attending

@@ -106,6 +106,53 @@ static void fixed_split_checks() {
                         need - 1, &plan) == DCP_ERR_WORKSPACE);
 }
 
+// dcp_mla_decode_merged: the counters first, the split partials after them;
+// EPILOGUE marks the plan fused (no separate split reduction or shard
+// merge), NONE and AUTO plan the shard merge over (o_part, lse_part) in the
+// FlashMLA layout; errors before anything could run.
+static void merged_plan_checks() {
+    const int64_t B = 3, T = 131072;
+    const int hq = 128, cp = 4;
+    int32_t nsplit;
+    int64_t split_len;
+    size_t part;
+    dcp::mla_split(B, hq, T, cp, &nsplit, &split_len, &part);
+    const size_t cnt = dcp::merged_counter_bytes(B, hq, cp);
+    CHECK(cnt == 256 && nsplit > 1);  // 3 row blocks x (4 + 1) counters, rounded to 256 bytes
+    size_t need = 0;
+    CHECK(dcp_mla_decode_merged_scratch_size(B, hq, T, cp, &need) == DCP_OK && need == cnt + part);
+    const uintptr_t q = uintptr_t{1} << 40, kv = uintptr_t{2} << 40, o = uintptr_t{3} << 40,
+                    l = uintptr_t{4} << 40, out = uintptr_t{5} << 40, scr = uintptr_t{6} << 40,
+                    ol = uintptr_t{7} << 40;
+    auto plan_it = [&](int fuse, size_t bytes, uintptr_t out_p, dcp::MlaPlan* plan) {
+        return dcp::plan_mla_merged(fake(q), B, hq, hq * 576, 576, fake(kv), T, 576, DCP_DTYPE_BF16, cp, 0.07f,
+                                    DCP_LSE_BASE_2, fake(o), cp * hq * 512, 512, reinterpret_cast<float*>(l),
+                                    cp * hq, fake(out_p), hq * 512, 512, reinterpret_cast<float*>(ol), hq, fuse,
+                                    fake(scr), bytes, plan);
+    };
+    dcp::MlaPlan plan;
+    CHECK(plan_it(DCP_FUSE_EPILOGUE, need, out, &plan) == DCP_OK);
+    CHECK(plan.args.fused == 1 && !plan.merge_shards);
+    CHECK(reinterpret_cast<uintptr_t>(plan.args.split_cnt) == scr);
+    CHECK(plan.args.rb_cnt == plan.args.split_cnt + 3 * cp);
+    CHECK(reinterpret_cast<uintptr_t>(plan.args.part_o) == scr + cnt);
+    CHECK(plan.args.to_log2 == 1.0f && plan.args.from_log2 == 1.0f);
+    for (int fuse : {DCP_FUSE_NONE, DCP_FUSE_AUTO}) {
+        CHECK(plan_it(fuse, need, out, &plan) == DCP_OK);
+        CHECK(plan.args.fused == 0 && plan.merge_shards);
+        const dcp::MergeArgs& m = plan.shard_merge;
+        CHECK(m.attn == fake(o) && m.a_sb == cp * hq * 512 && m.a_sj == 512 && m.a_ss == hq * 512);
+        CHECK(m.l_sb == cp * hq && m.l_sj == 1 && m.l_ss == hq && m.h_local == hq && m.cp == cp);
+        CHECK(reinterpret_cast<uintptr_t>(m.out) == out && m.o_sb == hq * 512 && m.o_sj == 512 && m.cached == 1);
+    }
+    CHECK(plan_it(DCP_FUSE_EPILOGUE, need - 1, out, &plan) == DCP_ERR_WORKSPACE);
+    CHECK(std::strstr(dcp_last_error(), "dcp_mla_decode_merged_scratch_size") != nullptr);
+    CHECK(plan_it(3, need, out, &plan) == DCP_ERR_INVALID_ARG);
+    CHECK(plan_it(DCP_FUSE_NONE, need, o + 1024, &plan) == DCP_ERR_INVALID_ARG);    // out inside o_part
+    CHECK(plan_it(DCP_FUSE_NONE, need, scr + 4096, &plan) == DCP_ERR_INVALID_ARG);  // out inside the scratch
+    CHECK(plan_it(DCP_FUSE_NONE, need, out + 8, &plan) == DCP_ERR_ALIGN);
+}
+
 // The plan's 32-bit shard sizes against their plain 64-bit definition.
 static void shard_formula_checks() {
     std::mt19937_64 rng(7);
@@ -354,6 +401,7 @@ int main() {
 
     varlen_plan_checks();
     fixed_split_checks();
+    merged_plan_checks();
 
     if (g_failures) {
         std::fprintf(stderr, "%d check(s) failed\n", g_failures);
