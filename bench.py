@@ -51,7 +51,8 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=600, help="timed layer-merges (a multiple of 60 above 60)")
     p.add_argument("--warmup", type=int, default=120)
-    p.add_argument("--workload", choices=["kimi", "dsv2", "stress", "kimi_f16", "dsv2_f16", "stress_f16"],
+    p.add_argument("--workload", choices=["kimi", "dsv2", "stress", "kimi_f16", "dsv2_f16", "stress_f16", "wide32",
+                                          "wide64"],
                    default="kimi")
     p.add_argument("--B", type=int, default=128)
     p.add_argument("--no-sweep", action="store_true", help="skip the B = 1..512 sweep")
@@ -60,6 +61,8 @@ def parse_args():
     p.add_argument("--no-hot", action="store_true", help="skip the hot-cache figure")
     p.add_argument("--no-producer", action="store_true", help="skip the MLA producer (B = 1, 8, 32, 64) leg")
     p.add_argument("--producer-B", type=int, nargs="*", default=[1, 8, 32, 64])
+    p.add_argument("--no-fused", action="store_true",
+                   help="skip the dcp_mla_decode_merged rows (separate vs fused epilogue) of the producer leg")
     p.add_argument("--calibrate", action="store_true",
                    help="also run a plain 256 MiB elementwise copy kernel (reference for HBM byte counters)")
     return p.parse_args()
@@ -74,13 +77,17 @@ def make_case(workload, B):
         return synth.kimi_merge(B, dtype=dtype)
     if base == "dsv2":
         return synth.dsv2_merge(B, dtype=dtype)
+    if base.startswith("wide"):
+        return synth.wide_merge(B, int(base[4:]), dtype=dtype)
     return synth.stress_merge(B, dtype=dtype)
 
 
 def workload_name(case, workload):
     desc = {"kimi": "Kimi-K2.5-like merge, [B,H/cp,cp] base-e LSE",
             "dsv2": "DeepSeek-V2-236B-like merge, FlashMLA [B,H,1] base-2 LSE",
-            "stress": "stress merge, 10% empty shards, capacity 128 (ordered chunks)"}[workload.replace("_f16", "")]
+            "stress": "stress merge, 10% empty shards, capacity 128 (ordered chunks)",
+            "wide32": "wide merge (16 local heads), [B,H/cp,cp] base-e LSE",
+            "wide64": "wide merge (16 local heads), [B,H/cp,cp] base-e LSE"}[workload.replace("_f16", "")]
     return "%s: B=%d H=%d cp=%d H_local=%d D=512 %s" % (desc, case.B, case.H, case.cp, case.h_local,
                                                          "fp16" if workload.endswith("_f16") else "bf16")
 
@@ -474,7 +481,76 @@ def measure_producer(B, kv_copies, reps=8, seq_lens=None, replays=5):
     return prod, mrg
 
 
-def producer_leg(Bs):
+def measure_merged(B, kv_copies, fuse, reps=8, replays=5):
+    """dcp_mla_decode_merged (the producer's partials and their shard merge in one call) on the full-size MLA
+    decode workload, timed as measure_producer times the producer: a HIP graph of `reps` calls over the rotated
+    cache copies, warmed up for ~50 ms, then the median replay / reps."""
+    import torch
+    import context_lse_merge_amd as dcp
+    import synth
+    dev = torch.device("cuda:0")
+    hq, cp, T = 128, 4, kv_copies[0].shape[-2]
+    dtype = kv_copies[0].dtype
+    q = synth.normal_16((B, hq, 576), synth.gen(3000 + B), dtype).to(dev)
+    o = torch.empty((B, cp * hq, 512), dtype=dtype, device=dev)
+    l = torch.empty((B, cp * hq), dtype=torch.float32, device=dev)
+    out = torch.empty((B, hq, 512), dtype=dtype, device=dev)
+    out_lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    scratch = torch.zeros(dcp.dcp_mla_decode_merged_scratch_size(B, hq, T, cp), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+
+    def call(kv):
+        dcp.dcp_mla_decode_merged(q, kv, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, out, out_lse, fuse=fuse,
+                                  scratch=scratch, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for k in range(2):
+            call(kv_copies[k % len(kv_copies)])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for r in range(reps):
+            call(kv_copies[r % len(kv_copies)])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    once_ms = max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(int(math.ceil(50.0 / once_ms))):
+        g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(max(replays, int(math.ceil(20.0 / once_ms)))):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gpu_delay(0.2)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del g
+    return sorted(ts)[len(ts) // 2] * 1000.0 / reps
+
+
+def fused_rows(Bs, copies):
+    """N1: the producer with the split reduction and the shard merge in its epilogue (one launch) against the same
+    work as separate launches, at each B."""
+    import context_lse_merge_amd as dcp
+    rows = []
+    for B in Bs:
+        r = {"B": B}
+        for name, fuse in (("separate_us", dcp.DCP_FUSE_NONE), ("fused_us", dcp.DCP_FUSE_EPILOGUE),
+                           ("auto_us", dcp.DCP_FUSE_AUTO)):
+            r[name] = round(measure_merged(B, copies, fuse), 1)
+        rows.append(r)
+        print("[bench] producer + shard merge B=%d: separate launches %.1f us, fused epilogue %.1f us, auto %.1f us"
+              % (B, r["separate_us"], r["fused_us"], r["auto_us"]), file=sys.stderr, flush=True)
+    return rows
+
+
+def producer_leg(Bs, with_fused=True):
     import torch
     import synth
     _, kv = synth.mla_decode(1)
@@ -491,6 +567,7 @@ def producer_leg(Bs):
                      "kv_GBps": round(kv_gbs, 1), "flop": fl})
         print("[bench] producer B=%d: %.1f us (%.1f TFLOP/s, %.1f%% of bf16 peak), merge %.2f us"
               % (B, us, tflops, 100 * tflops / MFMA_BF16_PEAK_TFLOPS, us_m), file=sys.stderr, flush=True)
+    fused = fused_rows(Bs, copies) if with_fused else []
     # the other payload type and the variable-length entry point, at B = 64
     import numpy as np
     seq = np.random.default_rng(64).integers(1, kv.shape[0] + 1, 64).astype(np.int32)
@@ -533,7 +610,7 @@ def producer_leg(Bs):
           % (us, tflops, 100 * tflops / MFMA_FP16_PEAK_TFLOPS, us_m), file=sys.stderr, flush=True)
     del copies
     torch.cuda.empty_cache()
-    return rows
+    return rows, fused
 
 
 def producer_oracle_baseline():
@@ -635,7 +712,7 @@ def main():
     if not args.no_sweep:
         for wl, Bs in (("kimi", [1, 8, 16, 32, 64, 128, 256, 512]), ("dsv2", [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]),
                        ("kimi_f16", [64, 128, 512]), ("dsv2_f16", [512]),
-                       ("stress", [512])):
+                       ("stress", [512]), ("wide32", [16, 32, 64]), ("wide64", [8, 16, 32])):
             for B in Bs:
                 c = make_case(wl, B)
                 cap = 128 if wl.startswith("stress") else B
@@ -670,7 +747,7 @@ def main():
                "one_thread": {"value": round(alg / (cu1 * 1e-6) / 1e9, 3), "unit": "GB/s",
                               "us_per_layer_merge": round(cu1, 1), "sample": "%d whole layer-merges, median" % reps1}}
 
-    producer = [] if args.no_producer else producer_leg(args.producer_B)
+    producer, fused = ([], []) if args.no_producer else producer_leg(args.producer_B, not args.no_fused)
     producer_cpu = None
     if not args.no_producer and not args.no_cpu_baseline:
         producer_cpu = producer_oracle_baseline()
@@ -723,7 +800,12 @@ def main():
                      "bound": "mfma (B >= 2), hbm (B = 1)", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
                      "timing": "HIP graphs of 8 calls (each of 8 cache copies once) and of 8 merges, replayed "
                                "for ~50 ms of warm-up, then timed per replay; median replay / 8",
-                     "rows": producer, "cpu_baseline": producer_cpu},
+                     "rows": producer, "cpu_baseline": producer_cpu,
+                     "merged": {"what": "dcp_mla_decode_merged: the partials and their shard merge in one call; "
+                                        "separate = decode + split reduction + shard merge launches (DCP_FUSE_NONE), "
+                                        "fused = one launch whose last-arriving workgroups reduce and merge "
+                                        "(DCP_FUSE_EPILOGUE), auto = DCP_FUSE_AUTO",
+                                "rows": fused}},
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -17,6 +17,7 @@ Workloads (shapes and value distributions of the pages' decode geometries;
 * ``dsv2_merge``        H=128, cp=8 (16 heads/rank), D=512; O ~ N(0,1); base-2 LSE ~ N(10,4),
                         FlashMLA [B, H, 1] layout (the 8-GPU DeepSeek-V2-236B geometry of
                         sglang PR #40539, Speed Tests).
+* ``wide_merge``        cp = 32 or 64 shards of 16 local heads (H = 16 cp), base-e LSE ~ U[0,20], [B, H/cp, cp].
 * ``stress_merge``      B=512, in-place [B,64,512] viewed as [B,16,4,512]; LSE ~ U[-30,30] base-e;
                         round(0.1*B*cp) (token, shard) pairs set to -inf (empty shards, all 16 heads
                         of the pair) and their O rows filled with NaN.
@@ -125,6 +126,16 @@ def dsv2_merge(B: int, seed: int = SEED_BASE + 3, dtype=torch.bfloat16) -> Merge
     attn = normal_16((B, H, D), g, dtype)
     lse = normal_f32((B, H, 1), g, 10.0, 4.0)
     return MergeCase("dsv2-236b-like H=128 cp=8 B=%d" % B + _sfx(dtype), attn, lse, cp, "bh1", "2")
+
+
+def wide_merge(B: int, cp: int, seed: int = SEED_BASE + 6, dtype=torch.bfloat16) -> MergeCase:
+    """More than 16 shards: 16 local heads per rank (the per-rank head count of both geometries above), H = 16 cp,
+    base-e LSE ~ U[0, 20] in the [B, H/cp, cp] layout."""
+    g = gen(seed * 1009 + B * 131 + cp)
+    H = 16 * cp
+    attn = normal_16((B, H, D), g, dtype)
+    lse = uniform_f32((B, 16, cp), g, 0.0, 20.0)
+    return MergeCase("wide H=%d cp=%d B=%d" % (H, cp, B) + _sfx(dtype), attn, lse, cp, "bhc", "e")
 
 
 def empty_pairs(B: int, cp: int, frac: float, g: torch.Generator) -> torch.Tensor:
