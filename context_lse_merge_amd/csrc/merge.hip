@@ -24,10 +24,11 @@
 //    with no cross-lane step; a row whose weights are all nonzero takes a
 //    plain FMA path, a row with an empty shard (weight exactly 0, which covers
 //    lse = -inf) zeroes that shard's payload first, so it is never used;
-//  * cp > 16: lane s holds lse_s; the maximum and the sum run over the lanes
-//    in ascending shard order (the same order as for cp <= 16), and the
-//    payloads stream in 16 shards at a time, each group's loads issued before
-//    the previous group's FMAs;
+//  * cp > 16: two or four wavefronts per row, each with 16 shards' loads in
+//    flight; lane s holds lse_s, the maximum and the sum are DPP reductions
+//    over the lanes (the sum in the one fixed tree every path uses for more
+//    than 16 parts), and the fp32 accumulators pass from wavefront to
+//    wavefront through LDS, so the FMAs run in ascending shard order;
 //  * fp32 FMAs in ascending shard order, then the hardware round-to-nearest-
 //    even convert to the payload type and one 16-byte store per lane.  The
 //    payload is bf16 or fp16 (both are the pages' payload types); one kernel
@@ -176,19 +177,63 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const void* attn, const f
     store_row<Out>(t, r, lane, acc, mrow::merged_lse(M, S, t.from_log2));
 }
 
-// 16 < cp <= 64: the same row arithmetic with the shards taken G at a time
-// (mrow::merge_row_any).
-template <int G, typename In, typename Out>
+// 16 < cp <= 64: W wavefronts per row, wavefront w holding shards
+// [16w, 16w + 16) of it, so that all of a row's loads are in flight at once
+// (a row has few enough shards per wavefront, and rows enough wavefronts, to
+// fill the chip even at small B).  Every wavefront forms the row's M, S and
+// 1/S itself (mrow::row_max_sum: a DPP tree over the shards); the accumulation
+// then runs in ascending shard order across the wavefronts: wavefront w takes
+// the accumulators of w - 1 from LDS (exact fp32 values), adds its 16
+// shards, and hands them on; the last one stores the row.  The result is
+// merge_row_any's, bit for bit.  A block of kWavesPerBlock wavefronts holds
+// kWavesPerBlock / W rows; spare rows of the last group repeat row
+// h_local - 1 (same reads, same bits to the same place).
+template <int W, typename In, typename Out>
 __global__ __launch_bounds__(kBlock) void merge_kernel_wide(const void* attn, const float* lse, int32_t a_sb,
                                                             int32_t a_sj, int32_t a_ss, int32_t l_sb, int32_t l_sj,
                                                             int32_t l_ss, int32_t h_local, MergeTail t) {
+    constexpr int kRows = kWavesPerBlock / W;
+    constexpr int kPer = 16;  // shards per wavefront
+    __shared__ float hand[kRows][8][64];
     const int lane = threadIdx.x & 63;
-    const Row r = row_of(h_local);
+    const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ri = v / W, w = v - ri * W;
+    Row r;
+    r.b = blockIdx.y;
+    const int jr = blockIdx.x * kRows + ri;
+    r.j = jr < h_local ? jr : h_local - 1;
+    const int cp = t.cp;
     const int64_t orow = static_cast<int64_t>(r.b) * a_sb + static_cast<int64_t>(r.j) * a_sj + lane * 8;
     const float* lrow = lse + static_cast<int64_t>(r.b) * l_sb + static_cast<int64_t>(r.j) * l_sj;
-    float acc[8], M, S;
-    mrow::merge_row_any<G, In>(attn, orow, a_ss, lrow, l_ss, t.sc_off, t.cp, t.to_log2, acc, M, S);
-    store_row<Out>(t, r, lane, acc, mrow::merged_lse(M, S, t.from_log2));
+    const int s0 = w * kPer;
+    typename In::row_t vals[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) vals[i] = In::load(attn, orow + static_cast<int64_t>(min(s0 + i, cp - 1)) * a_ss);
+
+    // M, S and 1/S over all cp shards (mrow::row_max_sum; lane s holds shard s, cp <= 64).
+    float M, S;
+    mrow::row_max_sum(lrow, l_ss, cp, t.to_log2, M, S);
+    const float inv = mrow::inv_sum(S);
+    const float x = lane < cp ? lrow[static_cast<int64_t>(lane) * l_ss] : -INFINITY;
+    float wl = mrow::shard_weight(x, M, t.to_log2) * inv;
+    if (In::kScaled) wl *= lane < cp ? lrow[static_cast<int64_t>(lane) * l_ss + t.sc_off] : 0.0f;
+
+    float acc[8];
+    for (int step = 0; step < W; ++step) {
+        if (w == step) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = step == 0 ? 0.0f : hand[ri][i][lane];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i)
+                if (s0 + i < cp) mrow::fma8<In>(acc, mrow::lane_value(wl, s0 + i), vals[i]);
+            if (step + 1 < W) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) hand[ri][i][lane] = acc[i];
+            }
+        }
+        if (step + 1 < W) __syncthreads();
+    }
+    if (w == W - 1) store_row<Out>(t, r, lane, acc, mrow::merged_lse(M, S, t.from_log2));
 }
 
 typedef void (*MergeKernel)(const void*, const float*, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
@@ -206,6 +251,12 @@ void launch_merge(MergeKernel k, const MergeArgs& a, dim3 grid, hipStream_t stre
 template <int CP, typename In, typename Out>
 void launch_fixed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
     launch_merge(merge_kernel<CP, In, Out>, a, grid, stream);
+}
+
+template <int W, typename In, typename Out>
+void launch_wide(const MergeArgs& a, dim3 grid, hipStream_t stream) {
+    constexpr int kRows = kWavesPerBlock / W;
+    launch_merge(merge_kernel_wide<W, In, Out>, a, dim3((a.h_local + kRows - 1) / kRows, grid.y), stream);
 }
 
 template <typename In, typename Out>
@@ -227,7 +278,12 @@ void launch_typed(const MergeArgs& a, dim3 grid, hipStream_t stream) {
         case 14: launch_fixed<14, In, Out>(a, grid, stream); break;
         case 15: launch_fixed<15, In, Out>(a, grid, stream); break;
         case 16: launch_fixed<16, In, Out>(a, grid, stream); break;
-        default: launch_merge(merge_kernel_wide<16, In, Out>, a, grid, stream); break;
+        default:
+            if (a.cp <= 32)
+                launch_wide<2, In, Out>(a, grid, stream);
+            else
+                launch_wide<4, In, Out>(a, grid, stream);
+            break;
     }
 }
 

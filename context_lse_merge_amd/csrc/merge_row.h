@@ -5,8 +5,10 @@
 // kernel over scratch partials, the variable-length reducer in mla_varlen.hip,
 // and the fused epilogue of mla_decode.hip) -- forms one row's result with the
 // functions below, so they all give the same bits for the same inputs:
-//     M = max over s, ascending;   w_s = 2^((lse_s - M) * c), 0 for lse_s = -inf;
-//     S = sum of w_s, ascending from 0;   inv = 1/S (0 when S = 0);
+//     M = max over s (exact in any order);   w_s = 2^((lse_s - M) * c), 0 for lse_s = -inf;
+//     S = sum of w_s: for n <= 16 ascending from 0; for n > 16 per group of
+//         64 shards a fixed tree (tree_sum), the groups' sums added in
+//         ascending order from 0;   inv = 1/S (0 when S = 0);
 //     w^_s = w_s * inv (* the row's scale factor, for scaled partials);
 //     acc = sum of w^_s * O_s, ascending, fp32 FMA, a shard of weight 0 adding +0;
 //     L = M + log2(S) / c.
@@ -140,14 +142,75 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// DPP controls (gfx9 encoding): quad_perm [1,0,3,2] and [2,3,0,1], then
+// row_half_mirror and row_mirror.  Applied in that order they combine all 16
+// lanes of a row, and every lane of the row ends up holding the result.
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+
+// Maximum over the first m <= 64 lanes (lanes >= m must hold -inf), in a
+// scalar register.  fmaxf is exact, so any order gives the same value.
+__device__ __forceinline__ float wave_max(float v, int m) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    float r = lane_value(v, 0);
+    if (m > 16) r = fmaxf(r, lane_value(v, 16));
+    if (m > 32) r = fmaxf(fmaxf(r, lane_value(v, 32)), lane_value(v, 48));
+    return r;
+}
+
+// Sum over the first m <= 64 lanes (lanes >= m must hold 0) in one fixed
+// order: within each 16-lane row the DPP tree (pairs, quads, halves, rows),
+// then row 0 + row 1, plus (row 2 + row 3).  Every path that merges more than
+// 16 parts sums them this way, so they agree bit for bit.
+__device__ __forceinline__ float tree_sum(float v, int m) {
+    v = v + dpp<0xB1>(v);
+    v = v + dpp<0x4E>(v);
+    v = v + dpp<0x141>(v);
+    v = v + dpp<0x140>(v);
+    float r = lane_value(v, 0);
+    if (m > 16) r = r + lane_value(v, 16);
+    if (m > 32) r = r + (lane_value(v, 32) + lane_value(v, 48));
+    return r;
+}
+
+// M and S of a row of n parts whose LSEs are lrow[s * l_ss], by the rules
+// above (wave-uniform arguments, all 64 lanes).
+__device__ __forceinline__ void row_max_sum(const float* lrow, int64_t l_ss, int n, float to_log2, float& M,
+                                            float& S) {
+    const int lane = threadIdx.x & 63;
+    M = 0.0f;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+        const int m = min(64, n - c0);
+        const float x = lane < m ? lrow[static_cast<int64_t>(c0 + lane) * l_ss] : -INFINITY;
+        const float cm = wave_max(x, m);
+        M = c0 == 0 ? cm : fmaxf(M, cm);
+    }
+    S = 0.0f;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+        const int m = min(64, n - c0);
+        const float x = lane < m ? lrow[static_cast<int64_t>(c0 + lane) * l_ss] : -INFINITY;
+        const float w = shard_weight(x, M, to_log2);
+        if (n <= 16) {
+            for (int i = 0; i < m; ++i) S += lane_value(w, i);
+        } else {
+            S += tree_sum(w, m);
+        }
+    }
+}
+
 // Merge of one row over a runtime number n >= 1 of shards, called by all 64
 // lanes of a wavefront with wave-uniform arguments.  Shard s's 8 columns of
 // this lane are In elements at attn + o0 + s*a_ss (o0 includes the lane's
 // column offset); its LSE is lrow[s*l_ss] and, for scaled payloads, its
 // factor lrow[s*l_ss + sc_off].  The LSEs come in 64 at a time, shard c0 + l
-// in lane l, and the sequential maximum and sum read them lane by lane; the
+// in lane l, for the maximum and the sum (row_max_sum); the
 // payloads come G shards at a time, the next group's loads issued before the
-// current group's FMAs.  Returns the accumulators, M and S.
+// current group's FMAs.  Returns the accumulators, M and S (row_max_sum).
 template <int G, typename In>
 __device__ __forceinline__ void merge_row_any(const void* attn, int64_t o0, int64_t a_ss, const float* lrow,
                                               int64_t l_ss, int64_t sc_off, int n, float to_log2, float (&acc)[8],
@@ -158,22 +221,7 @@ __device__ __forceinline__ void merge_row_any(const void* attn, int64_t o0, int6
 #pragma unroll
     for (int i = 0; i < G; ++i) cur[i] = In::load(attn, o0 + static_cast<int64_t>(min(i, n - 1)) * a_ss);
 
-    M = 0.0f;
-    for (int c0 = 0; c0 < n; c0 += 64) {
-        const int m = min(64, n - c0);
-        const float x = lane < m ? lrow[static_cast<int64_t>(c0 + lane) * l_ss] : -INFINITY;
-        for (int i = 0; i < m; ++i) {
-            const float xi = lane_value(x, i);
-            M = (c0 + i == 0) ? xi : fmaxf(M, xi);
-        }
-    }
-    S = 0.0f;
-    for (int c0 = 0; c0 < n; c0 += 64) {
-        const int m = min(64, n - c0);
-        const float x = lane < m ? lrow[static_cast<int64_t>(c0 + lane) * l_ss] : -INFINITY;
-        const float w = shard_weight(x, M, to_log2);
-        for (int i = 0; i < m; ++i) S += lane_value(w, i);
-    }
+    row_max_sum(lrow, l_ss, n, to_log2, M, S);
     const float inv = inv_sum(S);
 
 #pragma unroll
