@@ -178,28 +178,38 @@ __device__ __forceinline__ float tree_sum(float v, int m) {
     return r;
 }
 
-// M and S of a row of n parts whose LSEs are lrow[s * l_ss], by the rules
-// above (wave-uniform arguments, all 64 lanes).
+// M and S of m <= 64 parts held one per lane (x: the lane's LSE, -inf in
+// lanes >= m), by the rules above.  All 64 lanes, wave-uniform m.
+__device__ __forceinline__ void lane_max_sum(float x, int m, float to_log2, float& M, float& S) {
+    M = wave_max(x, m);
+    const float w = shard_weight(x, M, to_log2);
+    if (m <= 16) {
+        S = 0.0f;
+        for (int i = 0; i < m; ++i) S += lane_value(w, i);
+    } else {
+        S = 0.0f + tree_sum(w, m);
+    }
+}
+
+// The lane's LSE of part c0 + lane of a row (-inf past the m-th).
+__device__ __forceinline__ float lane_lse(const float* lrow, int64_t l_ss, int c0, int m) {
+    const int lane = threadIdx.x & 63;
+    return lane < m ? lrow[static_cast<int64_t>(c0 + lane) * l_ss] : -INFINITY;
+}
+
+// M and S of a row of n > 64 parts whose LSEs are lrow[s * l_ss], 64 at a
+// time (all 64 lanes, wave-uniform arguments).
 __device__ __forceinline__ void row_max_sum(const float* lrow, int64_t l_ss, int n, float to_log2, float& M,
                                             float& S) {
-    const int lane = threadIdx.x & 63;
     M = 0.0f;
     for (int c0 = 0; c0 < n; c0 += 64) {
-        const int m = min(64, n - c0);
-        const float x = lane < m ? lrow[static_cast<int64_t>(c0 + lane) * l_ss] : -INFINITY;
-        const float cm = wave_max(x, m);
+        const float cm = wave_max(lane_lse(lrow, l_ss, c0, min(64, n - c0)), min(64, n - c0));
         M = c0 == 0 ? cm : fmaxf(M, cm);
     }
     S = 0.0f;
     for (int c0 = 0; c0 < n; c0 += 64) {
         const int m = min(64, n - c0);
-        const float x = lane < m ? lrow[static_cast<int64_t>(c0 + lane) * l_ss] : -INFINITY;
-        const float w = shard_weight(x, M, to_log2);
-        if (n <= 16) {
-            for (int i = 0; i < m; ++i) S += lane_value(w, i);
-        } else {
-            S += tree_sum(w, m);
-        }
+        S += tree_sum(shard_weight(lane_lse(lrow, l_ss, c0, m), M, to_log2), m);
     }
 }
 
@@ -208,29 +218,38 @@ __device__ __forceinline__ void row_max_sum(const float* lrow, int64_t l_ss, int
 // this lane are In elements at attn + o0 + s*a_ss (o0 includes the lane's
 // column offset); its LSE is lrow[s*l_ss] and, for scaled payloads, its
 // factor lrow[s*l_ss + sc_off].  The LSEs come in 64 at a time, shard c0 + l
-// in lane l, for the maximum and the sum (row_max_sum); the
+// in lane l, for the maximum and the sum (lane_max_sum, row_max_sum); the
 // payloads come G shards at a time, the next group's loads issued before the
-// current group's FMAs.  Returns the accumulators, M and S (row_max_sum).
+// current group's FMAs.  Returns the accumulators, M and S.
 template <int G, typename In>
 __device__ __forceinline__ void merge_row_any(const void* attn, int64_t o0, int64_t a_ss, const float* lrow,
                                               int64_t l_ss, int64_t sc_off, int n, float to_log2, float (&acc)[8],
                                               float& M, float& S) {
     const int lane = threadIdx.x & 63;
     typedef typename In::row_t row_t;
+    // The first 64 parts' LSEs (and factors) are read once, with the first
+    // payload loads, so that only one memory round trip precedes the weights.
+    const int m0 = min(64, n);
+    const float x0 = lane_lse(lrow, l_ss, 0, m0);
+    const float sc0 = In::kScaled && lane < m0 ? lrow[static_cast<int64_t>(lane) * l_ss + sc_off] : 0.0f;
     row_t cur[G], nxt[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) cur[i] = In::load(attn, o0 + static_cast<int64_t>(min(i, n - 1)) * a_ss);
 
-    row_max_sum(lrow, l_ss, n, to_log2, M, S);
+    if (n <= 64) {
+        lane_max_sum(x0, n, to_log2, M, S);
+    } else {
+        row_max_sum(lrow, l_ss, n, to_log2, M, S);
+    }
     const float inv = inv_sum(S);
 
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
     for (int c0 = 0; c0 < n; c0 += 64) {
         const int m = min(64, n - c0);
-        const int64_t ls = static_cast<int64_t>(c0 + (lane < m ? lane : 0)) * l_ss;
-        float wl = shard_weight(lane < m ? lrow[ls] : -INFINITY, M, to_log2) * inv;
-        if (In::kScaled) wl *= lrow[ls + sc_off];
+        float wl = shard_weight(c0 == 0 ? x0 : lane_lse(lrow, l_ss, c0, m), M, to_log2) * inv;
+        if (In::kScaled)
+            wl *= c0 == 0 ? sc0 : (lane < m ? lrow[static_cast<int64_t>(c0 + lane) * l_ss + sc_off] : 0.0f);
         for (int g0 = 0; g0 < m; g0 += G) {
             const int s_next = c0 + g0 + G;  // first shard of the next group
             if (s_next < n) {
