@@ -7,12 +7,13 @@ adapter, chunk planner, LSE reduction, weighted accumulation, store.
 
 Timing.  Inputs are resident in HBM before the timed region starts.  Calls
 are captured into HIP graphs of min(60, steps) calls each (60: one per MLA
-layer of a decode step).  The timed calls read input sets of their own: all
-distinct when they fit in 1 GiB, else cycled so that the same bytes come back
-only after at least 1 GiB of other inputs -- more than the 256 MB Infinity
-Cache.  Warm-up calls run on a separate set in a separate graph; then 1 GiB of
-unrelated data is read, so every timed input comes from HBM (a cold-cache
-figure).  A bounded spin kernel queued before the start event keeps the GPU
+layer of a decode step).  Every timed call reads an input set of its own (up
+to 32 GiB of sets; past that the sets are cycled, tens of gigabytes apart):
+measured, a set read again even 1.27 GB of other inputs later -- five times
+the 256 MB Infinity Cache -- still comes back about 9% faster, so no timed
+call re-reads another's bytes.  Warm-up calls run on a separate set in a
+separate graph; then 1 GiB of unrelated data is read, so every timed input
+comes from HBM (a cold-cache figure).  A bounded spin kernel queued before the start event keeps the GPU
 busy while the host submits the timed graph launches, so the region holds GPU
 work only.  The region is bracketed by a barrier and torch.cuda.synchronize()
 and measured with HIP events on the stream the graphs are launched on.  A
@@ -40,7 +41,9 @@ if ROOT not in sys.path:
 
 METRIC = "µs per layer-merge + achieved HBM GB/s (% of peak) at B=1..512, 1×MI355X"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
-COLD_BYTES = 1 << 30            # distance between reuses of the same input bytes
+COLD_BYTES = 1 << 30            # unrelated bytes read before the timed region (cache eviction)
+DISTINCT_BYTES = 32 << 30       # timed input sets up to this footprint are all distinct
+KV_COPIES = 24                  # producer: cache copies in rotation (3.6 GB; a copy is re-read 3.5 GB later)
 GRAPH_CALLS = 60                # calls per captured graph (one per MLA layer)
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "dcp_merge_kimi_b128_counters.txt")
 MERGE_SRC = os.path.join(ROOT, "context_lse_merge_amd", "csrc", "merge.hip")
@@ -234,16 +237,18 @@ def warm_up(graph, calls, warmup):
 def plan_sets(per_set, steps, cold):
     """Which input set each timed call reads.  Returns (calls per graph, timed sets, one list of set indices per
     timed graph, the warm-up set).  The timed region replays the graphs in order, round-robin, steps / calls times.
-    cold: the timed calls read sets [0, n) -- every call a different one when steps fit in the reuse distance, else
-    n >= 1 GiB / per_set sets cycled in order -- and the warm-up reads set n, which no timed call reads.  hot: set 0
-    throughout."""
+    cold: every timed call reads a set of its own while steps * per_set <= DISTINCT_BYTES, else the calls cycle
+    over as many sets as fit in DISTINCT_BYTES (a whole number of graphs, at least one); the warm-up reads the
+    next set, which no timed call reads.  hot: set 0 throughout."""
     calls = min(GRAPH_CALLS, steps)
     if steps <= 0 or steps % calls:
         raise SystemExit("--steps must be a positive multiple of %d" % calls)
     if not cold:
         return calls, 1, [[0] * calls], 0
-    reuse = math.ceil(COLD_BYTES / per_set)
-    n_sets = min(steps, math.ceil(reuse / calls) * calls)
+    if steps * per_set <= DISTINCT_BYTES:
+        n_sets = steps
+    else:
+        n_sets = max(1, DISTINCT_BYTES // (per_set * calls)) * calls
     timed = [list(range(g * calls, (g + 1) * calls)) for g in range(n_sets // calls)]
     return calls, n_sets, timed, n_sets
 
@@ -251,9 +256,8 @@ def plan_sets(per_set, steps, cold):
 def measure(case, steps, warmup, capacity=None, cold=True, cached=False):
     """Time `steps` layer-merges in HIP graphs of `calls` calls each.
 
-    cold: the timed calls use input sets of their own, all distinct when they fit in the reuse distance, else
-    cycled so that the same bytes come back only after >= 1 GiB of other inputs; warm-up runs on a separate set
-    and separate graphs; then 1 GiB of unrelated data is read, so every timed input comes from HBM.  hot: every
+    cold: every timed call reads an input set of its own (plan_sets); warm-up runs on a separate set and separate
+    graphs; then 1 GiB of unrelated data is read, so every timed input comes from HBM.  hot: every
     call (warm-up and timed) uses one set.  ``cached``: the workspace's DCP_LOAD_CACHED policy.
     Returns a dict: us per layer-merge, calls per graph, timed input sets, warm-up calls, footprint, first set."""
     per_set = case.attn.numel() * 2 + case.lse.numel() * 4 + case.B * case.h_local * (1024 + 4)
@@ -291,35 +295,44 @@ def launch_floor(steps, warmup):
 
 
 def copy_ceiling(headline_bytes):
-    """Cold device-to-device copies (torch copy_) in the same harness: graphs of
-    GRAPH_CALLS copies cycling over >= 1 GiB of buffers.  Returns GB/s (bytes
-    read + written) for 256 MiB copies, and us per copy that reads and writes
-    half of `headline_bytes` each (the same total bytes as one layer-merge)."""
+    """Cold device-to-device copies (torch copy_) in the same harness: graphs of GRAPH_CALLS copies, replayed five
+    times after the eviction read.  Returns GB/s (bytes read + written) for 256 MiB copies (over buffers cycling
+    through >= 1 GiB; each copy streams more than the Infinity Cache holds), and us per copy that reads and writes
+    half of `headline_bytes` each (the same total bytes as one layer-merge; every timed copy has buffers of its
+    own, as the merge's timed calls do)."""
     import torch
     res = {}
+    replays = 5
     for label, nbytes in (("256MiB", 256 << 20), ("headline", headline_bytes // 2)):
         n = max(1, nbytes // 2)
-        sets = max(2, math.ceil((1 << 30) / (2 * n * 2)))
+        calls = GRAPH_CALLS
+        if replays * calls * 2 * n * 2 <= DISTINCT_BYTES:
+            sets = replays * calls
+        else:
+            sets = max(2, math.ceil((1 << 30) / (2 * n * 2)))
         src = [torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0) for _ in range(sets)]
         dst = [torch.empty_like(x) for x in src]
-        calls = min(GRAPH_CALLS, 4 * sets)
         stream = torch.cuda.Stream()
         with torch.cuda.stream(stream):
             dst[0].copy_(src[0])
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(calls):
-                dst[i % sets].copy_(src[i % sets])
-        warm_up(g, calls, 2 * calls)
-        us = time_graphs([g], 5, evict=True) * 1000.0 / (5 * calls)
+        graphs = []
+        for r in range(replays if sets == replays * calls else 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(calls):
+                    k = (r * calls + i) % sets
+                    dst[k].copy_(src[k])
+            graphs.append(g)
+        warm_up(graphs[0], calls, 2 * calls)
+        us = time_graphs(graphs, replays, evict=True) * 1000.0 / (replays * calls)
         res[label] = (us, 2.0 * n * 2 / (us * 1e-6) / 1e9)
-        del src, dst, g
+        del src, dst, graphs
         torch.cuda.empty_cache()
     return {"GBps_256MiB": round(res["256MiB"][1], 1),
             "us_at_headline_bytes": round(res["headline"][0], 3),
-            "kernel": "torch copy_ of bf16 buffers, cold (>= 1 GiB cycled), graphs of %d copies; GB/s counts "
-                      "bytes read plus bytes written" % GRAPH_CALLS}
+            "kernel": "torch copy_ of bf16 buffers, cold, graphs of %d copies; at the headline's bytes every timed "
+                      "copy has buffers of its own; GB/s counts bytes read plus bytes written" % GRAPH_CALLS}
 
 
 def parity_check(case, out, out_lse):
@@ -395,17 +408,15 @@ def producer_flops(B, hq, T):
 def measure_producer(B, kv_copies, reps=8, seq_lens=None, replays=5):
     """dcp_mla_partial_decode (+ the merge of its output) on the full-size MLA
     decode workload: q [B,128,576], one 131072 x 576 cache, 4 shards.  The cache
-    is rotated over `kv_copies` device copies (>= 1 GiB together) so every call
-    reads it from HBM.  With `seq_lens` (int32 [B] on the GPU) the
-    variable-length entry point runs instead: every token up to its own length,
-    interleaved ownership, over the shared cache (kv_sb = 0) or, when the
-    copies are [B, T, 576], over its own cache.  q, the cache and the outputs
-    take the cache's dtype.  Both steps are timed as a serving decode loop runs
-    them, captured in HIP graphs: one graph of `reps` producer calls (each cache
-    copy in turn) and one of `reps` merges of its output, each warmed up for
-    about 50 ms and then replayed at least `replays` times (and for at least
-    20 ms) with HIP events around every replay on the stream it is launched
-    on.
+    is rotated over `kv_copies` device copies (KV_COPIES: a copy is read again
+    only after 3.5 GB of other copies) so every call reads it from HBM.  With
+    `seq_lens` (int32 [B] on the GPU) the variable-length entry point runs
+    instead: every token up to its own length, interleaved ownership, over the
+    shared cache (kv_sb = 0) or, when the copies are [B, T, 576], over its own
+    cache.  q, the cache and the outputs take the cache's dtype.  Both steps are
+    timed as a serving decode loop runs them, captured in HIP graphs: graphs of
+    `reps` producer calls (each over its own cache copies, replayed in turn) and
+    one of `reps` merges of its output, timed by graph_call_us.
     Returns (producer us, merge us) per call, medians over the replays."""
     import torch
     import context_lse_merge_amd as dcp
@@ -443,42 +454,49 @@ def measure_producer(B, kv_copies, reps=8, seq_lens=None, replays=5):
             produce(kv_copies[k % len(kv_copies)])
             merge()
     torch.cuda.synchronize()
-    g_prod, g_merge = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_prod, stream=stream):
-        for r in range(reps):
-            produce(kv_copies[r % len(kv_copies)])
+    g_prod = []
+    for i in range(max(1, len(kv_copies) // reps)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(reps):
+                produce(kv_copies[(i * reps + r) % len(kv_copies)])
+        g_prod.append(g)
+    g_merge = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_merge, stream=stream):
         for r in range(reps):
             merge()
     torch.cuda.synchronize()
-
-    def per_call_us(g):
-        # Warm up for about 50 ms of this work: the first ~20 ms of sustained
-        # load run measurably slower (seen in eager and graph runs alike).
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        once_ms = max(e0.elapsed_time(e1), 1e-3)
-        for _ in range(int(math.ceil(50.0 / once_ms))):
-            g.replay()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(max(replays, int(math.ceil(20.0 / once_ms)))):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            gpu_delay(0.2)                # covers the host's submission of the replay
-            e0.record()                   # a replay runs on the current stream
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return sorted(ts)[len(ts) // 2] * 1000.0 / reps
-
-    prod, mrg = per_call_us(g_prod), per_call_us(g_merge)
+    prod, mrg = graph_call_us(g_prod, reps, replays), graph_call_us([g_merge], reps, replays)
     del g_prod, g_merge
     ws.close()
     return prod, mrg
+
+
+def graph_call_us(graphs, reps, replays):
+    """us per call of graphs of `reps` calls each, replayed in turn: warmed up for about 50 ms of this work (the
+    first ~20 ms of sustained load run measurably slower, seen in eager and graph runs alike), then at least
+    `replays` replays and at least 20 ms, HIP events around every replay on the stream it is launched on, a spin
+    kernel ahead of each start event covering the host's submission; the median replay / reps."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graphs[0].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    once_ms = max(e0.elapsed_time(e1), 1e-3)
+    for i in range(int(math.ceil(50.0 / once_ms))):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(max(replays, int(math.ceil(20.0 / once_ms)))):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gpu_delay(0.2)
+        e0.record()                   # a replay runs on the current stream
+        graphs[i % len(graphs)].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return sorted(ts)[len(ts) // 2] * 1000.0 / reps
 
 
 def measure_merged(B, kv_copies, fuse, reps=8, replays=5):
@@ -507,31 +525,17 @@ def measure_merged(B, kv_copies, fuse, reps=8, replays=5):
         for k in range(2):
             call(kv_copies[k % len(kv_copies)])
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for r in range(reps):
-            call(kv_copies[r % len(kv_copies)])
+    graphs = []
+    for i in range(max(1, len(kv_copies) // reps)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(reps):
+                call(kv_copies[(i * reps + r) % len(kv_copies)])
+        graphs.append(g)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    once_ms = max(e0.elapsed_time(e1), 1e-3)
-    for _ in range(int(math.ceil(50.0 / once_ms))):
-        g.replay()
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(max(replays, int(math.ceil(20.0 / once_ms)))):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        gpu_delay(0.2)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    del g
-    return sorted(ts)[len(ts) // 2] * 1000.0 / reps
+    us = graph_call_us(graphs, reps, replays)
+    del graphs
+    return us
 
 
 def fused_rows(Bs, copies):
@@ -555,7 +559,7 @@ def producer_leg(Bs, with_fused=True):
     import synth
     _, kv = synth.mla_decode(1)
     kv_dev = kv.to("cuda:0")
-    copies = [kv_dev] + [kv_dev.clone() for _ in range(7)]   # 8 x 151 MB
+    copies = [kv_dev] + [kv_dev.clone() for _ in range(KV_COPIES - 1)]
     rows = []
     for B in Bs:
         us, us_m = measure_producer(B, copies)
@@ -598,7 +602,7 @@ def producer_leg(Bs, with_fused=True):
           % (us, tflops, 100 * tflops / MFMA_BF16_PEAK_TFLOPS), file=sys.stderr, flush=True)
     del copies
     copies = [kv_dev.to(torch.float16)]
-    copies += [copies[0].clone() for _ in range(7)]
+    copies += [copies[0].clone() for _ in range(KV_COPIES - 1)]
     del kv_dev
     us, us_m = measure_producer(64, copies)
     fl = producer_flops(64, 128, kv.shape[0])
@@ -675,7 +679,7 @@ def cache_note(m):
     if m["reuse_distance_bytes"] is None:
         reuse = "each timed call reads an input set no other timed call uses"
     else:
-        reuse = "the timed calls cycle over %d input sets, so the same bytes come back only after %.2f GB of " \
+        reuse = "the timed calls cycle over %d input sets, so the same bytes come back only after %.1f GB of " \
                 "other inputs" % (m["sets"], m["reuse_distance_bytes"] / 1e9)
     return ("cold: %s; warm-up ran on a separate set and separate graphs, then 1 GiB of unrelated data was read "
             "before the timed region" % reuse)
@@ -798,8 +802,10 @@ def main():
         "producer": {"workload": "MLA split-KV decode, q [B,128,576] bf16, latent KV cache 131072 x 576 bf16 in "
                                  "4 contiguous shards, scale 1/sqrt(192), then the merge of its partials",
                      "bound": "mfma (B >= 2), hbm (B = 1)", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
-                     "timing": "HIP graphs of 8 calls (each of 8 cache copies once) and of 8 merges, replayed "
-                               "for ~50 ms of warm-up, then timed per replay; median replay / 8",
+                     "timing": "HIP graphs of 8 calls, %d graphs over %d cache copies replayed in turn (a copy "
+                               "is read again only after %d others), and a graph of 8 merges of the just-written "
+                               "partials; ~50 ms of warm-up, then timed per replay; median replay / 8"
+                               % (KV_COPIES // 8, KV_COPIES, KV_COPIES - 1),
                      "rows": producer, "cpu_baseline": producer_cpu,
                      "merged": {"what": "dcp_mla_decode_merged: the partials and their shard merge in one call; "
                                         "separate = decode + split reduction + shard merge launches (DCP_FUSE_NONE), "

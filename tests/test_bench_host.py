@@ -22,12 +22,13 @@ def test_help_lists_the_contract_options():
 
 
 def test_cold_set_plan_meets_its_stated_conditions():
-    """The timed calls of a cold measurement read each input set either once, or again only after >= 1 GiB of other
-    sets; the warm-up set is never read by a timed call; the graphs hold the calls the line reports."""
+    """The timed calls of a cold measurement read each input set once while the sets fit in DISTINCT_BYTES, else
+    again only after about DISTINCT_BYTES of other sets; the warm-up set is never read by a timed call; the graphs
+    hold the calls the line reports."""
     sys.path.insert(0, ROOT)
     import bench
     for per_set in (82_240 + 1024, 10_526_720 + 4096, 75_800_000, 300_000_000):
-        for steps in (20, 60, 120, 600, 1200):
+        for steps in (20, 60, 120, 600, 1200, 6000):
             calls, n, timed, warm = bench.plan_sets(per_set, steps, cold=True)
             assert calls == min(60, steps) and all(len(g) == calls for g in timed)
             order = [k for r in range(steps // calls) for k in timed[r % len(timed)]]
@@ -35,9 +36,10 @@ def test_cold_set_plan_meets_its_stated_conditions():
             last = {}
             for i, k in enumerate(order):
                 if k in last:
-                    assert (i - last[k]) * per_set >= bench.COLD_BYTES, (per_set, steps)
+                    assert (i - last[k]) * per_set >= bench.DISTINCT_BYTES - per_set * calls, (per_set, steps)
                 last[k] = i
-            if steps * per_set <= bench.COLD_BYTES:
+            assert n * per_set <= max(bench.DISTINCT_BYTES, per_set * calls)
+            if steps * per_set <= bench.DISTINCT_BYTES:
                 assert len(set(order)) == steps
     calls, n, timed, warm = bench.plan_sets(10_530_816, 20, cold=False)
     assert (calls, n, warm) == (20, 1, 0) and timed == [[0] * 20]
