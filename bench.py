@@ -5,19 +5,23 @@ A step is one layer-merge: one dcp_lse_combine call over all B tokens of one
 synthetic batch (every chunk included), i.e. the whole hot path -- layout
 adapter, chunk planner, LSE reduction, weighted accumulation, store.
 
-Timing.  Inputs are resident in HBM before the timed region starts.  Calls
-are captured into HIP graphs of min(60, steps) calls each (60: one per MLA
-layer of a decode step).  Every timed call reads an input set of its own (up
-to 32 GiB of sets; past that the sets are cycled, tens of gigabytes apart):
-measured, a set read again even 1.27 GB of other inputs later -- five times
-the 256 MB Infinity Cache -- still comes back about 9% faster, so no timed
-call re-reads another's bytes.  Warm-up calls run on a separate set in a
-separate graph; then 1 GiB of unrelated data is read, so every timed input
-comes from HBM (a cold-cache figure).  A bounded spin kernel queued before the start event keeps the GPU
-busy while the host submits the timed graph launches, so the region holds GPU
-work only.  The region is bracketed by a barrier and torch.cuda.synchronize()
-and measured with HIP events on the stream the graphs are launched on.  A
-hot-cache figure (same buffers every call) is reported beside it.
+Timing.  Inputs are resident in HBM before the timed region starts.  Every
+timed call reads an input set of its own (up to 32 GiB of sets; past that the
+sets are cycled, tens of gigabytes apart): measured, a set read again even
+1.27 GB of other inputs later -- five times the 256 MB Infinity Cache -- still
+comes back about 9% faster, so no timed call re-reads another's bytes.  After
+one untimed call on every set, warm-up calls run on a separate set; then 1 GiB
+of unrelated data is read, so every timed input comes from HBM (a cold-cache
+figure).  The timed calls are eager launches on one stream, back to back; a
+bounded spin kernel queued before the start event keeps the GPU busy while the
+host enqueues them (the line reports both times), so the region holds GPU work
+only.  The region is bracketed by a barrier and torch.cuda.synchronize() and
+measured with HIP events on that stream.  The same calls captured in HIP graphs
+of min(60, steps) calls (60: one per MLA layer of a decode step) are reported
+beside it: every graph replay adds ~7.5 us of the graph runtime's own start-up
+on the GPU, which a 20-call region cannot amortise, while a decode step's graph
+pays it once for thousands of kernels.  A hot-cache figure (same buffers every
+call) is reported too.
 
 Output: one JSON line (rank 0).  ``value`` is achieved HBM throughput in GB/s
 = algorithmic bytes per layer-merge / time per layer-merge, where algorithmic
@@ -136,6 +140,16 @@ class GpuCase:
         attn, lse, out, out_lse = self.sets[k]
         self.dcp.dcp_lse_combine(ws, attn, lse, self.layout, self.mode, out, out_lse, stream=stream)
 
+    def workspace(self, stream, cached=False):
+        """A workspace for this case bound to `stream`."""
+        import torch
+        dtype = self.dcp.DCP_DTYPE_FP16 if self.case.attn.dtype == torch.float16 else self.dcp.DCP_DTYPE_BF16
+        ws = self.dcp.dcp_workspace_create(self.capacity, self.case.h_local, self.case.cp, dtype=dtype,
+                                           stream=stream)
+        if cached:
+            self.dcp.dcp_workspace_set_load_policy(ws, self.dcp.DCP_LOAD_CACHED)
+        return ws
+
     def capture(self, set_lists):
         """One HIP graph per list of set indices, calling the sets in that order."""
         import torch
@@ -222,6 +236,37 @@ def time_graphs(graphs, replays, evict=False):
     return start.elapsed_time(end)
 
 
+SPIN_MS_PER_CALL = 0.03   # spin time queued per timed call: covers the host's enqueue of one eager call
+
+
+def time_eager(enqueue, n, evict=False):
+    """Run enqueue(i) for i in range(n) -- each one eager launch on the current stream -- as one timed region;
+    returns (elapsed ms, host enqueue ms, spin ms).  HIP events on that stream, bracketed by a barrier and a
+    synchronize on both sides.  A spin kernel of SPIN_MS_PER_CALL per call queued before the start event keeps
+    the GPU busy while the host enqueues the launches, so the region holds GPU work only as long as the host
+    enqueue took less than the spin (reported, so a reader can check it); with `evict`, 1 GiB of unrelated data is
+    read between the spin kernel and the start event."""
+    import torch
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    barrier()
+    torch.cuda.synchronize()
+    spin_ms = 1.0 + SPIN_MS_PER_CALL * n
+    gpu_delay(spin_ms)
+    if evict:
+        evict_caches()
+    start.record(stream)
+    t0 = time.perf_counter()
+    for i in range(n):
+        enqueue(i)
+    host_ms = (time.perf_counter() - t0) * 1000.0
+    end.record(stream)
+    torch.cuda.synchronize()
+    barrier()
+    return start.elapsed_time(end), host_ms, spin_ms
+
+
 def warm_up(graph, calls, warmup):
     """Replay a warm-up graph of `calls` calls until at least `warmup` calls ran; returns how many ran."""
     import torch
@@ -254,33 +299,59 @@ def plan_sets(per_set, steps, cold):
 
 
 def measure(case, steps, warmup, capacity=None, cold=True, cached=False):
-    """Time `steps` layer-merges in HIP graphs of `calls` calls each.
+    """Time `steps` layer-merges, each an eager launch (time_eager).
 
-    cold: every timed call reads an input set of its own (plan_sets); warm-up runs on a separate set and separate
-    graphs; then 1 GiB of unrelated data is read, so every timed input comes from HBM.  hot: every
-    call (warm-up and timed) uses one set.  ``cached``: the workspace's DCP_LOAD_CACHED policy.
-    Returns a dict: us per layer-merge, calls per graph, timed input sets, warm-up calls, footprint, first set."""
+    cold: every timed call reads an input set of its own (plan_sets); after one untimed call on every set, the
+    warm-up calls run on a separate set; then 1 GiB of unrelated data is read, so every timed input comes from
+    HBM.  hot: every call (warm-up and timed) uses one set.  ``cached``: the workspace's DCP_LOAD_CACHED policy.
+    Returns a dict: us per layer-merge, timed input sets, warm-up calls, footprint, first set, host enqueue and
+    spin ms."""
+    import torch
+    per_set = case.attn.numel() * 2 + case.lse.numel() * 4 + case.B * case.h_local * (1024 + 4)
+    calls, n_sets, timed, warm_set = plan_sets(per_set, steps, cold)
+    order = [k for r in range(steps // calls) for k in timed[r % len(timed)]]
+    g = GpuCase(case, max(n_sets, warm_set + 1), capacity or case.B)
+    stream = torch.cuda.current_stream()
+    ws = g.workspace(stream, cached)
+    for k in range(len(g.sets)):
+        g.call(ws, k, stream)
+    for _ in range(max(0, warmup)):
+        g.call(ws, warm_set, stream)
+    torch.cuda.synchronize()
+    ms, host_ms, spin_ms = time_eager(lambda i: g.call(ws, order[i], stream), steps, evict=cold)
+    first = g.sets[0]
+    ws.close()
+    return {"us": ms * 1000.0 / steps, "sets": n_sets, "warm_calls": max(0, warmup), "footprint": n_sets * per_set,
+            "first": first, "reuse_distance_bytes": (n_sets * per_set if steps > n_sets else None),
+            "host_ms": host_ms, "spin_ms": spin_ms}
+
+
+def measure_graphs(case, steps, warmup, capacity=None, cold=True):
+    """The same measurement with the calls captured in HIP graphs of min(60, steps) calls, replayed round-robin
+    (one replay per 60 calls): every replay adds the graph runtime's own start-up on the GPU, ~7.5 us on MI355X,
+    which a 20-call region cannot amortise.  Returns us per layer-merge and the calls per graph."""
     per_set = case.attn.numel() * 2 + case.lse.numel() * 4 + case.B * case.h_local * (1024 + 4)
     calls, n_sets, timed, warm_set = plan_sets(per_set, steps, cold)
     g = GpuCase(case, max(n_sets, warm_set + 1), capacity or case.B)
-    g.cached = cached
     w_calls = max(1, min(warmup, calls))
     graphs = g.capture(timed + [[warm_set] * w_calls])
-    warm_calls = warm_up(graphs[-1], w_calls, warmup)
+    warm_up(graphs[-1], w_calls, warmup)
     ms = time_graphs(graphs[:-1], steps // calls, evict=cold)
-    us = ms * 1000.0 / steps
-    first = g.sets[0]
     g.ws.close()
-    return {"us": us, "calls": calls, "sets": n_sets, "warm_calls": warm_calls, "footprint": n_sets * per_set,
-            "first": first, "reuse_distance_bytes": (n_sets * per_set if steps > n_sets else None)}
+    return {"us": ms * 1000.0 / steps, "calls": calls, "replays": steps // calls}
 
 
 def launch_floor(steps, warmup):
-    """us per launch of a one-element fill kernel (one workgroup) in the same harness -- graphs of GRAPH_CALLS
-    launches on one stream, warmed up, a spin kernel ahead of the start event: the fixed cost every layer-merge
-    pays before moving any bytes."""
+    """us per launch of a one-element fill kernel (one workgroup) in the same harness as the headline -- eager
+    launches on one stream behind a spin kernel -- and, for comparison, in graphs of GRAPH_CALLS launches: the
+    fixed cost every layer-merge pays before moving any bytes."""
     import torch
     buf = torch.zeros(1, device="cuda:0")
+    for _ in range(max(1, warmup)):
+        buf.fill_(1.0)
+    torch.cuda.synchronize()
+    ms, _, _ = time_eager(lambda i: buf.fill_(1.0), steps)
+    eager = ms * 1000.0 / steps
     calls = min(GRAPH_CALLS, steps)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -291,48 +362,40 @@ def launch_floor(steps, warmup):
         for _ in range(calls):
             buf.fill_(1.0)
     warm_up(g, calls, warmup)
-    return time_graphs([g], steps // calls) * 1000.0 / steps
+    graph = time_graphs([g], steps // calls) * 1000.0 / steps
+    return eager, graph
 
 
 def copy_ceiling(headline_bytes):
-    """Cold device-to-device copies (torch copy_) in the same harness: graphs of GRAPH_CALLS copies, replayed five
-    times after the eviction read.  Returns GB/s (bytes read + written) for 256 MiB copies (over buffers cycling
-    through >= 1 GiB; each copy streams more than the Infinity Cache holds), and us per copy that reads and writes
-    half of `headline_bytes` each (the same total bytes as one layer-merge; every timed copy has buffers of its
-    own, as the merge's timed calls do)."""
+    """Cold device-to-device copies (torch copy_) in the same harness as the headline: eager launches behind a
+    spin kernel, after the eviction read.  Returns GB/s (bytes read + written) for 256 MiB copies (over buffers
+    cycling through >= 1 GiB; each copy streams more than the Infinity Cache holds), and us per copy that reads and
+    writes half of `headline_bytes` each (the same total bytes as one layer-merge; every timed copy has buffers of
+    its own, as the merge's timed calls do)."""
     import torch
     res = {}
-    replays = 5
+    n_copies = 5 * GRAPH_CALLS
     for label, nbytes in (("256MiB", 256 << 20), ("headline", headline_bytes // 2)):
         n = max(1, nbytes // 2)
-        calls = GRAPH_CALLS
-        if replays * calls * 2 * n * 2 <= DISTINCT_BYTES:
-            sets = replays * calls
+        if n_copies * 2 * n * 2 <= DISTINCT_BYTES:
+            sets = n_copies
         else:
             sets = max(2, math.ceil((1 << 30) / (2 * n * 2)))
         src = [torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0) for _ in range(sets)]
         dst = [torch.empty_like(x) for x in src]
-        stream = torch.cuda.Stream()
-        with torch.cuda.stream(stream):
-            dst[0].copy_(src[0])
+        for k in range(min(sets, 4)):
+            dst[k].copy_(src[k])
         torch.cuda.synchronize()
-        graphs = []
-        for r in range(replays if sets == replays * calls else 1):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for i in range(calls):
-                    k = (r * calls + i) % sets
-                    dst[k].copy_(src[k])
-            graphs.append(g)
-        warm_up(graphs[0], calls, 2 * calls)
-        us = time_graphs(graphs, replays, evict=True) * 1000.0 / (replays * calls)
+        ms, _, _ = time_eager(lambda i: dst[i % sets].copy_(src[i % sets]), n_copies, evict=True)
+        us = ms * 1000.0 / n_copies
         res[label] = (us, 2.0 * n * 2 / (us * 1e-6) / 1e9)
-        del src, dst, graphs
+        del src, dst
         torch.cuda.empty_cache()
     return {"GBps_256MiB": round(res["256MiB"][1], 1),
             "us_at_headline_bytes": round(res["headline"][0], 3),
-            "kernel": "torch copy_ of bf16 buffers, cold, graphs of %d copies; at the headline's bytes every timed "
-                      "copy has buffers of its own; GB/s counts bytes read plus bytes written" % GRAPH_CALLS}
+            "kernel": "torch copy_ of bf16 buffers, cold, eager launches behind a spin kernel (as the headline); at "
+                      "the headline's bytes every timed copy has buffers of its own; GB/s counts bytes read plus "
+                      "bytes written"}
 
 
 def parity_check(case, out, out_lse):
@@ -681,8 +744,8 @@ def cache_note(m):
     else:
         reuse = "the timed calls cycle over %d input sets, so the same bytes come back only after %.1f GB of " \
                 "other inputs" % (m["sets"], m["reuse_distance_bytes"] / 1e9)
-    return ("cold: %s; warm-up ran on a separate set and separate graphs, then 1 GiB of unrelated data was read "
-            "before the timed region" % reuse)
+    return ("cold: %s; after one untimed call on every set, the warm-up ran on a separate set, then 1 GiB of "
+            "unrelated data was read before the timed region" % reuse)
 
 
 def main():
@@ -702,6 +765,8 @@ def main():
     alg = algorithmic_bytes(case)
     print("[bench] %s: %d algorithmic bytes per layer-merge" % (workload_name(case, args.workload), alg),
           file=sys.stderr, flush=True)
+    # the same calls in HIP graphs first, for comparison (the timed eager calls are then the last merges run)
+    head_graph = measure_graphs(case, args.steps, args.warmup, capacity=capacity, cold=True)
     head = measure(case, args.steps, args.warmup, capacity=capacity, cold=True)
     us = head["us"]
     ok = parity_check(case, head["first"][2], head["first"][3])
@@ -709,8 +774,10 @@ def main():
     us_hot_cached = None if args.no_hot else measure(case, args.steps, args.warmup, capacity=capacity, cold=False,
                                                      cached=True)["us"]
     gbs = alg / (us * 1e-6) / 1e9
-    print("[bench] cold %.3f us (%.1f GB/s), hot %s us, hot with DCP_LOAD_CACHED %s us, parity %s"
-          % (us, gbs, us_hot, us_hot_cached, ok), file=sys.stderr, flush=True)
+    print("[bench] cold %.3f us (%.1f GB/s; host enqueue %.2f ms behind a %.2f ms spin), in HIP graphs %.3f us, "
+          "hot %s us, hot with DCP_LOAD_CACHED %s us, parity %s"
+          % (us, gbs, head["host_ms"], head["spin_ms"], head_graph["us"], us_hot, us_hot_cached, ok),
+          file=sys.stderr, flush=True)
 
     sweep = []
     if not args.no_sweep:
@@ -758,9 +825,9 @@ def main():
     if args.calibrate:
         calibration_copy()
     traffic = counters_traffic()
-    floor_us = launch_floor(args.steps, args.warmup)
-    print("[bench] launch floor: a one-element fill kernel in the same graph harness takes %.3f us per launch"
-          % floor_us, file=sys.stderr, flush=True)
+    floor_us, floor_graph_us = launch_floor(args.steps, args.warmup)
+    print("[bench] launch floor: a one-element fill kernel takes %.3f us per launch in the same harness (%.3f us in "
+          "HIP graphs of %d)" % (floor_us, floor_graph_us, GRAPH_CALLS), file=sys.stderr, flush=True)
     copy = copy_ceiling(alg)
     print("[bench] copy ceiling: torch copy_ moves 256 MiB at %.1f GB/s (read + write); a copy of the headline's "
           "%d bytes takes %.3f us" % (copy["GBps_256MiB"], alg, copy["us_at_headline_bytes"]), file=sys.stderr,
@@ -781,17 +848,24 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_name(case, args.workload), "B": case.B, "H": case.H, "cp": case.cp,
                    "D": 512, "lse_layout": case.lse_layout, "lse_mode": case.lse_mode, "capacity": capacity,
-                   "graph_calls": head["calls"], "timed_graph_replays": args.steps // head["calls"],
+                   "launch": "each timed call an eager launch on one stream, behind a spin kernel that covers "
+                             "the host's enqueue (host %.2f ms, spin %.2f ms)" % (head["host_ms"], head["spin_ms"]),
+                   "host_enqueue_covered": head["host_ms"] < head["spin_ms"],
                    "input_sets": head["sets"], "footprint_MB": round(head["footprint"] / 1e6, 1),
                    "warmup_calls_run": head["warm_calls"],
                    "cache": cache_note(head)},
         "us_per_layer_merge": round(us, 3),
+        "us_per_layer_merge_hip_graphs": {"us": round(head_graph["us"], 3), "graph_calls": head_graph["calls"],
+                                          "replays": head_graph["replays"],
+                                          "note": "the same cold calls captured in HIP graphs; each replay adds "
+                                                  "the graph runtime's start-up on the GPU, which few calls per "
+                                                  "replay cannot amortise"},
         "us_per_layer_merge_hot": None if us_hot is None else round(us_hot, 3),
         "us_per_layer_merge_hot_cached_policy": None if us_hot_cached is None else round(us_hot_cached, 3),
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "launch_floor_us": {"us": round(floor_us, 3),
-                            "kernel": "one-element fill (one workgroup) in the same graphs of %d launches"
-                                      % GRAPH_CALLS},
+        "launch_floor_us": {"us": round(floor_us, 3), "us_hip_graphs": round(floor_graph_us, 3),
+                            "kernel": "one-element fill (one workgroup), eager launches behind a spin kernel as the "
+                                      "headline (and in graphs of %d launches)" % GRAPH_CALLS},
         "copy_ceiling": copy,
         "parity_vs_oracle": ok,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
