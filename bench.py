@@ -477,9 +477,9 @@ def measure_producer(B, kv_copies, reps=8, seq_lens=None, replays=5):
     instead: every token up to its own length, interleaved ownership, over the
     shared cache (kv_sb = 0) or, when the copies are [B, T, 576], over its own
     cache.  q, the cache and the outputs take the cache's dtype.  Both steps are
-    timed as a serving decode loop runs them, captured in HIP graphs: graphs of
-    `reps` producer calls (each over its own cache copies, replayed in turn) and
-    one of `reps` merges of its output, timed by graph_call_us.
+    timed by batch_call_us in batches of `reps` eager calls: the producer's
+    batches each over their own cache copies, in turn, and batches of `reps`
+    merges of its output.
     Returns (producer us, merge us) per call, medians over the replays."""
     import torch
     import context_lse_merge_amd as dcp
@@ -512,50 +512,53 @@ def measure_producer(B, kv_copies, reps=8, seq_lens=None, replays=5):
     def merge():
         dcp.dcp_lse_combine(ws, o, l, dcp.DCP_LSE_BH1, dcp.DCP_LSE_BASE_E, out, out_lse)
 
-    with torch.cuda.stream(stream):       # eager passes on the capture stream first
+    with torch.cuda.stream(stream):
         for k in range(2):
             produce(kv_copies[k % len(kv_copies)])
             merge()
-    torch.cuda.synchronize()
-    g_prod = []
-    for i in range(max(1, len(kv_copies) // reps)):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
+        torch.cuda.synchronize()
+        n_batches = max(1, len(kv_copies) // reps)
+
+        def produce_batch(i):
             for r in range(reps):
                 produce(kv_copies[(i * reps + r) % len(kv_copies)])
-        g_prod.append(g)
-    g_merge = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_merge, stream=stream):
-        for r in range(reps):
-            merge()
-    torch.cuda.synchronize()
-    prod, mrg = graph_call_us(g_prod, reps, replays), graph_call_us([g_merge], reps, replays)
-    del g_prod, g_merge
+
+        def merge_batch(i):
+            for _ in range(reps):
+                merge()
+
+        prod = batch_call_us(produce_batch, n_batches, reps, replays)
+        mrg = batch_call_us(merge_batch, 1, reps, replays)
     ws.close()
     return prod, mrg
 
 
-def graph_call_us(graphs, reps, replays):
-    """us per call of graphs of `reps` calls each, replayed in turn: warmed up for about 50 ms of this work (the
-    first ~20 ms of sustained load run measurably slower, seen in eager and graph runs alike), then at least
-    `replays` replays and at least 20 ms, HIP events around every replay on the stream it is launched on, a spin
-    kernel ahead of each start event covering the host's submission; the median replay / reps."""
+PRODUCER_SPIN_MS_PER_CALL = 0.1   # covers the host's enqueue of one producer call (its launches and checks)
+
+
+def batch_call_us(run_batch, n_batches, reps, replays):
+    """us per call of batches of `reps` eager calls on the current stream (run_batch(i) enqueues batch
+    i % n_batches): warmed up for about 50 ms of this work (the first ~20 ms of sustained load run measurably
+    slower), then at least `replays` batches and at least 20 ms, HIP events around every batch, a spin kernel
+    ahead of each start event covering the host's enqueue; the median batch / reps."""
     import torch
+    spin = 0.2 + PRODUCER_SPIN_MS_PER_CALL * reps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gpu_delay(spin)
     e0.record()
-    graphs[0].replay()
+    run_batch(0)
     e1.record()
     torch.cuda.synchronize()
     once_ms = max(e0.elapsed_time(e1), 1e-3)
     for i in range(int(math.ceil(50.0 / once_ms))):
-        graphs[i % len(graphs)].replay()
+        run_batch(i % n_batches)
     torch.cuda.synchronize()
     ts = []
     for i in range(max(replays, int(math.ceil(20.0 / once_ms)))):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        gpu_delay(0.2)
-        e0.record()                   # a replay runs on the current stream
-        graphs[i % len(graphs)].replay()
+        gpu_delay(spin)
+        e0.record()
+        run_batch(i % n_batches)
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
@@ -564,8 +567,8 @@ def graph_call_us(graphs, reps, replays):
 
 def measure_merged(B, kv_copies, fuse, reps=8, replays=5):
     """dcp_mla_decode_merged (the producer's partials and their shard merge in one call) on the full-size MLA
-    decode workload, timed as measure_producer times the producer: a HIP graph of `reps` calls over the rotated
-    cache copies, warmed up for ~50 ms, then the median replay / reps."""
+    decode workload, timed as measure_producer times the producer: batches of `reps` eager calls over the rotated
+    cache copies (batch_call_us)."""
     import torch
     import context_lse_merge_amd as dcp
     import synth
@@ -587,17 +590,13 @@ def measure_merged(B, kv_copies, fuse, reps=8, replays=5):
     with torch.cuda.stream(stream):
         for k in range(2):
             call(kv_copies[k % len(kv_copies)])
-    torch.cuda.synchronize()
-    graphs = []
-    for i in range(max(1, len(kv_copies) // reps)):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
+        torch.cuda.synchronize()
+
+        def batch(i):
             for r in range(reps):
                 call(kv_copies[(i * reps + r) % len(kv_copies)])
-        graphs.append(g)
-    torch.cuda.synchronize()
-    us = graph_call_us(graphs, reps, replays)
-    del graphs
+
+        us = batch_call_us(batch, max(1, len(kv_copies) // reps), reps, replays)
     return us
 
 
@@ -876,9 +875,9 @@ def main():
         "producer": {"workload": "MLA split-KV decode, q [B,128,576] bf16, latent KV cache 131072 x 576 bf16 in "
                                  "4 contiguous shards, scale 1/sqrt(192), then the merge of its partials",
                      "bound": "mfma (B >= 2), hbm (B = 1)", "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
-                     "timing": "HIP graphs of 8 calls, %d graphs over %d cache copies replayed in turn (a copy "
-                               "is read again only after %d others), and a graph of 8 merges of the just-written "
-                               "partials; ~50 ms of warm-up, then timed per replay; median replay / 8"
+                     "timing": "batches of 8 eager calls behind a spin kernel, %d batches over %d cache copies "
+                               "in turn (a copy is read again only after %d others), and batches of 8 merges of "
+                               "the just-written partials; ~50 ms of warm-up, then timed per batch; median batch / 8"
                                % (KV_COPIES // 8, KV_COPIES, KV_COPIES - 1),
                      "rows": producer, "cpu_baseline": producer_cpu,
                      "merged": {"what": "dcp_mla_decode_merged: the partials and their shard merge in one call; "
