@@ -23,10 +23,10 @@
 //    in consecutive slots (fp16, each row scaled by a power of two whose
 //    inverse is stored beside its LSE), and the reduction kernel below
 //    merges them.
-// The reduction is the merge's own row arithmetic (merge_row.h: sequential
-// maximum and sum in ascending split order, normalised weights times the
-// rows' scale factors, fp32 FMAs in ascending split order), so a pair split
-// at the same boundaries gives the same bits on either path.  Which
+// The reduction is the merge's own row arithmetic (merge_row.h: the row
+// maximum, the sum in its fixed order, normalised weights times the rows'
+// scale factors, fp32 FMAs in ascending split order), so a pair split at the
+// same boundaries gives the same bits on either path.  Which
 // workgroup runs which split, and which slots a pair gets, depend on the
 // order of LDS atomics; the arithmetic of a split does not, so the results
 // are deterministic.
