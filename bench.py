@@ -601,18 +601,19 @@ def measure_merged(B, kv_copies, fuse, reps=8, replays=5):
 
 
 def fused_rows(Bs, copies):
-    """N1: the producer with the split reduction and the shard merge in its epilogue (one launch) against the same
-    work as separate launches, at each B."""
+    """N1: the producer with the split reduction and the shard merge in its epilogue (one launch), and with the two
+    reductions in one launch after the decode, against the same work as separate launches, at each B."""
     import context_lse_merge_amd as dcp
     rows = []
     for B in Bs:
         r = {"B": B}
         for name, fuse in (("separate_us", dcp.DCP_FUSE_NONE), ("fused_us", dcp.DCP_FUSE_EPILOGUE),
-                           ("auto_us", dcp.DCP_FUSE_AUTO)):
+                           ("reductions_us", dcp.DCP_FUSE_REDUCTIONS), ("auto_us", dcp.DCP_FUSE_AUTO)):
             r[name] = round(measure_merged(B, copies, fuse), 1)
         rows.append(r)
-        print("[bench] producer + shard merge B=%d: separate launches %.1f us, fused epilogue %.1f us, auto %.1f us"
-              % (B, r["separate_us"], r["fused_us"], r["auto_us"]), file=sys.stderr, flush=True)
+        print("[bench] producer + shard merge B=%d: separate launches %.1f us, fused epilogue %.1f us, "
+              "combined reductions %.1f us, auto %.1f us"
+              % (B, r["separate_us"], r["fused_us"], r["reductions_us"], r["auto_us"]), file=sys.stderr, flush=True)
     return rows
 
 
@@ -886,7 +887,9 @@ def main():
                      "merged": {"what": "dcp_mla_decode_merged: the partials and their shard merge in one call; "
                                         "separate = decode + split reduction + shard merge launches (DCP_FUSE_NONE), "
                                         "fused = one launch whose last-arriving workgroups reduce and merge "
-                                        "(DCP_FUSE_EPILOGUE), auto = DCP_FUSE_AUTO",
+                                        "(DCP_FUSE_EPILOGUE), reductions = decode + one launch that reduces the "
+                                        "splits and merges each head's shards in LDS (DCP_FUSE_REDUCTIONS), "
+                                        "auto = DCP_FUSE_AUTO",
                                 "rows": fused}},
     }
     print(json.dumps(line), flush=True)

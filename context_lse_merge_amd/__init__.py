@@ -52,6 +52,7 @@ DCP_NOALLOC_SCRATCH_BYTES = _C["DCP_NOALLOC_SCRATCH_BYTES"]
 DCP_FUSE_NONE = _C["DCP_FUSE_NONE"]
 DCP_FUSE_EPILOGUE = _C["DCP_FUSE_EPILOGUE"]
 DCP_FUSE_AUTO = _C["DCP_FUSE_AUTO"]
+DCP_FUSE_REDUCTIONS = _C["DCP_FUSE_REDUCTIONS"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -337,7 +338,7 @@ def dcp_mla_decode_merged_scratch_size(B: int, hq: int, kv_tokens: int, cp: int)
 def dcp_mla_decode_merged(q, kv, cp: int, softmax_scale: float, lse_mode: int, o_part, lse_part, out, out_lse=None,
                           fuse: int = DCP_FUSE_AUTO, scratch=None, stream=None):
     """The producer's per-shard partials and their LSE merge in one call.  ``out`` [B, hq, 512] in the
-    element type of q, ``out_lse`` [B, hq] fp32 or None; ``fuse`` DCP_FUSE_NONE / _EPILOGUE / _AUTO.
+    element type of q, ``out_lse`` [B, hq] fp32 or None; ``fuse`` DCP_FUSE_NONE / _EPILOGUE / _REDUCTIONS / _AUTO.
     ``scratch``: a GPU tensor of dcp_mla_decode_merged_scratch_size() bytes that was zero-filled before its
     first use (every call leaves its counters at zero); None allocates a zeroed one for this call."""
     import torch

@@ -476,8 +476,9 @@ int plan_mla_merged(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh
                     float* out_lse, int64_t out_lse_sb, int fuse, void* scratch, size_t scratch_bytes,
                     MlaPlan* plan) {
     const char* fn = "dcp_mla_decode_merged";
-    if (fuse != DCP_FUSE_NONE && fuse != DCP_FUSE_EPILOGUE && fuse != DCP_FUSE_AUTO)
-        return fail(DCP_ERR_INVALID_ARG, "%s: fuse %d is not DCP_FUSE_NONE, DCP_FUSE_EPILOGUE or DCP_FUSE_AUTO", fn,
+    if (fuse != DCP_FUSE_NONE && fuse != DCP_FUSE_EPILOGUE && fuse != DCP_FUSE_AUTO && fuse != DCP_FUSE_REDUCTIONS)
+        return fail(DCP_ERR_INVALID_ARG,
+                    "%s: fuse %d is not DCP_FUSE_NONE, DCP_FUSE_EPILOGUE, DCP_FUSE_REDUCTIONS or DCP_FUSE_AUTO", fn,
                     fuse);
     if (B < 0 || hq < 1 || T < 0 || cp < 1 || cp > DCP_MAX_CP || B * static_cast<int64_t>(hq) > (int64_t{1} << 30))
         return fail(DCP_ERR_INVALID_ARG, "%s: need B >= 0, hq >= 1, kv_tokens >= 0, 1 <= cp <= %d and B * hq <= 2^30",
@@ -495,6 +496,7 @@ int plan_mla_merged(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh
                             o_sh, lse, lse_sb, parts, scratch ? scratch_bytes - cnt : 0, plan, fn);
     if (rc != DCP_OK) return rc;
     plan->merge_shards = false;
+    plan->reduce_merge = false;
     if (B == 0) return ok();
     if (!out) return fail(DCP_ERR_INVALID_ARG, "%s: out must be non-null when B > 0", fn);
     if (out_sb < 0 || out_sh < 0 || out_lse_sb < 0) return fail(DCP_ERR_LAYOUT, "%s: strides must be non-negative", fn);
@@ -526,9 +528,10 @@ int plan_mla_merged(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh
     }
 
     MlaArgs& a = plan->args;
-    // DCP_FUSE_AUTO takes the separate launches: measured faster at every
-    // shape (the agent-scope publication of each workgroup's part costs more
-    // than the launches the epilogue saves).
+    // DCP_FUSE_AUTO never takes the fused epilogue (measured slower at every
+    // shape: the agent-scope publication of each workgroup's part costs more
+    // than the launches it saves); with many key splits and cp <= 16 it takes
+    // the combined reduction launch, else the separate launches.
     a.fused = fuse == DCP_FUSE_EPILOGUE ? 1 : 0;
     a.split_cnt = static_cast<int32_t*>(scratch);
     a.rb_cnt = a.split_cnt + static_cast<int64_t>(a.row_blocks) * cp;
@@ -567,6 +570,12 @@ int plan_mla_merged(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh
             return fail(DCP_ERR_LAYOUT, "%s: o_part / lse_part strides must be below 2^31 elements", fn);
         plan->merge_shards = true;
         plan->shard_merge = m;
+        // The combined launch needs the split reduction (several splits)
+        // and at most 16 shards (one block holds every shard of a head).
+        // AUTO takes it from 16 splits per shard on: measured (128 heads,
+        // 4 shards) 1% faster at 64 and 32 splits, even at 8, 0.2% slower at 2.
+        const bool can = a.nsplit > 1 && cp <= 16;
+        plan->reduce_merge = can && (fuse == DCP_FUSE_REDUCTIONS || (fuse == DCP_FUSE_AUTO && a.nsplit >= 16));
     }
     return ok();
 }

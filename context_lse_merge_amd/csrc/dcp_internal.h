@@ -297,11 +297,17 @@ struct MlaPlan {
     // o / lse into out / out_lse (all B tokens; launched in token chunks).
     bool merge_shards;
     MergeArgs shard_merge;
+    // DCP_FUSE_REDUCTIONS (nsplit > 1, cp <= 16): the split reduction and the
+    // shard merge in one launch (reduce_merge_launch) instead of two.
+    bool reduce_merge;
 };
 
 // Launch a merge over all B tokens of `m` in chunks of at most
 // kMaxLaunchTokens tokens and 2^30 rows; returns the first HIP error.
 int merge_launch_all(const MergeArgs& m, int64_t B, void* stream);
+// The split reduction `r` and the shard merge `m` of dcp_mla_decode_merged in
+// one launch per token chunk (merge.hip); m.cp <= 16.
+int reduce_merge_launch(const MergeArgs& r, const MergeArgs& m, int64_t B, int hq, void* stream);
 
 // Scratch of dcp_mla_decode_merged: the arrival counters (row_blocks * (cp + 1)
 // int32, rounded to 256 bytes), then the split partials as for

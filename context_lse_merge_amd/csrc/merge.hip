@@ -261,6 +261,62 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_any(const void* attn, con
     store_row<Out>(t, r, lane, acc, mrow::merged_lse(M, S, t.from_log2));
 }
 
+// The MLA decode's split reduction and its shard merge in one launch
+// (dcp_mla_decode_merged with DCP_FUSE_REDUCTIONS): wavefront (hi, s) of a
+// block reduces the key splits of shard s of head h = kRmWaves / cp * x + hi
+// (merge_row_any over the scaled fp16 partials, as merge_kernel_any and
+// merge_kernel<n> do), stores that row of o_part / lse_part, and leaves it,
+// rounded to the output type as stored, with its LSE in LDS; after the
+// barrier wavefront (hi, 0) merges the head's cp rows from LDS into out /
+// out_lse with merge_kernel<CP>'s arithmetic (sequential maximum and sum,
+// normalised weights, FMAs in ascending shard order).  Every value is the one
+// the separate launches compute and read back, so the bits are theirs; what
+// is saved is the shard merge's launch and its re-read of o_part.  cp <= 16
+// (the host checks): a block holds hb heads, hb * cp <= kRmWaves wavefronts.
+constexpr int kRmWaves = 16;
+
+template <typename Out>
+__global__ __launch_bounds__(64 * kRmWaves) void reduce_merge_kernel(MergeArgs r, MergeArgs m, int32_t hq,
+                                                                      int32_t hb) {
+    typedef Payload16<F16, false, true> In;   // the split partials
+    typedef Payload16<Out, false> Shard;      // a shard's row as stored in o_part
+    __shared__ u32x4 rows[kRmWaves][64];
+    __shared__ float lses[kRmWaves];
+    const int cp = m.cp;
+    const int lane = threadIdx.x & 63;
+    const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hi = v / cp, s = v - hi * cp;
+    const int b = blockIdx.y;
+    const bool active = hi < hb;
+    const int h0 = blockIdx.x * hb + hi;
+    const int h = h0 < hq ? h0 : hq - 1;  // spare heads of the last block repeat the last one: same bits, same place
+    if (active) {
+        const int64_t j = static_cast<int64_t>(s) * hq + h;  // the row of o_part / lse_part within the token
+        float acc[8], M, S;
+        mrow::merge_row_any<8, In>(r.attn, b * r.a_sb + j * r.a_sj + lane * 8, r.a_ss, r.lse + b * r.l_sb + j * r.l_sj,
+                                   r.l_ss, r.sc_off, r.cp, r.to_log2, acc, M, S);
+        const u32x4 packed = mrow::pack8<Out>(acc);
+        const float L = mrow::merged_lse(M, S, r.from_log2);
+        __builtin_nontemporal_store(packed, reinterpret_cast<u32x4*>(r.out + b * r.o_sb + j * r.o_sj + lane * 8));
+        if (lane == 0) r.out_lse[b * r.ol_sb + j] = L;
+        rows[v][lane] = packed;
+        if (lane == 0) lses[v] = L;
+    }
+    __syncthreads();
+    if (!active || s != 0) return;
+    const int v0 = hi * cp;
+    float M = lses[v0];
+    for (int t = 1; t < cp; ++t) M = fmaxf(M, lses[v0 + t]);
+    float S = 0.0f;
+    for (int t = 0; t < cp; ++t) S += mrow::shard_weight(lses[v0 + t], M, m.to_log2);
+    const float inv = mrow::inv_sum(S);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < cp; ++t)
+        mrow::fma8<Shard>(acc, mrow::shard_weight(lses[v0 + t], M, m.to_log2) * inv, rows[v0 + t][lane]);
+    __builtin_nontemporal_store(mrow::pack8<Out>(acc), reinterpret_cast<u32x4*>(m.out + b * m.o_sb + h * m.o_sj + lane * 8));
+    if (m.out_lse && lane == 0) m.out_lse[b * m.ol_sb + h] = mrow::merged_lse(M, S, m.from_log2);
+}
+
 typedef void (*MergeKernel)(const void*, const float*, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
                             MergeTail);
 
@@ -353,6 +409,26 @@ int merge_launch_all(const MergeArgs& m, int64_t B, void* stream) {
     for (int64_t t0 = 0; t0 < B; t0 += chunk) {
         const int64_t n = B - t0 < chunk ? B - t0 : chunk;
         const hipError_t e = launch(merge_args_at(m, t0, n), static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return static_cast<int>(e);
+    }
+    return 0;
+}
+
+int reduce_merge_launch(const MergeArgs& r, const MergeArgs& m, int64_t B, int hq, void* stream) {
+    // One head (cp wavefronts) per block: measured against two and four heads
+    // per block (producer B = 1, 64 splits: 64.0 against 66.9 and 74.0 us per
+    // call) -- more blocks in flight beat the longer runs of adjacent rows.
+    const int hb = 1;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int64_t t0 = 0; t0 < B; t0 += kMaxLaunchTokens) {
+        const int64_t n = B - t0 < kMaxLaunchTokens ? B - t0 : kMaxLaunchTokens;
+        const MergeArgs rc = merge_args_at(r, t0, n), mc = merge_args_at(m, t0, n);
+        const dim3 grid((hq + hb - 1) / hb, static_cast<unsigned>(n));
+        if (m.dtype == DCP_DTYPE_FP16)
+            reduce_merge_kernel<F16><<<grid, dim3(64 * hb * m.cp), 0, st>>>(rc, mc, hq, hb);
+        else
+            reduce_merge_kernel<Bf16><<<grid, dim3(64 * hb * m.cp), 0, st>>>(rc, mc, hq, hb);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return static_cast<int>(e);
     }
     return 0;

@@ -792,10 +792,15 @@ int run_mla(const MlaPlan& plan, void* hip_stream, const char* fn) {
     if (e == hipSuccess && plan.varlen) {
         if (plan.args.slots > 0) e = static_cast<hipError_t>(varlen_reduce_launch(plan.args, stream));
     } else if (e == hipSuccess && plan.args.nsplit > 1 && !plan.args.fused) {
-        // The splits of every (token, shard, head) are merged like DCP shards.
-        e = static_cast<hipError_t>(merge_launch_all(plan.reduce, plan.B, stream));
+        // The splits of every (token, shard, head) are merged like DCP shards;
+        // with reduce_merge the same launch also merges each head's shards.
+        if (plan.reduce_merge)
+            e = static_cast<hipError_t>(
+                reduce_merge_launch(plan.reduce, plan.shard_merge, plan.B, plan.args.hq, stream));
+        else
+            e = static_cast<hipError_t>(merge_launch_all(plan.reduce, plan.B, stream));
     }
-    if (e == hipSuccess && plan.merge_shards)
+    if (e == hipSuccess && plan.merge_shards && !plan.reduce_merge)
         e = static_cast<hipError_t>(merge_launch_all(plan.shard_merge, plan.B, stream));
     if (e != hipSuccess) return fail(DCP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();

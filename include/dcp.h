@@ -278,9 +278,10 @@ int dcp_mla_partial_decode_noalloc(const void* q, int64_t B, int hq, int64_t q_s
                                    int64_t lse_sb, void* hip_stream);
 
 /* How dcp_mla_decode_merged reduces the key splits and merges the shards. */
-#define DCP_FUSE_NONE 0     /* separate launches: decode, split reduction, shard merge             */
-#define DCP_FUSE_EPILOGUE 1 /* one launch: the decode kernel's last arrivals reduce and merge      */
-#define DCP_FUSE_AUTO 2     /* whichever measured faster on MI355X: NONE at every shape measured   */
+#define DCP_FUSE_NONE 0       /* separate launches: decode, split reduction, shard merge            */
+#define DCP_FUSE_EPILOGUE 1   /* one launch: the decode kernel's last arrivals reduce and merge     */
+#define DCP_FUSE_AUTO 2       /* the fastest measured on MI355X: REDUCTIONS at >= 16 splits, else NONE */
+#define DCP_FUSE_REDUCTIONS 3 /* decode, then one launch that reduces the splits and merges the shards */
 
 /*
  * MLA decode over cp shards followed by the LSE merge of the shards: the
@@ -299,10 +300,17 @@ int dcp_mla_partial_decode_noalloc(const void* q, int64_t B, int hq, int64_t q_s
  *  - DCP_FUSE_NONE: the decode kernel, the split reduction and the shard
  *    merge as separate launches (what dcp_mla_partial_decode followed by
  *    dcp_lse_combine does).
- *  - DCP_FUSE_AUTO: the faster of the two as measured on MI355X, which is
- *    NONE at every shape measured (128 heads, 4 shards, 131072 keys, B = 1,
- *    8, 32, 64): publishing a workgroup's part at agent scope writes back
- *    the L2 of its XCD, and that costs more than the launches it saves.
+ *  - DCP_FUSE_REDUCTIONS: the decode kernel, then one launch in which each
+ *    head's shards are merged, in LDS, by the workgroup that has just
+ *    reduced their key splits: no separate shard-merge launch, and o_part is
+ *    not read back.  It applies when the shards' keys are split (small B)
+ *    and cp <= 16; otherwise it runs as DCP_FUSE_NONE.
+ *  - DCP_FUSE_AUTO: the fastest as measured on MI355X (128 heads, 4 shards,
+ *    131072 keys, B = 1, 2, 8, 32, 64): REDUCTIONS where the shards' keys
+ *    are split 16 ways or more (about 1% faster at B = 1 and 2), else NONE.
+ *    The fused epilogue is slower at every shape measured: publishing a
+ *    workgroup's part at agent scope writes back the L2 of its XCD, and that
+ *    costs more than the launches it saves.
  * Every mode gives the same bits: o_part / lse_part equal
  * dcp_mla_partial_decode's, and out / out_lse equal dcp_lse_combine over them
  * (DCP_LSE_BH1, the same lse_mode).

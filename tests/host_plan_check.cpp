@@ -108,8 +108,10 @@ static void fixed_split_checks() {
 
 // dcp_mla_decode_merged: the counters first, the split partials after them;
 // EPILOGUE marks the plan fused (no separate split reduction or shard
-// merge), NONE and AUTO plan the shard merge over (o_part, lse_part) in the
-// FlashMLA layout; errors before anything could run.
+// merge), NONE, REDUCTIONS and AUTO plan the shard merge over (o_part,
+// lse_part) in the FlashMLA layout, REDUCTIONS and AUTO as part of the
+// combined reduction launch where the keys are split and cp <= 16; errors
+// before anything could run.
 static void merged_plan_checks() {
     const int64_t B = 3, T = 131072;
     const int hq = 128, cp = 4;
@@ -137,9 +139,10 @@ static void merged_plan_checks() {
     CHECK(plan.args.rb_cnt == plan.args.split_cnt + 3 * cp);
     CHECK(reinterpret_cast<uintptr_t>(plan.args.part_o) == scr + cnt);
     CHECK(plan.args.to_log2 == 1.0f && plan.args.from_log2 == 1.0f);
-    for (int fuse : {DCP_FUSE_NONE, DCP_FUSE_AUTO}) {
+    for (int fuse : {DCP_FUSE_NONE, DCP_FUSE_REDUCTIONS, DCP_FUSE_AUTO}) {
         CHECK(plan_it(fuse, need, out, &plan) == DCP_OK);
         CHECK(plan.args.fused == 0 && plan.merge_shards);
+        CHECK(plan.reduce_merge == (fuse == DCP_FUSE_REDUCTIONS || (fuse == DCP_FUSE_AUTO && nsplit >= 16)));
         const dcp::MergeArgs& m = plan.shard_merge;
         CHECK(m.attn == fake(o) && m.a_sb == cp * hq * 512 && m.a_sj == 512 && m.a_ss == hq * 512);
         CHECK(m.l_sb == cp * hq && m.l_sj == 1 && m.l_ss == hq && m.h_local == hq && m.cp == cp);
@@ -147,7 +150,25 @@ static void merged_plan_checks() {
     }
     CHECK(plan_it(DCP_FUSE_EPILOGUE, need - 1, out, &plan) == DCP_ERR_WORKSPACE);
     CHECK(std::strstr(dcp_last_error(), "dcp_mla_decode_merged_scratch_size") != nullptr);
-    CHECK(plan_it(3, need, out, &plan) == DCP_ERR_INVALID_ARG);
+    CHECK(plan_it(4, need, out, &plan) == DCP_ERR_INVALID_ARG);
+    // The combined launch is not taken with one split per shard, nor above 16 shards.
+    for (const int64_t Bx : {int64_t{64}, int64_t{3}}) {
+        const int cpx = Bx == 3 ? 32 : 4;
+        int32_t nx;
+        int64_t lx;
+        size_t px;
+        dcp::mla_split(Bx, hq, T, cpx, &nx, &lx, &px);
+        CHECK((Bx == 64) == (nx == 1));
+        size_t needx = 0;
+        CHECK(dcp_mla_decode_merged_scratch_size(Bx, hq, T, cpx, &needx) == DCP_OK);
+        for (int fuse : {DCP_FUSE_REDUCTIONS, DCP_FUSE_AUTO}) {
+            CHECK(dcp::plan_mla_merged(fake(q), Bx, hq, hq * 576, 576, fake(kv), T, 576, DCP_DTYPE_BF16, cpx, 0.07f,
+                                       DCP_LSE_BASE_2, fake(o), cpx * hq * 512, 512, reinterpret_cast<float*>(l),
+                                       cpx * hq, fake(out), hq * 512, 512, reinterpret_cast<float*>(ol), hq, fuse,
+                                       fake(scr), needx, &plan) == DCP_OK);
+            CHECK(plan.merge_shards && !plan.reduce_merge);
+        }
+    }
     CHECK(plan_it(DCP_FUSE_NONE, need, o + 1024, &plan) == DCP_ERR_INVALID_ARG);    // out inside o_part
     CHECK(plan_it(DCP_FUSE_NONE, need, scr + 4096, &plan) == DCP_ERR_INVALID_ARG);  // out inside the scratch
     CHECK(plan_it(DCP_FUSE_NONE, need, out + 8, &plan) == DCP_ERR_ALIGN);

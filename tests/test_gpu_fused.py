@@ -1,6 +1,7 @@
 """dcp_mla_decode_merged: the producer with the split reduction and the shard
 merge fused into its epilogue (DCP_FUSE_EPILOGUE), or run as separate launches
-(DCP_FUSE_NONE), or chosen by shape (DCP_FUSE_AUTO).
+(DCP_FUSE_NONE), or with the two reductions in one launch after the decode
+(DCP_FUSE_REDUCTIONS), or chosen by shape (DCP_FUSE_AUTO).
 
 Every mode must give the same bits as the unfused pipeline --
 dcp_mla_partial_decode followed by dcp_lse_combine over its partials (FlashMLA
@@ -26,7 +27,8 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 THREADS = len(os.sched_getaffinity(0))
 OMODE = {dcp.DCP_LSE_BASE_E: oracle.BASE_E, dcp.DCP_LSE_BASE_2: oracle.BASE_2}
-MODES = {"none": dcp.DCP_FUSE_NONE, "epilogue": dcp.DCP_FUSE_EPILOGUE, "auto": dcp.DCP_FUSE_AUTO}
+MODES = {"none": dcp.DCP_FUSE_NONE, "epilogue": dcp.DCP_FUSE_EPILOGUE, "reductions": dcp.DCP_FUSE_REDUCTIONS,
+         "auto": dcp.DCP_FUSE_AUTO}
 
 
 @pytest.fixture(autouse=True)
@@ -113,7 +115,8 @@ def test_repeated_calls_and_graph_replays_on_one_scratch():
     kvd = kv.to(DEV)
     qd = torch.empty_like(q0, device=DEV)
     scratch = torch.zeros(dcp.dcp_mla_decode_merged_scratch_size(B, hq, T, cp), dtype=torch.uint8, device=DEV)
-    for k, fuse in enumerate([dcp.DCP_FUSE_EPILOGUE, dcp.DCP_FUSE_EPILOGUE, dcp.DCP_FUSE_NONE, dcp.DCP_FUSE_EPILOGUE]):
+    for k, fuse in enumerate([dcp.DCP_FUSE_EPILOGUE, dcp.DCP_FUSE_REDUCTIONS, dcp.DCP_FUSE_NONE,
+                              dcp.DCP_FUSE_EPILOGUE, dcp.DCP_FUSE_REDUCTIONS]):
         qd.copy_(synth.normal_bf16((B, hq, 576), synth.gen(9300 + k)).to(DEV))
         announce("merged producer repeated call %d fuse=%d" % (k, fuse))
         assert_all_equal(merged(qd, kvd, cp, dcp.DCP_LSE_BASE_E, fuse, scratch=scratch),
@@ -124,30 +127,53 @@ def test_repeated_calls_and_graph_replays_on_one_scratch():
     out = torch.empty((B, hq, 512), dtype=torch.bfloat16, device=DEV)
     out_lse = torch.empty((B, hq), dtype=torch.float32, device=DEV)
 
-    def call():
-        dcp.dcp_mla_decode_merged(qd, kvd, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, out, out_lse,
-                                  fuse=dcp.DCP_FUSE_EPILOGUE, scratch=scratch, stream=s)
+    for fuse in (dcp.DCP_FUSE_EPILOGUE, dcp.DCP_FUSE_REDUCTIONS):
+        def call():
+            dcp.dcp_mla_decode_merged(qd, kvd, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o, l, out, out_lse,
+                                      fuse=fuse, scratch=scratch, stream=s)
 
-    with torch.cuda.stream(s):
-        call()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    announce("merged producer graph capture")
-    with torch.cuda.graph(g, stream=s):
-        call()
-    torch.cuda.synchronize()
-    for k in range(3):
-        qd.copy_(synth.normal_bf16((B, hq, 576), synth.gen(9400 + k)).to(DEV))
+        with torch.cuda.stream(s):
+            call()
         torch.cuda.synchronize()
-        announce("merged producer graph replay %d" % k)
-        g.replay()
+        g = torch.cuda.CUDAGraph()
+        announce("merged producer graph capture, fuse=%d" % fuse)
+        with torch.cuda.graph(g, stream=s):
+            call()
         torch.cuda.synchronize()
-        assert_all_equal((o.clone(), l.clone(), out.clone(), out_lse.clone()),
-                         unfused(qd, kvd, cp, dcp.DCP_LSE_BASE_E), "replay %d" % k)
-        assert_all_equal(merged(qd, kvd, cp, dcp.DCP_LSE_BASE_E, dcp.DCP_FUSE_EPILOGUE, scratch=scratch),
-                         unfused(qd, kvd, cp, dcp.DCP_LSE_BASE_E), "eager after replay %d" % k)
+        for k in range(3):
+            qd.copy_(synth.normal_bf16((B, hq, 576), synth.gen(9400 + k)).to(DEV))
+            torch.cuda.synchronize()
+            announce("merged producer graph replay %d" % k)
+            g.replay()
+            torch.cuda.synchronize()
+            assert_all_equal((o.clone(), l.clone(), out.clone(), out_lse.clone()),
+                             unfused(qd, kvd, cp, dcp.DCP_LSE_BASE_E), "replay %d" % k)
+            assert_all_equal(merged(qd, kvd, cp, dcp.DCP_LSE_BASE_E, fuse, scratch=scratch),
+                             unfused(qd, kvd, cp, dcp.DCP_LSE_BASE_E), "eager after replay %d" % k)
+        del g
     assert torch.all(scratch[:dcp.dcp_mla_decode_merged_scratch_size(B, hq, T, cp)
                              - dcp.dcp_mla_partial_decode_scratch_size(B, hq, T, cp)] == 0)
+
+
+@pytest.mark.parametrize("cp", [4, 16])
+def test_combined_reductions_without_out_lse(cp):
+    """DCP_FUSE_REDUCTIONS with out_lse = NULL, at 4 shards and at the largest shard count it takes (16: one block
+    of 16 wavefronts per head): o_part, lse_part and out equal the unfused pipeline's bits."""
+    B, hq, T = 3, 40, 8192
+    q, kv = synth.mla_decode(B, T=T, hq=hq, seed=9700 + cp)
+    qd, kvd = q.to(DEV), kv.to(DEV)
+    assert dcp.dcp_mla_partial_decode_scratch_size(B, hq, T, cp) > 0, "the shape must split the shards' keys"
+    announce("merged producer, combined reductions, cp=%d, out_lse NULL" % cp)
+    ref = unfused(qd, kvd, cp, dcp.DCP_LSE_BASE_2)
+    o = torch.full((B, cp * hq, 512), 3.0, dtype=qd.dtype, device=DEV)
+    l = torch.full((B, cp * hq), 3.0, dtype=torch.float32, device=DEV)
+    out = torch.full((B, hq, 512), 3.0, dtype=qd.dtype, device=DEV)
+    scratch = torch.zeros(dcp.dcp_mla_decode_merged_scratch_size(B, hq, T, cp), dtype=torch.uint8, device=DEV)
+    dcp.dcp_mla_decode_merged(qd, kvd, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_2, o, l, out, None,
+                              fuse=dcp.DCP_FUSE_REDUCTIONS, scratch=scratch)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("o_part", "lse_part", "out"), (o, l, out), ref[:3]):
+        assert same_bits(g, r), "%s differs from the unfused pipeline" % name
 
 
 @pytest.mark.parametrize("B,T", [(2, 16384), (32, 32768)])
