@@ -14,15 +14,22 @@
 // shard is a flash-attention pass over M = B*hq query rows: a dense
 // contraction, run on MFMA (v_mfma_f32_16x16x32_bf16, or _f16 for fp16
 // inputs; fp32 accumulate).
-//  * A workgroup owns 128 query rows, 16 per wavefront, 8 wavefronts (two per
-//    SIMD, so one wavefront's softmax and waits overlap the other's MFMAs),
-//    and one key range (a split of one shard).  Each wavefront keeps its 16
-//    query rows in registers for the whole kernel, as 18 MFMA operand
-//    fragments of 32 columns.
+//  * A workgroup owns 128 query rows and one key range (a split of one
+//    shard), with 8 wavefronts (two per SIMD, so one wavefront's softmax and
+//    waits overlap the other's MFMAs).  The two products are split
+//    differently: wavefront w computes the scores and the online softmax of
+//    its own 16 query rows (kept in registers for the whole kernel as 18 MFMA
+//    operand fragments of 32 columns), but accumulates p.v for 64 of the 512
+//    value columns of all 128 rows.  Each wavefront publishes its rows' p (the
+//    p.v operand, 1 KiB) and rescale factors in LDS, and every wavefront
+//    reads all eight: a value fragment read from LDS then feeds eight MFMAs
+//    instead of one, which cuts the p.v operand reads from 32 to 12 KiB per
+//    wavefront and tile (the q.k reads stay 36 KiB).
 //  * Keys stream through LDS 32 at a time in three buffers (one barrier per
 //    tile).  Tiles are copied global -> LDS by the gfx950 direct loads
-//    (global_load_lds_dwordx4), issued two tiles ahead, with no register
-//    staging; each barrier waits only for the older tile.
+//    (global_load_lds_dwordx4), with no register staging.  The scores of a
+//    tile are computed one interval before its p.v, so a buffer is busy for
+//    two intervals and each copy is issued one tile ahead.
 //  * LDS layout of a tile: 36 blocks of 1 KiB, block (h, b) holding the 16-byte
 //    chunks 4b..4b+3 of keys 16h..16h+15, chunk c of key k at slot
 //    16 (c % 4) + ((k % 16) ^ 8 (b % 2)).  Measured on gfx950, a 16-byte LDS
@@ -41,11 +48,12 @@
 //  * The wavefront computes S^T = K Q^T (A = K, B = Q^T) and O^T += V^T P^T
 //    (A = V^T, B = P^T).  In this orientation a lane holds eight scores of
 //    query row lane % 16 and, with the k index of p.v permuted the same way in
-//    V^T and P^T, exactly the B operand of the p.v MFMA: no shuffle between
-//    the two products, and the running max/sum of row lane % 16 sit in the
-//    same lanes as that row's output accumulators.  The q.k operand is read
-//    as 16-byte LDS words; the p.v operand, which needs the value transposed,
-//    is read from the same row-major tile with the transpose load
+//    V^T and P^T, exactly its share of the B operand of the p.v MFMA: the
+//    exchange is a 16-byte LDS write per lane, and the reading wavefront's
+//    lane l takes slot l, in the lane order that reads LDS at full rate.  The
+//    q.k operand is read as 16-byte LDS words; the p.v operand, which needs
+//    the value transposed, is read from the same row-major tile with the
+//    transpose load
 //    ds_read_b64_tr_b16: within each 16-lane group it returns lane j element
 //    i of the 8-byte chunk lane 4i + j/4 pointed at, so lanes pointing at
 //    V[key][d0 + 4(j%4)] of four keys receive a column of V^T.
@@ -89,7 +97,6 @@ constexpr int kTileChunks = kKeys * kRowChunks;  // 2304 per tile
 constexpr int kTileElems = kKeys * kDqk;
 constexpr int kDmaPerTile = kTileChunks / 64;    // 36 wavefront-wide 1 KiB copies
 constexpr int kQSteps = kDqk / 32;               // 18 fragments of 32 columns
-constexpr int kDTiles = kDv / 16;                // 32 output tiles of 16 columns
 constexpr int kXcds = 8;
 
 static_assert(kRowsPerWave * kWaves == kMlaRowsPerBlock, "rows per workgroup");
@@ -262,16 +269,6 @@ __device__ __forceinline__ void dma_tile(const KeyRows& kr, uint16_t* dst, int64
     }
 }
 
-// Wait until this wavefront's copies of all but the newest tile have landed
-// (vmcnt <= kDmaPerWave: the newest tile's copies may still be in flight;
-// expcnt and lgkmcnt untouched), then synchronise the workgroup: the older
-// tile is then complete for every wavefront.
-__device__ __forceinline__ void older_tile_ready() {
-    static_assert(kDmaPerWave < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerWave);
-    __syncthreads();
-}
-
 // Wait for all of this wavefront's tile copies, then synchronise.
 __device__ __forceinline__ void all_tiles_ready() {
     __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -284,20 +281,29 @@ struct LaneOffsets {
     int tr[4];          // p.v operand (keys 0..15), output tile t with t % 4 == u, before + 1024 (t / 4)
 };
 
-struct RowState {
-    f32x4 oacc[kDTiles];
-    float m_run, l_run;
+// What the wavefronts of a workgroup exchange per key tile.  Wavefront w
+// computes the scores and softmax of its own 16 query rows (row tile w) and
+// publishes their p.v operand P^T -- lane l's eight 16-bit p at slot l of
+// block w -- and, on a tile where its rows' reference maximum moved, the
+// rescale factor of each of those rows.  The p.v product is split by output
+// columns instead: wavefront w accumulates columns 64w .. 64w+63 of all 128
+// rows, reading the eight P^T blocks.
+struct TileExchange {
+    u32x4 p[kWaves][64];
+    float alpha[kMlaRowsPerBlock];
+    uint8_t moved[kWaves];
 };
 
 // The running maximum of the online softmax lags the true one by at most
 // this much (log2 units): p <= 2^8.
 constexpr float kLazyLog2 = 8.0f;
 
-// One 32-key tile: scores, online softmax, p.v.
+// Scores and online softmax of this wavefront's 16 rows for one 32-key tile;
+// publishes P^T and the rescale factors in `ex`.
 template <typename T>
-__device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* kt, const LaneOffsets& off,
-                                             const typename T::v8 (&qf)[kQSteps], RowState& st, int64_t t0, int64_t k1,
-                                             int g) {
+__device__ __forceinline__ void qk_tile(const MlaArgs& a, const uint16_t* kt, const LaneOffsets& off,
+                                        const typename T::v8 (&qf)[kQSteps], float& m_run, float& l_run, int64_t t0,
+                                        int64_t k1, int g, int wave, int lane, TileExchange& ex) {
     // S^T = K Q^T for keys [t0, t0+16) (sa) and [t0+16, t0+32) (sb): the lane
     // holds the scores of row r16 with keys 4g+i and 16+4g+i.
     // Operand fragments are read kAhead steps before the MFMA that uses them
@@ -345,103 +351,183 @@ __device__ __forceinline__ void compute_tile(const MlaArgs& a, const uint16_t* k
     // more than kLazyLog2; otherwise the tile's p = 2^(z - m_run) stay below
     // 2^kLazyLog2 (safe in the 16-bit p and the fp32 sums), and O / l and
     // m_run + log2 l do not depend on which reference was used.  Rescaling
-    // the 128 accumulators then happens on the first tile of a split and
-    // rarely after, instead of on every tile where some row's maximum grows.
-    if (__any(tmax > st.m_run + kLazyLog2)) {
-        const float m_new = fmaxf(st.m_run, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);  // 0 on the first tile, 1 for unchanged rows
-        st.l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < kDTiles; ++t) st.oacc[t] *= alpha;
-        st.m_run = m_new;
+    // the accumulators then happens on the first tile of a split and rarely
+    // after, instead of on every tile where some row's maximum grows.
+    const bool moved = __any(tmax > m_run + kLazyLog2);
+    if (moved) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile, 1 for unchanged rows
+        l_run *= alpha;
+        m_run = m_new;
+        if (g == 0) ex.alpha[kRowsPerWave * wave + (lane & 15)] = alpha;
     }
+    if (lane == 0) ex.moved[wave] = moved ? 1 : 0;
     float psum = 0.0f;
     typename T::v8 pb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(z[i] - st.m_run);
+        const float p = __builtin_amdgcn_exp2f(z[i] - m_run);
         psum += p;
         pb[i] = static_cast<typename T::elem>(p);
     }
-    st.l_run += psum;
+    l_run += psum;
+    ex.p[wave][lane] = __builtin_bit_cast(u32x4, pb);
+}
 
-    // O^T += V^T P^T: output tile t = 4j + u holds value columns 8c..8c+7 and
-    // 8c+32..8c+39 with c = 8j + u (chunks c and c + 4); the k index runs over
-    // keys 4g..4g+3 and 16+4g..16+4g+3, in P^T (pb) and V^T alike.
+// O^T += V^T P^T for this wavefront's output columns and all 128 rows: output
+// tile t = 4 wave + u holds value columns 8c..8c+7 and 8c+32..8c+39 with
+// c = 8 wave + u (chunks c and c + 4), acc[rt][u] its rows 16 rt .. 16 rt + 15.
+// The k index runs over keys 4g..4g+3 and 16+4g..16+4g+3, in P^T and V^T
+// alike.  Rows whose reference maximum moved on this tile are rescaled first.
+template <typename T>
+__device__ __forceinline__ void pv_tile(const uint16_t* kt, const LaneOffsets& off, f32x4 (&acc)[kWaves][4],
+                                        const TileExchange& ex, int wave, int lane) {
+    const uint2 mvw = *reinterpret_cast<const uint2*>(ex.moved);
+    typename T::v8 va[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int o = off.tr[u] + 2 * kBlockElems * wave;
+        const typename T::v4 lo = ds_read_tr<T>(kt, o), hi = ds_read_tr<T>(kt, o + kHalfElems);
+        va[u] = typename T::v8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    const uint32_t m_lo = __builtin_amdgcn_readfirstlane(mvw.x), m_hi = __builtin_amdgcn_readfirstlane(mvw.y);
+    if (m_lo | m_hi) {
+#pragma unroll
+        for (int rt = 0; rt < kWaves; ++rt) {
+            const bool mv = (((rt < 4 ? m_lo : m_hi) >> (8 * (rt & 3))) & 0xffu) != 0;
+            const float al = mv ? ex.alpha[kRowsPerWave * rt + (lane & 15)] : 1.0f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[rt][u] *= al;
+        }
+    }
     {
         constexpr int kAhead = 2;
-        typename T::v4 rl[kAhead + 1], rh[kAhead + 1];
+        u32x4 pr[kAhead + 1];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < kDTiles + kAhead; ++t) {
-            if (t < kDTiles) {
-                const int o = off.tr[t & 3] + 2 * kBlockElems * (t >> 2);
-                rl[t % (kAhead + 1)] = ds_read_tr<T>(kt, o);
-                rh[t % (kAhead + 1)] = ds_read_tr<T>(kt, o + kHalfElems);
-            }
-            if (t >= kAhead) {
-                const int u = t - kAhead;
-                const typename T::v4 lo = rl[u % (kAhead + 1)], hi = rh[u % (kAhead + 1)];
-                const typename T::v8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                st.oacc[u] = T::mfma(va, pb, st.oacc[u]);
+        for (int r = 0; r < kWaves + kAhead; ++r) {
+            if (r < kWaves) pr[r % (kAhead + 1)] = ex.p[r][lane];
+            if (r >= kAhead) {
+                const int q = r - kAhead;
+                const typename T::v8 pf = as_v8<T>(pr[q % (kAhead + 1)]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[q][u] = T::mfma(va[u], pf, acc[q][u]);
             }
         }
 #pragma unroll
-        for (int t = 0; t < kDTiles + kAhead; ++t) {
-            if (t < kDTiles) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 transpose reads
-            if (t >= kAhead) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        for (int r = 0; r < kWaves + kAhead; ++r) {
+            if (r < kWaves) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 P^T read
+            if (r >= kAhead) __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // 4 MFMAs
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// The epilogue's stores of a lane's row: O / l and the LSE in the caller's
-// base; an empty shard or split gives 0 and -inf.  One split: the element
-// type, straight into o_part / lse_part.  Several: into the scratch -- as
-// head p*cp*hq + s*hq + h, for the merge kernel to reduce over the splits, or
-// with seq_lens as row wave*16 + r16 of the item's slot, for the split
-// reduction -- in fp16, the row multiplied by 2^k so that its largest
-// magnitude lies in [2^14, 2^15) (fp16 then carries 11 significant bits
-// relative to the row's largest value), with 2^-k stored beside the LSE.
-template <typename T>
-__device__ __forceinline__ void store_rows(const MlaArgs& a, const Work& wk, int b, int h, int wave, int r16, int g,
-                                           int ocol, const RowState& st, float m_run, float l_tot, float amax,
-                                           bool direct) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * a.lse_scale : -INFINITY;
-    if (direct) {
-        const int64_t u = static_cast<int64_t>(wk.s) * a.hq + h;
-        uint16_t* orow = a.o + b * a.o_sb + u * a.o_sh + ocol;
-#pragma unroll
-        for (int t = 0; t < kDTiles; ++t) {
-            const f32x4 v = st.oacc[t];
-            const uint32_t lo = to_bits<T>(v[0] * inv) | (to_bits<T>(v[1] * inv) << 16);
-            const uint32_t hi = to_bits<T>(v[2] * inv) | (to_bits<T>(v[3] * inv) << 16);
-            *reinterpret_cast<uint2*>(orow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
-        }
-        if (g == 0) a.lse[b * a.lse_sb + u] = lse;
+// Where the rows of a workgroup go: query row rr (0..127) of the workgroup
+// is (b, h), stored if valid.  One shared cache: rows of 128 consecutive
+// (token, head) pairs; with seq_lens, heads h_base .. of token b_tok.
+struct RowPlace {
+    int rb, b_tok, h_base;
+    bool varlen;
+};
+
+__device__ __forceinline__ void place_row(const MlaArgs& a, const RowPlace& rp, int rr, int& b, int& h, bool& valid) {
+    if (rp.varlen) {
+        const int h_raw = rp.h_base + rr;
+        valid = h_raw < a.hq;
+        b = rp.b_tok;
+        h = min(h_raw, a.hq - 1);
     } else {
-        int64_t prow_idx;  // partial row of the scratch
-        if (a.seq_lens)
-            prow_idx = static_cast<int64_t>(wk.slot) * kMlaRowsPerBlock + wave * kRowsPerWave + r16;
-        else
-            prow_idx = b * a.part_sb + (static_cast<int64_t>(wk.p) * a.cp + wk.s) * a.hq + h;
-        // amax * inv = m 2^e with m in [0.5, 1): k = 15 - e.  Capped at 100
-        // so that 2^-k stays a normal float (rows below 2^-85 keep fewer bits;
-        // an all-zero row gets k = 15).  1/l <= 1, so inv * 2^k stays finite.
-        const int k = min(15 - __builtin_amdgcn_frexp_expf(amax * inv), 100);
-        const float mul = __builtin_amdgcn_ldexpf(inv, k);
-        uint16_t* prow = a.part_o + prow_idx * kDv + ocol;
+        const int row_raw = rp.rb * kMlaRowsPerBlock + rr;
+        valid = row_raw < a.rows;
+        const int row = min(row_raw, a.rows - 1);
+        b = row / a.hq;
+        h = row - b * a.hq;
+    }
+}
+
+// The epilogue: O / l and the LSE in the caller's base; an empty shard or
+// split gives 0 and -inf.  Wavefront w stores columns 64w .. 64w+63 of all
+// 128 rows, and the LSE (and scale) of its own row tile, whose softmax state
+// it holds.  One split: the element type, straight into o_part / lse_part.
+// Several: into the scratch -- as head p*cp*hq + s*hq + h, for the merge
+// kernel to reduce over the splits, or with seq_lens as row rr of the item's
+// slot, for the split reduction -- in fp16, the row multiplied by 2^k so that
+// its largest magnitude lies in [2^14, 2^15) (fp16 then carries 11
+// significant bits relative to the row's largest value), with 2^-k stored
+// beside the LSE.  The row sums and the rows' largest magnitudes (per
+// 64-column slice) travel through LDS.
+template <typename T>
+__device__ __forceinline__ void store_block(const MlaArgs& a, const Work& wk, const RowPlace& rp, int wave, int lane,
+                                            const f32x4 (&acc)[kWaves][4], float m_run, float l_run, bool direct,
+                                            float* lsum, float (*amaxp)[kMlaRowsPerBlock]) {
+    const int r16 = lane & 15, g = lane >> 4;
+    // Row sums across the four lane groups; every lane of a row ends with the same l.
+    const float l_own = sum_xor32(sum_xor16(l_run));
+    if (g == 0) lsum[kRowsPerWave * wave + r16] = l_own;
+    if (!direct) {
 #pragma unroll
-        for (int t = 0; t < kDTiles; ++t) {
-            const f32x4 v = st.oacc[t];
-            const uint32_t lo = to_bits<F16>(v[0] * mul) | (to_bits<F16>(v[1] * mul) << 16);
-            const uint32_t hi = to_bits<F16>(v[2] * mul) | (to_bits<F16>(v[3] * mul) << 16);
-            *reinterpret_cast<uint2*>(prow + 64 * (t >> 2) + 8 * (t & 3)) = make_uint2(lo, hi);
+        for (int rt = 0; rt < kWaves; ++rt) {
+            float am = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(acc[rt][u][i]));
+            am = max_xor32(max_xor16(am));
+            if (g == 0) amaxp[wave][kRowsPerWave * rt + r16] = am;
         }
-        if (g == 0) {
-            a.part_lse[prow_idx] = lse;
-            a.part_scale[prow_idx] = __builtin_amdgcn_ldexpf(1.0f, -k);
+    }
+    __syncthreads();
+    // Output columns of this lane in tile u: 64 wave + 8 u + 4 (g % 2) + 32 (g / 2).
+    const int ocol = 64 * wave + 4 * (g & 1) + 32 * (g >> 1);
+#pragma unroll
+    for (int rt = 0; rt < kWaves; ++rt) {
+        const int rr = kRowsPerWave * rt + r16;
+        int b, h;
+        bool valid;
+        place_row(a, rp, rr, b, h, valid);
+        if (!valid) continue;
+        const float l_tot = lsum[rr];
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        const bool own = rt == wave;  // this wavefront's softmax rows: m_run is theirs
+        const float lse = own && l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * a.lse_scale : -INFINITY;
+        if (direct) {
+            const int64_t u = static_cast<int64_t>(wk.s) * a.hq + h;
+            uint16_t* orow = a.o + b * a.o_sb + u * a.o_sh + ocol;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f32x4 v = acc[rt][t];
+                const uint32_t lo = to_bits<T>(v[0] * inv) | (to_bits<T>(v[1] * inv) << 16);
+                const uint32_t hi = to_bits<T>(v[2] * inv) | (to_bits<T>(v[3] * inv) << 16);
+                *reinterpret_cast<uint2*>(orow + 8 * t) = make_uint2(lo, hi);
+            }
+            if (own && g == 0) a.lse[b * a.lse_sb + u] = lse;
+        } else {
+            float amax = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, amaxp[w][rr]);
+            int64_t prow_idx;  // partial row of the scratch
+            if (rp.varlen)
+                prow_idx = static_cast<int64_t>(wk.slot) * kMlaRowsPerBlock + rr;
+            else
+                prow_idx = b * a.part_sb + (static_cast<int64_t>(wk.p) * a.cp + wk.s) * a.hq + h;
+            // amax * inv = m 2^e with m in [0.5, 1): k = 15 - e.  Capped at 100
+            // so that 2^-k stays a normal float (rows below 2^-85 keep fewer bits;
+            // an all-zero row gets k = 15).  1/l <= 1, so inv * 2^k stays finite.
+            const int k = min(15 - __builtin_amdgcn_frexp_expf(amax * inv), 100);
+            const float mul = __builtin_amdgcn_ldexpf(inv, k);
+            uint16_t* prow = a.part_o + prow_idx * kDv + ocol;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f32x4 v = acc[rt][t];
+                const uint32_t lo = to_bits<F16>(v[0] * mul) | (to_bits<F16>(v[1] * mul) << 16);
+                const uint32_t hi = to_bits<F16>(v[2] * mul) | (to_bits<F16>(v[3] * mul) << 16);
+                *reinterpret_cast<uint2*>(prow + 8 * t) = make_uint2(lo, hi);
+            }
+            if (own && g == 0) {
+                a.part_lse[prow_idx] = lse;
+                a.part_scale[prow_idx] = __builtin_amdgcn_ldexpf(1.0f, -k);
+            }
         }
     }
 }
@@ -606,9 +692,10 @@ __device__ __forceinline__ void fused_epilogue(const int* work) {
 
 template <typename T, bool Fused>
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t tile0[kTileAlloc];
-    __shared__ __attribute__((aligned(16))) uint16_t tile1[kTileAlloc];
-    __shared__ __attribute__((aligned(16))) uint16_t tile2[kTileAlloc];
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[3][kTileAlloc];
+    __shared__ TileExchange exs[3];
+    __shared__ float lsum[kMlaRowsPerBlock];
+    __shared__ float amaxp[kWaves][kMlaRowsPerBlock];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -667,24 +754,14 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     const int64_t k0 = static_cast<int64_t>(wk.p) * split_len;
     const int64_t k1 = min(k0 + split_len, n_s);
     const int ntiles = k0 < k1 ? static_cast<int>((k1 - k0 + kKeys - 1) / kKeys) : 0;
-    if (ntiles > 0) dma_tile(kr, tile0, k0, k1, wave, lane);
+    if (ntiles > 0) dma_tile(kr, tiles[0], k0, k1, wave, lane);
 
-    // Query row (b, h) of this lane; rows past the end repeat the last row and
-    // are not stored.
+    // Query row (b, h) of this lane's softmax (row 16 wave + r16 of the
+    // workgroup); rows past the end repeat the last row and are not stored.
+    const RowPlace rp{wk.rb, b_tok, h_base, a.seq_lens != nullptr};
     int b, h;
     bool valid;
-    if (a.seq_lens) {
-        const int h_raw = h_base + wave * kRowsPerWave + r16;
-        valid = h_raw < a.hq;
-        b = b_tok;
-        h = min(h_raw, a.hq - 1);
-    } else {
-        const int row_raw = wk.rb * kMlaRowsPerBlock + wave * kRowsPerWave + r16;
-        valid = row_raw < a.rows;
-        const int row = min(row_raw, a.rows - 1);
-        b = row / a.hq;
-        h = row - b * a.hq;
-    }
+    place_row(a, rp, kRowsPerWave * wave + r16, b, h, valid);
 
     // Q fragments: fragment f holds columns 32f + 8g .. +7 of this lane's row.
     typename T::v8 qf[kQSteps];
@@ -692,8 +769,8 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
         const uint16_t* qrow = a.q + b * a.q_sb + h * a.q_sh + 8 * g;
 #pragma unroll
         for (int f = 0; f < kQSteps; ++f) qf[f] = as_v8<T>(*reinterpret_cast<const u32x4*>(qrow + 32 * f));
-        // Settle these loads here: a wait for them left inside the key loop
-        // would also wait for the tile copies in flight there.
+        // Settle these loads (and tile 0's copies) here: a wait for them left
+        // inside the key loop would also wait for the tile copies in flight there.
         __builtin_amdgcn_s_waitcnt(0x0F70);
     }
 
@@ -712,52 +789,43 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) off.tr[u] = tr0 + 128 * u;
     }
-    // Output columns of this lane in tile t: 4 (g % 2) + 32 (g / 2) + 64 (t / 4) + 8 (t % 4).
-    const int ocol = 4 * (g & 1) + 32 * (g >> 1);
 
-    RowState st;
+    f32x4 acc[kWaves][4];
 #pragma unroll
-    for (int t = 0; t < kDTiles; ++t) st.oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.m_run = -INFINITY;  // running max of row r16, log2 units
-    st.l_run = 0.0f;       // lane-partial running sum of row r16
+    for (int rt = 0; rt < kWaves; ++rt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[rt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;  // running max of row r16, log2 units
+    float l_run = 0.0f;       // lane-partial running sum of row r16
 
-    // Tile it lives in buffer it % 3 and is copied two tiles ahead: while
-    // tile it is computed, tiles it+1 and it+2 may be in flight, and the
-    // barrier that ends tile it waits only for tile it+1.
-    if (ntiles > 1) dma_tile(kr, tile1, k0 + kKeys, k1, wave, lane);
-    if (ntiles > 0) {
-        if (ntiles > 1) older_tile_ready(); else all_tiles_ready();
-    }
-    for (int it = 0; it < ntiles; it += 3) {
+    // Tile i lives in buffer i % 3 with exchange i % 3.  Its scores and
+    // softmax run one interval before its p.v: between barriers i and i + 1
+    // every wavefront runs p.v of tile i (which needs every wavefront's P^T
+    // of tile i, published before barrier i) and the scores of tile i + 1.
+    // A buffer is therefore busy for two intervals, and the copy of tile
+    // i + 2, issued after barrier i into the buffer tile i - 1 left, has one
+    // interval to land (barrier i + 1 waits for it).
+    if (ntiles > 1) dma_tile(kr, tiles[1], k0 + kKeys, k1, wave, lane);
+    __syncthreads();  // tile 0: every wavefront waited for its own copies above
+    if (ntiles > 0) qk_tile<T>(a, tiles[0], off, qf, m_run, l_run, k0, k1, g, wave, lane, exs[0]);
+    // A rolled loop: the buffer and exchange indices are wave-uniform, so
+    // the LDS addresses are formed per tile instead of being held in
+    // registers for every buffer (unrolled by three, the loop spills).
+    int cur = 0;
+    for (int it = 0; it < ntiles; ++it) {
         const int64_t t0 = k0 + static_cast<int64_t>(it) * kKeys;
-        if (it + 2 < ntiles) dma_tile(kr, tile2, t0 + 2 * kKeys, k1, wave, lane);
-        compute_tile<T>(a, tile0, off, qf, st, t0, k1, g);
+        const int nxt = cur == 2 ? 0 : cur + 1;
+        const int prv = cur == 0 ? 2 : cur - 1;
+        all_tiles_ready();
+        if (it + 2 < ntiles) dma_tile(kr, tiles[prv], t0 + 2 * kKeys, k1, wave, lane);
+        pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
         if (it + 1 >= ntiles) break;
-        if (it + 2 < ntiles) older_tile_ready(); else all_tiles_ready();
-        if (it + 3 < ntiles) dma_tile(kr, tile0, t0 + 3 * kKeys, k1, wave, lane);
-        compute_tile<T>(a, tile1, off, qf, st, t0 + kKeys, k1, g);
-        if (it + 2 >= ntiles) break;
-        if (it + 3 < ntiles) older_tile_ready(); else all_tiles_ready();
-        if (it + 4 < ntiles) dma_tile(kr, tile1, t0 + 4 * kKeys, k1, wave, lane);
-        compute_tile<T>(a, tile2, off, qf, st, t0 + 2 * kKeys, k1, g);
-        if (it + 3 >= ntiles) break;
-        if (it + 4 < ntiles) older_tile_ready(); else all_tiles_ready();
+        qk_tile<T>(a, tiles[nxt], off, qf, m_run, l_run, t0 + kKeys, k1, g, wave, lane, exs[nxt]);
+        cur = nxt;
     }
 
-    // Row sums across the four lane groups; every lane of a row ends with the same l.
-    const float l_run = st.l_run;
-    const float m_run = st.m_run;
-    const float l_tot = sum_xor32(sum_xor16(l_run));
     const bool direct = a.seq_lens ? wk.slot < 0 : a.nsplit == 1;
-    float amax = 0.0f;  // several splits: the row's largest accumulator magnitude
-    if (!direct) {
-#pragma unroll
-        for (int t = 0; t < kDTiles; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st.oacc[t][i]));
-        amax = max_xor32(max_xor16(amax));
-    }
-    if (valid) store_rows<T>(a, wk, b, h, wave, r16, g, ocol, st, m_run, l_tot, amax, direct);
+    store_block<T>(a, wk, rp, wave, lane, acc, m_run, l_run, direct, lsum, amaxp);
     if (Fused) fused_epilogue<T>(fused_work);
 }
 
