@@ -810,18 +810,23 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     if (ntiles > 0) qk_tile<T>(a, tiles[0], off, qf, m_run, l_run, k0, k1, g, wave, lane, exs[0]);
     // A rolled loop: the buffer and exchange indices are wave-uniform, so
     // the LDS addresses are formed per tile instead of being held in
-    // registers for every buffer (unrolled by three, the loop spills).
+    // registers for every buffer (unrolled by three, the loop spills).  The
+    // last tile's p.v runs after the loop, so that inside it p.v and the
+    // next scores form one block of straight-line code.
     int cur = 0;
-    for (int it = 0; it < ntiles; ++it) {
+    for (int it = 0; it + 1 < ntiles; ++it) {
         const int64_t t0 = k0 + static_cast<int64_t>(it) * kKeys;
         const int nxt = cur == 2 ? 0 : cur + 1;
         const int prv = cur == 0 ? 2 : cur - 1;
         all_tiles_ready();
         if (it + 2 < ntiles) dma_tile(kr, tiles[prv], t0 + 2 * kKeys, k1, wave, lane);
         pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
-        if (it + 1 >= ntiles) break;
         qk_tile<T>(a, tiles[nxt], off, qf, m_run, l_run, t0 + kKeys, k1, g, wave, lane, exs[nxt]);
         cur = nxt;
+    }
+    if (ntiles > 0) {
+        all_tiles_ready();
+        pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
     }
 
     const bool direct = a.seq_lens ? wk.slot < 0 : a.nsplit == 1;
