@@ -27,11 +27,13 @@
 //  * cp > 16: two or four wavefronts per row, each with 16 shards' loads in
 //    flight; lane s holds lse_s, the maximum and the sum are DPP reductions
 //    over the lanes (the sum in the one fixed tree every path uses for more
-//    than 16 parts), and the fp32 accumulators pass from wavefront to
-//    wavefront through LDS, so the FMAs run in ascending shard order (the
-//    split partials of the MLA decode, many rows with adjacent parts, take
-//    one wavefront per row instead, with the same arithmetic);
-//  * fp32 FMAs in ascending shard order, then the hardware round-to-nearest-
+//    than 16 parts), each wavefront sums its 16 shards (one accumulation
+//    group of the shared arithmetic) and one adds the groups' sums from LDS
+//    in ascending order (the split partials of the MLA decode, many rows with
+//    adjacent parts, take one wavefront per row instead, with the same
+//    arithmetic);
+//  * fp32 FMAs in ascending shard order (for cp > 16 within each group of
+//    16), then the hardware round-to-nearest-
 //    even convert to the payload type and one 16-byte store per lane.  The
 //    payload is bf16 or fp16 (both are the pages' payload types); one kernel
 //    instance per type, differing only in the widening and narrowing.  A
@@ -183,20 +185,20 @@ __global__ __launch_bounds__(kBlock) void merge_kernel(const void* attn, const f
 // [16w, 16w + 16) of it, so that all of a row's loads are in flight at once
 // (a row has few enough shards per wavefront, and rows enough wavefronts, to
 // fill the chip even at small B).  Every wavefront forms the row's M, S and
-// 1/S itself (mrow::lane_max_sum: a DPP tree over the shards); the accumulation
-// then runs in ascending shard order across the wavefronts: wavefront w takes
-// the accumulators of w - 1 from LDS (exact fp32 values), adds its 16
-// shards, and hands them on; the last one stores the row.  The result is
-// merge_row_any's, bit for bit.  A block of kWavesPerBlock wavefronts holds
-// kWavesPerBlock / W rows; spare rows of the last group repeat row
-// h_local - 1 (same reads, same bits to the same place).
+// 1/S itself (mrow::lane_max_sum: a DPP tree over the shards) and the sum of
+// its 16 shards, which is one accumulation group of the shared arithmetic,
+// all wavefronts at once; after one barrier wavefront 0 adds the groups'
+// sums (exact fp32 values in LDS) in ascending order and stores the row.  The
+// result is merge_row_any's, bit for bit.  A block of kWavesPerBlock
+// wavefronts holds kWavesPerBlock / W rows; spare rows of the last group
+// repeat row h_local - 1 (same reads, same bits to the same place).
 template <int W, typename In, typename Out>
 __global__ __launch_bounds__(kBlock) void merge_kernel_wide(const void* attn, const float* lse, int32_t a_sb,
                                                             int32_t a_sj, int32_t a_ss, int32_t l_sb, int32_t l_sj,
                                                             int32_t l_ss, int32_t h_local, MergeTail t) {
     constexpr int kRows = kWavesPerBlock / W;
-    constexpr int kPer = 16;  // shards per wavefront
-    __shared__ float hand[kRows][8][64];
+    constexpr int kPer = mrow::kAccGroup;  // shards per wavefront: one accumulation group
+    __shared__ float hand[kRows][W][8][64];
     const int lane = threadIdx.x & 63;
     const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ri = v / W, w = v - ri * W;
@@ -224,21 +226,23 @@ __global__ __launch_bounds__(kBlock) void merge_kernel_wide(const void* attn, co
     if (In::kScaled) wl *= sc;
 
     float acc[8];
-    for (int step = 0; step < W; ++step) {
-        if (w == step) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = step == 0 ? 0.0f : hand[ri][i][lane];
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
-            for (int i = 0; i < kPer; ++i)
-                if (s0 + i < cp) mrow::fma8<In>(acc, mrow::lane_value(wl, s0 + i), vals[i]);
-            if (step + 1 < W) {
+    for (int i = 0; i < kPer; ++i)
+        if (s0 + i < cp) mrow::fma8<In>(acc, mrow::lane_value(wl, s0 + i), vals[i]);
+    if (w > 0) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) hand[ri][i][lane] = acc[i];
-            }
-        }
-        if (step + 1 < W) __syncthreads();
+        for (int i = 0; i < 8; ++i) hand[ri][w][i][lane] = acc[i];
     }
-    if (w == W - 1) store_row<Out>(t, r, lane, acc, mrow::merged_lse(M, S, t.from_log2));
+    __syncthreads();
+    if (w == 0) {
+        for (int k = 1; k < W && k * kPer < cp; ++k) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = acc[i] + hand[ri][k][i][lane];
+        }
+        store_row<Out>(t, r, lane, acc, mrow::merged_lse(M, S, t.from_log2));
+    }
 }
 
 // 16 < cp <= 64, one wavefront per row: merge_row_any over the cp parts, 16

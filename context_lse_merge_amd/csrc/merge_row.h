@@ -10,7 +10,10 @@
 //         64 shards a fixed tree (tree_sum), the groups' sums added in
 //         ascending order from 0;   inv = 1/S (0 when S = 0);
 //     w^_s = w_s * inv (* the row's scale factor, for scaled partials);
-//     acc = sum of w^_s * O_s, ascending, fp32 FMA, a shard of weight 0 adding +0;
+//     acc = sum of w^_s * O_s in fp32 FMAs, a shard of weight 0 adding +0:
+//         for n <= 16 ascending from 0; for n > 16 per group of 16 shards
+//         (16q .. 16q+15) ascending from 0, the groups' sums then added in
+//         ascending order (so the groups of a row can run in parallel);
 //     L = M + log2(S) / c.
 // ("[DCP] Run fi_a2a on FlashInfer's fused all-to-all + LSE reduce", sglang PR
 // #40539, Motivation; "[Attention] Add direct symmetric-memory DCP A2A", vLLM
@@ -219,8 +222,10 @@ __device__ __forceinline__ void row_max_sum(const float* lrow, int64_t l_ss, int
 // column offset); its LSE is lrow[s*l_ss] and, for scaled payloads, its
 // factor lrow[s*l_ss + sc_off].  The LSEs come in 64 at a time, shard c0 + l
 // in lane l, for the maximum and the sum (lane_max_sum, row_max_sum); the
-// payloads come G shards at a time, the next group's loads issued before the
-// current group's FMAs.  Returns the accumulators, M and S.
+// payloads come G shards at a time (G divides kAccGroup), the next group's
+// loads issued before the current group's FMAs.  Returns the accumulators, M
+// and S.
+constexpr int kAccGroup = 16;  // shards per group of the accumulation
 template <int G, typename In>
 __device__ __forceinline__ void merge_row_any(const void* attn, int64_t o0, int64_t a_ss, const float* lrow,
                                               int64_t l_ss, int64_t sc_off, int n, float to_log2, float (&acc)[8],
@@ -243,23 +248,34 @@ __device__ __forceinline__ void merge_row_any(const void* attn, int64_t o0, int6
     }
     const float inv = inv_sum(S);
 
+    static_assert(kAccGroup % G == 0 && 64 % kAccGroup == 0, "load groups tile the accumulation groups");
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;  // n = 0; otherwise the first group's sum replaces it
+    float grp[8];  // the current accumulation group's sum
     for (int c0 = 0; c0 < n; c0 += 64) {
         const int m = min(64, n - c0);
         float wl = shard_weight(c0 == 0 ? x0 : lane_lse(lrow, l_ss, c0, m), M, to_log2) * inv;
         if (In::kScaled)
             wl *= c0 == 0 ? sc0 : (lane < m ? lrow[static_cast<int64_t>(c0 + lane) * l_ss + sc_off] : 0.0f);
         for (int g0 = 0; g0 < m; g0 += G) {
-            const int s_next = c0 + g0 + G;  // first shard of the next group
+            const int s0 = c0 + g0;     // first shard of this load group
+            const int s_next = s0 + G;  // first shard of the next one
             if (s_next < n) {
 #pragma unroll
                 for (int i = 0; i < G; ++i)
                     nxt[i] = In::load(attn, o0 + static_cast<int64_t>(min(s_next + i, n - 1)) * a_ss);
             }
+            if (s0 % kAccGroup == 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) grp[i] = 0.0f;
+            }
 #pragma unroll
             for (int i = 0; i < G; ++i)
-                if (g0 + i < m) fma8<In>(acc, lane_value(wl, g0 + i), cur[i]);
+                if (g0 + i < m) fma8<In>(grp, lane_value(wl, g0 + i), cur[i]);
+            if (s_next % kAccGroup == 0 || s_next >= n) {  // the accumulation group is complete
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = s0 < kAccGroup ? grp[i] : acc[i] + grp[i];
+            }
             if (s_next < n) {
 #pragma unroll
                 for (int i = 0; i < G; ++i) cur[i] = nxt[i];

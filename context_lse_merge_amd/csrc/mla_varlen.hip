@@ -25,8 +25,9 @@
 //    merges them.
 // The reduction is the merge's own row arithmetic (merge_row.h: the row
 // maximum, the sum in its fixed order, normalised weights times the rows'
-// scale factors, fp32 FMAs in ascending split order), so a pair split at the
-// same boundaries gives the same bits on either path.  Which
+// scale factors, fp32 FMAs in ascending split order within groups of 16
+// splits, the groups' sums added in order), so a pair split at the same
+// boundaries gives the same bits on either path.  Which
 // workgroup runs which split, and which slots a pair gets, depend on the
 // order of LDS atomics; the arithmetic of a split does not, so the results
 // are deterministic.

@@ -178,9 +178,10 @@ int dcp_workspace_set_load_policy(dcp_workspace* ws, int policy);
  * out_lse   [B, h_local] fp32 merged LSE at out_lse + b*out_lse_sb + j, or NULL.
  *
  * A row whose shards are all empty gives out = +0.0 and out_lse = -inf (sglang
- * PR #32851, commit log: such rows give 0, not NaN).  Arithmetic is fp32 with
- * a fixed, ascending shard order that does not depend on B, the chunking or
- * the launch, so chunked and unchunked calls give identical bits.
+ * PR #32851, commit log: such rows give 0, not NaN).  Arithmetic is fp32 in a
+ * fixed shard order (ascending; above 16 shards ascending within each group
+ * of 16, the groups' sums then added in order) that does not depend on B, the
+ * chunking or the launch, so chunked and unchunked calls give identical bits.
  * B = 0 is a no-op.  B > capacity runs ceil(B / capacity) launches over
  * consecutive token ranges, in order, on hip_stream (PR #40539, Modifications).
  *
