@@ -57,7 +57,9 @@
 //    ds_read_b64_tr_b16: within each 16-lane group it returns lane j element
 //    i of the 8-byte chunk lane 4i + j/4 pointed at, so lanes pointing at
 //    V[key][d0 + 4(j%4)] of four keys receive a column of V^T.
-//  * Online softmax in base 2 (scale * log2 e folded into one multiply); the
+//  * Online softmax in base 2 (scale * log2 e applied once to the tile
+//    maximum and inside each exponent's FMA, p = 2^(s c - m) with one
+//    rounding; a key mask only on a split's last, partial tile); the
 //    row max is a 4-lane reduction per tile, the row sum stays lane-partial
 //    until the end, and the reference maximum moves (rescaling the output
 //    accumulators) only when some row's score exceeds it by more than 8
@@ -336,16 +338,25 @@ __device__ __forceinline__ void qk_tile(const MlaArgs& a, const uint16_t* kt, co
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    float z[8];
+    float z[8];  // raw scores; the scale is applied in the exponent
+    if (k1 - t0 >= kKeys) {  // a full tile: no key to mask
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        z[i] = (t0 + 4 * g + i < k1) ? sa[i] * a.scale_log2 : -INFINITY;
-        z[4 + i] = (t0 + 16 + 4 * g + i < k1) ? sb[i] * a.scale_log2 : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+            z[i] = sa[i];
+            z[4 + i] = sb[i];
+        }
+    } else {
+        const int rem = static_cast<int>(k1 - t0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            z[i] = (4 * g + i < rem) ? sa[i] : -INFINITY;
+            z[4 + i] = (16 + 4 * g + i < rem) ? sb[i] : -INFINITY;
+        }
     }
     float tmax = z[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
-    tmax = max_xor32(max_xor16(tmax));  // finite: the tile has a valid key
+    tmax = max_xor32(max_xor16(tmax)) * a.scale_log2;  // finite: the tile has a valid key
     // Lazy rescaling: the running maximum m_run (the reference of the
     // exponentials) moves only when some row's tile maximum exceeds it by
     // more than kLazyLog2; otherwise the tile's p = 2^(z - m_run) stay below
@@ -366,7 +377,7 @@ __device__ __forceinline__ void qk_tile(const MlaArgs& a, const uint16_t* kt, co
     typename T::v8 pb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(z[i] - m_run);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(z[i], a.scale_log2, -m_run));
         psum += p;
         pb[i] = static_cast<typename T::elem>(p);
     }
