@@ -27,9 +27,12 @@
 //    wavefront and tile (the q.k reads stay 36 KiB).
 //  * Keys stream through LDS 32 at a time in three buffers (one barrier per
 //    tile).  Tiles are copied global -> LDS by the gfx950 direct loads
-//    (global_load_lds_dwordx4), with no register staging.  The scores of a
-//    tile are computed one interval before its p.v, so a buffer is busy for
-//    two intervals and each copy is issued one tile ahead.
+//    (global_load_lds_dwordx4), with no register staging; every tile but a
+//    split's last is copied with a scalar base address and one per-lane
+//    offset fixed for the whole kernel, so the copies cost no vector
+//    instructions.  The scores of a tile are computed one interval before
+//    its p.v, so a buffer is busy for two intervals and each copy is issued
+//    one tile ahead.
 //  * LDS layout of a tile: 36 blocks of 1 KiB, block (h, b) holding the 16-byte
 //    chunks 4b..4b+3 of keys 16h..16h+15, chunk c of key k at slot
 //    16 (c % 4) + ((k % 16) ^ 8 (b % 2)).  Measured on gfx950, a 16-byte LDS
@@ -238,12 +241,8 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
 
-constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;
-// Every wavefront issues kDmaPerWave copies per tile, so its count of
-// outstanding tile copies is always a multiple of kDmaPerWave; the copies past
-// the tile's end refill a slack area behind it with the tile's last row.
-constexpr int kTileSlack = (kDmaPerWave * kWaves - kDmaPerTile) * 64 * 8;  // elements
-constexpr int kTileAlloc = kTileElems + kTileSlack;
+constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;  // copies per wavefront, at most
+constexpr int kTileAlloc = kTileElems;
 
 // The keys a workgroup visits: logical key j (0, 1, ... within its shard) is
 // cache row rows0 + j * rstride elements (rstride = kv_st, or cp * kv_st when
@@ -260,14 +259,50 @@ __device__ __forceinline__ void dma_tile(const KeyRows& kr, uint16_t* dst, int64
     const int lane = opaque(lane_in);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-        const int copy = wave + kWaves * i;
-        const int n = min(copy, kDmaPerTile - 1);  // slack copies repeat the last block's source
-        const int h = n >= kHalfBlocks ? 1 : 0;
-        const int blk = n - h * kHalfBlocks;
-        const int key = 16 * h + ((lane & 15) ^ (8 * (blk & 1)));
-        const int chunk = 4 * blk + (lane >> 4);
-        const int o = min(key, last) * kr.rstride + 8 * chunk;
-        lds_dma16(base + o, lds_addr(dst + kBlockElems * copy));
+        const int n = wave + kWaves * i;
+        if (n < kDmaPerTile) {
+            const int h = n >= kHalfBlocks ? 1 : 0;
+            const int blk = n - h * kHalfBlocks;
+            const int key = 16 * h + ((lane & 15) ^ (8 * (blk & 1)));
+            const int chunk = 4 * blk + (lane >> 4);
+            const int o = min(key, last) * kr.rstride + 8 * chunk;
+            lds_dma16(base + o, lds_addr(dst + kBlockElems * n));
+        }
+    }
+}
+
+// The same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset: the address arithmetic stays scalar.
+__device__ __forceinline__ void lds_dma16_s(const uint16_t* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
+// Byte offset of lane `lane`'s 16 bytes within every block wavefront `wave`
+// copies of a full tile: key (lane % 16) ^ 8 (b % 2), chunk lane / 16 of the
+// block's four, and b % 2 = wave % 2 for every copy n = wave + 8 i of the
+// wavefront (n % 18 and n have the same parity).  Fits 32 bits for row
+// strides below kFullTileMaxStride elements.
+constexpr int32_t kFullTileMaxStride = 1 << 26;
+__device__ __forceinline__ uint32_t full_tile_lane_offset(int32_t rstride, int wave, int lane) {
+    const int key = (lane & 15) ^ (8 * (wave & 1));
+    return 2u * (static_cast<uint32_t>(key) * static_cast<uint32_t>(rstride) + 8u * static_cast<uint32_t>(lane >> 4));
+}
+
+// dma_tile for a tile whose 32 keys are all valid: block n = 18 h + b of the
+// tile reads rows 16 h .. of it from 32 b elements on, a scalar offset; the
+// lane's part is full_tile_lane_offset.  The same bytes as dma_tile.
+__device__ __forceinline__ void dma_tile_full(const KeyRows& kr, uint16_t* dst, int64_t t0, uint32_t lane_off,
+                                              int wave) {
+    const uint16_t* base = kr.rows0 + t0 * kr.rstride;
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+        const int n = wave + kWaves * i;
+        if (n < kDmaPerTile) {
+            const int h = n >= kHalfBlocks ? 1 : 0;
+            const int blk = n - h * kHalfBlocks;
+            lds_dma16_s(base + static_cast<int64_t>(16 * h) * kr.rstride + 32 * blk, lane_off,
+                        lds_addr(dst + kBlockElems * n));
+        }
     }
 }
 
@@ -301,8 +336,9 @@ struct TileExchange {
 constexpr float kLazyLog2 = 8.0f;
 
 // Scores and online softmax of this wavefront's 16 rows for one 32-key tile;
-// publishes P^T and the rescale factors in `ex`.
-template <typename T>
+// publishes P^T and the rescale factors in `ex`.  kMask: the tile may hold
+// keys at or past k1 (a split's last tile), whose scores are masked.
+template <typename T, bool kMask>
 __device__ __forceinline__ void qk_tile(const MlaArgs& a, const uint16_t* kt, const LaneOffsets& off,
                                         const typename T::v8 (&qf)[kQSteps], float& m_run, float& l_run, int64_t t0,
                                         int64_t k1, int g, int wave, int lane, TileExchange& ex) {
@@ -339,18 +375,18 @@ __device__ __forceinline__ void qk_tile(const MlaArgs& a, const uint16_t* kt, co
     }
 
     float z[8];  // raw scores; the scale is applied in the exponent
-    if (k1 - t0 >= kKeys) {  // a full tile: no key to mask
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            z[i] = sa[i];
-            z[4 + i] = sb[i];
-        }
-    } else {
-        const int rem = static_cast<int>(k1 - t0);
+    if (kMask) {
+        const int rem = static_cast<int>(min(k1 - t0, static_cast<int64_t>(kKeys)));  // valid keys of the tile
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             z[i] = (4 * g + i < rem) ? sa[i] : -INFINITY;
             z[4 + i] = (16 + 4 * g + i < rem) ? sb[i] : -INFINITY;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            z[i] = sa[i];
+            z[4 + i] = sb[i];
         }
     }
     float tmax = z[0];
@@ -765,7 +801,16 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     const int64_t k0 = static_cast<int64_t>(wk.p) * split_len;
     const int64_t k1 = min(k0 + split_len, n_s);
     const int ntiles = k0 < k1 ? static_cast<int>((k1 - k0 + kKeys - 1) / kKeys) : 0;
-    if (ntiles > 0) dma_tile(kr, tiles[0], k0, k1, wave, lane);
+    // Every tile but a split's last is full and takes the scalar-address copy.
+    const bool full_ok = kr.rstride < kFullTileMaxStride;
+    const uint32_t lane_off = full_tile_lane_offset(kr.rstride, wave, lane);
+    auto copy_tile = [&](int j, uint16_t* dst) {
+        if (full_ok && j + 1 < ntiles)
+            dma_tile_full(kr, dst, k0 + static_cast<int64_t>(j) * kKeys, lane_off, wave);
+        else
+            dma_tile(kr, dst, k0 + static_cast<int64_t>(j) * kKeys, k1, wave, lane);
+    };
+    if (ntiles > 0) copy_tile(0, tiles[0]);
 
     // Query row (b, h) of this lane's softmax (row 16 wave + r16 of the
     // workgroup); rows past the end repeat the last row and are not stored.
@@ -816,23 +861,33 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     // A buffer is therefore busy for two intervals, and the copy of tile
     // i + 2, issued after barrier i into the buffer tile i - 1 left, has one
     // interval to land (barrier i + 1 waits for it).
-    if (ntiles > 1) dma_tile(kr, tiles[1], k0 + kKeys, k1, wave, lane);
+    if (ntiles > 1) copy_tile(1, tiles[1]);
     __syncthreads();  // tile 0: every wavefront waited for its own copies above
-    if (ntiles > 0) qk_tile<T>(a, tiles[0], off, qf, m_run, l_run, k0, k1, g, wave, lane, exs[0]);
+    if (ntiles > 0) qk_tile<T, true>(a, tiles[0], off, qf, m_run, l_run, k0, k1, g, wave, lane, exs[0]);
     // A rolled loop: the buffer and exchange indices are wave-uniform, so
     // the LDS addresses are formed per tile instead of being held in
     // registers for every buffer (unrolled by three, the loop spills).  The
     // last tile's p.v runs after the loop, so that inside it p.v and the
     // next scores form one block of straight-line code.
+    // Tiles 1 .. ntiles - 2 are full; only the last one's scores need the
+    // key mask, so its interval runs after the loop.
     int cur = 0;
-    for (int it = 0; it + 1 < ntiles; ++it) {
+    for (int it = 0; it + 2 < ntiles; ++it) {
         const int64_t t0 = k0 + static_cast<int64_t>(it) * kKeys;
         const int nxt = cur == 2 ? 0 : cur + 1;
         const int prv = cur == 0 ? 2 : cur - 1;
         all_tiles_ready();
-        if (it + 2 < ntiles) dma_tile(kr, tiles[prv], t0 + 2 * kKeys, k1, wave, lane);
+        copy_tile(it + 2, tiles[prv]);
         pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
-        qk_tile<T>(a, tiles[nxt], off, qf, m_run, l_run, t0 + kKeys, k1, g, wave, lane, exs[nxt]);
+        qk_tile<T, false>(a, tiles[nxt], off, qf, m_run, l_run, t0 + kKeys, k1, g, wave, lane, exs[nxt]);
+        cur = nxt;
+    }
+    if (ntiles > 1) {
+        const int nxt = cur == 2 ? 0 : cur + 1;
+        all_tiles_ready();
+        pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
+        qk_tile<T, true>(a, tiles[nxt], off, qf, m_run, l_run, k0 + static_cast<int64_t>(ntiles - 1) * kKeys, k1, g,
+                         wave, lane, exs[nxt]);
         cur = nxt;
     }
     if (ntiles > 0) {
