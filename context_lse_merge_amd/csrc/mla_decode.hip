@@ -217,11 +217,6 @@ __device__ __forceinline__ int opaque(int v) {
     return v;
 }
 
-// Copy the K tile of keys [t0, t0 + 32) into LDS tile `dst` with direct
-// loads: copy n = w + 8 i of wavefront w fills block n = 18 h + b, its lane l
-// slot l, i.e. chunk 4b + l / 16 of key 16 h + ((l % 16) ^ 8 (b % 2)).  In a
-// ragged last tile, keys at or past k1 re-read key k1 - 1 (their scores are
-// masked).
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS
 // byte address lds + 16 l.  Issued as inline assembly so that the compiler
 // does not track it: its automatic waits would otherwise stall every tile on
@@ -252,6 +247,13 @@ struct KeyRows {
     int32_t rstride;
 };
 
+// Copy the K tile of keys [t0, t0 + 32) into LDS tile `dst` with direct
+// loads: copy n = w + 8 i (n < 36: wavefronts 0-3 issue five, 4-7 four) of
+// wavefront w fills block n = 18 h + b, its lane l slot l, i.e. chunk
+// 4b + l / 16 of key 16 h + ((l % 16) ^ 8 (b % 2)).  In a ragged last tile,
+// keys at or past k1 re-read key k1 - 1 (their scores are masked).  Every
+// wait for these copies is a wait for all of them (vmcnt(0)), so the counts
+// may differ between wavefronts.
 __device__ __forceinline__ void dma_tile(const KeyRows& kr, uint16_t* dst, int64_t t0, int64_t k1, int wave,
                                          int lane_in) {
     const uint16_t* base = kr.rows0 + t0 * kr.rstride;
