@@ -528,10 +528,11 @@ int plan_mla_merged(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh
     }
 
     MlaArgs& a = plan->args;
-    // DCP_FUSE_AUTO never takes the fused epilogue (measured slower at every
-    // shape: the agent-scope publication of each workgroup's part costs more
-    // than the launches it saves); with many key splits and cp <= 16 it takes
-    // the combined reduction launch, else the separate launches.
+    // DCP_FUSE_AUTO never takes the fused epilogue (measured slower at small
+    // B, where the agent-scope publication of each workgroup's part costs more
+    // than the launches it saves, and even from B = 32 on); with many key
+    // splits and cp <= 16 it takes the combined reduction launch, else the
+    // separate launches.
     a.fused = fuse == DCP_FUSE_EPILOGUE ? 1 : 0;
     a.split_cnt = static_cast<int32_t*>(scratch);
     a.rb_cnt = a.split_cnt + static_cast<int64_t>(a.row_blocks) * cp;

@@ -309,9 +309,10 @@ int dcp_mla_partial_decode_noalloc(const void* q, int64_t B, int hq, int64_t q_s
  *  - DCP_FUSE_AUTO: the fastest as measured on MI355X (128 heads, 4 shards,
  *    131072 keys, B = 1, 2, 8, 32, 64): REDUCTIONS where the shards' keys
  *    are split 16 ways or more (about 1% faster at B = 1 and 2), else NONE.
- *    The fused epilogue is slower at every shape measured: publishing a
- *    workgroup's part at agent scope writes back the L2 of its XCD, and that
- *    costs more than the launches it saves.
+ *    The fused epilogue is nowhere faster: at B <= 16 it is slower
+ *    (publishing a workgroup's part at agent scope writes back the L2 of its
+ *    XCD, and that costs more than the launches it saves), from B = 32 on
+ *    even with the separate launches.
  * Every mode gives the same bits: o_part / lse_part equal
  * dcp_mla_partial_decode's, and out / out_lse equal dcp_lse_combine over them
  * (DCP_LSE_BH1, the same lse_mode).
