@@ -127,13 +127,26 @@ constexpr int kHalfElems = kHalfBlocks * kBlockElems;        // keys 16..31 star
 // Reductions over lane pairs (l, l ^ 16) and (l, l ^ 32) without an LDS round
 // trip: v_permlane16_swap / v_permlane32_swap of a value with itself return
 // the two rows (halves) of each pair, one in each result.
+// max(a, b) of values that are never NaN here, as a bare v_max_f32: fmaxf
+// would first pass each operand the compiler cannot prove canonical (a
+// permlane result, say) through a NaN-quieting v_max_f32 x, x of its own.
+// Only for operands written by ordinary vector instructions: an MFMA result
+// needs wait states before it is read, which the compiler inserts only ahead
+// of instructions it generates itself.
+__device__ __forceinline__ float max_nn(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+
 __device__ __forceinline__ float max_xor16(float v) {
     const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    return max_nn(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float max_xor32(float v) {
     const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    return max_nn(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float sum_xor16(float v) {
     const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -391,6 +404,8 @@ __device__ __forceinline__ void qk_tile(const MlaArgs& a, const uint16_t* kt, co
             z[4 + i] = sb[i];
         }
     }
+    // fmaxf here: its operands are MFMA results, whose wait states before a
+    // vector read the compiler inserts only for instructions it generates.
     float tmax = z[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
@@ -404,7 +419,7 @@ __device__ __forceinline__ void qk_tile(const MlaArgs& a, const uint16_t* kt, co
     // after, instead of on every tile where some row's maximum grows.
     const bool moved = __any(tmax > m_run + kLazyLog2);
     if (moved) {
-        const float m_new = fmaxf(m_run, tmax);
+        const float m_new = max_nn(m_run, tmax);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile, 1 for unchanged rows
         l_run *= alpha;
         m_run = m_new;
