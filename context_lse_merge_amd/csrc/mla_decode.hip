@@ -295,8 +295,11 @@ __device__ __forceinline__ void lds_dma16_s(const uint16_t* sbase, uint32_t voff
 // Byte offset of lane `lane`'s 16 bytes within every block wavefront `wave`
 // copies of a full tile: key (lane % 16) ^ 8 (b % 2), chunk lane / 16 of the
 // block's four, and b % 2 = wave % 2 for every copy n = wave + 8 i of the
-// wavefront (n % 18 and n have the same parity).  Fits 32 bits for row
-// strides below kFullTileMaxStride elements.
+// wavefront (n % 18 and n have the same parity).  The key is at most 15 (the
+// half's 16 rows go into the scalar base), so for row strides below
+// kFullTileMaxStride elements the offset stays below 2^31.  The host limits
+// the row stride to (2^31 - 576) / 32 elements, so validated calls always
+// take this path; the check keeps the kernel's own assumption explicit.
 constexpr int32_t kFullTileMaxStride = 1 << 26;
 __device__ __forceinline__ uint32_t full_tile_lane_offset(int32_t rstride, int wave, int lane) {
     const int key = (lane & 15) ^ (8 * (wave & 1));

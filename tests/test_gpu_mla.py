@@ -183,6 +183,29 @@ def test_strided_query_and_padded_output():
     assert torch.all(host[:, :, :32] == 5.0) and torch.all(host[:, :, 32 + 512:] == 5.0)
 
 
+def test_largest_kv_row_stride():
+    """The cache at the largest row stride the planner accepts ((2^31 - 576) / 32 elements, rounded down to a
+    multiple of 8; a 4.4 GB strided view): the tile copies' addresses then reach their largest lane offsets
+    (about 2.0e9 bytes) and scalar bases (16 rows apart).  34 keys in one shard: a full first tile and a ragged
+    second one, so both copy paths run."""
+    B, hq, T, cp = 1, 16, 34, 1
+    kv_st = ((((1 << 31) - 576) // 32) // 8) * 8
+    q, kv = synth.mla_decode(B, T=T, hq=hq, seed=83)
+    backing = torch.empty((T - 1) * kv_st + 576, dtype=torch.bfloat16, device=DEV)
+    kv_view = backing.as_strided((T, 576), (kv_st, 1))
+    kv_view.copy_(kv.to(DEV))
+    o_part = torch.empty((B, cp * hq, 512), dtype=q.dtype, device=DEV)
+    lse_part = torch.empty((B, cp * hq), dtype=torch.float32, device=DEV)
+    nbytes = dcp.dcp_mla_partial_decode_scratch_size(B, hq, T, cp)
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=DEV) if nbytes else None
+    announce("dcp_mla_partial_decode bf16 B=%d hq=%d T=%d cp=%d kv_st=%d (largest accepted)" % (B, hq, T, cp, kv_st))
+    dcp.dcp_mla_partial_decode(q.to(DEV), kv_view, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o_part, lse_part, scratch)
+    torch.cuda.synchronize()
+    del kv_view, backing
+    torch.cuda.empty_cache()
+    check_partials(q, kv, cp, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o_part, lse_part)
+
+
 def test_too_small_scratch_is_rejected_before_launch():
     B, hq, T, cp = 1, 128, 8192, 4
     need = dcp.dcp_mla_partial_decode_scratch_size(B, hq, T, cp)
