@@ -250,6 +250,7 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint32_t lds) {
 }
 
 constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;  // copies per wavefront, at most
+static_assert(kWaves * (kDmaPerWave - 2) + kWaves - 1 < kDmaPerTile, "all but a wavefront's last copy exist");
 constexpr int kTileAlloc = kTileElems;
 
 // The keys a workgroup visits: logical key j (0, 1, ... within its shard) is
@@ -275,7 +276,7 @@ __device__ __forceinline__ void dma_tile(const KeyRows& kr, uint16_t* dst, int64
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
         const int n = wave + kWaves * i;
-        if (n < kDmaPerTile) {
+        if (i + 1 < kDmaPerWave || n < kDmaPerTile) {  // only the last copy can fall past block 35
             const int h = n >= kHalfBlocks ? 1 : 0;
             const int blk = n - h * kHalfBlocks;
             const int key = 16 * h + ((lane & 15) ^ (8 * (blk & 1)));
@@ -315,7 +316,7 @@ __device__ __forceinline__ void dma_tile_full(const KeyRows& kr, uint16_t* dst, 
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
         const int n = wave + kWaves * i;
-        if (n < kDmaPerTile) {
+        if (i + 1 < kDmaPerWave || n < kDmaPerTile) {  // only the last copy can fall past block 35
             const int h = n >= kHalfBlocks ? 1 : 0;
             const int blk = n - h * kHalfBlocks;
             lds_dma16_s(base + static_cast<int64_t>(16 * h) * kr.rstride + 32 * blk, lane_off,
