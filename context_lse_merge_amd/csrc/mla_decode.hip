@@ -514,6 +514,37 @@ __device__ __forceinline__ void place_row(const MlaArgs& a, const RowPlace& rp, 
     }
 }
 
+// Lane group g of a row holds, in d[t] (t = 0..3), the packed 16-bit values
+// of columns 8t + 4 (g % 2) + 32 (g / 2) .. +3 of its wavefront's 64-column
+// slice.  A 4 x 4 transpose of these 8-byte items over the row's four lane
+// groups (lanes r16, r16 + 16, r16 + 32, r16 + 48; two permlane stages, all
+// lanes active) leaves group g with columns 8g .. 8g + 7 in d[0], d[1] and
+// 32 + 8g .. 32 + 8g + 7 in d[2], d[3]: each lane then stores two 16-byte
+// words, and one store instruction writes 64 contiguous bytes of each of its
+// 16 rows instead of two 16-byte pieces.
+__device__ __forceinline__ void regroup_slice(uint32_t (&d)[4][2]) {
+    // Groups g and g ^ 2: items 2 + t0 of groups 0, 1 trade places with items
+    // t0 of groups 2, 3.
+#pragma unroll
+    for (int t0 = 0; t0 < 2; ++t0)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const auto p = __builtin_amdgcn_permlane32_swap(d[t0][w], d[2 + t0][w], false, false);
+            d[t0][w] = p[0];
+            d[2 + t0][w] = p[1];
+        }
+    // Groups g and g ^ 1: items 2c + 1 of the even groups trade places with
+    // items 2c of the odd ones.
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const auto p = __builtin_amdgcn_permlane16_swap(d[2 * c][w], d[2 * c + 1][w], false, false);
+            d[2 * c][w] = p[0];
+            d[2 * c + 1][w] = p[1];
+        }
+}
+
 // The epilogue: O / l and the LSE in the caller's base; an empty shard or
 // split gives 0 and -inf.  Wavefront w stores columns 64w .. 64w+63 of all
 // 128 rows, and the LSE (and scale) of its own row tile, whose softmax state
@@ -546,35 +577,35 @@ __device__ __forceinline__ void store_block(const MlaArgs& a, const Work& wk, co
         }
     }
     __syncthreads();
-    // Output columns of this lane in tile u: 64 wave + 8 u + 4 (g % 2) + 32 (g / 2).
-    const int ocol = 64 * wave + 4 * (g & 1) + 32 * (g >> 1);
+    // After regroup_slice this lane's columns are 64 wave + 8 g (+ 32).
+    const int ocol = 64 * wave + 8 * g;
 #pragma unroll
     for (int rt = 0; rt < kWaves; ++rt) {
         const int rr = kRowsPerWave * rt + r16;
         int b, h;
-        bool valid;
+        bool valid;  // the same for the four lanes of a row: the regrouping stays within a row
         place_row(a, rp, rr, b, h, valid);
-        if (!valid) continue;
         const float l_tot = lsum[rr];
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         const bool own = rt == wave;  // this wavefront's softmax rows: m_run is theirs
         const float lse = own && l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * a.lse_scale : -INFINITY;
+        uint32_t d[4][2];
+        uint16_t* orow;
+        int64_t prow_idx = 0;  // partial row of the scratch
+        int k = 0;
         if (direct) {
             const int64_t u = static_cast<int64_t>(wk.s) * a.hq + h;
-            uint16_t* orow = a.o + b * a.o_sb + u * a.o_sh + ocol;
+            orow = a.o + b * a.o_sb + u * a.o_sh + ocol;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const f32x4 v = acc[rt][t];
-                const uint32_t lo = to_bits<T>(v[0] * inv) | (to_bits<T>(v[1] * inv) << 16);
-                const uint32_t hi = to_bits<T>(v[2] * inv) | (to_bits<T>(v[3] * inv) << 16);
-                *reinterpret_cast<uint2*>(orow + 8 * t) = make_uint2(lo, hi);
+                d[t][0] = to_bits<T>(v[0] * inv) | (to_bits<T>(v[1] * inv) << 16);
+                d[t][1] = to_bits<T>(v[2] * inv) | (to_bits<T>(v[3] * inv) << 16);
             }
-            if (own && g == 0) a.lse[b * a.lse_sb + u] = lse;
         } else {
             float amax = 0.0f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, amaxp[w][rr]);
-            int64_t prow_idx;  // partial row of the scratch
             if (rp.varlen)
                 prow_idx = static_cast<int64_t>(wk.slot) * kMlaRowsPerBlock + rr;
             else
@@ -582,17 +613,24 @@ __device__ __forceinline__ void store_block(const MlaArgs& a, const Work& wk, co
             // amax * inv = m 2^e with m in [0.5, 1): k = 15 - e.  Capped at 100
             // so that 2^-k stays a normal float (rows below 2^-85 keep fewer bits;
             // an all-zero row gets k = 15).  1/l <= 1, so inv * 2^k stays finite.
-            const int k = min(15 - __builtin_amdgcn_frexp_expf(amax * inv), 100);
+            k = min(15 - __builtin_amdgcn_frexp_expf(amax * inv), 100);
             const float mul = __builtin_amdgcn_ldexpf(inv, k);
-            uint16_t* prow = a.part_o + prow_idx * kDv + ocol;
+            orow = a.part_o + prow_idx * kDv + ocol;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const f32x4 v = acc[rt][t];
-                const uint32_t lo = to_bits<F16>(v[0] * mul) | (to_bits<F16>(v[1] * mul) << 16);
-                const uint32_t hi = to_bits<F16>(v[2] * mul) | (to_bits<F16>(v[3] * mul) << 16);
-                *reinterpret_cast<uint2*>(prow + 8 * t) = make_uint2(lo, hi);
+                d[t][0] = to_bits<F16>(v[0] * mul) | (to_bits<F16>(v[1] * mul) << 16);
+                d[t][1] = to_bits<F16>(v[2] * mul) | (to_bits<F16>(v[3] * mul) << 16);
             }
-            if (own && g == 0) {
+        }
+        regroup_slice(d);
+        if (!valid) continue;
+        *reinterpret_cast<u32x4*>(orow) = u32x4{d[0][0], d[0][1], d[1][0], d[1][1]};
+        *reinterpret_cast<u32x4*>(orow + 32) = u32x4{d[2][0], d[2][1], d[3][0], d[3][1]};
+        if (own && g == 0) {
+            if (direct) {
+                a.lse[b * a.lse_sb + static_cast<int64_t>(wk.s) * a.hq + h] = lse;
+            } else {
                 a.part_lse[prow_idx] = lse;
                 a.part_scale[prow_idx] = __builtin_amdgcn_ldexpf(1.0f, -k);
             }
