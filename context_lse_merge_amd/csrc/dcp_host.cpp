@@ -435,6 +435,9 @@ int plan_mla(const void* q, int64_t B, int hq, int64_t q_sb, int64_t q_sh, const
     plan->scratch_bytes = need;
     plan->blocks = vl ? vlay.items : static_cast<int64_t>(a.row_blocks) * cp * nsplit;
     plan->varlen = vl != nullptr;
+    // One row block: no other workgroup reads a key range, so every tile comes
+    // from HBM; the decode keeps two tiles in flight instead of one.
+    plan->deep = vl == nullptr && a.row_blocks == 1;
     if (plan->blocks >= (int64_t{1} << 31))
         return fail(DCP_ERR_INVALID_ARG, "%s: %lld workgroups exceed one launch (fewer tokens per call)", fn,
                     (long long)plan->blocks);

@@ -291,6 +291,7 @@ struct MlaPlan {
     size_t scratch_bytes;   // needed scratch (0 when nsplit == 1)
     int64_t blocks;         // workgroups of the main kernel (0: nothing to do)
     bool varlen;            // planning kernel, decode over the work list, split reduction
+    bool deep;              // the decode loop with two tiles in flight (one row block)
     MergeArgs reduce;       // nsplit > 1: the merge over splits (all B tokens; launched in token chunks)
     int64_t B;
     // dcp_mla_decode_merged without the fused epilogue: the shard merge of

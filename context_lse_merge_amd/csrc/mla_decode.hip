@@ -796,7 +796,7 @@ __device__ __forceinline__ void fused_epilogue(const int* work) {
                                            a.to_log2, addr, store);
 }
 
-template <typename T, bool Fused>
+template <typename T, bool Fused, bool Deep>
 __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t tiles[3][kTileAlloc];
     __shared__ TileExchange exs[3];
@@ -913,45 +913,81 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     float m_run = -INFINITY;  // running max of row r16, log2 units
     float l_run = 0.0f;       // lane-partial running sum of row r16
 
-    // Tile i lives in buffer i % 3 with exchange i % 3.  Its scores and
-    // softmax run one interval before its p.v: between barriers i and i + 1
-    // every wavefront runs p.v of tile i (which needs every wavefront's P^T
-    // of tile i, published before barrier i) and the scores of tile i + 1.
-    // A buffer is therefore busy for two intervals, and the copy of tile
-    // i + 2, issued after barrier i into the buffer tile i - 1 left, has one
-    // interval to land (barrier i + 1 waits for it).
-    if (ntiles > 1) copy_tile(1, tiles[1]);
-    __syncthreads();  // tile 0: every wavefront waited for its own copies above
-    if (ntiles > 0) qk_tile<T, true>(a, tiles[0], off, qf, m_run, l_run, k0, k1, g, wave, lane, exs[0]);
-    // A rolled loop: the buffer and exchange indices are wave-uniform, so
-    // the LDS addresses are formed per tile instead of being held in
-    // registers for every buffer (unrolled by three, the loop spills).  The
-    // last tile's p.v runs after the loop, so that inside it p.v and the
-    // next scores form one block of straight-line code.
-    // Tiles 1 .. ntiles - 2 are full; only the last one's scores need the
-    // key mask, so its interval runs after the loop.
-    int cur = 0;
-    for (int it = 0; it + 2 < ntiles; ++it) {
-        const int64_t t0 = k0 + static_cast<int64_t>(it) * kKeys;
-        const int nxt = cur == 2 ? 0 : cur + 1;
-        const int prv = cur == 0 ? 2 : cur - 1;
-        all_tiles_ready();
-        copy_tile(it + 2, tiles[prv]);
-        pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
-        qk_tile<T, false>(a, tiles[nxt], off, qf, m_run, l_run, t0 + kKeys, k1, g, wave, lane, exs[nxt]);
-        cur = nxt;
-    }
-    if (ntiles > 1) {
-        const int nxt = cur == 2 ? 0 : cur + 1;
-        all_tiles_ready();
-        pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
-        qk_tile<T, true>(a, tiles[nxt], off, qf, m_run, l_run, k0 + static_cast<int64_t>(ntiles - 1) * kKeys, k1, g,
-                         wave, lane, exs[nxt]);
-        cur = nxt;
-    }
-    if (ntiles > 0) {
-        all_tiles_ready();
-        pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
+    if constexpr (Deep) {
+        // Two tiles in flight: tile i lives in buffer i % 3 and runs its
+        // scores and its p.v in one interval, with a barrier between them (the
+        // p.v needs every wavefront's P^T); the copies of tiles i + 1 and
+        // i + 2 are in flight meanwhile, so each has two intervals to land.
+        // For workgroups whose key range no other workgroup reads (one row
+        // block), where every tile comes from HBM rather than the L2.
+        // Every tile copy is four (wavefronts 4-7) or five (0-3) loads, and
+        // nothing else in the loop touches vector memory, so vmcnt(4) leaves
+        // at most the newest copy's loads in flight: the older tile is in.
+        if (ntiles > 1) copy_tile(1, tiles[1]);
+        int cur = 0;
+        // Every tile but the last: its copy and the next one's were issued
+        // two intervals and one interval ago.
+        for (int it = 0; it + 1 < ntiles; ++it) {
+            if (it > 0) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): tile it is in, it + 1 may not be
+            __syncthreads();  // tile it visible; tile it - 1's buffer and the exchange are free
+            const int far = cur == 0 ? 2 : cur - 1;
+            if (it + 2 < ntiles) copy_tile(it + 2, tiles[far]);
+            qk_tile<T, false>(a, tiles[cur], off, qf, m_run, l_run, k0 + static_cast<int64_t>(it) * kKeys, k1, g,
+                              wave, lane, exs[0]);
+            __syncthreads();
+            pv_tile<T>(tiles[cur], off, acc, exs[0], wave, lane);
+            cur = cur == 2 ? 0 : cur + 1;
+        }
+        // The last tile, with the key mask.
+        if (ntiles > 0) {
+            if (ntiles > 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __syncthreads();
+            qk_tile<T, true>(a, tiles[cur], off, qf, m_run, l_run, k0 + static_cast<int64_t>(ntiles - 1) * kKeys, k1,
+                             g, wave, lane, exs[0]);
+            __syncthreads();
+            pv_tile<T>(tiles[cur], off, acc, exs[0], wave, lane);
+        }
+    } else {
+        // Tile i lives in buffer i % 3 with exchange i % 3.  Its scores and
+        // softmax run one interval before its p.v: between barriers i and i + 1
+        // every wavefront runs p.v of tile i (which needs every wavefront's P^T
+        // of tile i, published before barrier i) and the scores of tile i + 1.
+        // A buffer is therefore busy for two intervals, and the copy of tile
+        // i + 2, issued after barrier i into the buffer tile i - 1 left, has one
+        // interval to land (barrier i + 1 waits for it).
+        if (ntiles > 1) copy_tile(1, tiles[1]);
+        __syncthreads();  // tile 0: every wavefront waited for its own copies above
+        if (ntiles > 0) qk_tile<T, true>(a, tiles[0], off, qf, m_run, l_run, k0, k1, g, wave, lane, exs[0]);
+        // A rolled loop: the buffer and exchange indices are wave-uniform, so
+        // the LDS addresses are formed per tile instead of being held in
+        // registers for every buffer (unrolled by three, the loop spills).  The
+        // last tile's p.v runs after the loop, so that inside it p.v and the
+        // next scores form one block of straight-line code.
+        // Tiles 1 .. ntiles - 2 are full; only the last one's scores need the
+        // key mask, so its interval runs after the loop.
+        int cur = 0;
+        for (int it = 0; it + 2 < ntiles; ++it) {
+            const int64_t t0 = k0 + static_cast<int64_t>(it) * kKeys;
+            const int nxt = cur == 2 ? 0 : cur + 1;
+            const int prv = cur == 0 ? 2 : cur - 1;
+            all_tiles_ready();
+            copy_tile(it + 2, tiles[prv]);
+            pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
+            qk_tile<T, false>(a, tiles[nxt], off, qf, m_run, l_run, t0 + kKeys, k1, g, wave, lane, exs[nxt]);
+            cur = nxt;
+        }
+        if (ntiles > 1) {
+            const int nxt = cur == 2 ? 0 : cur + 1;
+            all_tiles_ready();
+            pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
+            qk_tile<T, true>(a, tiles[nxt], off, qf, m_run, l_run, k0 + static_cast<int64_t>(ntiles - 1) * kKeys, k1, g,
+                             wave, lane, exs[nxt]);
+            cur = nxt;
+        }
+        if (ntiles > 0) {
+            all_tiles_ready();
+            pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
+        }
     }
 
     const bool direct = a.seq_lens ? wk.slot < 0 : a.nsplit == 1;
@@ -978,13 +1014,18 @@ int run_mla(const MlaPlan& plan, void* hip_stream, const char* fn) {
     const bool f16 = plan.args.dtype == DCP_DTYPE_FP16;
     if (plan.args.fused) {
         if (f16)
-            mla_decode_kernel<F16, true><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
+            mla_decode_kernel<F16, true, false><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
         else
-            mla_decode_kernel<Bf16, true><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
+            mla_decode_kernel<Bf16, true, false><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
+    } else if (plan.deep) {
+        if (f16)
+            mla_decode_kernel<F16, false, true><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
+        else
+            mla_decode_kernel<Bf16, false, true><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
     } else if (f16) {
-        mla_decode_kernel<F16, false><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
+        mla_decode_kernel<F16, false, false><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
     } else {
-        mla_decode_kernel<Bf16, false><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
+        mla_decode_kernel<Bf16, false, false><<<grid, dim3(kThreads), 0, stream>>>(plan.args);
     }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && plan.varlen) {
