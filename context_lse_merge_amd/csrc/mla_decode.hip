@@ -427,7 +427,7 @@ __device__ __forceinline__ void qk_tile(const MlaArgs& a, const uint16_t* kt, co
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile, 1 for unchanged rows
         l_run *= alpha;
         m_run = m_new;
-        if (g == 0) ex.alpha[kRowsPerWave * wave + (lane & 15)] = alpha;
+        if (g == 0) ex.alpha[kRowsPerWave * wave + (opaque(lane) & 15)] = alpha;  // address formed here, not kept live
     }
     if (lane == 0) ex.moved[wave] = moved ? 1 : 0;
     float psum = 0.0f;
@@ -871,22 +871,36 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
     };
     if (ntiles > 0) copy_tile(0, tiles[0]);
 
-    // Query row (b, h) of this lane's softmax (row 16 wave + r16 of the
-    // workgroup); rows past the end repeat the last row and are not stored.
+    // Q fragments: fragment f holds columns 32f + 8g .. +7 of this lane's
+    // query row, row 16 wave + r16 of the workgroup (rows past the end repeat
+    // the last row and are not stored).  In that layout each 16-lane pass of a
+    // load instruction would read 16 rows, 16 B apiece: 16 cache lines.  The
+    // vector memory unit serves a 16-byte load at about one cache line per
+    // clock and pass (measured on L2-resident data: 18 B per clock and
+    // compute unit for 16 rows x 16 B per pass, 53 for 4 rows x 64 B, 127 for
+    // 256 contiguous bytes).  So lane 4R + c loads columns 32f + 8c .. of row
+    // R (each pass: 4 rows x 64 B), and a lane permutation (ds_bpermute, no
+    // LDS storage) hands lane 16g + r16 the words of lane 4 r16 + g.
     const RowPlace rp{wk.rb, b_tok, h_base, a.seq_lens != nullptr};
-    int b, h;
-    bool valid;
-    place_row(a, rp, kRowsPerWave * wave + r16, b, h, valid);
-
-    // Q fragments: fragment f holds columns 32f + 8g .. +7 of this lane's row.
     typename T::v8 qf[kQSteps];
     {
-        const uint16_t* qrow = a.q + b * a.q_sb + h * a.q_sh + 8 * g;
+        int bq, hq;
+        bool vq;
+        place_row(a, rp, kRowsPerWave * wave + (lane >> 2), bq, hq, vq);
+        const uint16_t* qsrc = a.q + bq * a.q_sb + hq * a.q_sh + 8 * (lane & 3);
 #pragma unroll
-        for (int f = 0; f < kQSteps; ++f) qf[f] = as_v8<T>(*reinterpret_cast<const u32x4*>(qrow + 32 * f));
+        for (int f = 0; f < kQSteps; ++f) qf[f] = as_v8<T>(*reinterpret_cast<const u32x4*>(qsrc + 32 * f));
         // Settle these loads (and tile 0's copies) here: a wait for them left
         // inside the key loop would also wait for the tile copies in flight there.
         __builtin_amdgcn_s_waitcnt(0x0F70);
+        const int src = 4 * (4 * r16 + g);  // byte address of the source lane
+#pragma unroll
+        for (int f = 0; f < kQSteps; ++f) {
+            u32x4 w = __builtin_bit_cast(u32x4, qf[f]);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) w[d] = __builtin_amdgcn_ds_bpermute(src, w[d]);
+            qf[f] = as_v8<T>(w);
+        }
     }
 
     // Operand offsets.  q.k step f: key r16, chunk 4f + g, in block f at slot
