@@ -309,12 +309,14 @@ __device__ __forceinline__ uint32_t full_tile_lane_offset(int32_t rstride, int w
 
 // dma_tile for a tile whose 32 keys are all valid: block n = 18 h + b of the
 // tile reads rows 16 h .. of it from 32 b elements on, a scalar offset; the
-// lane's part is full_tile_lane_offset.  The same bytes as dma_tile.
+// lane's part is full_tile_lane_offset.  The same bytes as dma_tile.  Copies
+// I0 .. I1 - 1 of the wavefront's (all of them by default).
+template <int I0 = 0, int I1 = kDmaPerWave>
 __device__ __forceinline__ void dma_tile_full(const KeyRows& kr, uint16_t* dst, int64_t t0, uint32_t lane_off,
                                               int wave) {
     const uint16_t* base = kr.rows0 + t0 * kr.rstride;
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) {
+    for (int i = I0; i < I1; ++i) {
         const int n = wave + kWaves * i;
         if (i + 1 < kDmaPerWave || n < kDmaPerTile) {  // only the last copy can fall past block 35
             const int h = n >= kHalfBlocks ? 1 : 0;
@@ -985,8 +987,20 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
             const int nxt = cur == 2 ? 0 : cur + 1;
             const int prv = cur == 0 ? 2 : cur - 1;
             all_tiles_ready();
-            copy_tile(it + 2, tiles[prv]);
+            // Each copy holds the vector memory unit for about 64 clocks (16
+            // keys x 64 B: 16 cache lines per 16-lane pass), ~2300 per tile
+            // and workgroup; a wavefront issuing all of its copies at once
+            // waits at the issue behind the other wavefronts' copies.  Three
+            // go out before p.v and the rest after it (measured: 1-1.5%
+            // faster than all five before, 3.5% faster than all after).
+            const bool split_copy = full_ok && it + 3 < ntiles;  // tile it + 2 is full
+            const int64_t tc = k0 + static_cast<int64_t>(it + 2) * kKeys;
+            if (split_copy)
+                dma_tile_full<0, 3>(kr, tiles[prv], tc, lane_off, wave);
+            else
+                copy_tile(it + 2, tiles[prv]);
             pv_tile<T>(tiles[cur], off, acc, exs[cur], wave, lane);
+            if (split_copy) dma_tile_full<3>(kr, tiles[prv], tc, lane_off, wave);
             qk_tile<T, false>(a, tiles[nxt], off, qf, m_run, l_run, t0 + kKeys, k1, g, wave, lane, exs[nxt]);
             cur = nxt;
         }
