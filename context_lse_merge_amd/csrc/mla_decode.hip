@@ -32,7 +32,15 @@
 //    offset fixed for the whole kernel, so the copies cost no vector
 //    instructions.  The scores of a tile are computed one interval before
 //    its p.v, so a buffer is busy for two intervals and each copy is issued
-//    one tile ahead.
+//    one tile ahead, in two parts around the p.v (a copy holds the vector
+//    memory unit for about 64 clocks, one per cache line and 16-lane pass).
+//    With a single row block, where no other workgroup shares a key range in
+//    the L2, scores and p.v of a tile share an interval (two barriers) and
+//    two tiles are in flight instead.
+//  * Q is loaded as 4 rows x 64 B per 16-lane pass and moved into the MFMA
+//    operand layout with ds_bpermute; the epilogue regroups each row's pieces
+//    over its four lane groups (permlane swaps) so that every lane stores
+//    16-byte words.
 //  * LDS layout of a tile: 36 blocks of 1 KiB, block (h, b) holding the 16-byte
 //    chunks 4b..4b+3 of keys 16h..16h+15, chunk c of key k at slot
 //    16 (c % 4) + ((k % 16) ^ 8 (b % 2)).  Measured on gfx950, a 16-byte LDS
