@@ -947,6 +947,7 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(MlaArgs a) {
         // Every tile copy is four (wavefronts 4-7) or five (0-3) loads, and
         // nothing else in the loop touches vector memory, so vmcnt(4) leaves
         // at most the newest copy's loads in flight: the older tile is in.
+        static_assert(kDmaPerTile / kWaves >= 4, "vmcnt(4) needs at least four copies per wavefront and tile");
         if (ntiles > 1) copy_tile(1, tiles[1]);
         int cur = 0;
         // Every tile but the last: its copy and the next one's were issued
