@@ -140,20 +140,24 @@ def test_fp16_varlen():
     check(q, kv, seq, dcp.DCP_KV_INTERLEAVED, 4, dcp.DCP_LSE_BASE_E, o, l)
 
 
-def test_shared_cache_full_length_matches_fixed_length_bitwise():
+@pytest.mark.parametrize("B,T", [(2, 4096), (1, 4096), (1, 4000)])
+def test_shared_cache_full_length_matches_fixed_length_bitwise(B, T):
     """Every token sharing one cache at its full length, contiguous ownership.
-    At this shape the planning kernel picks the fixed-length path's split
-    length (256 keys: 4 splits per shard), so every split runs the same tiles
-    in the same order, and the split reduction forms the weights exactly as
-    the merge kernel does: the same bits."""
-    q, kv = synth.mla_decode(2, T=4096, hq=128, seed=705)
+    At these shapes the planning kernel picks the fixed-length path's split
+    length (256 keys: 4 splits per shard; T = 4000 ends each shard on a
+    partial tile), so every split runs the same tiles in the same order, and
+    the split reduction forms the weights exactly as the merge kernel does:
+    the same bits.  With B = 1 (a single row block) the fixed-length decode
+    runs its two-tiles-in-flight loop and the variable-length one its
+    one-tile-ahead loop, so the two loops are checked against each other."""
+    q, kv = synth.mla_decode(B, T=T, hq=128, seed=705)
     kv_dev = kv.to(DEV)
-    o_v, l_v = run_varlen(q, kv, [4096, 4096], 4096, dcp.DCP_KV_CONTIGUOUS, 4, dcp.DCP_LSE_BASE_E, kv_dev=kv_dev)
+    o_v, l_v = run_varlen(q, kv, [T] * B, T, dcp.DCP_KV_CONTIGUOUS, 4, dcp.DCP_LSE_BASE_E, kv_dev=kv_dev)
     o_f = torch.empty_like(o_v)
     l_f = torch.empty_like(l_v)
-    nbytes = dcp.dcp_mla_partial_decode_scratch_size(2, 128, 4096, 4)
+    nbytes = dcp.dcp_mla_partial_decode_scratch_size(B, 128, T, 4)
     scratch = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV) if nbytes else None
-    announce("fixed-length producer on the same shared cache")
+    announce("fixed-length producer on the same shared cache (B=%d T=%d)" % (B, T))
     dcp.dcp_mla_partial_decode(q.to(DEV), kv_dev, 4, synth.MLA_SCALE, dcp.DCP_LSE_BASE_E, o_f, l_f, scratch)
     torch.cuda.synchronize()
     assert torch.equal(o_v.view(torch.int16), o_f.view(torch.int16))
