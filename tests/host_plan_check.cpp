@@ -101,9 +101,21 @@ static void fixed_split_checks() {
     CHECK(plan.reduce.in_dtype == dcp::kPayloadF16Scaled && plan.reduce.sc_off == B * heads);
     CHECK(plan.reduce.attn == plan.args.part_o && plan.reduce.lse == plan.args.part_lse);
     CHECK(plan.reduce.cp == nsplit && plan.reduce.h_local == cp * hq && plan.reduce.a_sb == heads * dcp::kMlaVDim);
+    CHECK(!plan.deep);  // three row blocks share each key range: the one-tile-ahead loop
     CHECK(dcp::plan_mla(fake(q), B, hq, hq * 576, 576, fake(kv), T, 576, nullptr, DCP_DTYPE_BF16, cp, 0.07f,
                         DCP_LSE_BASE_E, fake(o), cp * hq * 512, 512, reinterpret_cast<float*>(l), cp * hq, fake(scr),
                         need - 1, &plan) == DCP_ERR_WORKSPACE);
+    // One row block (B * hq <= 128): two tiles in flight; two row blocks: one tile ahead.
+    const struct { int64_t B; int hq; bool deep; } rb[] = {{1, 128, true}, {3, 40, true}, {1, 1, true},
+                                                           {2, 128, false}, {1, 160, false}, {129, 1, false}};
+    for (const auto& c : rb) {
+        size_t n;
+        dcp::mla_split(c.B, c.hq, T, cp, &nsplit, &split_len, &n);
+        CHECK(dcp::plan_mla(fake(q), c.B, c.hq, c.hq * 576, 576, fake(kv), T, 576, nullptr, DCP_DTYPE_BF16, cp, 0.07f,
+                            DCP_LSE_BASE_E, fake(o), cp * c.hq * 512, 512, reinterpret_cast<float*>(l), cp * c.hq,
+                            fake(scr), n, &plan) == DCP_OK);
+        CHECK(plan.deep == c.deep);
+    }
 }
 
 // dcp_mla_decode_merged: the counters first, the split partials after them;
@@ -240,6 +252,7 @@ static void varlen_plan_checks() {
                         DCP_LSE_BASE_E, fake(o), 512 * 512, 512, reinterpret_cast<float*>(l), 512, fake(scr),
                         lay.bytes, &plan) == DCP_OK);
     CHECK(plan.varlen && plan.blocks == lay.items && plan.args.slots == lay.slots);
+    CHECK(!plan.deep);  // the variable-length decode always runs the one-tile-ahead loop
     CHECK(reinterpret_cast<uintptr_t>(plan.args.part_lse) == scr + lay.off_lse);
     CHECK(reinterpret_cast<uintptr_t>(plan.args.part_scale) == scr + lay.off_scale);
     CHECK(reinterpret_cast<uintptr_t>(plan.args.vl_hdr) == scr + lay.off_hdr);
